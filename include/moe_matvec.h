@@ -1,0 +1,236 @@
+/*
+ * moe_matvec.h -- C ABI of the decode matrix-vector library for AMD Instinct
+ * MI355X (CDNA4, gfx950).
+ *
+ * The library computes the products that dominate single-token (and up to
+ * 8-row) LLM decode, y = W x, streaming every weight byte once per call:
+ * dense BF16 GEMV, Q4_0 x Q8_1 GEMV with on-the-fly activation quantization,
+ * and the mixture-of-experts path (F32 router, softmax, top-k, gathered
+ * per-expert gate/up/down products, shared expert).
+ *
+ * Sources (web pages, cited by title and section):
+ *  [STRATA]   "Beating llama.cpp from Scratch on Consumer AMD: Building
+ *             Strata" -- The Optimization Passes, Pass 3 (HIP graph replay;
+ *             custom vectorized BF16 GEMV for M = 1); The Kernel Execution
+ *             Profile (GEMV share of decode; the memory-bandwidth wall).
+ *  [FOURTEEN] "Fourteen hours to 100 tokens per second" -- kernel-class table
+ *             in "The trace that changed everything"; "Eight levers that
+ *             worked"; "The router with 257 rows"; "Four levers that did not
+ *             work"; "Two bugs nobody was looking for".
+ *  [STRIX]    "Flash-Next on Strix Halo" -- Expert GEMMs (per-expert row
+ *             lists); Correctness fixes (split-nibble Q4_0 loaders).
+ *
+ * Conventions for every entry point
+ *  - Matrices are N x K (out x in), row-major: y[b][n] = sum_k W[n][k] x[b][k].
+ *  - B is the number of activation rows (tokens), 1 <= B <= MMV_MAX_BATCH.
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  `stream`
+ *    is a hipStream_t passed as void* (NULL = the default stream).
+ *  - Calls only enqueue work on `stream`: they never allocate, free,
+ *    synchronize or read device memory on the host, so they can be captured
+ *    in a HIP graph.  Outputs are fully overwritten, never accumulated.
+ *  - Every argument check runs on the host before any launch; a negative
+ *    return means nothing was enqueued.  MMV_E_HIP reports a failed launch
+ *    (see mmv_last_hip_error).  Faults inside a kernel surface at the
+ *    caller's next synchronization.
+ *  - Results are deterministic: no floating-point atomics; repeated calls
+ *    on the same inputs give bit-identical outputs, and each row of a
+ *    B-row call equals the 1-row call on that row, bit for bit.
+ *  - Outputs must not overlap inputs (MMV_E_ALIAS).
+ *
+ * Data formats
+ *  - BF16 weights: uint16 bit patterns of bfloat16.
+ *  - Q4_0 matrix (planar): blocks of 32 consecutive weights of one row.
+ *      qs : uint8  [N][K/32][16]  block byte i = code[i] | code[i+16] << 4
+ *                                  (split-nibble), codes 0..15
+ *      d  : fp16   [N][K/32]      block scale
+ *    weight = d * (code - 8).  The 16 code bytes of a block are one aligned
+ *    128-bit word; the scales sit in their own plane.
+ *  - Q8_1 activations (planar), B rows of K, K % 32 == 0, one buffer of
+ *    mmv_q8_1_bytes(K, B) bytes:
+ *      bytes [0, B*K)                 int8 codes, row-major [B][K]
+ *      bytes [B*K, B*K + 4*B*K/32)    fp16 pairs {d, s} per block [B][K/32]
+ *    Per block of 32 values x_i:  amax = max|x_i|, d32 = amax / 127 (fp32);
+ *    if fp16(d32) == 0 the block is all zero (d = s = 0, codes 0); else
+ *    q_i = clamp(roundf(x_i * (1/d32)), -127, 127) with roundf rounding
+ *    halves away from zero, d = fp16(d32), s = fp16(d32 * sum_i q_i).
+ *    Inputs must be finite.
+ */
+#ifndef MOE_MATVEC_H
+#define MOE_MATVEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MMV_MAX_BATCH   8     /* rows per call                              */
+#define MMV_MAX_EXPERTS 1024  /* router rows E                              */
+#define MMV_MAX_TOPK    16    /* experts per row k                          */
+#define MMV_Q4_MAX_XK   49152 /* B*K limit of gemv_q4_0 (x staged in LDS)   */
+
+typedef enum {
+  MMV_OK = 0,
+  MMV_E_NULL = -1,      /* a required pointer is NULL                       */
+  MMV_E_SHAPE = -2,     /* a size is out of range or not a block multiple   */
+  MMV_E_ALIGN = -3,     /* a pointer or leading dimension is misaligned     */
+  MMV_E_BATCH = -4,     /* B outside 1..MMV_MAX_BATCH                        */
+  MMV_E_TOPK = -5,      /* k outside 1..min(E, MMV_MAX_TOPK)                 */
+  MMV_E_WORKSPACE = -6, /* workspace NULL or smaller than required          */
+  MMV_E_ALIAS = -7,     /* an output overlaps an input                      */
+  MMV_E_HIP = -8,       /* the HIP runtime rejected a launch                */
+  MMV_E_ARG = -9        /* inconsistent arguments (e.g. both X and Xq)      */
+} mmv_status;
+
+/* Human-readable text for a status code (static storage). */
+const char *mmv_status_str(int status);
+/* hipError_t of the last MMV_E_HIP on the calling thread (0 if none). */
+int mmv_last_hip_error(void);
+
+/* Q4_0 matrix descriptor (planar layout above).  qs 16-byte aligned,
+ * d 2-byte aligned, K % 32 == 0. */
+typedef struct {
+  const uint8_t *qs;
+  const uint16_t *d;
+  int32_t N;
+  int32_t K;
+} mmv_q4_0;
+
+/* Size in bytes of a planar Q8_1 buffer for B rows of K. */
+size_t mmv_q8_1_bytes(int32_t K, int32_t B);
+
+/* --------------------------------------------------------------------------
+ * gemv_bf16 -- dense BF16 GEMV.  [STRATA: Pass 3 item 2]
+ *   Y[b*ldy + n] = sum_k bf16(W[n*ldw + k]) * X[b*ldx + k]   (fp32 accumulate)
+ *   W: N x K bf16, rows 16-byte aligned (W 16-byte aligned, ldw % 8 == 0,
+ *      ldw >= K); K % 8 == 0.  Gate and up projections stored as one
+ *      [2I x H] matrix are one call.
+ *   X: B x K fp32, 16-byte aligned, ldx % 4 == 0, ldx >= K.
+ *   Y: B x N fp32, ldy >= N.
+ * ------------------------------------------------------------------------ */
+int gemv_bf16(const uint16_t *W, int32_t N, int32_t K, int64_t ldw,
+              const float *X, int64_t ldx, int32_t B,
+              float *Y, int64_t ldy, void *stream);
+
+/* --------------------------------------------------------------------------
+ * quantize_q8_1 -- fp32 activations to planar Q8_1.
+ *   [FOURTEEN: kernel-class table, "Activation quantization (quantize_q8_1)"]
+ *   X: B x K fp32 (K % 32 == 0, 16-byte aligned, ldx % 4 == 0).
+ *   Xq: mmv_q8_1_bytes(K, B) bytes, 16-byte aligned.
+ *   The same device routine quantizes inside gemv_q4_0 and moe_mul_mat_id,
+ *   so their codes are identical to this call's.
+ * ------------------------------------------------------------------------ */
+int quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B,
+                  void *Xq, void *stream);
+
+/* --------------------------------------------------------------------------
+ * gemv_q4_0 -- Q4_0 weights x Q8_1 activations.
+ *   [FOURTEEN: "Dense matvecs (warp_coop Q4_0)"; four rows per wave for
+ *    K <= 512 in "Eight levers that worked"]
+ *   Y[b*ldy + n] = sum_j d_w[n][j] * d_x[b][j] * I[b][n][j],
+ *   I[b][n][j] = sum_i (code_i - 8) * q_x[b][32j + i]  (exact int32).
+ *   Exactly one of X (fp32 B x K, quantized on the fly, bit-identical to
+ *   quantize_q8_1) and Xq (planar Q8_1 of B rows of K) must be non-NULL.
+ *   B*K <= MMV_Q4_MAX_XK.  Y: B x N fp32, ldy >= N.
+ * ------------------------------------------------------------------------ */
+int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,
+              int32_t B, float *Y, int64_t ldy, void *stream);
+
+/* --------------------------------------------------------------------------
+ * moe_route_topk -- F32 router, softmax, top-k, renormalised gate weights.
+ *   [FOURTEEN: "F32 router (mul_mat_vec_f)", "Top-k routing"; the F16
+ *    router was rejected because ties broke differently; "The router with
+ *    257 rows": top-k writes ids and weights straight into the buffers the
+ *    expert products read]
+ *   router: E x H fp32 (16-byte aligned, H % 4 == 0), or NULL: then X holds
+ *           B rows of E logits (ldx >= E) and the matvec is skipped.
+ *   logits: B x (E+1) fp32 output: logits[b*(E+1) + e]; column E holds the
+ *           shared-gate logit when shared_gate_row != NULL.
+ *   ids:    B x k int32: the k largest logits of row b, in descending
+ *           order; equal logits rank by lower expert index.
+ *   weights:B x k fp32: softmax over all E renormalised over the selected
+ *           k, i.e. exp(l_j - l_max) / sum over selected.
+ *   shared_w: B fp32 (may be NULL): sigmoid(shared_gate_row . x_b), or 1
+ *           when shared_gate_row is NULL.
+ *   1 <= k <= min(E, MMV_MAX_TOPK), E <= MMV_MAX_EXPERTS.
+ * ------------------------------------------------------------------------ */
+int moe_route_topk(const float *router, int32_t E, int32_t H,
+                   const float *X, int64_t ldx, int32_t B, int32_t k,
+                   const float *shared_gate_row, float *logits,
+                   int32_t *ids, float *weights, float *shared_w,
+                   void *stream);
+
+/* One MoE layer's weights.  Routed experts are stacked expert-major and
+ * contiguous: expert e's gate block (i, j) is at
+ * gate_qs + ((e*I + i)*(H/32) + j)*16 and gate_d[(e*I + i)*(H/32) + j];
+ * up likewise; down is H x I per expert.  The shared expert has one
+ * matrix of each (sh_*_qs == NULL: no shared expert).  H % 32 == 0,
+ * I % 32 == 0. */
+typedef struct {
+  int32_t n_experts;              /* E */
+  int32_t hidden;                 /* H */
+  int32_t inter;                  /* I */
+  int32_t top_k;                  /* k */
+  const float *router;            /* E x H fp32                              */
+  const float *shared_gate_row;   /* H fp32, NULL: shared weight 1           */
+  const uint8_t *gate_qs, *up_qs, *down_qs;
+  const uint16_t *gate_d, *up_d, *down_d;
+  const uint8_t *sh_gate_qs, *sh_up_qs, *sh_down_qs;
+  const uint16_t *sh_gate_d, *sh_up_d, *sh_down_d;
+} mmv_moe_layer;
+
+/* Optional staged outputs of moe_mul_mat_id, for tests (each may be NULL). */
+typedef struct {
+  float *h;            /* P x I fp32: silu(gate) * up for each pair          */
+  int32_t *unique;     /* [B*k]: sorted unique routed experts               */
+  int32_t *offsets;    /* [B*k + 1]: pair ranges per unique expert          */
+  int32_t *pairs;      /* [B*k]: b*k + j grouped by expert, then b, then j  */
+  int32_t *n_unique;   /* [1]                                               */
+} mmv_moe_debug;
+
+/* Workspace bytes for moe_mul_mat_id / moe_layer_decode at B rows.
+ * Layout: bytes [0, mmv_q8_1_bytes(I, P)) hold Q8_1(h) for the P pairs
+ * (P = B*k routed pairs p = b*k + j, then B shared pairs p = B*k + b),
+ * followed by the routing buffers moe_layer_decode uses.  256-byte
+ * aligned workspace required. */
+size_t moe_workspace_bytes(const mmv_moe_layer *L, int32_t B);
+
+/* --------------------------------------------------------------------------
+ * moe_mul_mat_id -- routed + shared expert FFN for B rows.
+ *   [FOURTEEN: "Expert matvecs (mul_mat_id)"; "Q8 epilogue in the gated
+ *    kernel"; "Four rows per wave (K <= 512)" for the down projection;
+ *    STRIX: per-expert row lists]
+ *   For each pair (b, j) with expert e = ids[b*k + j] (and the shared
+ *   expert for every row):  g = Gate_e (x) Q8_1(x_b),  u = Up_e (x) Q8_1(x_b)
+ *   (Q4_0 x Q8_1 products), h = silu(g) * u in fp32, then Q8_1(h) along I,
+ *   and
+ *     Y[b*ldy + n] = sum_j weights[b*k+j] * (Down_e (x) Q8_1(h))[n]
+ *                    + shared_w[b] * (Down_sh (x) Q8_1(h_sh))[n].
+ *   Each unique expert's weights are read once for all rows that chose it.
+ *   ids: B x k int32 in [0, E), distinct within a row; weights: B x k fp32;
+ *   shared_w: B fp32 or NULL (weight 1).  X: B x H fp32, ldx % 4 == 0.
+ *   Y: B x H fp32.  workspace: moe_workspace_bytes(L, B) bytes.
+ * ------------------------------------------------------------------------ */
+int moe_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx,
+                   int32_t B, const int32_t *ids, const float *weights,
+                   const float *shared_w, float *Y, int64_t ldy,
+                   void *workspace, size_t ws_bytes,
+                   const mmv_moe_debug *dbg, void *stream);
+
+/* --------------------------------------------------------------------------
+ * moe_layer_decode -- the whole MoE layer in the fewest launches:
+ *   moe_route_topk followed by moe_mul_mat_id, with routing kept in the
+ *   workspace.  ids / weights (B x k) may be NULL; when given they receive
+ *   the routing decision.  [STRATA: Pass 3 item 1, graph replay;
+ *   FOURTEEN: launches below five microseconds cost more than they run]
+ * ------------------------------------------------------------------------ */
+int moe_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx,
+                     int32_t B, float *Y, int64_t ldy,
+                     int32_t *ids, float *weights,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MATVEC_H */

@@ -1,0 +1,116 @@
+// api.hip -- the extern "C" entry points of moe_matvec.h: validate on the
+// host (validate.cpp, no device access), then enqueue on the caller's
+// stream.  No allocation, no synchronization, no host reads of device data.
+#include "../../include/moe_matvec.h"
+#include "launch.hpp"
+#include "layout.hpp"
+#include "validate.hpp"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MMV_OK;
+  g_last_hip = (int)e;
+  return MMV_E_HIP;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *mmv_status_str(int status) {
+  switch (status) {
+    case MMV_OK: return "ok";
+    case MMV_E_NULL: return "a required pointer is NULL";
+    case MMV_E_SHAPE: return "a size is out of range or not a multiple of the block size";
+    case MMV_E_ALIGN: return "a pointer or leading dimension is misaligned";
+    case MMV_E_BATCH: return "batch rows outside 1..8";
+    case MMV_E_TOPK: return "top_k outside 1..min(E, 16)";
+    case MMV_E_WORKSPACE: return "workspace missing or too small";
+    case MMV_E_ALIAS: return "an output overlaps an input";
+    case MMV_E_HIP: return "HIP launch failed";
+    case MMV_E_ARG: return "inconsistent arguments";
+  }
+  return "unknown status";
+}
+
+int mmv_last_hip_error(void) { return g_last_hip; }
+
+size_t mmv_q8_1_bytes(int32_t K, int32_t B) {
+  if (K < 32 || K % 32 != 0 || B < 1) return 0;
+  return mmv::q8_1_bytes(K, B);
+}
+
+int gemv_bf16(const uint16_t *W, int32_t N, int32_t K, int64_t ldw, const float *X,
+              int64_t ldx, int32_t B, float *Y, int64_t ldy, void *stream) {
+  const int st = mmv::check_gemv_bf16(W, N, K, ldw, X, ldx, B, Y, ldy);
+  if (st != MMV_OK) return st;
+  return hip_status(mmv::run_gemv_bf16(W, N, K, ldw, X, ldx, B, Y, ldy, as_stream(stream)));
+}
+
+int quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B, void *Xq, void *stream) {
+  const int st = mmv::check_quantize_q8_1(X, K, ldx, B, Xq);
+  if (st != MMV_OK) return st;
+  return hip_status(mmv::run_quantize_q8_1(X, K, ldx, B, static_cast<uint8_t *>(Xq),
+                                           as_stream(stream)));
+}
+
+int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq, int32_t B,
+              float *Y, int64_t ldy, void *stream) {
+  const int st = mmv::check_gemv_q4_0(W, X, ldx, Xq, B, Y, ldy);
+  if (st != MMV_OK) return st;
+  return hip_status(mmv::run_gemv_q4_0(W->qs, W->d, W->N, W->K, X, ldx,
+                                       static_cast<const uint8_t *>(Xq), B, Y, ldy,
+                                       as_stream(stream)));
+}
+
+int moe_route_topk(const float *router, int32_t E, int32_t H, const float *X, int64_t ldx,
+                   int32_t B, int32_t k, const float *shared_gate_row, float *logits,
+                   int32_t *ids, float *weights, float *shared_w, void *stream) {
+  const int st = mmv::check_route(router, E, H, X, ldx, B, k, shared_gate_row, logits, ids,
+                                  weights, shared_w);
+  if (st != MMV_OK) return st;
+  return hip_status(mmv::run_moe_route(router, E, H, X, ldx, B, k, shared_gate_row, logits,
+                                       ids, weights, shared_w, as_stream(stream)));
+}
+
+size_t moe_workspace_bytes(const mmv_moe_layer *L, int32_t B) { return mmv::moe_ws_bytes(L, B); }
+
+int moe_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_t B,
+                   const int32_t *ids, const float *weights, const float *shared_w, float *Y,
+                   int64_t ldy, void *workspace, size_t ws_bytes, const mmv_moe_debug *dbg,
+                   void *stream) {
+  const int st = mmv::check_mul_mat_id(L, X, ldx, B, ids, weights, shared_w, Y, ldy,
+                                       workspace, ws_bytes);
+  if (st != MMV_OK) return st;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  return hip_status(mmv::run_moe_experts(*L, X, ldx, B, ids, weights, shared_w, Y, ldy, ws,
+                                         dbg, as_stream(stream)));
+}
+
+int moe_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_t B, float *Y,
+                     int64_t ldy, int32_t *ids, float *weights, void *workspace,
+                     size_t ws_bytes, void *stream) {
+  const int st =
+      mmv::check_layer_decode(L, X, ldx, B, Y, ldy, ids, weights, workspace, ws_bytes);
+  if (st != MMV_OK) return st;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const mmv::MoeWsLayout lay =
+      mmv::moe_ws_layout(L->n_experts, L->inter, L->top_k, B, L->sh_gate_qs != nullptr);
+  float *logits = reinterpret_cast<float *>(ws + lay.logits);
+  int32_t *id = ids ? ids : reinterpret_cast<int32_t *>(ws + lay.ids);
+  float *w = weights ? weights : reinterpret_cast<float *>(ws + lay.weights);
+  float *sw = reinterpret_cast<float *>(ws + lay.shared_w);
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = mmv::run_moe_route(L->router, L->n_experts, L->hidden, X, ldx, B, L->top_k,
+                                    L->shared_gate_row, logits, id, w, sw, s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(
+      mmv::run_moe_experts(*L, X, ldx, B, id, w, sw, Y, ldy, ws + lay.hq, nullptr, s));
+}
+
+}  // extern "C"

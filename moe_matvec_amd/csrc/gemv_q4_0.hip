@@ -1,0 +1,180 @@
+// gemv_q4_0.hip -- Q4_0 weights x Q8_1 activations, and the standalone
+// activation quantizer.
+//
+// "Fourteen hours to 100 tokens per second" (The trace that changed
+// everything) lists the dense Q4_0 matvecs and quantize_q8_1 as separate
+// kernel classes; "Eight levers that worked" gives the down projection
+// (K <= 512) four rows per wave with 16 lanes per row.  On gfx950:
+//  - a row is owned by a lane group of G lanes (G = 16 for K <= 512, up to 64
+//    for long rows); lane s of the group reads Q4_0 blocks s, s+G, ... of the
+//    row: one 128-bit code load + one fp16 scale per block, coalesced across
+//    the group (G*16 contiguous bytes per row per instruction);
+//  - the workgroup first issues its first weight loads, then stages x as
+//    Q8_1 in LDS (quantizing fp32 x with the shared routine, or copying a
+//    Q8_1 buffer) while those loads are in flight;
+//  - per block: nibble unpack with two masks, 8 v_dot4 on int8, exact int32
+//    sum, then one fp32 scale and fma per activation row;
+//  - each x block read from LDS is reused for the RP rows a lane owns;
+//  - group partials are combined by a fixed xor butterfly; the per-row
+//    arithmetic is the same for every B, so rows of a batched call match
+//    single-row calls bit for bit.
+#include "common.hpp"
+#include "launch.hpp"
+#include "q4_0.hpp"
+#include "q8_1.hpp"
+
+namespace mmv {
+
+// ---- standalone quantize_q8_1 ------------------------------------------
+// 8 lanes per block; a workgroup of 256 threads quantizes 32 blocks.
+__global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__ X, int K,
+                                                       int64_t ldx, int B, uint8_t *__restrict__ Xq) {
+  const int nb = K >> 5;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * nb * 8;
+  // keep whole 8-lane groups active: total is a multiple of 8
+  if (t >= total) return;
+  const int b = (int)(t / (nb * 8));
+  const int rem = (int)(t - (int64_t)b * nb * 8);
+  const int j = rem >> 3, s = rem & 7;
+  const f32x4 v = load_f4(X + (int64_t)b * ldx + 32 * j + 4 * s);
+  const Q8Block q = q8_1_quantize8(v);
+  *reinterpret_cast<uint32_t *>(Xq + (size_t)b * K + 32 * j + 4 * s) = q.codes;
+  if (s == 0) {
+    uint16_t *ds = reinterpret_cast<uint16_t *>(Xq + (size_t)B * K);
+    ds[((size_t)b * nb + j) * 2 + 0] = q.d16;
+    ds[((size_t)b * nb + j) * 2 + 1] = q.s16;
+  }
+}
+
+hipError_t run_quantize_q8_1(const float *X, int K, int64_t ldx, int B, uint8_t *Xq,
+                             hipStream_t s) {
+  const int64_t total = (int64_t)B * (K / 32) * 8;
+  const int blocks = (int)((total + 255) / 256);
+  hipLaunchKernelGGL(k_quantize_q8_1, dim3(blocks), dim3(256), 0, s, X, K, ldx, B, Xq);
+  return hipGetLastError();
+}
+
+// ---- Q4_0 GEMV -----------------------------------------------------------
+// B activation rows; G lanes per weight row; RP rows per lane group.
+// A wave covers RP * (64/G) rows, a 256-thread workgroup 4x that.
+template <int B, int G, int RP>
+__global__ __launch_bounds__(256) void k_gemv_q4_0(
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
+    const float *__restrict__ X, int64_t ldx, const uint8_t *__restrict__ Xq,
+    float *__restrict__ Y, int64_t ldy) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int RPP = 64 / G;
+  constexpr int ROWS_WAVE = RP * RPP;
+  const int nb = K >> 5;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G, grp = lane / G;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rbase = wave * ROWS_WAVE + grp;  // row of pass p: rbase + p * RPP
+
+  int rowc[RP];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) rowc[p] = min(rbase + p * RPP, N - 1);
+
+  // first weight blocks in flight before the activation prologue
+  u32x4 w0[RP];
+  float d0[RP];
+  const bool have0 = sub < nb;
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int64_t blk = (int64_t)rowc[p] * nb + (have0 ? sub : 0);
+    w0[p] = load_stream16(qs + blk * 16);
+    d0[p] = f16_bits_to_f32(load_stream2(dw + blk));
+  }
+
+  const XStage st = xstage_at(smem, B, K);
+  if (X) stage_quantize(X, ldx, nullptr, B, K, st);
+  else stage_copy_q8(Xq, B, B, K, st);
+  __syncthreads();
+
+  float acc[RP][B];
+#pragma unroll
+  for (int p = 0; p < RP; ++p)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[p][b] = 0.0f;
+
+  for (int j = sub; j < nb; j += G) {
+    u32x4 w[RP];
+    float dwf[RP];
+    if (j == sub) {
+#pragma unroll
+      for (int p = 0; p < RP; ++p) { w[p] = w0[p]; dwf[p] = d0[p]; }
+    } else {
+#pragma unroll
+      for (int p = 0; p < RP; ++p) {
+        const int64_t blk = (int64_t)rowc[p] * nb + j;
+        w[p] = load_stream16(qs + blk * 16);
+        dwf[p] = f16_bits_to_f32(load_stream2(dw + blk));
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int8_t *xc = st.codes + (size_t)b * K + 32 * j;
+      const i32x4 xa = *reinterpret_cast<const i32x4 *>(xc);
+      const i32x4 xb = *reinterpret_cast<const i32x4 *>(xc + 16);
+      const int xs = st.qsum[b * nb + j];
+      const float dx = st.d[b * nb + j];
+#pragma unroll
+      for (int p = 0; p < RP; ++p) {
+        const int I = q4_block_isum(w[p], xa, xb, xs);
+        acc[p][b] = fmaf(dwf[p] * dx, (float)I, acc[p][b]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int row = rbase + p * RPP;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float v = group_sum<G>(acc[p][b]);
+      if (sub == 0 && row < N) Y[(int64_t)b * ldy + row] = v;
+    }
+  }
+}
+
+template <int B, int G, int RP>
+static hipError_t launch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
+                            const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
+                            int64_t ldy, hipStream_t s) {
+  constexpr int rows_wg = 4 * RP * (64 / G);
+  const int blocks = (N + rows_wg - 1) / rows_wg;
+  const size_t lds = xstage_bytes(B, K);
+  hipLaunchKernelGGL((k_gemv_q4_0<B, G, RP>), dim3(blocks), dim3(256), lds, s, qs, d, N, K,
+                     X, ldx, Xq, Y, ldy);
+  return hipGetLastError();
+}
+
+template <int B>
+static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
+                              const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
+                              int64_t ldy, hipStream_t s) {
+  const int nb = K / 32;
+  constexpr int RP = B <= 2 ? 2 : 4;
+  if (nb <= 16) return launch_q4<B, 16, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  if (nb <= 32) return launch_q4<B, 32, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  return launch_q4<B, 64, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+}
+
+hipError_t run_gemv_q4_0(const uint8_t *qs, const uint16_t *d, int N, int K,
+                         const float *X, int64_t ldx, const uint8_t *Xq, int B,
+                         float *Y, int64_t ldy, hipStream_t s) {
+  switch (B) {
+    case 1: return dispatch_q4<1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 2: return dispatch_q4<2>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 3: return dispatch_q4<3>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 4: return dispatch_q4<4>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 5: return dispatch_q4<5>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 6: return dispatch_q4<6>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 7: return dispatch_q4<7>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 8: return dispatch_q4<8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mmv

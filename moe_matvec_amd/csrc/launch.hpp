@@ -1,0 +1,35 @@
+// launch.hpp -- internal host-side launchers (one per kernel family).
+// Arguments have been validated by the C ABI layer (api.cpp) before these
+// are called; each returns hipGetLastError() after its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_matvec.h"
+
+namespace mmv {
+
+hipError_t run_gemv_bf16(const uint16_t *W, int N, int K, int64_t ldw,
+                         const float *X, int64_t ldx, int B, float *Y, int64_t ldy,
+                         hipStream_t s);
+
+hipError_t run_quantize_q8_1(const float *X, int K, int64_t ldx, int B,
+                             uint8_t *Xq, hipStream_t s);
+
+hipError_t run_gemv_q4_0(const uint8_t *qs, const uint16_t *d, int N, int K,
+                         const float *X, int64_t ldx, const uint8_t *Xq, int B,
+                         float *Y, int64_t ldy, hipStream_t s);
+
+// router logits (+ shared-gate logit in column E), then top-k and weights
+hipError_t run_moe_route(const float *router, int E, int H, const float *X,
+                         int64_t ldx, int B, int k, const float *shared_gate_row,
+                         float *logits, int32_t *ids, float *weights,
+                         float *shared_w, hipStream_t s);
+
+hipError_t run_moe_experts(const mmv_moe_layer &L, const float *X, int64_t ldx,
+                           int B, const int32_t *ids, const float *weights,
+                           const float *shared_w, float *Y, int64_t ldy,
+                           uint8_t *hq, const mmv_moe_debug *dbg, hipStream_t s);
+
+}  // namespace mmv

@@ -1,0 +1,233 @@
+// validate.cpp -- host-side argument checks of the C ABI (pure C++).
+#include "validate.hpp"
+
+#include "layout.hpp"
+
+namespace mmv {
+namespace {
+
+constexpr int64_t kMaxLd = int64_t(1) << 40;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range rng(const void *p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+Range none() { return Range{0, 0}; }
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+// bytes spanned by `rows` rows of `cols` elements with leading dimension ld
+size_t span(int64_t rows, int64_t ld, int64_t cols, size_t elem) {
+  return (size_t)(((rows - 1) * ld + cols) * (int64_t)elem);
+}
+bool bad_batch(int32_t B) { return B < 1 || B > MMV_MAX_BATCH; }
+
+template <int NO, int NI>
+bool any_overlap(const Range (&outs)[NO], const Range (&ins)[NI]) {
+  for (int i = 0; i < NO; ++i) {
+    for (int j = 0; j < NI; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < NO; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+Range q4_qs(const uint8_t *qs, int64_t N, int64_t K) { return rng(qs, (size_t)(N * K / 2)); }
+Range q4_d(const uint16_t *d, int64_t N, int64_t K) { return rng(d, (size_t)(N * K / 32 * 2)); }
+
+}  // namespace
+
+int check_gemv_bf16(const uint16_t *W, int32_t N, int32_t K, int64_t ldw, const float *X,
+                    int64_t ldx, int32_t B, const float *Y, int64_t ldy) {
+  if (!W || !X || !Y) return MMV_E_NULL;
+  if (bad_batch(B)) return MMV_E_BATCH;
+  if (N < 1 || K < 8 || K % 8 != 0 || ldw < K || ldx < K || ldy < N) return MMV_E_SHAPE;
+  if (ldw > kMaxLd || ldx > kMaxLd || ldy > kMaxLd) return MMV_E_SHAPE;
+  if (!aligned(W, 16) || ldw % 8 != 0 || !aligned(X, 16) || ldx % 4 != 0 || !aligned(Y, 4))
+    return MMV_E_ALIGN;
+  const Range outs[1] = {rng(Y, span(B, ldy, N, 4))};
+  const Range ins[2] = {rng(W, span(N, ldw, K, 2)), rng(X, span(B, ldx, K, 4))};
+  if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+  return MMV_OK;
+}
+
+int check_quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B, const void *Xq) {
+  if (!X || !Xq) return MMV_E_NULL;
+  if (bad_batch(B)) return MMV_E_BATCH;
+  if (K < 32 || K % 32 != 0 || ldx < K || ldx > kMaxLd) return MMV_E_SHAPE;
+  if (!aligned(X, 16) || ldx % 4 != 0 || !aligned(Xq, 16)) return MMV_E_ALIGN;
+  const Range outs[1] = {rng(Xq, q8_1_bytes(K, B))};
+  const Range ins[1] = {rng(X, span(B, ldx, K, 4))};
+  if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+  return MMV_OK;
+}
+
+int check_gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,
+                    int32_t B, const float *Y, int64_t ldy) {
+  if (!W || !W->qs || !W->d || !Y) return MMV_E_NULL;
+  if ((X == nullptr) == (Xq == nullptr)) return MMV_E_ARG;
+  if (bad_batch(B)) return MMV_E_BATCH;
+  const int32_t N = W->N, K = W->K;
+  if (N < 1 || K < 32 || K % 32 != 0 || ldy < N || ldy > kMaxLd) return MMV_E_SHAPE;
+  if (X && (ldx < K || ldx > kMaxLd)) return MMV_E_SHAPE;
+  if ((int64_t)B * K > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
+  if (!aligned(W->qs, 16) || !aligned(W->d, 2) || !aligned(Y, 4)) return MMV_E_ALIGN;
+  if (X && (!aligned(X, 16) || ldx % 4 != 0)) return MMV_E_ALIGN;
+  if (Xq && !aligned(Xq, 16)) return MMV_E_ALIGN;
+  const Range outs[1] = {rng(Y, span(B, ldy, N, 4))};
+  const Range ins[3] = {q4_qs(W->qs, N, K), q4_d(W->d, N, K),
+                        X ? rng(X, span(B, ldx, K, 4)) : rng(Xq, q8_1_bytes(K, B))};
+  if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+  return MMV_OK;
+}
+
+int check_route(const float *router, int32_t E, int32_t H, const float *X, int64_t ldx,
+                int32_t B, int32_t k, const float *shg, const float *logits,
+                const int32_t *ids, const float *weights, const float *shared_w) {
+  if (!X || !ids || !weights) return MMV_E_NULL;
+  if (router && !logits) return MMV_E_NULL;
+  if (bad_batch(B)) return MMV_E_BATCH;
+  if (E < 1 || E > MMV_MAX_EXPERTS) return MMV_E_SHAPE;
+  if (k < 1 || k > E || k > MMV_MAX_TOPK) return MMV_E_TOPK;
+  if (!router && shg) return MMV_E_ARG;
+  const int32_t xcols = router ? H : E;
+  if (router && (H < 4 || H % 4 != 0)) return MMV_E_SHAPE;
+  if (ldx < xcols || ldx > kMaxLd) return MMV_E_SHAPE;
+  if (router) {
+    if (!aligned(router, 16) || !aligned(X, 16) || ldx % 4 != 0 || !aligned(logits, 4))
+      return MMV_E_ALIGN;
+    if (shg && !aligned(shg, 16)) return MMV_E_ALIGN;
+  } else if (!aligned(X, 4)) {
+    return MMV_E_ALIGN;
+  }
+  if (!aligned(ids, 4) || !aligned(weights, 4) || !aligned(shared_w, 4)) return MMV_E_ALIGN;
+  const Range outs[4] = {router ? rng(logits, (size_t)4 * B * (E + 1)) : none(),
+                         rng(ids, (size_t)4 * B * k), rng(weights, (size_t)4 * B * k),
+                         shared_w ? rng(shared_w, (size_t)4 * B) : none()};
+  const Range ins[3] = {router ? rng(router, (size_t)4 * E * H) : none(),
+                        rng(X, span(B, ldx, xcols, 4)),
+                        shg ? rng(shg, (size_t)4 * H) : none()};
+  if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+  return MMV_OK;
+}
+
+int check_moe_layer(const mmv_moe_layer *L) {
+  if (!L) return MMV_E_NULL;
+  const int32_t E = L->n_experts, H = L->hidden, I = L->inter, k = L->top_k;
+  if (E < 1 || E > MMV_MAX_EXPERTS) return MMV_E_SHAPE;
+  if (k < 1 || k > E || k > MMV_MAX_TOPK) return MMV_E_TOPK;
+  if (H < 32 || H % 32 != 0 || I < 32 || I % 32 != 0) return MMV_E_SHAPE;
+  if (!L->router || !L->gate_qs || !L->up_qs || !L->down_qs || !L->gate_d || !L->up_d ||
+      !L->down_d)
+    return MMV_E_NULL;
+  const int nsh = (L->sh_gate_qs != nullptr) + (L->sh_up_qs != nullptr) +
+                  (L->sh_down_qs != nullptr) + (L->sh_gate_d != nullptr) +
+                  (L->sh_up_d != nullptr) + (L->sh_down_d != nullptr);
+  if (nsh != 0 && nsh != 6) return MMV_E_ARG;
+  if (!aligned(L->router, 16) || !aligned(L->gate_qs, 16) || !aligned(L->up_qs, 16) ||
+      !aligned(L->down_qs, 16) || !aligned(L->gate_d, 2) || !aligned(L->up_d, 2) ||
+      !aligned(L->down_d, 2))
+    return MMV_E_ALIGN;
+  if (nsh && (!aligned(L->sh_gate_qs, 16) || !aligned(L->sh_up_qs, 16) ||
+              !aligned(L->sh_down_qs, 16) || !aligned(L->sh_gate_d, 2) ||
+              !aligned(L->sh_up_d, 2) || !aligned(L->sh_down_d, 2)))
+    return MMV_E_ALIGN;
+  if (L->shared_gate_row && !aligned(L->shared_gate_row, 16)) return MMV_E_ALIGN;
+  return MMV_OK;
+}
+
+size_t moe_ws_bytes(const mmv_moe_layer *L, int32_t B) {
+  if (check_moe_layer(L) != MMV_OK || bad_batch(B)) return 0;
+  return moe_ws_layout(L->n_experts, L->inter, L->top_k, B, L->sh_gate_qs != nullptr).total;
+}
+
+namespace {
+// ranges of every weight plane of a layer (inputs)
+struct LayerRanges {
+  Range r[13];
+};
+LayerRanges layer_ranges(const mmv_moe_layer *L) {
+  const int64_t E = L->n_experts, H = L->hidden, I = L->inter;
+  LayerRanges lr;
+  lr.r[0] = rng(L->router, (size_t)(4 * E * H));
+  lr.r[1] = L->shared_gate_row ? rng(L->shared_gate_row, (size_t)(4 * H)) : none();
+  lr.r[2] = q4_qs(L->gate_qs, E * I, H);
+  lr.r[3] = q4_qs(L->up_qs, E * I, H);
+  lr.r[4] = q4_qs(L->down_qs, E * H, I);
+  lr.r[5] = q4_d(L->gate_d, E * I, H);
+  lr.r[6] = q4_d(L->up_d, E * I, H);
+  lr.r[7] = q4_d(L->down_d, E * H, I);
+  const bool sh = L->sh_gate_qs != nullptr;
+  lr.r[8] = sh ? q4_qs(L->sh_gate_qs, I, H) : none();
+  lr.r[9] = sh ? q4_qs(L->sh_up_qs, I, H) : none();
+  lr.r[10] = sh ? q4_qs(L->sh_down_qs, H, I) : none();
+  lr.r[11] = sh ? q4_d(L->sh_gate_d, I, H) : none();
+  lr.r[12] = sh ? q4_d(L->sh_up_d, I, H) : none();
+  // sh_down_d is checked separately below (13 slots suffice for the others)
+  return lr;
+}
+bool hits_layer(Range out, const mmv_moe_layer *L) {
+  const LayerRanges lr = layer_ranges(L);
+  for (const Range &r : lr.r)
+    if (overlap(out, r)) return true;
+  if (L->sh_down_d && overlap(out, q4_d(L->sh_down_d, L->hidden, L->inter))) return true;
+  return false;
+}
+}  // namespace
+
+int check_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_t B,
+                     const int32_t *ids, const float *weights, const float *shared_w,
+                     const float *Y, int64_t ldy, const void *ws, size_t ws_bytes) {
+  const int st = check_moe_layer(L);
+  if (st != MMV_OK) return st;
+  if (!X || !ids || !weights || !Y) return MMV_E_NULL;
+  if (bad_batch(B)) return MMV_E_BATCH;
+  const int32_t H = L->hidden, k = L->top_k;
+  if (ldx < H || ldy < H || ldx > kMaxLd || ldy > kMaxLd) return MMV_E_SHAPE;
+  if ((int64_t)B * H > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
+  if (!aligned(X, 16) || ldx % 4 != 0 || !aligned(ids, 4) || !aligned(weights, 4) ||
+      !aligned(shared_w, 4) || !aligned(Y, 4))
+    return MMV_E_ALIGN;
+  if (!ws || ws_bytes < moe_ws_bytes(L, B)) return MMV_E_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return MMV_E_ALIGN;
+  const Range outs[2] = {rng(Y, span(B, ldy, H, 4)), rng(ws, ws_bytes)};
+  const Range ins[4] = {rng(X, span(B, ldx, H, 4)), rng(ids, (size_t)4 * B * k),
+                        rng(weights, (size_t)4 * B * k),
+                        shared_w ? rng(shared_w, (size_t)4 * B) : none()};
+  if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+  if (hits_layer(outs[0], L) || hits_layer(outs[1], L)) return MMV_E_ALIAS;
+  return MMV_OK;
+}
+
+int check_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_t B,
+                       const float *Y, int64_t ldy, const int32_t *ids, const float *weights,
+                       const void *ws, size_t ws_bytes) {
+  const int st = check_moe_layer(L);
+  if (st != MMV_OK) return st;
+  if (!X || !Y) return MMV_E_NULL;
+  if (bad_batch(B)) return MMV_E_BATCH;
+  const int32_t H = L->hidden, k = L->top_k;
+  if (ldx < H || ldy < H || ldx > kMaxLd || ldy > kMaxLd) return MMV_E_SHAPE;
+  if ((int64_t)B * H > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
+  if (!aligned(X, 16) || ldx % 4 != 0 || !aligned(ids, 4) || !aligned(weights, 4) ||
+      !aligned(Y, 4))
+    return MMV_E_ALIGN;
+  if (!ws || ws_bytes < moe_ws_bytes(L, B)) return MMV_E_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return MMV_E_ALIGN;
+  const Range outs[4] = {rng(Y, span(B, ldy, H, 4)), rng(ws, ws_bytes),
+                         ids ? rng(ids, (size_t)4 * B * k) : none(),
+                         weights ? rng(weights, (size_t)4 * B * k) : none()};
+  const Range ins[1] = {rng(X, span(B, ldx, H, 4))};
+  if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+  for (const Range &o : outs)
+    if (hits_layer(o, L)) return MMV_E_ALIAS;
+  return MMV_OK;
+}
+
+}  // namespace mmv

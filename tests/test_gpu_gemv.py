@@ -1,0 +1,151 @@
+"""GPU parity of gemv_bf16, quantize_q8_1 and gemv_q4_0 against the oracle,
+through the C ABI (moe_matvec_amd binding)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests._util import np16, npc, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 1e-3   # rel-L2 per output row for BF16 GEMV
+Q4_TOL = 2e-3     # rel-L2 per output row for Q4_0 x Q8_1 GEMV (vs the W4A8 result)
+
+
+# ---------------------------------------------------------------------------
+# BF16
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,B", [
+    (1024, 1024, 1),      # the 1024 x 1024 correctness case (seed 0)
+    (1000, 1016, 3),      # ragged rows and a ragged chunk tail
+    (37, 72, 8),
+    (4097, 2560, 2),
+    (2560, 9728, 1),
+    (513, 8, 5),
+    (9, 4096, 8),
+])
+def test_bf16_parity(mm, orc, dev, N, K, B):
+    W = synth.bf16_weights(N, K, 0, "bf16", N, K, device=dev)
+    X = synth.activations(B, K, 0, "bf16", N, K, device=dev)
+    y = mm.gemv_bf16(W, X)
+    torch.cuda.synchronize()
+    ref = orc.gemv_bf16(np16(W), npc(X))
+    assert rel_l2_rows(npc(y), ref) <= BF16_TOL
+
+
+def test_bf16_integer_pin_bit_exact(mm, orc, dev):
+    g = torch.Generator().manual_seed(1)
+    N, K, B = 777, 1032, 8
+    Wf = torch.randint(-8, 9, (N, K), generator=g).float()
+    Xf = torch.randint(-16, 17, (B, K), generator=g).float()
+    y = mm.gemv_bf16(Wf.to(torch.bfloat16).to(dev), Xf.to(dev))
+    want = (Xf.double() @ Wf.double().T).numpy()
+    assert np.array_equal(npc(y).astype(np.float64), want)
+
+
+def test_bf16_batch_invariance_and_determinism(mm, dev):
+    N, K = 3000, 2560
+    W = synth.bf16_weights(N, K, 0, "inv", device=dev)
+    X = synth.activations(8, K, 0, "inv", device=dev)
+    y8 = mm.gemv_bf16(W, X)
+    y8b = mm.gemv_bf16(W, X)
+    assert torch.equal(y8, y8b)
+    for b in range(8):
+        assert torch.equal(mm.gemv_bf16(W, X[b].clone())[None], y8[b:b + 1])
+    for B in (2, 3, 4, 5):
+        assert torch.equal(mm.gemv_bf16(W, X[:B].contiguous()), y8[:B])
+
+
+def test_bf16_leading_dimensions(mm, orc, dev):
+    N, K = 300, 512
+    Wp = synth.bf16_weights(N, K + 64, 0, "ld", device=dev)
+    Xp = synth.activations(3, K + 8, 0, "ld", device=dev)
+    W, X = Wp[:, :K], Xp[:, :K]
+    out = torch.full((3, N + 5), 7.0, device=dev)
+    mm.gemv_bf16(W, X, out=out[:, :N])
+    ref = orc.gemv_bf16(np16(Wp), npc(Xp), K=K)
+    assert rel_l2_rows(npc(out[:, :N]), ref) <= BF16_TOL
+    assert (out[:, N:] == 7.0).all()
+
+
+# ---------------------------------------------------------------------------
+# Q8_1
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,K,scale", [(1, 4096, 1.0), (8, 2048, 1.0), (3, 96, 1e-3),
+                                       (2, 32, 3e4), (5, 512, 1e-6)])
+def test_quantize_q8_1_bit_exact(mm, orc, dev, B, K, scale):
+    X = synth.activations(B, K, 0, "q8", B, K, device=dev) * scale
+    X[0, :32] = 0.0                                  # an all-zero block
+    if K >= 96:
+        X[-1, 64:96] = 0.0
+        X[-1, 70] = -2.5                             # a single-value block
+    buf = mm.quantize_q8_1(X)
+    torch.cuda.synchronize()
+    q_ref, ds_ref = orc.quantize_q8_1(npc(X))
+    codes, ds = mm.split_q8_1(buf, B, K)
+    assert np.array_equal(npc(codes), q_ref)
+    assert np.array_equal(np16(ds), ds_ref)
+
+
+def test_quantize_q8_1_worked_example(mm, dev):
+    from tests.test_oracle_q8_1 import _golden
+    x, q, d, s = _golden()
+    buf = mm.quantize_q8_1(torch.from_numpy(x)[None].to(dev))
+    codes, ds = mm.split_q8_1(buf, 1, 32)
+    assert np.array_equal(npc(codes)[0], q)
+    assert np16(ds)[0, 0, 0] == d and np16(ds)[0, 0, 1] == s
+
+
+# ---------------------------------------------------------------------------
+# Q4_0
+# ---------------------------------------------------------------------------
+
+def _q4(mm, N, K, dev, *tags):
+    qs, d = synth.q4_0_weights(N, K, 0, "q4", N, K, *tags, device=dev)
+    return mm.Q4_0(qs, d), npc(qs), np16(d)
+
+
+@pytest.mark.parametrize("N,K,B", [
+    (4096, 4096, 1), (1100, 4096, 8), (2048, 512, 1), (515, 512, 8),
+    (333, 2048, 3), (77, 96, 2), (64, 32, 1), (130, 1024, 6),
+])
+def test_q4_0_parity(mm, orc, dev, N, K, B):
+    W, qs, d = _q4(mm, N, K, dev)
+    X = synth.activations(B, K, 0, "q4x", N, K, device=dev)
+    y_x = mm.gemv_q4_0(W, x=X)
+    xq = mm.quantize_q8_1(X)
+    y_q = mm.gemv_q4_0(W, xq=xq, B=B)
+    torch.cuda.synchronize()
+    # on-the-fly quantization inside the GEMV equals quantize_q8_1 + Xq bit for bit
+    assert torch.equal(y_x, y_q)
+    q_ref, ds_ref = orc.quantize_q8_1(npc(X))
+    ref = orc.gemv_q4_0(qs, d, q_ref, ds_ref)
+    assert rel_l2_rows(npc(y_x), ref) <= Q4_TOL
+
+
+def test_q4_0_unit_scale_pin_bit_exact(mm, dev):
+    g = torch.Generator().manual_seed(2)
+    N, K, B = 700, 2048, 8
+    codes = torch.randint(0, 16, (N, K // 32, 32), generator=g, dtype=torch.uint8)
+    qs = (codes[..., :16] | (codes[..., 16:] << 4)).contiguous()
+    d = torch.ones((N, K // 32), dtype=torch.float16)
+    # x integer-valued with a +-127 in every block: Q8_1 gives d = 1, q = x
+    x = torch.randint(-127, 128, (B, K), generator=g).float()
+    x.view(B, -1, 32)[:, :, 3] = 127.0
+    W = mm.Q4_0(qs.to(dev), d.to(dev))
+    y = mm.gemv_q4_0(W, x=x.to(dev))
+    want = x.double() @ (codes.reshape(N, K).double() - 8).T
+    assert np.array_equal(npc(y).astype(np.float64), want.numpy())
+
+
+def test_q4_0_batch_invariance(mm, dev):
+    N, K = 1500, 4096
+    W, _, _ = _q4(mm, N, K, dev, "inv")
+    X = synth.activations(8, K, 0, "q4inv", device=dev)
+    y8 = mm.gemv_q4_0(W, x=X)
+    assert torch.equal(y8, mm.gemv_q4_0(W, x=X))
+    for b in range(8):
+        assert torch.equal(mm.gemv_q4_0(W, x=X[b:b + 1].clone()), y8[b:b + 1])

@@ -1,0 +1,145 @@
+"""GPU parity of the MoE path (moe_route_topk, moe_mul_mat_id,
+moe_layer_decode) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests._util import build_moe, check_route, npc, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+MOE_TOL = 2e-3
+
+
+def _route_and_check(mm, orc, layer, ref, X):
+    ids, w, sw, logits = mm.moe_route_topk(layer.router, X, layer.k,
+                                           shared_gate_row=layer.shared_gate_row)
+    torch.cuda.synchronize()
+    near = check_route(orc, ref.router, npc(X), npc(logits), npc(ids), layer.k, layer.E)
+    # weights: softmax renormalised over the selected, from the GPU's ids
+    lg_ref = orc.router_logits(ref.router, npc(X))
+    w_ref = orc.gate_weights(lg_ref, npc(ids))
+    np.testing.assert_allclose(npc(w), w_ref, rtol=2e-5, atol=1e-6)
+    if layer.shared_gate_row is not None:
+        z = npc(X).astype(np.float64) @ npc(layer.shared_gate_row).astype(np.float64)
+        np.testing.assert_allclose(npc(sw), 1 / (1 + np.exp(-z)), rtol=2e-5, atol=1e-6)
+    else:
+        assert (npc(sw) == 1.0).all()
+    return ids, w, sw, near
+
+
+@pytest.mark.parametrize("E,H,I,k,B,shared,sgate", [
+    (16, 256, 64, 4, 1, True, False),
+    (16, 256, 64, 4, 8, True, False),
+    (64, 512, 96, 6, 3, False, False),
+    (40, 256, 32, 16, 8, True, True),
+    (256, 2048, 512, 8, 1, True, False),     # the 256-expert decode layer
+    (512, 2048, 512, 10, 8, True, False),    # the 512-expert verify batch
+])
+def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
+    layer, ref = build_moe(mm, orc, E, H, I, k, 0, "moe", E, H, I, shared=shared,
+                           shared_gate=sgate, device=dev)
+    X = synth.activations(B, H, 0, "moe", E, B, device=dev)
+    ids, w, sw, _ = _route_and_check(mm, orc, layer, ref, X)
+
+    P = layer.npairs(B)
+    dbg = dict(h=torch.full((P, I), np.nan, device=dev),
+               unique=torch.full((B * k,), -1, dtype=torch.int32, device=dev),
+               offsets=torch.full((B * k + 1,), -1, dtype=torch.int32, device=dev),
+               pairs=torch.full((B * k,), -1, dtype=torch.int32, device=dev),
+               n_unique=torch.zeros(1, dtype=torch.int32, device=dev))
+    ws = torch.zeros(mm.moe_workspace_bytes(layer, B), dtype=torch.uint8, device=dev)
+    y = mm.moe_mul_mat_id(layer, X, ids, w, sw, workspace=ws, debug=dbg)
+    torch.cuda.synchronize()
+    ids_np = npc(ids)
+
+    # gather lists: bit-exact against the oracle's brute force
+    u_ref, o_ref, p_ref = orc.gather(ids_np)
+    U = int(npc(dbg["n_unique"])[0])
+    assert U == len(u_ref)
+    assert np.array_equal(npc(dbg["unique"])[:U], u_ref)
+    assert np.array_equal(npc(dbg["offsets"])[:U + 1], o_ref)
+    assert np.array_equal(npc(dbg["pairs"]), p_ref)
+
+    # gate/up stage: h within tolerance of the oracle (float64 sums)
+    h_ref = ref.gate_up(npc(X), ids_np)
+    h_gpu = npc(dbg["h"])
+    assert rel_l2_rows(h_gpu, h_ref) <= MOE_TOL
+    # Q8_1 epilogue: bit-exact against the oracle quantizer on the GPU's h
+    hq_ref, hds_ref = orc.quantize_q8_1(h_gpu)
+    raw = npc(ws)
+    hq_gpu = raw[:P * I].view(np.int8).reshape(P, I)
+    hds_gpu = raw[P * I:P * I + 4 * P * (I // 32)].view(np.uint16).reshape(P, I // 32, 2)
+    assert np.array_equal(hq_gpu, hq_ref)
+    assert np.array_equal(hds_gpu, hds_ref)
+
+    # down stage fed the GPU's own Q8_1(h): only fp32 accumulation differs
+    w64, s64 = npc(w).astype(np.float64), npc(sw).astype(np.float64)
+    y_staged = ref.down(hq_gpu, hds_gpu, ids_np, w64, s64)
+    assert rel_l2_rows(npc(y), y_staged) <= 1e-4
+    # end to end with the same routing
+    hq_o, hds_o = orc.quantize_q8_1(h_ref)
+    y_ref = ref.down(hq_o, hds_o, ids_np, w64, s64)
+    assert rel_l2_rows(npc(y), y_ref) <= MOE_TOL
+
+
+@pytest.mark.parametrize("E,H,I,k,B", [(256, 2048, 512, 8, 1), (512, 2048, 512, 10, 4),
+                                       (32, 512, 64, 4, 8)])
+def test_moe_layer_decode(mm, orc, dev, E, H, I, k, B):
+    layer, ref = build_moe(mm, orc, E, H, I, k, 0, "dec", E, H, I, device=dev)
+    X = synth.activations(B, H, 0, "dec", E, B, device=dev)
+    ids = torch.empty((B, k), dtype=torch.int32, device=dev)
+    w = torch.empty((B, k), dtype=torch.float32, device=dev)
+    y = mm.moe_layer_decode(layer, X, ids=ids, weights=w)
+    y2 = mm.moe_layer_decode(layer, X)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    out = ref.layer(npc(X))
+    same = [b for b in range(B) if np.array_equal(npc(ids)[b], out["ids"][b])]
+    assert len(same) >= B - 1            # near ties in float64 logits are rare
+    assert rel_l2_rows(npc(y)[same], out["y"][same]) <= MOE_TOL
+
+
+def test_topk_exact_ties_from_logits(mm, orc, dev):
+    E, k = 300, 10
+    g = torch.Generator().manual_seed(3)
+    L = torch.randint(-3, 4, (6, E), generator=g).float()      # many exact ties
+    L[1] = 0.0
+    L[2, 5] = -0.0
+    L[2, 9] = 0.0
+    ids, w, sw, _ = mm.moe_route_topk(None, L.to(dev), k, n_experts=E)
+    torch.cuda.synchronize()
+    assert np.array_equal(npc(ids), orc.topk(L.numpy(), k))
+    assert np.array_equal(npc(ids)[1], np.arange(k))
+    np.testing.assert_allclose(npc(w)[1], np.full(k, 1.0 / k), rtol=1e-6)
+    w_ref = orc.gate_weights(L.numpy().astype(np.float64), npc(ids))
+    np.testing.assert_allclose(npc(w), w_ref, rtol=2e-6, atol=1e-7)
+
+
+def test_moe_batch_invariance(mm, orc, dev):
+    E, H, I, k, B = 64, 1024, 128, 6, 8
+    layer, _ = build_moe(mm, orc, E, H, I, k, 0, "binv", device=dev)
+    X = synth.activations(B, H, 0, "binv", device=dev)
+    ids, w, sw, _ = mm.moe_route_topk(layer.router, X, k)
+    y8 = mm.moe_mul_mat_id(layer, X, ids, w, sw)
+    assert torch.equal(y8, mm.moe_mul_mat_id(layer, X, ids, w, sw))
+    for b in range(B):
+        yb = mm.moe_mul_mat_id(layer, X[b:b + 1].clone(), ids[b:b + 1].clone(),
+                               w[b:b + 1].clone(), sw[b:b + 1].clone())
+        assert torch.equal(yb, y8[b:b + 1])
+
+
+def test_moe_single_expert_and_no_shared(mm, orc, dev):
+    # k = 1 without a shared expert reduces to one down projection of Q8_1(h)
+    E, H, I = 8, 256, 64
+    layer, ref = build_moe(mm, orc, E, H, I, 1, 0, "single", shared=False, device=dev)
+    X = synth.activations(2, H, 0, "single", device=dev)
+    ids = torch.tensor([[3], [6]], dtype=torch.int32, device=dev)
+    w = torch.ones((2, 1), device=dev)
+    y = mm.moe_mul_mat_id(layer, X, ids, w)
+    h = ref.gate_up(npc(X), npc(ids))
+    hq, hds = orc.quantize_q8_1(h)
+    for b, e in enumerate((3, 6)):
+        want = orc.gemv_q4_0(ref.down_qs[e], ref.down_d[e], hq[b:b + 1], hds[b:b + 1])
+        assert rel_l2_rows(npc(y)[b:b + 1], want) <= MOE_TOL
