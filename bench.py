@@ -200,7 +200,7 @@ def moe_section(mm, dev, E, k, layers, Bs, steps, warmup, H=2048, I=512):
         X = synth.activations(layers * B, H, 0, "moebench-x", E, B, device=dev).view(layers, B, H)
         Y = torch.empty((layers, B, H), device=dev)
         ids = torch.empty((layers, B, k), dtype=torch.int32, device=dev)
-        ws = torch.empty((layers, mm.moe_workspace_bytes(lay[0], B)), dtype=torch.uint8,
+        ws = torch.zeros((layers, mm.moe_workspace_bytes(lay[0], B)), dtype=torch.uint8,
                          device=dev)
 
         def step():

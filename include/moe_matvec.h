@@ -192,8 +192,12 @@ typedef struct {
 /* Workspace bytes for moe_mul_mat_id / moe_layer_decode at B rows.
  * Layout: bytes [0, mmv_q8_1_bytes(I, P)) hold Q8_1(h) for the P pairs
  * (P = B*k routed pairs p = b*k + j, then B shared pairs p = B*k + b),
- * followed by the routing buffers moe_layer_decode uses.  256-byte
- * aligned workspace required. */
+ * followed by the integer code sums of those blocks, the per-expert row
+ * lists, and the routing buffers and one synchronization word that
+ * moe_layer_decode uses.  256-byte aligned workspace required.
+ * The down projection stages Q8_1(h) of all P pairs in LDS:
+ * P * I <= MMV_MOE_MAX_PI (else MMV_E_SHAPE). */
+#define MMV_MOE_MAX_PI 49152
 size_t moe_workspace_bytes(const mmv_moe_layer *L, int32_t B);
 
 /* --------------------------------------------------------------------------
@@ -219,16 +223,32 @@ int moe_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx,
                    const mmv_moe_debug *dbg, void *stream);
 
 /* --------------------------------------------------------------------------
- * moe_layer_decode -- the whole MoE layer in the fewest launches:
- *   moe_route_topk followed by moe_mul_mat_id, with routing kept in the
- *   workspace.  ids / weights (B x k) may be NULL; when given they receive
- *   the routing decision.  [STRATA: Pass 3 item 1, graph replay;
- *   FOURTEEN: launches below five microseconds cost more than they run]
+ * moe_layer_decode -- the whole MoE layer in three launches: router rows
+ *   and the shared expert's gate/up (routing-independent) in one grid whose
+ *   last router workgroup runs top-k; the routed gate/up; the down
+ *   projection with the combine.  Routing stays in device memory.
+ *   ids / weights (B x k) may be NULL; when given they receive the routing
+ *   decision.  The workspace must be zero-filled once before its first use
+ *   (its synchronization word must start at zero); every call leaves it
+ *   zero again.  Calls that share a workspace must not overlap.
+ *   [STRATA: Pass 3 item 1, graph replay; FOURTEEN: launches below five
+ *   microseconds cost more than they run; "The router with 257 rows"]
  * ------------------------------------------------------------------------ */
 int moe_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx,
                      int32_t B, float *Y, int64_t ldy,
                      int32_t *ids, float *weights,
                      void *workspace, size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Measurement utility: device read-bandwidth probe.  ["hanzo-engine: A
+ * Portable Single-Binary LLM Inference Engine", The Bandwidth Wall: decode
+ * bandwidth is compared with a measured device roofline probe]
+ *   Streams `bytes` (multiple of 16, buf 16-byte aligned) with 128-bit
+ *   non-temporal loads from a fixed grid and writes one xor-fold word per
+ *   wave to out[0 .. mmv_probe_slots()).  Timing is the caller's.
+ * ------------------------------------------------------------------------ */
+int mmv_probe_slots(void);
+int mmv_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ __all__ = [
     "MatvecError", "Q4_0", "MoeLayer", "library_path", "lib",
     "gemv_bf16", "quantize_q8_1", "q8_1_bytes", "gemv_q4_0",
     "moe_route_topk", "moe_mul_mat_id", "moe_layer_decode", "moe_workspace_bytes",
-    "MAX_BATCH", "MAX_EXPERTS", "MAX_TOPK", "Q4_MAX_XK",
+    "MAX_BATCH", "MAX_EXPERTS", "MAX_TOPK", "Q4_MAX_XK", "stream_read", "split_q8_1",
 ]
 
 MAX_BATCH = 8
@@ -85,6 +85,8 @@ def lib():
                                          _i64, _P, C.c_size_t, C.POINTER(_Debug), _P]),
             "moe_layer_decode": (C.c_int, [C.POINTER(_Layer), _P, _i64, _i32, _P, _i64, _P,
                                            _P, _P, C.c_size_t, _P]),
+            "mmv_probe_slots": (C.c_int, []),
+            "mmv_stream_read": (C.c_int, [_P, C.c_size_t, _P, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -319,16 +321,27 @@ def moe_mul_mat_id(layer: MoeLayer, x: torch.Tensor, ids: torch.Tensor, weights:
 
 def moe_layer_decode(layer: MoeLayer, x: torch.Tensor, out=None, workspace=None, ids=None,
                      weights=None, stream=None):
-    """Whole MoE layer (route + experts) on device; returns out [B, H]."""
+    """Whole MoE layer (route + experts) on device; returns out [B, H].
+    A workspace must be zero-filled before its first use (see moe_matvec.h)."""
     x2 = x.unsqueeze(0) if x.dim() == 1 else x
     B = x2.shape[0]
     if out is None:
         out = torch.empty((B, layer.H), dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace = torch.empty(moe_workspace_bytes(layer, B), dtype=torch.uint8,
+        workspace = torch.zeros(moe_workspace_bytes(layer, B), dtype=torch.uint8,
                                 device=x.device)
     y2 = out.unsqueeze(0) if out.dim() == 1 else out
     _check("moe_layer_decode", lib().moe_layer_decode(
         C.byref(layer._s), x2.data_ptr(), _ld(x2), B, y2.data_ptr(), _ld(y2), _ptr(ids),
         _ptr(weights), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+def stream_read(buf: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """Read-bandwidth probe: streams every byte of buf once (timing is the caller's)."""
+    if out is None:
+        out = torch.empty(lib().mmv_probe_slots(), dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check("mmv_stream_read", lib().mmv_stream_read(buf.data_ptr(), nbytes - nbytes % 16,
+                                                    out.data_ptr(), _stream(stream)))
     return out

@@ -101,16 +101,21 @@ int moe_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   const mmv::MoeWsLayout lay =
       mmv::moe_ws_layout(L->n_experts, L->inter, L->top_k, B, L->sh_gate_qs != nullptr);
-  float *logits = reinterpret_cast<float *>(ws + lay.logits);
   int32_t *id = ids ? ids : reinterpret_cast<int32_t *>(ws + lay.ids);
   float *w = weights ? weights : reinterpret_cast<float *>(ws + lay.weights);
-  float *sw = reinterpret_cast<float *>(ws + lay.shared_w);
-  const hipStream_t s = as_stream(stream);
-  hipError_t e = mmv::run_moe_route(L->router, L->n_experts, L->hidden, X, ldx, B, L->top_k,
-                                    L->shared_gate_row, logits, id, w, sw, s);
-  if (e != hipSuccess) return hip_status(e);
-  return hip_status(
-      mmv::run_moe_experts(*L, X, ldx, B, id, w, sw, Y, ldy, ws + lay.hq, nullptr, s));
+  return hip_status(mmv::run_moe_layer(*L, X, ldx, B, id, w, Y, ldy, ws, as_stream(stream)));
+}
+
+int mmv_probe_slots(void) { return mmv::probe_slots(); }
+
+int mmv_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream) {
+  if (!buf || !out) return MMV_E_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return MMV_E_SHAPE;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0)
+    return MMV_E_ALIGN;
+  const uintptr_t o = reinterpret_cast<uintptr_t>(out), b = reinterpret_cast<uintptr_t>(buf);
+  if (o < b + bytes && b < o + 4 * (size_t)mmv::probe_slots()) return MMV_E_ALIAS;
+  return hip_status(mmv::run_stream_read(buf, bytes, out, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -61,6 +61,98 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// ---- DPP lane exchanges (no LDS traffic) --------------------------------
+// quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror: after these
+// four steps every lane of a 16-lane row has combined all 16 values.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// sum over each 16-lane row, result in every lane of the row (fixed order)
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowHalfMirror>(v);
+  v += dpp_f32<kDppRowMirror>(v);
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64_step(uint64_t k) {
+  const uint32_t hi = dpp_u32<CTRL>((uint32_t)(k >> 32));
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)k);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+
+// maximum over the whole wave, returned in every lane (wave-uniform)
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = dpp_max_u64_step<kDppQuadXor1>(k);
+  k = dpp_max_u64_step<kDppQuadXor2>(k);
+  k = dpp_max_u64_step<kDppRowHalfMirror>(k);
+  k = dpp_max_u64_step<kDppRowMirror>(k);
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * r);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * r);
+    const uint64_t v = ((uint64_t)hi << 32) | lo;
+    best = v > best ? v : best;
+  }
+  return best;
+}
+
+// 8-lane groups (aligned): two quad steps and a half-row mirror
+__device__ __forceinline__ float group8_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+  return v;
+}
+__device__ __forceinline__ int group8_sum_i(int v) {
+  v += (int)dpp_u32<kDppQuadXor1>((uint32_t)v);
+  v += (int)dpp_u32<kDppQuadXor2>((uint32_t)v);
+  v += (int)dpp_u32<kDppRowHalfMirror>((uint32_t)v);
+  return v;
+}
+
+// sum over the whole wave: 16-lane rows by DPP, then the four row sums in a
+// fixed order; every lane gets the same value
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+// sum over aligned 32-lane halves
+__device__ __forceinline__ float half_sum(float v) {
+  v = row16_sum(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (threadIdx.x & 32) ? (c + d) : (a + b);
+}
+// group sum for G in {16, 32, 64}, every lane of the group gets the sum
+template <int G>
+__device__ __forceinline__ float gsum(float v) {
+  if constexpr (G == 16) return row16_sum(v);
+  else if constexpr (G == 32) return half_sum(v);
+  else return wave_sum(v);
+}
+
 __device__ __forceinline__ int sdot4(int a, int b, int c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
 }

@@ -15,6 +15,9 @@
 //  - each (row, b) sum runs over the same lanes and the same chunk order for
 //    every B, R and unroll, so a B-row call reproduces the 1-row call bit for
 //    bit; the 64 lane partials are combined by a fixed xor butterfly.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -99,38 +102,253 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(
   for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const float v = group_sum<64>(acc[r][b]);
+      const float v = wave_sum(acc[r][b]);
       if (lane == 0 && row0 + r < N) Y[(int64_t)b * ldy + row0 + r] = v;
     }
   }
 }
 
+// Fixed-K variant: K = 512 * NI exactly, so every lane owns NI chunks of
+// each row and all R * NI weight loads of a wave are issued before the first
+// FMA.  The per-(row, b) FMA order (chunk ascending, 8 products per chunk) is
+// the generic kernel's, so both variants give identical bits.
+template <int B, int R, int NI, int WPB>
+__global__ __launch_bounds__(WPB * 64) void k_gemv_bf16_ni(
+    const uint16_t *__restrict__ W, int N, int64_t ldw, const float *__restrict__ X,
+    int64_t ldx, float *__restrict__ Y, int64_t ldy) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * WPB + (threadIdx.x >> 6);
+  const int row0 = wave * R;
+  if (row0 >= N) return;
+  u32x4 w[R][NI];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint8_t *wr =
+        reinterpret_cast<const uint8_t *>(W + (int64_t)min(row0 + r, N - 1) * ldw);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) w[r][i] = load_stream16(wr + (int64_t)(lane + 64 * i) * 16);
+  }
+  float acc[R][B];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float *xp = X + (int64_t)b * ldx + 8 * (lane + 64 * i);
+      const f32x4 xa = load_f4(xp), xb = load_f4(xp + 4);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][b] = dot8_bf16(w[r][i], xa, xb, acc[r][b]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float v = wave_sum(acc[r][b]);
+      if (lane == 0 && row0 + r < N) Y[(int64_t)b * ldy + row0 + r] = v;
+    }
+  }
+}
+
+// B >= 2: the x rows form a small dense operand, and 8 fp32 FMAs per weight
+// would make the VALU, not HBM, the bound.  v_mfma_f32_16x16x32_bf16 takes a
+// 16-row x 32-k tile of W (one 128-bit load per lane: row l%16, k 8*(l/16)..)
+// against x^T (column l%16 = activation row b, zero for b >= B).  fp32 x is
+// split exactly into bf16 hi + lo (x - hi is exact in fp32; lo keeps the next
+// 8 bits), two MFMAs per step, so products keep ~2^-17 relative accuracy.
+// A workgroup owns one 16-row tile; its KS waves take interleaved k-steps
+// (wave w: steps w, w+KS, ...), so the workgroup streams each row
+// contiguously, and the KS partial tiles are summed in LDS in wave order.
+// Column b of the result depends only on x row b: rows agree bit for bit for
+// every B >= 2.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split_bf16(f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)v[j];
+    hi[j] = h;
+    lo[j] = (__bf16)(v[j] - (float)h);
+  }
+}
+
+template <int B, int KS, int U>
+__global__ __launch_bounds__(KS * 64) void k_gemv_bf16_mfma(
+    const uint16_t *__restrict__ W, int N, int K, int64_t ldw, const float *__restrict__ X,
+    int64_t ldx, float *__restrict__ Y, int64_t ldy) {
+  __shared__ float part[KS][16][B];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int r = lane & 15, g = lane >> 4;
+  const bool colv = r < B;  // B operand column = activation row
+  const uint8_t *wr = reinterpret_cast<const uint8_t *>(W + (int64_t)min(n0 + r, N - 1) * ldw);
+  const float *xr = X + (int64_t)min(r, B - 1) * ldx;
+  const int nsteps = (K + 31) >> 5;
+  const int nj = w < nsteps ? (nsteps - w + KS - 1) / KS : 0;  // this wave's steps
+  typedef float f32x4m __attribute__((ext_vector_type(4)));
+  f32x4m acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // Chunks of U steps with no branches inside: a step past the wave's last
+  // one re-reads that last step (same lines) with its x zeroed, and k >= K
+  // reads are clamped in bounds and zeroed; x is loaded before W so that,
+  // loads completing in order, step u waits only for its own loads.
+  for (int j0 = 0; j0 < nj; j0 += U) {
+    f32x4 xa[U], xb[U];
+    u32x4 a[U];
+    int kk[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = min(j0 + u, nj - 1);
+      const int k = (w + KS * j) * 32 + 8 * g;
+      ok[u] = colv && (j0 + u < nj) && (k < K);
+      kk[u] = min(k, K - 8);
+      xa[u] = load_f4(xr + kk[u]);
+      xb[u] = load_f4(xr + kk[u] + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = load_stream16(wr + 2 * (int64_t)kk[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      bf16x8 hi, lo;
+      split_bf16(ok[u] ? xa[u] : z, ok[u] ? xb[u] : z, hi, lo);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[u]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lo, acc, 0, 0, 0);
+    }
+  }
+  // lane holds rows 4g..4g+3 of column r
+  if (colv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[w][4 * g + i][r] = acc[i];
+  }
+  __syncthreads();
+  if (threadIdx.x < 16 * B) {
+    const int row = threadIdx.x / B, b = threadIdx.x - row * B;
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) v += part[q][row][b];
+    if (n0 + row < N) Y[(int64_t)b * ldy + n0 + row] = v;
+  }
+}
+
+namespace {
+
+struct Bf16Args {
+  const uint16_t *W;
+  int N, K;
+  int64_t ldw;
+  const float *X;
+  int64_t ldx;
+  float *Y;
+  int64_t ldy;
+  hipStream_t s;
+};
+
 template <int B, int R, int U>
-static hipError_t launch_bf16(const uint16_t *W, int N, int K, int64_t ldw,
-                              const float *X, int64_t ldx, float *Y, int64_t ldy,
-                              hipStream_t s) {
-  const int waves = (N + R - 1) / R;
-  const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((k_gemv_bf16<B, R, U>), dim3(blocks), dim3(256), 0, s,
-                     W, N, K, ldw, X, ldx, Y, ldy);
+hipError_t launch_generic(const Bf16Args &a) {
+  const int waves = (a.N + R - 1) / R;
+  hipLaunchKernelGGL((k_gemv_bf16<B, R, U>), dim3((waves + 3) / 4), dim3(256), 0, a.s, a.W,
+                     a.N, a.K, a.ldw, a.X, a.ldx, a.Y, a.ldy);
   return hipGetLastError();
 }
+
+template <int B, int R, int NI, int WPB>
+hipError_t launch_ni(const Bf16Args &a) {
+  const int waves = (a.N + R - 1) / R;
+  hipLaunchKernelGGL((k_gemv_bf16_ni<B, R, NI, WPB>), dim3((waves + WPB - 1) / WPB),
+                     dim3(WPB * 64), 0, a.s, a.W, a.N, a.ldw, a.X, a.ldx, a.Y, a.ldy);
+  return hipGetLastError();
+}
+
+// tuning knobs for experiments: MMV_BF16_R (rows per wave), MMV_BF16_WPB
+// (waves per workgroup); each prints one line the first time it is used
+int env_knob(const char *name) {
+  const char *v = getenv(name);
+  if (!v || !*v) return 0;
+  static thread_local bool printed[2] = {false, false};
+  const int idx = name[9] == 'R' ? 0 : 1;
+  if (!printed[idx]) {
+    fprintf(stderr, "[moe_matvec] %s=%s\n", name, v);
+    printed[idx] = true;
+  }
+  return atoi(v);
+}
+
+template <int B, int NI>
+hipError_t dispatch_ni(const Bf16Args &a, int R, int WPB) {
+  // all R * NI weight loads of a lane sit in registers (4 VGPRs each):
+  // only variants with R * NI <= 24 exist
+  if constexpr (NI * 4 <= 24 && B <= 2) {
+    if (R >= 4) return WPB == 1 ? launch_ni<B, 4, NI, 1>(a) : launch_ni<B, 4, NI, 4>(a);
+  }
+  if constexpr (NI * 2 <= 24) {
+    if (R >= 2) return WPB == 1 ? launch_ni<B, 2, NI, 1>(a) : launch_ni<B, 2, NI, 4>(a);
+  }
+  return WPB == 1 ? launch_ni<B, 1, NI, 1>(a) : launch_ni<B, 1, NI, 4>(a);
+}
+
+template <int B, int KS, int U>
+hipError_t launch_mfma(const Bf16Args &a) {
+  hipLaunchKernelGGL((k_gemv_bf16_mfma<B, KS, U>), dim3((a.N + 15) / 16), dim3(KS * 64), 0,
+                     a.s, a.W, a.N, a.K, a.ldw, a.X, a.ldx, a.Y, a.ldy);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t dispatch_b(const Bf16Args &a) {
+  if constexpr (B >= 2) {
+    // few 16-row tiles: more waves per tile keep enough loads in flight
+    const int kw = env_knob("MMV_BF16_WPB");
+    const int tiles = (a.N + 15) / 16;
+    const int KS = kw ? kw : (tiles < 1024 ? 16 : 8);
+    if (KS >= 16) return launch_mfma<B, 16, 8>(a);
+    if (KS >= 8) return launch_mfma<B, 8, 8>(a);
+    return launch_mfma<B, 4, 8>(a);
+  } else {
+    const int kr = env_knob("MMV_BF16_R"), kw = env_knob("MMV_BF16_WPB");
+    if (a.K % 512 == 0) {
+      const int NI = a.K / 512;
+      // enough rows per wave that a wave streams >= ~8 KiB; one-wave
+      // workgroups unless the grid is very large
+      const int R = kr ? kr : (NI >= 8 ? 1 : (a.N >= 4096 ? 2 : 1));
+      const int waves = (a.N + R - 1) / R;
+      const int WPB = kw ? kw : (waves >= 16384 ? 4 : 1);
+      switch (NI) {
+        case 1: return dispatch_ni<B, 1>(a, R, WPB);
+        case 2: return dispatch_ni<B, 2>(a, R, WPB);
+        case 4: return dispatch_ni<B, 4>(a, R, WPB);
+        case 5: return dispatch_ni<B, 5>(a, R, WPB);
+        case 8: return dispatch_ni<B, 8>(a, R, WPB);
+        case 19: return dispatch_ni<B, 19>(a, R, WPB);
+        default: break;
+      }
+    }
+    if (a.N >= 8192) return launch_generic<B, 4, 4>(a);
+    if (a.N >= 4096) return launch_generic<B, 2, 4>(a);
+    return launch_generic<B, 1, 4>(a);
+  }
+}
+
+}  // namespace
 
 hipError_t run_gemv_bf16(const uint16_t *W, int N, int K, int64_t ldw,
                          const float *X, int64_t ldx, int B, float *Y, int64_t ldy,
                          hipStream_t s) {
+  const Bf16Args a{W, N, K, ldw, X, ldx, Y, ldy, s};
   switch (B) {
-    case 1:
-      if (N >= 8192) return launch_bf16<1, 4, 4>(W, N, K, ldw, X, ldx, Y, ldy, s);
-      if (N >= 4096) return launch_bf16<1, 2, 4>(W, N, K, ldw, X, ldx, Y, ldy, s);
-      return launch_bf16<1, 1, 4>(W, N, K, ldw, X, ldx, Y, ldy, s);
-    case 2: return launch_bf16<2, 2, 2>(W, N, K, ldw, X, ldx, Y, ldy, s);
-    case 3: return launch_bf16<3, 2, 2>(W, N, K, ldw, X, ldx, Y, ldy, s);
-    case 4: return launch_bf16<4, 2, 2>(W, N, K, ldw, X, ldx, Y, ldy, s);
-    case 5: return launch_bf16<5, 4, 1>(W, N, K, ldw, X, ldx, Y, ldy, s);
-    case 6: return launch_bf16<6, 4, 1>(W, N, K, ldw, X, ldx, Y, ldy, s);
-    case 7: return launch_bf16<7, 4, 1>(W, N, K, ldw, X, ldx, Y, ldy, s);
-    case 8: return launch_bf16<8, 4, 1>(W, N, K, ldw, X, ldx, Y, ldy, s);
+    case 1: return dispatch_b<1>(a);
+    case 2: return dispatch_b<2>(a);
+    case 3: return dispatch_b<3>(a);
+    case 4: return dispatch_b<4>(a);
+    case 5: return dispatch_b<5>(a);
+    case 6: return dispatch_b<6>(a);
+    case 7: return dispatch_b<7>(a);
+    case 8: return dispatch_b<8>(a);
   }
   return hipErrorInvalidValue;
 }

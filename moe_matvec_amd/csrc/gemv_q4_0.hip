@@ -18,6 +18,9 @@
 //  - group partials are combined by a fixed xor butterfly; the per-row
 //    arithmetic is the same for every B, so rows of a batched call match
 //    single-row calls bit for bit.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "q4_0.hpp"
@@ -56,8 +59,13 @@ hipError_t run_quantize_q8_1(const float *X, int K, int64_t ldx, int B, uint8_t 
 }
 
 // ---- Q4_0 GEMV -----------------------------------------------------------
-// B activation rows; G lanes per weight row; RP rows per lane group.
-// A wave covers RP * (64/G) rows, a 256-thread workgroup 4x that.
+// B activation rows; G lanes per weight row; RP rows per lane group.  A wave
+// covers RP * (64/G) rows, a 256-thread workgroup 4x that ("row group").
+// The grid is at most a few workgroups per CU; each stages x once and walks
+// row groups blockIdx.x, blockIdx.x + gridDim.x, ...
+// activations preloaded in registers: 8 float4 per thread covers B*K <= 8192
+constexpr int XPRE_MAXT = 8;
+
 template <int B, int G, int RP>
 __global__ __launch_bounds__(256) void k_gemv_q4_0(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
@@ -66,84 +74,134 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int RPP = 64 / G;
   constexpr int ROWS_WAVE = RP * RPP;
+  constexpr int ROWS_WG = 4 * ROWS_WAVE;
   const int nb = K >> 5;
   const int lane = threadIdx.x & 63;
   const int sub = lane % G, grp = lane / G;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int rbase = wave * ROWS_WAVE + grp;  // row of pass p: rbase + p * RPP
+  const int wv = threadIdx.x >> 6;
+  const int ngroups = (N + ROWS_WG - 1) / ROWS_WG;
+  int gi = blockIdx.x;
 
-  int rowc[RP];
-#pragma unroll
-  for (int p = 0; p < RP; ++p) rowc[p] = min(rbase + p * RPP, N - 1);
+  // fp32 activations are loaded before the first weight blocks (loads
+  // complete in issue order), so quantizing them does not wait for HBM
+  constexpr int MAXT = XPRE_MAXT;
+  XPre<MAXT> xp;
+  const bool pre = X && (B * K <= MAXT * 4 * 256);
+  if (pre) xpre_load(X, ldx, nullptr, B, K, xp);
 
-  // first weight blocks in flight before the activation prologue
+  // first weight blocks of the first row group in flight before staging x
   u32x4 w0[RP];
   float d0[RP];
-  const bool have0 = sub < nb;
+  {
+    const int rbase = gi * ROWS_WG + wv * ROWS_WAVE + grp;
+    const int j0 = sub < nb ? sub : 0;
 #pragma unroll
-  for (int p = 0; p < RP; ++p) {
-    const int64_t blk = (int64_t)rowc[p] * nb + (have0 ? sub : 0);
-    w0[p] = load_stream16(qs + blk * 16);
-    d0[p] = f16_bits_to_f32(load_stream2(dw + blk));
+    for (int p = 0; p < RP; ++p) {
+      const int64_t blk = (int64_t)min(rbase + p * RPP, N - 1) * nb + j0;
+      w0[p] = load_stream16(qs + blk * 16);
+      d0[p] = f16_bits_to_f32(load_stream2(dw + blk));
+    }
   }
 
   const XStage st = xstage_at(smem, B, K);
-  if (X) stage_quantize(X, ldx, nullptr, B, K, st);
+  if (pre) xpre_quantize(xp, B, K, st);
+  else if (X) stage_quantize(X, ldx, nullptr, B, K, st);
   else stage_copy_q8(Xq, B, B, K, st);
   __syncthreads();
 
-  float acc[RP][B];
+  bool first = true;
+  for (; gi < ngroups; gi += gridDim.x) {
+    const int rbase = gi * ROWS_WG + wv * ROWS_WAVE + grp;  // row of pass p: + p * RPP
+    int rowc[RP];
 #pragma unroll
-  for (int p = 0; p < RP; ++p)
+    for (int p = 0; p < RP; ++p) rowc[p] = min(rbase + p * RPP, N - 1);
+    float acc[RP][B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[p][b] = 0.0f;
+    for (int p = 0; p < RP; ++p)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[p][b] = 0.0f;
 
-  for (int j = sub; j < nb; j += G) {
-    u32x4 w[RP];
-    float dwf[RP];
-    if (j == sub) {
+    for (int j = sub; j < nb; j += G) {
+      u32x4 w[RP];
+      float dwf[RP];
+      if (first && j == sub) {
 #pragma unroll
-      for (int p = 0; p < RP; ++p) { w[p] = w0[p]; dwf[p] = d0[p]; }
-    } else {
+        for (int p = 0; p < RP; ++p) { w[p] = w0[p]; dwf[p] = d0[p]; }
+      } else {
 #pragma unroll
-      for (int p = 0; p < RP; ++p) {
-        const int64_t blk = (int64_t)rowc[p] * nb + j;
-        w[p] = load_stream16(qs + blk * 16);
-        dwf[p] = f16_bits_to_f32(load_stream2(dw + blk));
+        for (int p = 0; p < RP; ++p) {
+          const int64_t blk = (int64_t)rowc[p] * nb + j;
+          w[p] = load_stream16(qs + blk * 16);
+          dwf[p] = f16_bits_to_f32(load_stream2(dw + blk));
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int8_t *xc = st.codes + (size_t)b * K + 32 * j;
+        const i32x4 xa = *reinterpret_cast<const i32x4 *>(xc);
+        const i32x4 xb = *reinterpret_cast<const i32x4 *>(xc + 16);
+        const int xs = st.qsum[b * nb + j];
+        const float dx = st.d[b * nb + j];
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+          const int I = q4_block_isum(w[p], xa, xb, xs);
+          acc[p][b] = fmaf(dwf[p] * dx, (float)I, acc[p][b]);
+        }
       }
     }
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const int8_t *xc = st.codes + (size_t)b * K + 32 * j;
-      const i32x4 xa = *reinterpret_cast<const i32x4 *>(xc);
-      const i32x4 xb = *reinterpret_cast<const i32x4 *>(xc + 16);
-      const int xs = st.qsum[b * nb + j];
-      const float dx = st.d[b * nb + j];
-#pragma unroll
-      for (int p = 0; p < RP; ++p) {
-        const int I = q4_block_isum(w[p], xa, xb, xs);
-        acc[p][b] = fmaf(dwf[p] * dx, (float)I, acc[p][b]);
-      }
-    }
-  }
 
 #pragma unroll
-  for (int p = 0; p < RP; ++p) {
-    const int row = rbase + p * RPP;
+    for (int p = 0; p < RP; ++p) {
+      const int row = rbase + p * RPP;
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const float v = group_sum<G>(acc[p][b]);
-      if (sub == 0 && row < N) Y[(int64_t)b * ldy + row] = v;
+      for (int b = 0; b < B; ++b) {
+        const float v = gsum<G>(acc[p][b]);
+        if (sub == 0 && row < N) Y[(int64_t)b * ldy + row] = v;
+      }
     }
+    first = false;
   }
 }
+
+namespace {
+
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int q4_knob(const char *name) {
+  const char *v = getenv(name);
+  if (!v || !*v) return 0;
+  static thread_local bool printed = false;
+  if (!printed) {
+    fprintf(stderr, "[moe_matvec] %s=%s\n", name, v);
+    printed = true;
+  }
+  return atoi(v);
+}
+
+}  // namespace
 
 template <int B, int G, int RP>
 static hipError_t launch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
                             const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                             int64_t ldy, hipStream_t s) {
   constexpr int rows_wg = 4 * RP * (64 / G);
-  const int blocks = (N + rows_wg - 1) / rows_wg;
+  const int ngroups = (N + rows_wg - 1) / rows_wg;
+  // workgroups per CU: each stages x once, so fewer when quantizing here
+  const int knob = q4_knob("MMV_Q4_WG_PER_CU");
+  const int per_cu = knob ? knob : (X ? 2 : 4);
+  const int blocks = min(ngroups, per_cu * cu_count());
   const size_t lds = xstage_bytes(B, K);
   hipLaunchKernelGGL((k_gemv_q4_0<B, G, RP>), dim3(blocks), dim3(256), lds, s, qs, d, N, K,
                      X, ldx, Xq, Y, ldy);

@@ -32,4 +32,13 @@ hipError_t run_moe_experts(const mmv_moe_layer &L, const float *X, int64_t ldx,
                            const float *shared_w, float *Y, int64_t ldy,
                            uint8_t *hq, const mmv_moe_debug *dbg, hipStream_t s);
 
+// whole layer in three launches (routing kept on the device)
+hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
+                         int32_t *ids, float *weights, float *Y, int64_t ldy, uint8_t *ws,
+                         hipStream_t s);
+
+// streaming-read bandwidth probe
+int probe_slots();
+hipError_t run_stream_read(const void *buf, size_t bytes, uint32_t *out, hipStream_t s);
+
 }  // namespace mmv

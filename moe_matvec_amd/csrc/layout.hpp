@@ -20,22 +20,26 @@ MMV_HD size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // planar Q8_1: codes [B][K] then {d, s} fp16 pairs [B][K/32]
 MMV_HD size_t q8_1_bytes(int K, int B) { return (size_t)B * K + (size_t)4 * B * (K / 32); }
 
-// Q8_1 of h for P pairs, followed by the integer code sum of every block
-MMV_HD size_t hq_bytes(int P, int I) { return q8_1_bytes(I, P) + (size_t)4 * P * (I / 32); }
+// Q8_1 of h for P pairs, followed by an internal {fp32 d, integer code sum}
+// record per block (8 bytes) that the down kernel reads in one load
+MMV_HD size_t hq_bytes(int P, int I) { return q8_1_bytes(I, P) + (size_t)8 * P * (I / 32); }
 
-// moe workspace: [hq][logits B x (E+1)][ids B x k][weights B x k][shared_w B]
+// moe workspace: [hq][gather lists][logits B x (E+1)][ids B x k]
+// [weights B x k][shared_w B][counter]
 struct MoeWsLayout {
-  size_t hq, logits, ids, weights, shared_w, total;
+  size_t hq, gather, logits, ids, weights, shared_w, counter, total;
 };
 MMV_HD MoeWsLayout moe_ws_layout(int E, int I, int k, int B, bool has_shared) {
   MoeWsLayout l;
   const int P = B * k + (has_shared ? B : 0);
   l.hq = 0;
-  l.logits = align_up(hq_bytes(P, I), kWsAlign);
+  l.gather = align_up(hq_bytes(P, I), kWsAlign);
+  l.logits = align_up(l.gather + (size_t)4 * (3 * B * k + 2), kWsAlign);
   l.ids = align_up(l.logits + (size_t)4 * B * (E + 1), kWsAlign);
   l.weights = align_up(l.ids + (size_t)4 * B * k, kWsAlign);
   l.shared_w = align_up(l.weights + (size_t)4 * B * k, kWsAlign);
-  l.total = align_up(l.shared_w + (size_t)4 * B, kWsAlign);
+  l.counter = align_up(l.shared_w + (size_t)4 * B, kWsAlign);
+  l.total = align_up(l.counter + 4, kWsAlign);
   return l;
 }
 
@@ -44,5 +48,7 @@ MMV_HD size_t xstage_lds_bytes(int nrows, int K) {
   return (size_t)nrows * K + (size_t)8 * nrows * (K / 32);
 }
 constexpr size_t kMaxXStageLds = 64 * 1024;
+// the down kernel stages Q8_1(h) of all P pairs in LDS: P * I limit
+constexpr int kMaxDownStageElems = 49152;
 
 }  // namespace mmv

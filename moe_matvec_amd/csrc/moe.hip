@@ -4,54 +4,57 @@
 //
 // "Fourteen hours to 100 tokens per second" traces one decode token as
 // separate kernel classes (F32 router, top-k routing, mul_mat_id expert
-// matvecs, quantize_q8_1, broadcast glue) and removes glue by fusion: the
-// top-k kernel writes ids and weights directly, silu(gate)*up is quantized
-// to Q8 in the producing kernel, and the K <= 512 down projection uses four
-// rows per wave.  "Flash-Next on Strix Halo" (Expert GEMMs) builds
+// matvecs, quantize_q8_1, broadcast glue), finds that kernels below five
+// microseconds cost more to launch than to run, and removes glue by fusion:
+// the top-k kernel writes ids and weights directly, silu(gate)*up is
+// quantized to Q8 in the producing kernel, the K <= 512 down projection uses
+// four rows per wave.  "Flash-Next on Strix Halo" (Expert GEMMs) builds
 // per-expert row lists so each expert's weights are read once for all rows
-// that chose it.  Here, on gfx950:
-//  - router: one wave per router row, 128-bit fp32 loads, fp32 sums;
-//  - top-k: one wave per token row; order-preserving 64-bit keys
-//    (value, ~index) make equal logits rank by lower index; the weights are
-//    exp(l - l_max) over the selected k, renormalised (the softmax
-//    denominator over all E cancels);
-//  - every expert workgroup rebuilds the row lists of the B*k (row, slot)
-//    pairs in LDS from ids (<= 128 entries), so routing stays on the device
-//    and the launch sequence can be captured in a HIP graph;
-//  - gate/up: a workgroup owns 32 consecutive rows of one expert's gate and
-//    up, so silu(g)*u of those rows forms exactly one Q8_1 block of the
-//    down projection's input, quantized in the epilogue;
-//  - down: each output row is owned by one 16-lane group that walks the
-//    unique experts in ascending id, then the shared expert, accumulating
-//    per-row partials in a fixed order; no atomics, one store per output.
+// that chose it.  Here, on gfx950, one layer is three launches:
+//  K1 router rows (one wave per row, all loads issued up front) and, in the
+//     same grid, the shared expert's gate/up tiles (they do not depend on
+//     routing); the last router workgroup to finish (atomic ticket) runs
+//     top-k: order-preserving 64-bit keys (value, ~index) so equal logits
+//     rank by lower index, DPP wave maxima, weights exp(l - l_max)
+//     renormalised over the selected k (the full-E denominator cancels);
+//  K2 routed gate/up: a workgroup owns 32 rows of one unique expert's gate
+//     and up (16 lanes per row, every weight load issued before x is staged
+//     as Q8_1 in LDS), silu(g)*u in registers, and the tile's 32 h values
+//     are exactly one Q8_1 block of the down input, quantized in the
+//     epilogue; the per-expert row lists are rebuilt in LDS from ids;
+//  K3 down + combine: a workgroup owns 4 output rows (16 lanes per row, one
+//     Q4_0 block per lane at I = 512); its 4 waves split the experts by
+//     expert id mod 4, each walking its experts in ascending id (the shared
+//     expert last, in wave 0), and the 4 wave partials are added in wave
+//     order: every row's sum has the same order whatever the other rows
+//     chose, no atomics, one store per output.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "launch.hpp"
+#include "layout.hpp"
 #include "q4_0.hpp"
 #include "q8_1.hpp"
-#include "layout.hpp"
 
 namespace mmv {
 
 constexpr int kMaxPairs = MMV_MAX_BATCH * MMV_MAX_TOPK;  // 128
 
 // ---------------------------------------------------------------------------
-// router logits: logits[b*(E+1) + e], e in [0, E] (row E = shared gate row)
+// router rows: logits[b * ldl + e] = R[e] . x_b (row E = shared gate row)
 // ---------------------------------------------------------------------------
-template <int B>
-__global__ __launch_bounds__(64) void k_router(const float *__restrict__ R, int E, int H,
-                                               const float *__restrict__ shg,
-                                               const float *__restrict__ X, int64_t ldx,
-                                               float *__restrict__ logits) {
-  const int e = blockIdx.x;
-  const float *row = e < E ? R + (int64_t)e * H : shg;
-  const int lane = threadIdx.x;
+// HC = H / 256 float4 chunks per lane (compile time: every load issued up
+// front), or 0 for any H % 4 == 0 (runtime loop).
+template <int B, int HC>
+__device__ __forceinline__ void router_row(const float *__restrict__ row, int H,
+                                           const float *__restrict__ X, int64_t ldx,
+                                           float *__restrict__ out, int64_t ldl) {
+  const int lane = threadIdx.x & 63;
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-  const int nc = H >> 2;
-#pragma unroll 4
-  for (int c = lane; c < nc; c += 64) {
-    const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row) + c);
+  auto step = [&](const f32x4 r, int c) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const f32x4 x = load_f4(X + (int64_t)b * ldx + 4 * c);
@@ -60,16 +63,27 @@ __global__ __launch_bounds__(64) void k_router(const float *__restrict__ R, int 
       acc[b] = fmaf(r.z, x.z, acc[b]);
       acc[b] = fmaf(r.w, x.w, acc[b]);
     }
+  };
+  if constexpr (HC > 0) {
+    f32x4 r[HC];
+#pragma unroll
+    for (int i = 0; i < HC; ++i)
+      r[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row) + lane + 64 * i);
+#pragma unroll
+    for (int i = 0; i < HC; ++i) step(r[i], lane + 64 * i);
+  } else {
+    for (int c = lane; c < (H >> 2); c += 64)
+      step(__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row) + c), c);
   }
 #pragma unroll
   for (int b = 0; b < B; ++b) {
-    const float v = group_sum<64>(acc[b]);
-    if (lane == 0) logits[(int64_t)b * (E + 1) + e] = v;
+    const float v = wave_sum(acc[b]);
+    if (lane == 0) out[(int64_t)b * ldl] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-// top-k + renormalised weights: one wave per token row
+// top-k of one row by one wave
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t topk_key(float v, int e) {
   v = v + 0.0f;  // -0 and +0 compare equal: map both to +0
@@ -78,53 +92,108 @@ __device__ __forceinline__ uint64_t topk_key(float v, int e) {
   return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+// Selects the k largest of l[0..E) (ties: lower index first), writes ids,
+// renormalised weights and the shared weight.  Whole wave, uniform control.
+// KPL = keys per lane (E <= 64 * KPL).  All loads are unconditional (clamped
+// in bounds) so they are in flight together.
+template <int KPL>
+__device__ void topk_row(const float *__restrict__ l, int E, int k, int has_shared,
+                         int32_t *__restrict__ ids, float *__restrict__ weights,
+                         float *__restrict__ shared_w) {
+  const int lane = threadIdx.x & 63;
+  float v[KPL];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t oh = __shfl_xor(hi, m, kWave), ol = __shfl_xor(lo, m, kWave);
-    if (oh > hi || (oh == hi && ol > lo)) { hi = oh; lo = ol; }
+  for (int i = 0; i < KPL; ++i) v[i] = l[min(lane + 64 * i, E - 1)];
+  const float lsh = has_shared ? l[E] : 0.0f;
+  uint64_t key[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? topk_key(v[i], e) : 0ull;  // 0 never wins: real keys are > 0
   }
-  return ((uint64_t)hi << 32) | lo;
+  int my_id = 0;
+  float my_l = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < KPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(~(uint32_t)best);
+    float le = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const bool hit = (lane + 64 * i) == e;
+      key[i] = hit ? 0ull : key[i];
+      le = hit ? v[i] : le;
+    }
+    const float lsel = __shfl(le, e & 63, kWave);  // the owner lane's logit
+    if (lane == j) { my_id = e; my_l = lsel; }
+  }
+  const float lmax = __shfl(my_l, 0, kWave);  // slot 0 holds the largest
+  const float ex = lane < k ? expf(my_l - lmax) : 0.0f;
+  const float den = row16_sum(ex);            // k <= 16: lanes 0..15
+  if (lane < k) {
+    ids[lane] = my_id;
+    weights[lane] = ex / den;
+  }
+  if (lane == 0 && shared_w) *shared_w = has_shared ? 1.0f / (1.0f + expf(-lsh)) : 1.0f;
 }
 
-constexpr int kKeysPerLane = MMV_MAX_EXPERTS / 64;  // 16
+template <int KPL>
+__device__ __forceinline__ void topk_rows(const float *__restrict__ L, int64_t ldl, int E, int B,
+                                          int k, int has_shared, int32_t *__restrict__ ids,
+                                          float *__restrict__ weights,
+                                          float *__restrict__ shared_w) {
+  for (int b = threadIdx.x >> 6; b < B; b += 4)
+    topk_row<KPL>(L + (int64_t)b * ldl, E, k, has_shared, ids + (int64_t)b * k,
+                  weights + (int64_t)b * k, shared_w ? shared_w + b : nullptr);
+}
 
-__global__ __launch_bounds__(512) void k_topk(const float *__restrict__ L, int64_t ldl, int E,
+// dispatch on the number of experts (keys per lane)
+__device__ __forceinline__ void topk_any(const float *__restrict__ L, int64_t ldl, int E, int B,
+                                         int k, int has_shared, int32_t *__restrict__ ids,
+                                         float *__restrict__ weights,
+                                         float *__restrict__ shared_w) {
+  if (E <= 64) topk_rows<1>(L, ldl, E, B, k, has_shared, ids, weights, shared_w);
+  else if (E <= 256) topk_rows<4>(L, ldl, E, B, k, has_shared, ids, weights, shared_w);
+  else if (E <= 512) topk_rows<8>(L, ldl, E, B, k, has_shared, ids, weights, shared_w);
+  else topk_rows<16>(L, ldl, E, B, k, has_shared, ids, weights, shared_w);
+}
+
+// ---------------------------------------------------------------------------
+// moe_route_topk: router kernel (4 rows per workgroup) + one top-k workgroup
+// ---------------------------------------------------------------------------
+template <int B, int HC>
+__global__ __launch_bounds__(256) void k_router(const float *__restrict__ R, int E, int H,
+                                                const float *__restrict__ shg,
+                                                const float *__restrict__ X, int64_t ldx,
+                                                float *__restrict__ logits) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rows = E + (shg ? 1 : 0);
+  if (e >= rows) return;
+  const float *row = e < E ? R + (int64_t)e * H : shg;
+  router_row<B, HC>(row, H, X, ldx, logits + e, E + 1);
+}
+
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int64_t ldl, int E,
                                               int B, int k, int has_shared,
                                               int32_t *__restrict__ ids,
                                               float *__restrict__ weights,
                                               float *__restrict__ shared_w) {
-  const int b = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (b >= B) return;
-  const float *l = L + (int64_t)b * ldl;
-  uint64_t key[kKeysPerLane];
-#pragma unroll
-  for (int i = 0; i < kKeysPerLane; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? topk_key(l[e], e) : 0ull;  // 0 never wins: real keys are > 0
+  topk_any(L, ldl, E, B, k, has_shared, ids, weights, shared_w);
+}
+
+template <int B>
+static void launch_router(const float *router, int E, int H, const float *shg, const float *X,
+                          int64_t ldx, float *logits, hipStream_t s) {
+  const int rows = E + (shg ? 1 : 0);
+  const dim3 grid((rows + 3) / 4), block(256);
+  switch (H) {
+    case 1024: hipLaunchKernelGGL((k_router<B, 4>), grid, block, 0, s, router, E, H, shg, X, ldx, logits); break;
+    case 2048: hipLaunchKernelGGL((k_router<B, 8>), grid, block, 0, s, router, E, H, shg, X, ldx, logits); break;
+    case 4096: hipLaunchKernelGGL((k_router<B, 16>), grid, block, 0, s, router, E, H, shg, X, ldx, logits); break;
+    default: hipLaunchKernelGGL((k_router<B, 0>), grid, block, 0, s, router, E, H, shg, X, ldx, logits); break;
   }
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(~(uint32_t)best);
-#pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i)
-      if (lane + 64 * i == e) key[i] = 0ull;
-    if (lane == j) my_id = e;
-  }
-  const float lmax = l[__shfl(my_id, 0, kWave)];
-  const float ex = lane < k ? expf(l[my_id] - lmax) : 0.0f;
-  const float den = group_sum<16>(ex);  // k <= 16: lanes 0..15
-  if (lane < k) {
-    ids[(int64_t)b * k + lane] = my_id;
-    weights[(int64_t)b * k + lane] = ex / den;
-  }
-  if (lane == 0 && shared_w)
-    shared_w[b] = has_shared ? 1.0f / (1.0f + expf(-l[E])) : 1.0f;
 }
 
 hipError_t run_moe_route(const float *router, int E, int H, const float *X, int64_t ldx,
@@ -133,25 +202,27 @@ hipError_t run_moe_route(const float *router, int E, int H, const float *X, int6
   const float *L = X;
   int64_t ldl = ldx;
   if (router) {
-    const int rows = E + (shg ? 1 : 0);
     switch (B) {
-#define MMV_ROUTER_CASE(BB) \
-  case BB: hipLaunchKernelGGL(k_router<BB>, dim3(rows), dim3(64), 0, s, router, E, H, shg, X, ldx, logits); break;
-      MMV_ROUTER_CASE(1) MMV_ROUTER_CASE(2) MMV_ROUTER_CASE(3) MMV_ROUTER_CASE(4)
-      MMV_ROUTER_CASE(5) MMV_ROUTER_CASE(6) MMV_ROUTER_CASE(7) MMV_ROUTER_CASE(8)
-#undef MMV_ROUTER_CASE
+      case 1: launch_router<1>(router, E, H, shg, X, ldx, logits, s); break;
+      case 2: launch_router<2>(router, E, H, shg, X, ldx, logits, s); break;
+      case 3: launch_router<3>(router, E, H, shg, X, ldx, logits, s); break;
+      case 4: launch_router<4>(router, E, H, shg, X, ldx, logits, s); break;
+      case 5: launch_router<5>(router, E, H, shg, X, ldx, logits, s); break;
+      case 6: launch_router<6>(router, E, H, shg, X, ldx, logits, s); break;
+      case 7: launch_router<7>(router, E, H, shg, X, ldx, logits, s); break;
+      case 8: launch_router<8>(router, E, H, shg, X, ldx, logits, s); break;
       default: return hipErrorInvalidValue;
     }
     L = logits;
     ldl = E + 1;
   }
-  hipLaunchKernelGGL(k_topk, dim3(1), dim3(64 * B), 0, s, L, ldl, E, B, k,
+  hipLaunchKernelGGL(k_topk, dim3(1), dim3(256), 0, s, L, ldl, E, B, k,
                      (router && shg) ? 1 : 0, ids, weights, shared_w);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// per-expert row lists, rebuilt in LDS by every expert workgroup
+// per-expert row lists, rebuilt in LDS by every routed expert workgroup
 // ---------------------------------------------------------------------------
 struct GatherLds {
   int sid[kMaxPairs];      // ids, or -1 for an id outside [0, E)
@@ -199,17 +270,20 @@ __device__ void build_gather(const int32_t *__restrict__ ids, int Bk, int E, Gat
   __syncthreads();
 }
 
-// Workspace view: Q8_1 of h for P pairs (planar), then integer code sums.
+// Workspace views: Q8_1 of h for P pairs (planar), then per block the
+// internal {fp32 d, integer code sum} record; the gather lists K2 publishes
+// for K3 (U, unique[Bk], offsets[Bk+1], pairs[Bk]) follow in their region.
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 struct HqView {
   uint8_t *codes;    // [P][I]
-  uint16_t *ds;      // [P][I/32][2]
-  int *qsum;         // [P][I/32]
+  uint16_t *ds;      // [P][I/32][2]  fp16 {d, s}
+  i32x2 *dq;         // [P][I/32]     {fp32 bits of d, sum of codes}
 };
 __device__ inline HqView hq_view(uint8_t *base, int P, int I) {
   HqView v;
   v.codes = base;
   v.ds = reinterpret_cast<uint16_t *>(base + (size_t)P * I);
-  v.qsum = reinterpret_cast<int *>(base + (size_t)P * I + (size_t)4 * P * (I / 32));
+  v.dq = reinterpret_cast<i32x2 *>(base + (size_t)P * I + (size_t)4 * P * (I / 32));
   return v;
 }
 
@@ -223,90 +297,71 @@ struct MoeArgs {
   float *Y;
   int64_t ldy;
   uint8_t *hq;
+  int32_t *gather;   // published row lists (workspace)
   int P;             // pairs: B*k (+ B with a shared expert)
+  int routed_shared; // 1: K2 also runs the shared expert's gate/up tiles
   mmv_moe_debug dbg;
   int has_dbg;
+  // fused routing (K1)
+  float *logits;     // B x (E+1)
+  int32_t *counter;  // zero before the launch; K1's last workgroup re-zeroes it
+  int32_t *ids_out;
+  float *weights_out;
+  float *shared_w_out;
+  int router_wgs;
+  int topk_in_k2;    // 1: every K2 workgroup runs top-k on the logits itself
 };
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------------------
-// gate/up + SiLU + Q8_1 epilogue.  grid = (B*k + shared) slots x (I/32) tiles.
-// 4 waves; wave w owns rows 8w..8w+7 of the tile in both gate and up;
-// 16 lanes per row (4 rows per pass), passes: gate lo/hi, up lo/hi.
+// one gate/up tile: 32 rows of gate and of up, for nr activation rows
 // ---------------------------------------------------------------------------
-template <int B>
-__global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
-  __shared__ GatherLds g;
-  __shared__ int rowmap[MMV_MAX_BATCH];
-  __shared__ int pairmap[MMV_MAX_BATCH];
-  __shared__ float hbuf[MMV_MAX_BATCH][32];
-  extern __shared__ __align__(16) uint8_t smem[];
-
-  const mmv_moe_layer &L = a.L;
-  const int k = L.top_k, H = L.hidden, I = L.inter;
-  const int Bk = B * k;
-  const int ntiles = I >> 5;
-  const int slot = blockIdx.x / ntiles, tile = blockIdx.x - slot * ntiles;
-  const bool has_sh = L.sh_gate_qs != nullptr;
-
-  build_gather(a.ids, Bk, L.n_experts, g);
-  if (blockIdx.x == 0 && a.has_dbg) {
-    const int t = threadIdx.x;
-    if (a.dbg.unique && t < g.U) a.dbg.unique[t] = g.unique[t];
-    if (a.dbg.offsets && t <= g.U) a.dbg.offsets[t] = g.offsets[t];
-    if (a.dbg.pairs && t < g.offsets[g.U]) a.dbg.pairs[t] = g.pairs[t];
-    if (a.dbg.n_unique && t == 0) a.dbg.n_unique[0] = g.U;
-  }
-  const bool shared_slot = has_sh && slot == Bk;
-  if (!shared_slot && slot >= g.U) return;  // uniform over the workgroup
-
-  const int nbh = H >> 5;
-  const uint8_t *gq, *uq;
-  const uint16_t *gd, *ud;
-  int nr;
-  if (shared_slot) {
-    gq = L.sh_gate_qs; gd = L.sh_gate_d; uq = L.sh_up_qs; ud = L.sh_up_d;
-    nr = B;
-  } else {
-    const int64_t e = g.unique[slot];
-    const int64_t eo = e * I * nbh;
-    gq = L.gate_qs + eo * 16; gd = L.gate_d + eo;
-    uq = L.up_qs + eo * 16; ud = L.up_d + eo;
-    // an expert appears at most once per row when ids are valid (distinct
-    // within a row); the clamp keeps duplicated ids memory-safe
-    nr = min(g.offsets[slot + 1] - g.offsets[slot], B);
-  }
-  if (threadIdx.x < (unsigned)nr) {
-    const int r = threadIdx.x;
-    const int p = shared_slot ? Bk + r : g.pairs[g.offsets[slot] + r];
-    pairmap[r] = p;
-    rowmap[r] = shared_slot ? r : p / k;
-  }
-
+// 4 waves; wave w owns rows 8w..8w+7 of the tile in gate and in up; 16 lanes
+// per row, 4 rows per pass; passes: gate rows 0-3, 4-7, up rows 0-3, 4-7, so
+// gate row n and up row n land in the same lane group.  T = H / 512 blocks per
+// lane per row (compile time: all 4*T weight loads issued before x is
+// staged), or 0 for a runtime loop over any H % 32 == 0.
+// rowmap / pairmap (LDS) must be written before the call; the call begins
+// with the barrier that publishes them.
+template <int B, int T>
+__device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq,
+                                             const uint16_t *gd, const uint8_t *uq,
+                                             const uint16_t *ud, int tile, int nr,
+                                             const int *rowmap, const int *pairmap,
+                                             uint8_t *smem, float (*hbuf)[32]) {
+  const int H = a.L.hidden, I = a.L.inter, nbh = H >> 5, ntiles = I >> 5;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int sub = lane & 15, q = lane >> 4;
-  // pass p: 0,1 gate rows (4p + q), 2,3 up rows (4(p-2) + q) of this wave's 8
   int64_t rowoff[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int n = tile * 32 + 8 * wv + 4 * (p & 1) + q;
-    rowoff[p] = (int64_t)n * nbh;
-  }
-  // first weight blocks in flight before staging x
-  u32x4 w0[4];
-  float d0[4];
-  const int j0 = sub < nbh ? sub : 0;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint8_t *wq = p < 2 ? gq : uq;
-    const uint16_t *wd = p < 2 ? gd : ud;
-    w0[p] = load_stream16(wq + (rowoff[p] + j0) * 16);
-    d0[p] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j0));
-  }
+  for (int p = 0; p < 4; ++p) rowoff[p] = (int64_t)(tile * 32 + 8 * wv + 4 * (p & 1) + q) * nbh;
+
+  constexpr int TT = T > 0 ? T : 1;
+  // activations first (loads complete in issue order), then the weights
+  // tasks of 4 values: nr * H / 4 <= B * 128 * T over 256 threads
+  constexpr int MAXT = T > 0 ? (B * T + 1) / 2 : 1;
+  XPre<MAXT> xp;
   __syncthreads();  // rowmap / pairmap visible
+  if constexpr (T > 0) xpre_load(a.X, a.ldx, rowmap, nr, H, xp);
+  u32x4 w[4][TT];
+  float dw[4][TT];
+  if constexpr (T > 0) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int j = sub + 16 * t;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint8_t *wq = p < 2 ? gq : uq;
+        const uint16_t *wd = p < 2 ? gd : ud;
+        w[p][t] = load_stream16(wq + (rowoff[p] + j) * 16);
+        dw[p][t] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
+      }
+    }
+  }
   const XStage st = xstage_at(smem, B, H);
-  stage_quantize(a.X, a.ldx, rowmap, nr, H, st);
+  if constexpr (T > 0) xpre_quantize(xp, nr, H, st);
+  else stage_quantize(a.X, a.ldx, rowmap, nr, H, st);
   __syncthreads();
 
   float acc[4][B];
@@ -314,22 +369,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
   for (int p = 0; p < 4; ++p)
 #pragma unroll
     for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
-
-  for (int j = sub; j < nbh; j += 16) {
-    u32x4 w[4];
-    float dw[4];
-    if (j == sub) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) { w[p] = w0[p]; dw[p] = d0[p]; }
-    } else {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint8_t *wq = p < 2 ? gq : uq;
-        const uint16_t *wd = p < 2 ? gd : ud;
-        w[p] = load_stream16(wq + (rowoff[p] + j) * 16);
-        dw[p] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
-      }
-    }
+  auto block = [&](const u32x4 (&wb)[4], const float (&db)[4], int j) {
 #pragma unroll
     for (int r = 0; r < B; ++r) {
       if (r < nr) {
@@ -340,10 +380,33 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
         const float dx = st.d[r * nbh + j];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const int Iv = q4_block_isum(w[p], xa, xb, xs);
-          acc[p][r] = fmaf(dw[p] * dx, (float)Iv, acc[p][r]);
+          const int Iv = q4_block_isum(wb[p], xa, xb, xs);
+          acc[p][r] = fmaf(db[p] * dx, (float)Iv, acc[p][r]);
         }
       }
+    }
+  };
+  if constexpr (T > 0) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      u32x4 wb[4];
+      float db[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) { wb[p] = w[p][t]; db[p] = dw[p][t]; }
+      block(wb, db, sub + 16 * t);
+    }
+  } else {
+    for (int j = sub; j < nbh; j += 16) {
+      u32x4 wb[4];
+      float db[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint8_t *wq = p < 2 ? gq : uq;
+        const uint16_t *wd = p < 2 ? gd : ud;
+        wb[p] = load_stream16(wq + (rowoff[p] + j) * 16);
+        db[p] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
+      }
+      block(wb, db, j);
     }
   }
 
@@ -352,8 +415,8 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     if (r < nr) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const float gv = group_sum<16>(acc[hh][r]);
-        const float uv = group_sum<16>(acc[2 + hh][r]);
+        const float gv = row16_sum(acc[hh][r]);
+        const float uv = row16_sum(acc[2 + hh][r]);
         const float h = silu_f(gv) * uv;
         const int nl = 8 * wv + 4 * hh + q;
         if (sub == 0) {
@@ -377,106 +440,327 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
       const size_t bi = (size_t)p * ntiles + tile;
       hv.ds[bi * 2 + 0] = qb.d16;
       hv.ds[bi * 2 + 1] = qb.s16;
-      hv.qsum[bi] = qb.qsum;
+      hv.dq[bi] = i32x2{(int32_t)__float_as_uint(f16_bits_to_f32(qb.d16)), qb.qsum};
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// down + weighted combine + shared expert.  128 threads = 2 waves, a 16-lane
-// group owns one output row (8 rows per workgroup); lane s reads blocks
-// s, s+16, ... of the I/32 blocks of the row for each expert.
+// K2: routed gate/up.  grid = (B*k [+1 shared]) slots x (I/32) tiles.
 // ---------------------------------------------------------------------------
-constexpr int kDownThreads = 128;
-constexpr int kDownRows = kDownThreads / 16;
-
-template <int B>
-__global__ __launch_bounds__(kDownThreads) void k_moe_down(MoeArgs a) {
+template <int B, int T>
+__global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
   __shared__ GatherLds g;
-  __shared__ float pw[kMaxPairs + MMV_MAX_BATCH];
+  __shared__ int rowmap[MMV_MAX_BATCH];
+  __shared__ int pairmap[MMV_MAX_BATCH];
+  __shared__ float hbuf[MMV_MAX_BATCH][32];
+  extern __shared__ __align__(16) uint8_t smem[];
+
+  __shared__ int s_ids[kMaxPairs];
+  __shared__ float s_w[kMaxPairs];
+  __shared__ float s_sw[MMV_MAX_BATCH];
 
   const mmv_moe_layer &L = a.L;
   const int k = L.top_k, H = L.hidden, I = L.inter;
   const int Bk = B * k;
+  const int ntiles = I >> 5;
+  const int slot = blockIdx.x / ntiles, tile = blockIdx.x - slot * ntiles;
+
+  const int32_t *ids = a.ids;
+  if (a.topk_in_k2) {
+    // routing from the logits K1 wrote; block 0 publishes it for K3
+    const int E = L.n_experts;
+    topk_any(a.logits, E + 1, E, B, k, L.shared_gate_row ? 1 : 0, s_ids, s_w, s_sw);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      const int t = threadIdx.x;
+      if (t < Bk) { a.ids_out[t] = s_ids[t]; a.weights_out[t] = s_w[t]; }
+      if (t < B) a.shared_w_out[t] = s_sw[t];
+    }
+    ids = s_ids;
+  }
+  build_gather(ids, Bk, L.n_experts, g);
+  if (blockIdx.x == 0) {
+    // publish the row lists for the down kernel (and the debug copies)
+    const int t = threadIdx.x;
+    int32_t *gl = a.gather;
+    if (t == 0) gl[0] = g.U;
+    if (t < g.U) gl[1 + t] = g.unique[t];
+    if (t <= g.U) gl[1 + Bk + t] = g.offsets[t];
+    if (t < g.offsets[g.U]) gl[2 + 2 * Bk + t] = g.pairs[t];
+    if (a.has_dbg) {
+      if (a.dbg.unique && t < g.U) a.dbg.unique[t] = g.unique[t];
+      if (a.dbg.offsets && t <= g.U) a.dbg.offsets[t] = g.offsets[t];
+      if (a.dbg.pairs && t < g.offsets[g.U]) a.dbg.pairs[t] = g.pairs[t];
+      if (a.dbg.n_unique && t == 0) a.dbg.n_unique[0] = g.U;
+    }
+  }
+  const bool shared_slot = a.routed_shared && slot == Bk;
+  if (!shared_slot && slot >= g.U) return;  // uniform over the workgroup
+
+  const int nbh = H >> 5;
+  const uint8_t *gq, *uq;
+  const uint16_t *gd, *ud;
+  int nr;
+  if (shared_slot) {
+    gq = L.sh_gate_qs; gd = L.sh_gate_d; uq = L.sh_up_qs; ud = L.sh_up_d;
+    nr = B;
+  } else {
+    const int64_t eo = (int64_t)g.unique[slot] * I * nbh;
+    gq = L.gate_qs + eo * 16; gd = L.gate_d + eo;
+    uq = L.up_qs + eo * 16; ud = L.up_d + eo;
+    // an expert appears at most once per row when ids are valid (distinct
+    // within a row); the clamp keeps duplicated ids memory-safe
+    nr = min(g.offsets[slot + 1] - g.offsets[slot], B);
+  }
+  if (threadIdx.x < (unsigned)nr) {
+    const int r = threadIdx.x;
+    const int p = shared_slot ? Bk + r : g.pairs[g.offsets[slot] + r];
+    pairmap[r] = p;
+    rowmap[r] = shared_slot ? r : p / k;
+  }
+  gate_up_tile<B, T>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf);
+}
+
+// ---------------------------------------------------------------------------
+// K1: router rows + shared expert gate/up tiles; last router workgroup: top-k
+// ---------------------------------------------------------------------------
+template <int B, int HC, int T>
+__global__ __launch_bounds__(256) void k_moe_route_fused(MoeArgs a) {
+  __shared__ int rowmap[MMV_MAX_BATCH];
+  __shared__ int pairmap[MMV_MAX_BATCH];
+  __shared__ float hbuf[MMV_MAX_BATCH][32];
+  __shared__ int is_last;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const mmv_moe_layer &L = a.L;
+  const int E = L.n_experts, H = L.hidden, k = L.top_k;
+  const bool has_sg = L.shared_gate_row != nullptr;
+
+  if ((int)blockIdx.x < a.router_wgs) {
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e < E + (has_sg ? 1 : 0)) {
+      const float *row = e < E ? L.router + (int64_t)e * H : L.shared_gate_row;
+      router_row<B, HC>(row, H, a.X, a.ldx, a.logits + e, E + 1);
+    }
+    if (a.topk_in_k2) return;  // the next kernel runs top-k
+    __threadfence();  // logits visible device-wide before the ticket
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = atomicAdd(a.counter, 1) == a.router_wgs - 1;
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    topk_any(a.logits, E + 1, E, B, k, has_sg ? 1 : 0, a.ids_out, a.weights_out,
+             a.shared_w_out);
+    if (threadIdx.x == 0) atomicExch(a.counter, 0);  // ready for the next launch
+    return;
+  }
+  // shared expert tile (routing-independent)
+  const int tile = blockIdx.x - a.router_wgs;
+  if (threadIdx.x < (unsigned)B) {
+    rowmap[threadIdx.x] = threadIdx.x;
+    pairmap[threadIdx.x] = B * k + threadIdx.x;
+  }
+  gate_up_tile<B, T>(a, L.sh_gate_qs, L.sh_gate_d, L.sh_up_qs, L.sh_up_d, tile, B, rowmap,
+                     pairmap, smem, hbuf);
+}
+
+// ---------------------------------------------------------------------------
+// K3: down + weighted combine + shared expert
+// ---------------------------------------------------------------------------
+// 256 threads = 4 waves; the workgroup owns 4 output rows (lane group q of
+// every wave = row 4*blockIdx + q).  Wave w takes the experts with id % 4 == w
+// (ascending), wave 0 also the shared expert last.  Q8_1(h) of every pair is
+// staged in LDS (codes, fp32 d, integer sums).  Every prologue load is issued
+// before the first wait; expert weights go in chunks of kDownCH experts whose
+// loads are unconditional (a chunk slot past the wave's list re-reads its
+// last expert and is not used).  TI = I / 512 blocks per lane per row
+// (compile time) or 0 (runtime loop over I % 32 == 0).
+constexpr int kDownCH = 4;
+constexpr int kDownStageChunks = kMaxDownStageElems / 16 / 256;  // 16-byte copies per thread
+constexpr int kDownStageBlocks = kMaxDownStageElems / 32 / 256 + 1;
+
+template <int B, int TI>
+__global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
+  __shared__ int s_unique[kMaxPairs];
+  __shared__ int s_off[kMaxPairs + 1];
+  __shared__ int s_pairs[kMaxPairs];
+  __shared__ int s_wl[4][kMaxPairs + 1];
+  __shared__ int s_wn[4];
+  __shared__ int s_U;
+  __shared__ float s_pw[kMaxPairs + MMV_MAX_BATCH];
+  __shared__ float part[4][4][B];
+  extern __shared__ __align__(16) uint8_t smem[];
+
+  const mmv_moe_layer &L = a.L;
+  const int k = L.top_k, H = L.hidden, I = L.inter;
+  const int Bk = B * k, P = a.P, nbi = I >> 5;
   const bool has_sh = L.sh_down_qs != nullptr;
-  build_gather(a.ids, Bk, L.n_experts, g);
-  for (int t = threadIdx.x; t < Bk + B; t += blockDim.x) {
-    float v;
-    if (t < Bk) v = a.weights[t];
-    else v = a.shared_w ? a.shared_w[t - Bk] : 1.0f;
-    pw[t] = v;
+  const int t = threadIdx.x;
+
+  // ---- prologue loads: row lists, pair weights, Q8_1(h) -- all in flight
+  const int gl_n = 3 * Bk + 2;
+  const int g0 = a.gather[min(t, gl_n - 1)];
+  const int g1 = a.gather[min(t + 256, gl_n - 1)];
+  const int pwi = min(t, Bk + B - 1);
+  const float pwv = pwi < Bk ? a.weights[pwi] : (a.shared_w ? a.shared_w[pwi - Bk] : 1.0f);
+  const HqView hv = hq_view(a.hq, P, I);
+  const int n16 = P * I / 16, nblk = P * nbi;
+  u32x4 cbuf[kDownStageChunks];
+  i32x2 dqbuf[kDownStageBlocks];
+#pragma unroll
+  for (int m = 0; m < kDownStageBlocks; ++m)  // 8-byte records, clamped in bounds
+    dqbuf[m] = hv.dq[min(t + 256 * m, nblk - 1)];
+#pragma unroll
+  for (int m = 0; m < kDownStageChunks; ++m)
+    if (m * 256 < n16) cbuf[m] = reinterpret_cast<const u32x4 *>(hv.codes)[min(t + 256 * m, n16 - 1)];
+  // keep every load above in flight before the first store below uses one
+  asm volatile("" ::: "memory");
+  // ---- LDS stores
+  // gather region: [0] U, [1, 1+Bk) unique, [1+Bk, 2+2Bk) offsets, [2+2Bk, 2+3Bk) pairs
+  auto put_gather = [&](int idx, int val) {
+    if (idx == 0) s_U = val;
+    else if (idx < 1 + Bk) s_unique[idx - 1] = val;
+    else if (idx >= 1 + Bk && idx < 2 + 2 * Bk) s_off[idx - 1 - Bk] = val;
+    else if (idx >= 2 + 2 * Bk && idx < gl_n) s_pairs[idx - 2 - 2 * Bk] = val;
+  };
+  put_gather(t, g0);
+  put_gather(t + 256, g1);
+  if (t < Bk + B) s_pw[t] = pwv;
+  const XStage hs = xstage_at(smem, P, I);
+#pragma unroll
+  for (int m = 0; m < kDownStageChunks; ++m)
+    if (t + 256 * m < n16) reinterpret_cast<u32x4 *>(hs.codes)[t + 256 * m] = cbuf[m];
+#pragma unroll
+  for (int m = 0; m < kDownStageBlocks; ++m) {
+    if (t + 256 * m < nblk) {
+      hs.d[t + 256 * m] = __uint_as_float((uint32_t)dqbuf[m].x);
+      hs.qsum[t + 256 * m] = dqbuf[m].y;
+    }
+  }
+  __syncthreads();
+  const int U = s_U;
+  // per-wave expert lists: class = id % 4, ascending; shared expert (index U)
+  // appended to wave 0
+  if (t < U) {
+    const int e = s_unique[t], cls = e & 3;
+    int rank = 0;
+    for (int u = 0; u < t; ++u) rank += (s_unique[u] & 3) == cls;
+    s_wl[cls][rank] = t;
+  }
+  if (t < 4) {
+    int n = 0;
+    for (int u = 0; u < U; ++u) n += (s_unique[u] & 3) == t;
+    if (t == 0 && has_sh) s_wl[0][n++] = U;
+    s_wn[t] = n;
   }
   __syncthreads();
 
-  const int nbi = I >> 5;
-  const int lane = threadIdx.x & 63, sub = lane & 15;
-  const int row = blockIdx.x * kDownRows + (threadIdx.x >> 4);
+  const int lane = t & 63, wv = t >> 6, sub = lane & 15, q = lane >> 4;
+  const int row = blockIdx.x * 4 + q;
   const int rowc = min(row, H - 1);
-  const HqView hv = hq_view(a.hq, a.P, I);
-  const int U = g.U;
-  const int Utot = U + (has_sh ? 1 : 0);
-
+  const int n = s_wn[wv];
+  const int *wl = s_wl[wv];
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
 
-  for (int j = sub; j < nbi; j += 16) {
-    for (int u0 = 0; u0 < Utot; u0 += 4) {
-      u32x4 w[4];
-      float dw[4];
+  auto expert_ptr = [&](int u, const uint8_t *&dq, const uint16_t *&dd) {
+    if (u < U) {
+      const int64_t eo = (int64_t)s_unique[u] * H * nbi;
+      dq = L.down_qs + eo * 16; dd = L.down_d + eo;
+    } else {
+      dq = L.sh_down_qs; dd = L.sh_down_d;
+    }
+  };
+  auto consume = [&](int u, const u32x4 wb, const float db, int j) {
+    const int pbeg = u < U ? s_off[u] : 0;
+    const int pend = u < U ? s_off[u + 1] : B;
+    for (int pi = pbeg; pi < pend; ++pi) {
+      const int p = u < U ? s_pairs[pi] : Bk + pi;
+      const int pb = u < U ? p / k : pi;
+      const int8_t *hc = hs.codes + (size_t)p * I + 32 * j;
+      const i32x4 xa = *reinterpret_cast<const i32x4 *>(hc);
+      const i32x4 xb = *reinterpret_cast<const i32x4 *>(hc + 16);
+      const int Iv = q4_block_isum(wb, xa, xb, hs.qsum[p * nbi + j]);
+      const float part_v = (db * hs.d[p * nbi + j]) * (float)Iv;
+      const float gw = s_pw[p];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int u = min(u0 + i, Utot - 1);
+      for (int b = 0; b < B; ++b)
+        if (b == pb) acc[b] = fmaf(gw, part_v, acc[b]);
+    }
+  };
+
+  if constexpr (TI > 0) {
+    for (int c0 = 0; c0 < n; c0 += kDownCH) {
+      u32x4 wbuf[kDownCH][TI];
+      float dbf[kDownCH][TI];
+#pragma unroll
+      for (int c = 0; c < kDownCH; ++c) {
         const uint8_t *dq;
         const uint16_t *dd;
-        if (u < U) {
-          const int64_t eo = (int64_t)g.unique[u] * H * nbi;
-          dq = L.down_qs + eo * 16; dd = L.down_d + eo;
-        } else {
-          dq = L.sh_down_qs; dd = L.sh_down_d;
+        expert_ptr(wl[min(c0 + c, n - 1)], dq, dd);
+#pragma unroll
+        for (int ti = 0; ti < TI; ++ti) {
+          const int64_t blk = (int64_t)rowc * nbi + sub + 16 * ti;
+          wbuf[c][ti] = load_stream16(dq + blk * 16);
+          dbf[c][ti] = f16_bits_to_f32(load_stream2(dd + blk));
         }
-        const int64_t blk = (int64_t)rowc * nbi + j;
-        w[i] = load_stream16(dq + blk * 16);
-        dw[i] = f16_bits_to_f32(load_stream2(dd + blk));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int u = u0 + i;
-        if (u < Utot) {
-          const int pbeg = u < U ? g.offsets[u] : 0;
-          const int pend = u < U ? g.offsets[u + 1] : B;
-          for (int pi = pbeg; pi < pend; ++pi) {
-            const int p = u < U ? g.pairs[pi] : Bk + pi;
-            const int pb = u < U ? p / k : pi;
-            const uint8_t *hc = hv.codes + (size_t)p * I + 32 * j;
-            const i32x4 xa = *reinterpret_cast<const i32x4 *>(hc);
-            const i32x4 xb = *reinterpret_cast<const i32x4 *>(hc + 16);
-            const size_t bi = (size_t)p * nbi + j;
-            const int xs = hv.qsum[bi];
-            const float dh = f16_bits_to_f32(hv.ds[bi * 2]);
-            const int Iv = q4_block_isum(w[i], xa, xb, xs);
-            const float part = (dw[i] * dh) * (float)Iv;
-            const float gw = pw[p];
+      for (int c = 0; c < kDownCH; ++c)
+        if (c0 + c < n)
 #pragma unroll
-            for (int b = 0; b < B; ++b)
-              if (b == pb) acc[b] = fmaf(gw, part, acc[b]);
-          }
-        }
+          for (int ti = 0; ti < TI; ++ti)
+            consume(wl[c0 + c], wbuf[c][ti], dbf[c][ti], sub + 16 * ti);
+    }
+  } else {
+    for (int c = 0; c < n; ++c) {
+      const uint8_t *dq;
+      const uint16_t *dd;
+      expert_ptr(wl[c], dq, dd);
+      for (int j = sub; j < nbi; j += 16) {
+        const int64_t blk = (int64_t)rowc * nbi + j;
+        consume(wl[c], load_stream16(dq + blk * 16), f16_bits_to_f32(load_stream2(dd + blk)), j);
       }
     }
   }
 
 #pragma unroll
   for (int b = 0; b < B; ++b) {
-    const float v = group_sum<16>(acc[b]);
-    if (sub == 0 && row < H) a.Y[(int64_t)b * a.ldy + row] = v;
+    const float v = row16_sum(acc[b]);
+    if (sub == 0) part[wv][q][b] = v;
+  }
+  __syncthreads();
+  if (t < 4 * B) {
+    const int qq = t / B, b = t - qq * B;
+    const float v = ((part[0][qq][b] + part[1][qq][b]) + part[2][qq][b]) + part[3][qq][b];
+    const int r = blockIdx.x * 4 + qq;
+    if (r < H) a.Y[(int64_t)b * a.ldy + r] = v;
   }
 }
 
-hipError_t run_moe_experts(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
-                           const int32_t *ids, const float *weights, const float *shared_w,
-                           float *Y, int64_t ldy, uint8_t *hq, const mmv_moe_debug *dbg,
-                           hipStream_t s) {
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+// MMV_MOE_TICKET=1: top-k by the last router workgroup (atomic ticket and
+// device-scope fences); =0: top-k in every gate/up workgroup; unset: by B.
+// Prints one line the first time it is read.  Returns 1, -1 or 0 (unset).
+int moe_ticket_knob() {
+  const char *v = getenv("MMV_MOE_TICKET");
+  if (!v || !*v) return 0;
+  static bool printed = false;
+  if (!printed) {
+    fprintf(stderr, "[moe_matvec] MMV_MOE_TICKET=%s\n", v);
+    printed = true;
+  }
+  return atoi(v) ? 1 : -1;
+}
+
+MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
+                  const int32_t *ids, const float *weights, const float *shared_w, float *Y,
+                  int64_t ldy, uint8_t *ws, const mmv_moe_debug *dbg) {
   MoeArgs a;
   a.L = L;
   a.X = X;
@@ -486,26 +770,119 @@ hipError_t run_moe_experts(const mmv_moe_layer &L, const float *X, int64_t ldx, 
   a.shared_w = shared_w;
   a.Y = Y;
   a.ldy = ldy;
-  a.hq = hq;
   const bool has_sh = L.sh_gate_qs != nullptr;
+  const MoeWsLayout lay = moe_ws_layout(L.n_experts, L.inter, L.top_k, B, has_sh);
+  a.hq = ws + lay.hq;
+  a.gather = reinterpret_cast<int32_t *>(ws + lay.gather);
   a.P = B * L.top_k + (has_sh ? B : 0);
+  a.routed_shared = has_sh ? 1 : 0;
   a.has_dbg = dbg != nullptr;
-  if (dbg) a.dbg = *dbg;
-  else a.dbg = mmv_moe_debug{nullptr, nullptr, nullptr, nullptr, nullptr};
+  a.dbg = dbg ? *dbg : mmv_moe_debug{nullptr, nullptr, nullptr, nullptr, nullptr};
+  a.logits = reinterpret_cast<float *>(ws + lay.logits);
+  a.counter = reinterpret_cast<int32_t *>(ws + lay.counter);
+  a.ids_out = nullptr;
+  a.weights_out = nullptr;
+  a.shared_w_out = nullptr;
+  a.router_wgs = 0;
+  a.topk_in_k2 = 0;
+  return a;
+}
 
-  const int slots = B * L.top_k + (has_sh ? 1 : 0);
-  const int ntiles = L.inter / 32;
-  const size_t lds = xstage_bytes(B, L.hidden);
-  const int down_blocks = (L.hidden + kDownRows - 1) / kDownRows;
+template <int B, int T>
+void launch_gate_up(const MoeArgs &a, hipStream_t s) {
+  const int slots = B * a.L.top_k + (a.routed_shared ? 1 : 0);
+  const int ntiles = a.L.inter / 32;
+  const size_t lds = xstage_bytes(B, a.L.hidden);
+  hipLaunchKernelGGL((k_moe_gate_up<B, T>), dim3(slots * ntiles), dim3(256), lds, s, a);
+}
+
+template <int B, int TI>
+void launch_down(const MoeArgs &a, hipStream_t s) {
+  const size_t lds = xstage_bytes(a.P, a.L.inter);
+  hipLaunchKernelGGL((k_moe_down<B, TI>), dim3((a.L.hidden + 3) / 4), dim3(256), lds, s, a);
+}
+
+template <int B, int HC, int T>
+void launch_route_fused(const MoeArgs &a, hipStream_t s) {
+  const int shared_tiles = a.L.sh_gate_qs ? a.L.inter / 32 : 0;
+  const size_t lds = xstage_bytes(B, a.L.hidden);
+  hipLaunchKernelGGL((k_moe_route_fused<B, HC, T>), dim3(a.router_wgs + shared_tiles),
+                     dim3(256), lds, s, a);
+}
+
+template <int B>
+void launch_experts(const MoeArgs &a, hipStream_t s) {
+  switch (a.L.hidden) {
+    case 512: launch_gate_up<B, 1>(a, s); break;
+    case 1024: launch_gate_up<B, 2>(a, s); break;
+    case 2048: launch_gate_up<B, 4>(a, s); break;
+    case 4096: launch_gate_up<B, 8>(a, s); break;
+    default: launch_gate_up<B, 0>(a, s); break;
+  }
+  switch (a.L.inter) {
+    case 512: launch_down<B, 1>(a, s); break;
+    case 1024: launch_down<B, 2>(a, s); break;
+    default: launch_down<B, 0>(a, s); break;
+  }
+}
+
+template <int B>
+void launch_route(const MoeArgs &a, hipStream_t s) {
+  switch (a.L.hidden) {
+    case 1024: launch_route_fused<B, 4, 2>(a, s); break;
+    case 2048: launch_route_fused<B, 8, 4>(a, s); break;
+    case 4096: launch_route_fused<B, 16, 8>(a, s); break;
+    default: launch_route_fused<B, 0, 0>(a, s); break;
+  }
+}
+
+}  // namespace
+
+hipError_t run_moe_experts(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
+                           const int32_t *ids, const float *weights, const float *shared_w,
+                           float *Y, int64_t ldy, uint8_t *ws, const mmv_moe_debug *dbg,
+                           hipStream_t s) {
+  const MoeArgs a = make_args(L, X, ldx, B, ids, weights, shared_w, Y, ldy, ws, dbg);
   switch (B) {
-#define MMV_MOE_CASE(BB)                                                                   \
-  case BB:                                                                                 \
-    hipLaunchKernelGGL(k_moe_gate_up<BB>, dim3(slots * ntiles), dim3(256), lds, s, a);     \
-    hipLaunchKernelGGL(k_moe_down<BB>, dim3(down_blocks), dim3(kDownThreads), 0, s, a);    \
+    case 1: launch_experts<1>(a, s); break;
+    case 2: launch_experts<2>(a, s); break;
+    case 3: launch_experts<3>(a, s); break;
+    case 4: launch_experts<4>(a, s); break;
+    case 5: launch_experts<5>(a, s); break;
+    case 6: launch_experts<6>(a, s); break;
+    case 7: launch_experts<7>(a, s); break;
+    case 8: launch_experts<8>(a, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
+                         int32_t *ids, float *weights, float *Y, int64_t ldy, uint8_t *ws,
+                         hipStream_t s) {
+  const bool has_sh = L.sh_gate_qs != nullptr;
+  const MoeWsLayout lay = moe_ws_layout(L.n_experts, L.inter, L.top_k, B, has_sh);
+  float *sw = reinterpret_cast<float *>(ws + lay.shared_w);
+  MoeArgs a = make_args(L, X, ldx, B, ids, weights, sw, Y, ldy, ws, nullptr);
+  a.ids_out = ids;
+  a.weights_out = weights;
+  a.shared_w_out = sw;
+  a.router_wgs = (L.n_experts + (L.shared_gate_row ? 1 : 0) + 3) / 4;
+  // top-k in every gate/up workgroup is cheapest for few rows; for more rows
+  // the ticket (one top-k, then device-scope fences) costs less
+  const int knob = moe_ticket_knob();
+  a.topk_in_k2 = knob > 0 ? 0 : (knob < 0 ? 1 : (B <= 2 ? 1 : 0));
+  // K1 already runs the shared expert's gate/up tiles
+  switch (B) {
+#define MMV_LAYER_CASE(BB)    \
+  case BB:                    \
+    launch_route<BB>(a, s);   \
+    a.routed_shared = 0;      \
+    launch_experts<BB>(a, s); \
     break;
-    MMV_MOE_CASE(1) MMV_MOE_CASE(2) MMV_MOE_CASE(3) MMV_MOE_CASE(4)
-    MMV_MOE_CASE(5) MMV_MOE_CASE(6) MMV_MOE_CASE(7) MMV_MOE_CASE(8)
-#undef MMV_MOE_CASE
+    MMV_LAYER_CASE(1) MMV_LAYER_CASE(2) MMV_LAYER_CASE(3) MMV_LAYER_CASE(4)
+    MMV_LAYER_CASE(5) MMV_LAYER_CASE(6) MMV_LAYER_CASE(7) MMV_LAYER_CASE(8)
+#undef MMV_LAYER_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

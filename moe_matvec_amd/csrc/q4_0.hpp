@@ -72,6 +72,50 @@ __device__ __forceinline__ void stage_quantize(const float *__restrict__ X, int6
   }
 }
 
+// Two-phase staging for callers that also prefetch weights: loads complete
+// in issue order, so the activation loads are issued first (xpre_load), the
+// weight loads next, and the quantization (xpre_quantize) then waits only
+// for the activations.  MAXT = tasks per thread (4 floats each) the caller
+// guarantees: nrows * K / 4 <= MAXT * blockDim.x.
+template <int MAXT>
+struct XPre {
+  f32x4 v[MAXT];
+};
+template <int MAXT>
+__device__ __forceinline__ void xpre_load(const float *__restrict__ X, int64_t ldx,
+                                          const int *rowmap, int nrows, int K, XPre<MAXT> &p) {
+  const int nb = K >> 5, total = nrows * nb * 8;
+#pragma unroll
+  for (int i = 0; i < MAXT; ++i) {
+    const int t = threadIdx.x + i * blockDim.x;
+    if (t < total) {
+      const int r = t / (nb * 8);
+      const int rem = t - r * nb * 8;
+      const int row = rowmap ? rowmap[r] : r;
+      p.v[i] = load_f4(X + (int64_t)row * ldx + 4 * rem);
+    }
+  }
+}
+template <int MAXT>
+__device__ __forceinline__ void xpre_quantize(const XPre<MAXT> &p, int nrows, int K, XStage st) {
+  const int nb = K >> 5, total = nrows * nb * 8;
+#pragma unroll
+  for (int i = 0; i < MAXT; ++i) {
+    const int t = threadIdx.x + i * blockDim.x;
+    if (t < total) {  // uniform over each 8-lane group: total % 8 == 0
+      const int r = t / (nb * 8);
+      const int rem = t - r * nb * 8;
+      const int j = rem >> 3, s = rem & 7;
+      const Q8Block q = q8_1_quantize8(p.v[i]);
+      *reinterpret_cast<uint32_t *>(st.codes + (size_t)r * K + 32 * j + 4 * s) = q.codes;
+      if (s == 0) {
+        st.d[r * nb + j] = f16_bits_to_f32(q.d16);
+        st.qsum[r * nb + j] = q.qsum;
+      }
+    }
+  }
+}
+
 // Copy rows of a planar Q8_1 buffer (B rows of K) into the stage.
 __device__ __forceinline__ void stage_copy_q8(const uint8_t *__restrict__ Xq, int B,
                                               int nrows, int K, XStage st) {
@@ -84,7 +128,7 @@ __device__ __forceinline__ void stage_copy_q8(const uint8_t *__restrict__ Xq, in
     const int j = rem >> 3, s = rem & 7;
     const uint32_t c = *reinterpret_cast<const uint32_t *>(Xq + (size_t)r * K + 32 * j + 4 * s);
     *reinterpret_cast<uint32_t *>(st.codes + (size_t)r * K + 32 * j + 4 * s) = c;
-    const int sum = group_sum_i<8>(sdot4((int)c, 0x01010101, 0));
+    const int sum = group8_sum_i(sdot4((int)c, 0x01010101, 0));
     if (s == 0) {
       st.d[r * nb + j] = f16_bits_to_f32(ds[((size_t)r * nb + j) * 2]);
       st.qsum[r * nb + j] = sum;

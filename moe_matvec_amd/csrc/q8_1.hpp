@@ -33,7 +33,7 @@ __device__ __forceinline__ int q8_code(float x, float id) {
 // holds values 4s .. 4s+3 of the block in v.  All 8 lanes must be active.
 __device__ __forceinline__ Q8Block q8_1_quantize8(f32x4 v) {
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  a = group_max<8>(a);
+  a = group8_max(a);
   const float d32 = a / 127.0f;
   const uint16_t d16 = f32_to_f16_bits(d32);
   const bool zero = (d16 & 0x7FFFu) == 0u;
@@ -43,7 +43,7 @@ __device__ __forceinline__ Q8Block q8_1_quantize8(f32x4 v) {
   Q8Block r;
   r.codes = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
             ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
-  r.qsum = group_sum_i<8>(q0 + q1 + q2 + q3);
+  r.qsum = group8_sum_i(q0 + q1 + q2 + q3);
   r.d16 = zero ? (uint16_t)0 : d16;
   r.s16 = zero ? (uint16_t)0 : f32_to_f16_bits(__fmul_rn(d32, (float)r.qsum));
   return r;

@@ -46,16 +46,51 @@ def test_bf16_integer_pin_bit_exact(mm, orc, dev):
 
 
 def test_bf16_batch_invariance_and_determinism(mm, dev):
+    # B = 1 runs fp32 FMAs on the VALU; B >= 2 runs the bf16 MFMA with x split
+    # into hi + lo.  Rows agree bit for bit among all B >= 2 calls, and with
+    # the B = 1 call within rounding.
     N, K = 3000, 2560
     W = synth.bf16_weights(N, K, 0, "inv", device=dev)
     X = synth.activations(8, K, 0, "inv", device=dev)
     y8 = mm.gemv_bf16(W, X)
-    y8b = mm.gemv_bf16(W, X)
-    assert torch.equal(y8, y8b)
+    assert torch.equal(y8, mm.gemv_bf16(W, X))
     for b in range(8):
-        assert torch.equal(mm.gemv_bf16(W, X[b].clone())[None], y8[b:b + 1])
-    for B in (2, 3, 4, 5):
+        pair = X[[b, (b + 3) % 8]].contiguous()
+        assert torch.equal(mm.gemv_bf16(W, pair)[0], y8[b])
+        y1 = mm.gemv_bf16(W, X[b].clone())
+        assert rel_l2_rows(npc(y1)[None], npc(y8[b])[None]) <= 1e-5
+    for B in (3, 4, 5, 6, 7):
         assert torch.equal(mm.gemv_bf16(W, X[:B].contiguous()), y8[:B])
+
+
+@pytest.mark.parametrize("knobs", [dict(MMV_BF16_R="1", MMV_BF16_WPB="1"),
+                                   dict(MMV_BF16_R="2", MMV_BF16_WPB="4"),
+                                   dict(MMV_BF16_R="4", MMV_BF16_WPB="1")])
+def test_bf16_b1_variants_identical(mm, dev, monkeypatch, knobs):
+    # every B = 1 variant (rows per wave, waves per workgroup) sums each row in
+    # the same order, so all give the same bits as the default choice
+    for N, K in ((1000, 2560), (2560, 9728), (333, 1016)):
+        W = synth.bf16_weights(N, K, 0, "var", N, K, device=dev)
+        x = synth.activations(1, K, 0, "var", N, K, device=dev)
+        y0 = mm.gemv_bf16(W, x)
+        for k, v in knobs.items():
+            monkeypatch.setenv(k, v)
+        y1 = mm.gemv_bf16(W, x)
+        for k in knobs:
+            monkeypatch.delenv(k)
+        assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("ks", ["4", "8", "16"])
+def test_bf16_mfma_split_variants(mm, orc, dev, monkeypatch, ks):
+    # the B >= 2 path with 4, 8 or 16 waves per 16-row tile
+    N, K, B = 100, 1016, 5
+    W = synth.bf16_weights(N, K, 0, "mfma", device=dev)
+    X = synth.activations(B, K, 0, "mfma", device=dev)
+    monkeypatch.setenv("MMV_BF16_WPB", ks)
+    y = mm.gemv_bf16(W, X)
+    monkeypatch.delenv("MMV_BF16_WPB")
+    assert rel_l2_rows(npc(y), orc.gemv_bf16(np16(W), npc(X))) <= BF16_TOL
 
 
 def test_bf16_leading_dimensions(mm, orc, dev):
@@ -149,3 +184,17 @@ def test_q4_0_batch_invariance(mm, dev):
     assert torch.equal(y8, mm.gemv_q4_0(W, x=X))
     for b in range(8):
         assert torch.equal(mm.gemv_q4_0(W, x=X[b:b + 1].clone()), y8[b:b + 1])
+
+
+@pytest.mark.parametrize("per_cu", ["1", "3", "16"])
+def test_q4_0_grid_variants_identical(mm, dev, monkeypatch, per_cu):
+    # the grid-stride walk over row groups does not change any row's sums
+    for N, K, B in ((4096, 4096, 1), (1100, 512, 8), (515, 2048, 3)):
+        W, _, _ = _q4(mm, N, K, dev, "grid")
+        X = synth.activations(B, K, 0, "q4grid", N, device=dev)
+        y0 = mm.gemv_q4_0(W, x=X)
+        monkeypatch.setenv("MMV_Q4_WG_PER_CU", per_cu)
+        y1 = mm.gemv_q4_0(W, x=X)
+        y2 = mm.gemv_q4_0(W, xq=mm.quantize_q8_1(X), B=B)
+        monkeypatch.delenv("MMV_Q4_WG_PER_CU")
+        assert torch.equal(y0, y1) and torch.equal(y0, y2)

@@ -84,9 +84,12 @@ def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
     assert rel_l2_rows(npc(y), y_ref) <= MOE_TOL
 
 
+@pytest.mark.parametrize("ticket", ["0", "1"])
 @pytest.mark.parametrize("E,H,I,k,B", [(256, 2048, 512, 8, 1), (512, 2048, 512, 10, 4),
-                                       (32, 512, 64, 4, 8)])
-def test_moe_layer_decode(mm, orc, dev, E, H, I, k, B):
+                                       (32, 512, 64, 4, 8), (20, 96, 64, 3, 2)])
+def test_moe_layer_decode(mm, orc, dev, monkeypatch, ticket, E, H, I, k, B):
+    # ticket "1": top-k by the last router workgroup; "0": in every gate/up workgroup
+    monkeypatch.setenv("MMV_MOE_TICKET", ticket)
     layer, ref = build_moe(mm, orc, E, H, I, k, 0, "dec", E, H, I, device=dev)
     X = synth.activations(B, H, 0, "dec", E, B, device=dev)
     ids = torch.empty((B, k), dtype=torch.int32, device=dev)
