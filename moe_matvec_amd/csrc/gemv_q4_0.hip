@@ -163,6 +163,85 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(
   }
 }
 
+// Whole-row variant: K = 32 * G * T exactly, so each lane owns T blocks of
+// each of its RP rows, and a workgroup owns one group of 4 * RP * (64 / G)
+// consecutive rows.  The activation loads are issued first, then all RP * T
+// weight loads of the group; the activation is quantized into LDS while the
+// weights are in flight (loads complete in issue order).  Per-row arithmetic
+// order is the same as in k_gemv_q4_0: block j's integer sum scaled by
+// d_w * d_x and accumulated over j = sub, sub + G, ..., then a G-lane sum.
+template <int B, int G, int RP, int T>
+__global__ __launch_bounds__(256) void k_gemv_q4_0_t(
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
+    const float *__restrict__ X, int64_t ldx, const uint8_t *__restrict__ Xq,
+    float *__restrict__ Y, int64_t ldy) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int RPP = 64 / G;
+  constexpr int ROWS_WAVE = RP * RPP;
+  constexpr int ROWS_WG = 4 * ROWS_WAVE;
+  const int nb = K >> 5;  // == G * T
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G, grp = lane / G;
+  const int wv = threadIdx.x >> 6;
+
+  constexpr int MAXT = XPRE_MAXT;
+  XPre<MAXT> xp;
+  const bool pre = X && (B * K <= MAXT * 4 * 256);
+  if (pre) xpre_load(X, ldx, nullptr, B, K, xp);
+
+  const int rbase = blockIdx.x * ROWS_WG + wv * ROWS_WAVE + grp;
+  u32x4 w[RP][T];
+  float d[RP][T];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int64_t rowblk = (int64_t)min(rbase + p * RPP, N - 1) * nb;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t blk = rowblk + sub + G * t;
+      w[p][t] = load_stream16(qs + blk * 16);
+      d[p][t] = f16_bits_to_f32(load_stream2(dw + blk));
+    }
+  }
+
+  const XStage st = xstage_at(smem, B, K);
+  if (pre) xpre_quantize(xp, B, K, st);
+  else if (X) stage_quantize(X, ldx, nullptr, B, K, st);
+  else stage_copy_q8(Xq, B, B, K, st);
+  __syncthreads();
+
+  float acc[RP][B];
+#pragma unroll
+  for (int p = 0; p < RP; ++p)
+#pragma unroll
+    for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int j = sub + G * t;
+#pragma unroll
+    for (int r = 0; r < B; ++r) {
+      const int8_t *xc = st.codes + (size_t)r * K + 32 * j;
+      const i32x4 xa = *reinterpret_cast<const i32x4 *>(xc);
+      const i32x4 xb = *reinterpret_cast<const i32x4 *>(xc + 16);
+      const int xs = st.qsum[r * nb + j];
+      const float dx = st.d[r * nb + j];
+#pragma unroll
+      for (int p = 0; p < RP; ++p) {
+        const int I = q4_block_isum(w[p][t], xa, xb, xs);
+        acc[p][r] = fmaf(d[p][t] * dx, (float)I, acc[p][r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int row = rbase + p * RPP;
+#pragma unroll
+    for (int r = 0; r < B; ++r) {
+      const float v = gsum<G>(acc[p][r]);
+      if (sub == 0 && row < N) Y[(int64_t)r * ldy + row] = v;
+    }
+  }
+}
+
 namespace {
 
 int cu_count() {
@@ -208,12 +287,58 @@ static hipError_t launch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
   return hipGetLastError();
 }
 
+template <int B, int G, int RP, int T>
+static hipError_t launch_q4_t(const uint8_t *qs, const uint16_t *d, int N, int K,
+                              const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
+                              int64_t ldy, hipStream_t s) {
+  constexpr int rows_wg = 4 * RP * (64 / G);
+  const int ngroups = (N + rows_wg - 1) / rows_wg;
+  const size_t lds = xstage_bytes(B, K);
+  hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T>), dim3(ngroups), dim3(256), lds, s, qs, d,
+                     N, K, X, ldx, Xq, Y, ldy);
+  return hipGetLastError();
+}
+
+// Rows per lane group: the fewest workgroups that still give every CU about
+// two, so each redundant activation quantization covers as many rows as it
+// can while the whole matrix is in flight at once.
+template <int B, int G, int T>
+static hipError_t launch_q4_rp(const uint8_t *qs, const uint16_t *d, int N, int K,
+                               const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
+                               int64_t ldy, hipStream_t s) {
+  int rp = q4_knob("MMV_Q4_RP");
+  if (rp == 0) {
+    const int target = 2 * cu_count();
+    const int per_rp = 4 * (64 / G);  // rows of a workgroup per unit of RP
+    rp = 2;
+    while (rp < 8 / T && (N + rp * per_rp - 1) / (rp * per_rp) > target) rp += 2;
+  }
+  // at most 8 weight loads per lane: RP * T <= 8
+  if constexpr (T <= 2)
+    if (rp > 2) {
+      if constexpr (T == 1) {
+        if (rp > 6) return launch_q4_t<B, G, 8, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+        if (rp > 4) return launch_q4_t<B, G, 6, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      }
+      return launch_q4_t<B, G, 4, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    }
+  return launch_q4_t<B, G, 2, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+}
+
 template <int B>
 static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
                               const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                               int64_t ldy, hipStream_t s) {
   const int nb = K / 32;
   constexpr int RP = B <= 2 ? 2 : 4;
+  // whole blocks per lane: every load of a row group in flight together
+  if (q4_knob("MMV_Q4_GENERIC") <= 0) {
+    if (nb == 16) return launch_q4_rp<B, 16, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    if (nb == 32) return launch_q4_rp<B, 32, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    if (nb == 64) return launch_q4_rp<B, 64, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    if (nb == 128) return launch_q4_rp<B, 64, 2>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    if (nb == 256) return launch_q4_rp<B, 64, 4>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  }
   if (nb <= 16) return launch_q4<B, 16, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   if (nb <= 32) return launch_q4<B, 32, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   return launch_q4<B, 64, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);

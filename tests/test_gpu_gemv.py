@@ -145,7 +145,7 @@ def _q4(mm, N, K, dev, *tags):
 
 @pytest.mark.parametrize("N,K,B", [
     (4096, 4096, 1), (1100, 4096, 8), (2048, 512, 1), (515, 512, 8),
-    (333, 2048, 3), (77, 96, 2), (64, 32, 1), (130, 1024, 6),
+    (333, 2048, 3), (77, 96, 2), (64, 32, 1), (130, 1024, 6), (700, 8192, 2),
 ])
 def test_q4_0_parity(mm, orc, dev, N, K, B):
     W, qs, d = _q4(mm, N, K, dev)
@@ -186,15 +186,24 @@ def test_q4_0_batch_invariance(mm, dev):
         assert torch.equal(mm.gemv_q4_0(W, x=X[b:b + 1].clone()), y8[b:b + 1])
 
 
-@pytest.mark.parametrize("per_cu", ["1", "3", "16"])
-def test_q4_0_grid_variants_identical(mm, dev, monkeypatch, per_cu):
-    # the grid-stride walk over row groups does not change any row's sums
-    for N, K, B in ((4096, 4096, 1), (1100, 512, 8), (515, 2048, 3)):
+@pytest.mark.parametrize("env", [
+    {"MMV_Q4_RP": "2"}, {"MMV_Q4_RP": "4"}, {"MMV_Q4_RP": "6"}, {"MMV_Q4_RP": "8"},
+    {"MMV_Q4_GENERIC": "1", "MMV_Q4_WG_PER_CU": "1"},
+    {"MMV_Q4_GENERIC": "1", "MMV_Q4_WG_PER_CU": "3"},
+    {"MMV_Q4_GENERIC": "1", "MMV_Q4_WG_PER_CU": "16"},
+])
+def test_q4_0_grid_variants_identical(mm, dev, monkeypatch, env):
+    # rows per workgroup, the whole-row kernel versus the grid-stride one:
+    # no row's sums change
+    for N, K, B in ((4096, 4096, 1), (1100, 512, 8), (515, 2048, 3), (300, 8192, 2),
+                    (2000, 1024, 1)):
         W, _, _ = _q4(mm, N, K, dev, "grid")
         X = synth.activations(B, K, 0, "q4grid", N, device=dev)
         y0 = mm.gemv_q4_0(W, x=X)
-        monkeypatch.setenv("MMV_Q4_WG_PER_CU", per_cu)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
         y1 = mm.gemv_q4_0(W, x=X)
         y2 = mm.gemv_q4_0(W, xq=mm.quantize_q8_1(X), B=B)
-        monkeypatch.delenv("MMV_Q4_WG_PER_CU")
+        for k in env:
+            monkeypatch.delenv(k)
         assert torch.equal(y0, y1) and torch.equal(y0, y2)
