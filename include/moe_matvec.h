@@ -130,8 +130,15 @@ int quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B,
  *    K <= 512 in "Eight levers that worked"]
  *   Y[b*ldy + n] = sum_j d_w[n][j] * d_x[b][j] * I[b][n][j],
  *   I[b][n][j] = sum_i (code_i - 8) * q_x[b][32j + i]  (exact int32).
- *   Exactly one of X (fp32 B x K, quantized on the fly, bit-identical to
- *   quantize_q8_1) and Xq (planar Q8_1 of B rows of K) must be non-NULL.
+ *   Activations, one of three ways (the codes are bit-identical in all):
+ *     X only:  fp32 B x K, quantized to Q8_1 inside every workgroup (one
+ *              launch; the better choice at B = 1);
+ *     Xq only: planar Q8_1 of B rows of K, read as given;
+ *     both:    X is first quantized into the caller's Xq buffer
+ *              (mmv_q8_1_bytes(K, B) bytes, an output, left holding
+ *              Q8_1(X)), then the product reads Xq (two launches; the
+ *              better choice at B >= 2, where repeating the quantization
+ *              in every workgroup costs more than the extra launch).
  *   B*K <= MMV_Q4_MAX_XK.  Y: B x N fp32, ldy >= N.
  * ------------------------------------------------------------------------ */
 int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,

@@ -189,10 +189,12 @@ def split_q8_1(buf: torch.Tensor, B: int, K: int):
 
 def gemv_q4_0(W: Q4_0, x: torch.Tensor | None = None, xq: torch.Tensor | None = None,
               B: int | None = None, out: torch.Tensor | None = None, stream=None):
-    """y = W (x) Q8_1(x); pass fp32 x [B, K] (quantized on the fly) or a planar
-    Q8_1 buffer xq with its row count B."""
-    if (x is None) == (xq is None):
-        raise ValueError("give exactly one of x and xq")
+    """y = W (x) Q8_1(x).  Pass fp32 x [B, K] (quantized inside the product),
+    or a planar Q8_1 buffer xq with its row count B, or both: then x is
+    quantized into xq (uint8, q8_1_bytes(K, B) bytes, overwritten) by a
+    separate pass and the product reads xq."""
+    if x is None and xq is None:
+        raise ValueError("give x, xq or both")
     if x is not None:
         x2 = x.unsqueeze(0) if x.dim() == 1 else x
         if x2.dtype != torch.float32 or x2.stride(-1) != 1:
@@ -204,6 +206,8 @@ def gemv_q4_0(W: Q4_0, x: torch.Tensor | None = None, xq: torch.Tensor | None = 
         if B is None:
             raise ValueError("B is required with xq")
         xp, ldx, dev = None, W.K, xq.device
+    if xq is not None and (xq.dtype != torch.uint8 or xq.numel() < q8_1_bytes(W.K, B)):
+        raise ValueError("xq must be uint8 with at least q8_1_bytes(K, B) bytes")
     if out is None:
         out = torch.empty((B, W.N), dtype=torch.float32, device=dev)
     y2 = out.unsqueeze(0) if out.dim() == 1 else out

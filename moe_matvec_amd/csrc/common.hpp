@@ -10,6 +10,9 @@
 
 namespace mmv {
 
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 constexpr int kWave = 64;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -69,9 +72,13 @@ constexpr int kDppQuadXor2 = 0x4E;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
+// Full row and bank masks with in-row permutations: every lane is written
+// from a valid source lane, so `old` and bound_ctrl never take effect; the
+// form (old = 0, bound_ctrl) lets the compiler fold the move into the DPP
+// operand of the instruction that consumes it.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
@@ -151,6 +158,52 @@ __device__ __forceinline__ float gsum(float v) {
   if constexpr (G == 16) return row16_sum(v);
   else if constexpr (G == 32) return half_sum(v);
   else return wave_sum(v);
+}
+
+// The same sums, bit for bit, left only in the last lane of each group
+// (lane G-1 of it): the row sums are combined by the row-broadcast DPP
+// steps (lane 15 of a row into the next row, lane 31 into rows 2 and 3)
+// instead of through scalar registers.  Floating-point addition is
+// commutative, so (r1 + r0) here equals (r0 + r1) in half_sum, and
+// (r3 + r2) + (r1 + r0) equals wave_sum's (r0 + r1) + (r2 + r3).
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows_or_zero(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float gsum_last(float v) {
+  v = row16_sum(v);
+  if constexpr (G >= 32) v += dpp_rows_or_zero<kDppRowBcast15, 0xA>(v);
+  if constexpr (G == 64) v += dpp_rows_or_zero<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+__device__ __forceinline__ float wave_sum_last(float v) { return gsum_last<64>(v); }
+
+// gsum_last over N independent values, one reduction step across all of
+// them at a time, so that each DPP read is separated from the write of its
+// source by independent work rather than by wait states.  Same sums, bit for
+// bit, as N calls of gsum_last<G>.
+template <int G, int N>
+__device__ __forceinline__ void gsum_last_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<kDppQuadXor1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<kDppQuadXor2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<kDppRowHalfMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<kDppRowMirror>(v[i]);
+  if constexpr (G >= 32) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_rows_or_zero<kDppRowBcast15, 0xA>(v[i]);
+  }
+  if constexpr (G == 64) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_rows_or_zero<kDppRowBcast31, 0xC>(v[i]);
+  }
 }
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) {

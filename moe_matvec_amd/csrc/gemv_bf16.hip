@@ -102,8 +102,8 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(
   for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const float v = wave_sum(acc[r][b]);
-      if (lane == 0 && row0 + r < N) Y[(int64_t)b * ldy + row0 + r] = v;
+      const float v = wave_sum_last(acc[r][b]);
+      if (lane == 63 && row0 + r < N) Y[(int64_t)b * ldy + row0 + r] = v;
     }
   }
 }
@@ -147,8 +147,8 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_bf16_ni(
   for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const float v = wave_sum(acc[r][b]);
-      if (lane == 0 && row0 + r < N) Y[(int64_t)b * ldy + row0 + r] = v;
+      const float v = wave_sum_last(acc[r][b]);
+      if (lane == 63 && row0 + r < N) Y[(int64_t)b * ldy + row0 + r] = v;
     }
   }
 }

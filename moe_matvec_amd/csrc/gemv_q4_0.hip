@@ -137,9 +137,8 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(
       }
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const int8_t *xc = st.codes + (size_t)b * K + 32 * j;
-        const i32x4 xa = *reinterpret_cast<const i32x4 *>(xc);
-        const i32x4 xb = *reinterpret_cast<const i32x4 *>(xc + 16);
+        const i32x4 xa = xstage_lo(st, b, K, j);
+        const i32x4 xb = xstage_hi(st, b, K, j);
         const int xs = st.qsum[b * nb + j];
         const float dx = st.d[b * nb + j];
 #pragma unroll
@@ -155,8 +154,8 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(
       const int row = rbase + p * RPP;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float v = gsum<G>(acc[p][b]);
-        if (sub == 0 && row < N) Y[(int64_t)b * ldy + row] = v;
+        const float v = gsum_last<G>(acc[p][b]);
+        if (sub == G - 1 && row < N) Y[(int64_t)b * ldy + row] = v;
       }
     }
     first = false;
@@ -170,24 +169,30 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(
 // weights are in flight (loads complete in issue order).  Per-row arithmetic
 // order is the same as in k_gemv_q4_0: block j's integer sum scaled by
 // d_w * d_x and accumulated over j = sub, sub + G, ..., then a G-lane sum.
-template <int B, int G, int RP, int T>
+template <int B, int G, int RP, int T, bool FROM_X>
 __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
-    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int /*K*/,
     const float *__restrict__ X, int64_t ldx, const uint8_t *__restrict__ Xq,
     float *__restrict__ Y, int64_t ldy) {
   extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int K = 32 * G * T;  // the launcher checks K against this
   constexpr int RPP = 64 / G;
   constexpr int ROWS_WAVE = RP * RPP;
   constexpr int ROWS_WG = 4 * ROWS_WAVE;
-  const int nb = K >> 5;  // == G * T
+  constexpr int nb = G * T;
   const int lane = threadIdx.x & 63;
   const int sub = lane % G, grp = lane / G;
   const int wv = threadIdx.x >> 6;
 
-  constexpr int MAXT = XPRE_MAXT;
-  XPre<MAXT> xp;
-  const bool pre = X && (B * K <= MAXT * 4 * 256);
-  if (pre) xpre_load(X, ldx, nullptr, B, K, xp);
+  // first pass of the activation loads, ahead of the weights: B * G * T / 32
+  // float4 tasks (or B * G * T / 128 16-byte code tasks) per thread in all
+  constexpr int MAXT = cmin(kStageMaxT, cmax(1, B * G * T / 32));
+  constexpr int MAXC = cmin(kStageMaxC, cmax(1, B * G * T / 128));
+  XPre<FROM_X ? MAXT : 1> xp;
+  XqPre<FROM_X ? 1 : MAXC> qp;
+  if constexpr (FROM_X) xpre_load(X, ldx, nullptr, B, K, xp, 0, 256);
+  else xq_pre_load(Xq, B, B, K, qp, 0, 256);
+  __builtin_amdgcn_sched_barrier(0);  // keep the weight loads behind these
 
   const int rbase = blockIdx.x * ROWS_WG + wv * ROWS_WAVE + grp;
   u32x4 w[RP][T];
@@ -202,11 +207,16 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
       d[p][t] = f16_bits_to_f32(load_stream2(dw + blk));
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // all weight loads issued before any wait
 
   const XStage st = xstage_at(smem, B, K);
-  if (pre) xpre_quantize(xp, B, K, st);
-  else if (X) stage_quantize(X, ldx, nullptr, B, K, st);
-  else stage_copy_q8(Xq, B, B, K, st);
+  if constexpr (FROM_X) {
+    xpre_quantize(xp, B, K, st, 0, 256);
+    stage_quantize(X, ldx, nullptr, B, K, st, MAXT * 256, 256);
+  } else {
+    xq_pre_store(qp, B, K, st, 0, 256);
+    stage_copy_q8(Xq, B, B, K, st, MAXC * 256, 256);
+  }
   __syncthreads();
 
   float acc[RP][B];
@@ -219,9 +229,8 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
     const int j = sub + G * t;
 #pragma unroll
     for (int r = 0; r < B; ++r) {
-      const int8_t *xc = st.codes + (size_t)r * K + 32 * j;
-      const i32x4 xa = *reinterpret_cast<const i32x4 *>(xc);
-      const i32x4 xb = *reinterpret_cast<const i32x4 *>(xc + 16);
+      const i32x4 xa = xstage_lo(st, r, K, j);
+      const i32x4 xb = xstage_hi(st, r, K, j);
       const int xs = st.qsum[r * nb + j];
       const float dx = st.d[r * nb + j];
 #pragma unroll
@@ -231,14 +240,14 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
       }
     }
   }
+  float (&flat)[RP * B] = *reinterpret_cast<float(*)[RP * B]>(&acc[0][0]);
+  gsum_last_n<G>(flat);
 #pragma unroll
   for (int p = 0; p < RP; ++p) {
     const int row = rbase + p * RPP;
 #pragma unroll
-    for (int r = 0; r < B; ++r) {
-      const float v = gsum<G>(acc[p][r]);
-      if (sub == 0 && row < N) Y[(int64_t)r * ldy + row] = v;
-    }
+    for (int r = 0; r < B; ++r)
+      if (sub == G - 1 && row < N) Y[(int64_t)r * ldy + row] = acc[p][r];
   }
 }
 
@@ -294,34 +303,34 @@ static hipError_t launch_q4_t(const uint8_t *qs, const uint16_t *d, int N, int K
   constexpr int rows_wg = 4 * RP * (64 / G);
   const int ngroups = (N + rows_wg - 1) / rows_wg;
   const size_t lds = xstage_bytes(B, K);
-  hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T>), dim3(ngroups), dim3(256), lds, s, qs, d,
-                     N, K, X, ldx, Xq, Y, ldy);
+  if (X)
+    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, true>), dim3(ngroups), dim3(256), lds, s, qs,
+                       d, N, K, X, ldx, Xq, Y, ldy);
+  else
+    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, false>), dim3(ngroups), dim3(256), lds, s,
+                       qs, d, N, K, X, ldx, Xq, Y, ldy);
   return hipGetLastError();
 }
 
-// Rows per lane group: the fewest workgroups that still give every CU about
-// two, so each redundant activation quantization covers as many rows as it
-// can while the whole matrix is in flight at once.
+// Rows per lane group (2, 4, 6 or 8; MMV_Q4_RP overrides): 4 by default.
+// Measured on the 4096 x 4096 and 11008 x 4096 shapes at B = 1, four rows
+// per lane group (16 per workgroup) beat both two (twice the workgroups,
+// each repeating the activation staging) and six or eight (fewer waves to
+// overlap).  A lane holds at most 16 (B <= 2) or 8 weight blocks in flight.
 template <int B, int G, int T>
 static hipError_t launch_q4_rp(const uint8_t *qs, const uint16_t *d, int N, int K,
                                const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                                int64_t ldy, hipStream_t s) {
+  constexpr int kMaxLoads = B <= 2 ? 16 : 8;
+  constexpr int kMaxRp = cmin(8, (kMaxLoads / T) & ~1);
   int rp = q4_knob("MMV_Q4_RP");
-  if (rp == 0) {
-    const int target = 2 * cu_count();
-    const int per_rp = 4 * (64 / G);  // rows of a workgroup per unit of RP
-    rp = 2;
-    while (rp < 8 / T && (N + rp * per_rp - 1) / (rp * per_rp) > target) rp += 2;
-  }
-  // at most 8 weight loads per lane: RP * T <= 8
-  if constexpr (T <= 2)
-    if (rp > 2) {
-      if constexpr (T == 1) {
-        if (rp > 6) return launch_q4_t<B, G, 8, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-        if (rp > 4) return launch_q4_t<B, G, 6, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-      }
-      return launch_q4_t<B, G, 4, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    }
+  if (rp == 0) rp = cmin(4, kMaxRp);
+  if constexpr (kMaxRp >= 8)
+    if (rp > 6) return launch_q4_t<B, G, 8, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  if constexpr (kMaxRp >= 6)
+    if (rp > 4) return launch_q4_t<B, G, 6, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  if constexpr (kMaxRp >= 4)
+    if (rp > 2) return launch_q4_t<B, G, 4, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   return launch_q4_t<B, G, 2, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
 }
 
@@ -347,6 +356,11 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
 hipError_t run_gemv_q4_0(const uint8_t *qs, const uint16_t *d, int N, int K,
                          const float *X, int64_t ldx, const uint8_t *Xq, int B,
                          float *Y, int64_t ldy, hipStream_t s) {
+  if (X && Xq) {  // quantize once into the caller's buffer, then read it
+    const hipError_t e = run_quantize_q8_1(X, K, ldx, B, const_cast<uint8_t *>(Xq), s);
+    if (e != hipSuccess) return e;
+    X = nullptr;
+  }
   switch (B) {
     case 1: return dispatch_q4<1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     case 2: return dispatch_q4<2>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);

@@ -77,8 +77,8 @@ __device__ __forceinline__ void router_row(const float *__restrict__ row, int H,
   }
 #pragma unroll
   for (int b = 0; b < B; ++b) {
-    const float v = wave_sum(acc[b]);
-    if (lane == 0) out[(int64_t)b * ldl] = v;
+    const float v = wave_sum_last(acc[b]);
+    if (lane == 63) out[(int64_t)b * ldl] = v;
   }
 }
 
@@ -373,9 +373,8 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
 #pragma unroll
     for (int r = 0; r < B; ++r) {
       if (r < nr) {
-        const int8_t *xc = st.codes + (size_t)r * H + 32 * j;
-        const i32x4 xa = *reinterpret_cast<const i32x4 *>(xc);
-        const i32x4 xb = *reinterpret_cast<const i32x4 *>(xc + 16);
+        const i32x4 xa = xstage_lo(st, r, H, j);
+        const i32x4 xb = xstage_hi(st, r, H, j);
         const int xs = st.qsum[r * nbh + j];
         const float dx = st.d[r * nbh + j];
 #pragma unroll
@@ -629,7 +628,8 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
   const XStage hs = xstage_at(smem, P, I);
 #pragma unroll
   for (int m = 0; m < kDownStageChunks; ++m)
-    if (t + 256 * m < n16) reinterpret_cast<u32x4 *>(hs.codes)[t + 256 * m] = cbuf[m];
+    if (t + 256 * m < n16)
+      *reinterpret_cast<u32x4 *>(hs.codes + xstage_chunk_off(t + 256 * m, I)) = cbuf[m];
 #pragma unroll
   for (int m = 0; m < kDownStageBlocks; ++m) {
     if (t + 256 * m < nblk) {
@@ -678,9 +678,8 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
     for (int pi = pbeg; pi < pend; ++pi) {
       const int p = u < U ? s_pairs[pi] : Bk + pi;
       const int pb = u < U ? p / k : pi;
-      const int8_t *hc = hs.codes + (size_t)p * I + 32 * j;
-      const i32x4 xa = *reinterpret_cast<const i32x4 *>(hc);
-      const i32x4 xb = *reinterpret_cast<const i32x4 *>(hc + 16);
+      const i32x4 xa = xstage_lo(hs, p, I, j);
+      const i32x4 xb = xstage_hi(hs, p, I, j);
       const int Iv = q4_block_isum(wb, xa, xb, hs.qsum[p * nbi + j]);
       const float part_v = (db * hs.d[p * nbi + j]) * (float)Iv;
       const float gw = s_pw[p];

@@ -20,7 +20,7 @@ namespace mmv {
 // xb: codes 16..31), minus 8 * xsum.
 __device__ __forceinline__ int q4_block_isum(u32x4 w, i32x4 xa, i32x4 xb, int xsum) {
   const uint32_t m = 0x0F0F0F0Fu;
-  int dot = sdot4((int)(w.x & m), xa.x, 0);
+  int dot = sdot4((int)(w.x & m), xa.x, -8 * xsum);  // exact: |I| <= 32 * 8 * 127
   dot = sdot4((int)(w.y & m), xa.y, dot);
   dot = sdot4((int)(w.z & m), xa.z, dot);
   dot = sdot4((int)(w.w & m), xa.w, dot);
@@ -28,16 +28,33 @@ __device__ __forceinline__ int q4_block_isum(u32x4 w, i32x4 xa, i32x4 xb, int xs
   dot = sdot4((int)((w.y >> 4) & m), xb.y, dot);
   dot = sdot4((int)((w.z >> 4) & m), xb.z, dot);
   dot = sdot4((int)((w.w >> 4) & m), xb.w, dot);
-  return dot - 8 * xsum;
+  return dot;
 }
 
 // Activations staged in LDS for nrows rows of K (K % 32 == 0):
-//   codes int8 [nrows][K] | d fp32 [nrows][K/32] | qsum int32 [nrows][K/32]
+//   codes int8 [nrows][2][K/2] | d fp32 [nrows][K/32] | qsum int32 [nrows][K/32]
+// Each row's codes are two half-planes: bytes 0..15 of every block (block j
+// at 16 j), then bytes 16..31.  Lanes that read consecutive blocks then read
+// consecutive 16-byte words, which the LDS serves without bank conflicts.
 struct XStage {
   int8_t *codes;
   float *d;
   int *qsum;
 };
+__device__ __forceinline__ size_t xstage_code_off(int r, int K, int j, int byte) {
+  return (size_t)r * K + (size_t)(byte >> 4) * (K >> 1) + 16 * j + (byte & 15);
+}
+__device__ __forceinline__ i32x4 xstage_lo(XStage st, int r, int K, int j) {
+  return *reinterpret_cast<const i32x4 *>(st.codes + (size_t)r * K + 16 * j);
+}
+__device__ __forceinline__ i32x4 xstage_hi(XStage st, int r, int K, int j) {
+  return *reinterpret_cast<const i32x4 *>(st.codes + (size_t)r * K + (K >> 1) + 16 * j);
+}
+// LDS offset of 16-byte chunk c of a row-major [rows][K] code buffer
+__device__ __forceinline__ size_t xstage_chunk_off(int c, int K) {
+  const int nb = K >> 5, r = c / (2 * nb), rem = c - r * 2 * nb;
+  return (size_t)r * K + (size_t)(rem & 1) * (K >> 1) + 16 * (rem >> 1);
+}
 __host__ __device__ inline size_t xstage_bytes(int nrows, int K) {
   return xstage_lds_bytes(nrows, K);
 }
@@ -49,65 +66,50 @@ __device__ __forceinline__ XStage xstage_at(uint8_t *base, int nrows, int K) {
   return s;
 }
 
-// Quantize rows rowmap[0..nrows) of fp32 X into the stage (all threads of
-// the workgroup call this; blockDim.x % 64 == 0).  rowmap == nullptr means
-// rows 0..nrows-1.  Codes are those of q8_1_quantize8.
-__device__ __forceinline__ void stage_quantize(const float *__restrict__ X, int64_t ldx,
-                                               const int *rowmap, int nrows, int K,
-                                               XStage st) {
-  const int nb = K >> 5;
-  const int total = nrows * nb * 8;
-  for (int t = threadIdx.x; t < total; t += blockDim.x) {
-    const int r = t / (nb * 8);
-    const int rem = t - r * nb * 8;
-    const int j = rem >> 3, s = rem & 7;
-    const int row = rowmap ? rowmap[r] : r;
-    const f32x4 v = load_f4(X + (int64_t)row * ldx + 32 * j + 4 * s);
-    const Q8Block q = q8_1_quantize8(v);
-    *reinterpret_cast<uint32_t *>(st.codes + (size_t)r * K + 32 * j + 4 * s) = q.codes;
-    if (s == 0) {
-      st.d[r * nb + j] = f16_bits_to_f32(q.d16);
-      st.qsum[r * nb + j] = q.qsum;
-    }
-  }
-}
-
 // Two-phase staging for callers that also prefetch weights: loads complete
 // in issue order, so the activation loads are issued first (xpre_load), the
 // weight loads next, and the quantization (xpre_quantize) then waits only
-// for the activations.  MAXT = tasks per thread (4 floats each) the caller
-// guarantees: nrows * K / 4 <= MAXT * blockDim.x.
+// for the activations.  One pass covers MAXT tasks (4 floats each) per
+// thread, tasks base + threadIdx.x + i * nth (nth: the workgroup's thread
+// count, 0 = blockDim.x; a constant lets the index math fold).  Loads are
+// unconditional (clamped to the last task) so that they all issue back to
+// back; only the stores are guarded.  rowmap == nullptr means rows
+// 0..nrows-1, else stage row r holds X row rowmap[r].
 template <int MAXT>
 struct XPre {
   f32x4 v[MAXT];
 };
 template <int MAXT>
 __device__ __forceinline__ void xpre_load(const float *__restrict__ X, int64_t ldx,
-                                          const int *rowmap, int nrows, int K, XPre<MAXT> &p) {
+                                          const int *rowmap, int nrows, int K, XPre<MAXT> &p,
+                                          int base = 0, int nth = 0) {
   const int nb = K >> 5, total = nrows * nb * 8;
+  if (nth == 0) nth = blockDim.x;
 #pragma unroll
   for (int i = 0; i < MAXT; ++i) {
-    const int t = threadIdx.x + i * blockDim.x;
-    if (t < total) {
-      const int r = t / (nb * 8);
-      const int rem = t - r * nb * 8;
-      const int row = rowmap ? rowmap[r] : r;
-      p.v[i] = load_f4(X + (int64_t)row * ldx + 4 * rem);
-    }
+    const int t = min(base + (int)threadIdx.x + i * nth, total - 1);
+    const int r = t / (nb * 8);
+    const int rem = t - r * nb * 8;
+    const int row = rowmap ? rowmap[r] : r;
+    p.v[i] = load_f4(X + (int64_t)row * ldx + 4 * rem);
   }
 }
 template <int MAXT>
-__device__ __forceinline__ void xpre_quantize(const XPre<MAXT> &p, int nrows, int K, XStage st) {
+__device__ __forceinline__ void xpre_quantize(const XPre<MAXT> &p, int nrows, int K, XStage st,
+                                              int base = 0, int nth = 0) {
   const int nb = K >> 5, total = nrows * nb * 8;
+  if (nth == 0) nth = blockDim.x;
 #pragma unroll
   for (int i = 0; i < MAXT; ++i) {
-    const int t = threadIdx.x + i * blockDim.x;
+    const int t = base + (int)threadIdx.x + i * nth;
+    // quantized unconditionally: the cross-lane steps keep the loads that
+    // feed them in place (ahead of any later weight loads)
+    const Q8Block q = q8_1_quantize8(p.v[i]);
     if (t < total) {  // uniform over each 8-lane group: total % 8 == 0
       const int r = t / (nb * 8);
       const int rem = t - r * nb * 8;
       const int j = rem >> 3, s = rem & 7;
-      const Q8Block q = q8_1_quantize8(p.v[i]);
-      *reinterpret_cast<uint32_t *>(st.codes + (size_t)r * K + 32 * j + 4 * s) = q.codes;
+      *reinterpret_cast<uint32_t *>(st.codes + xstage_code_off(r, K, j, 4 * s)) = q.codes;
       if (s == 0) {
         st.d[r * nb + j] = f16_bits_to_f32(q.d16);
         st.qsum[r * nb + j] = q.qsum;
@@ -116,23 +118,78 @@ __device__ __forceinline__ void xpre_quantize(const XPre<MAXT> &p, int nrows, in
   }
 }
 
-// Copy rows of a planar Q8_1 buffer (B rows of K) into the stage.
-__device__ __forceinline__ void stage_copy_q8(const uint8_t *__restrict__ Xq, int B,
-                                              int nrows, int K, XStage st) {
-  const int nb = K >> 5;
-  const int total = nrows * nb * 8;
-  const uint16_t *ds = reinterpret_cast<const uint16_t *>(Xq + (size_t)B * K);
-  for (int t = threadIdx.x; t < total; t += blockDim.x) {
-    const int r = t / (nb * 8);
-    const int rem = t - r * nb * 8;
-    const int j = rem >> 3, s = rem & 7;
-    const uint32_t c = *reinterpret_cast<const uint32_t *>(Xq + (size_t)r * K + 32 * j + 4 * s);
-    *reinterpret_cast<uint32_t *>(st.codes + (size_t)r * K + 32 * j + 4 * s) = c;
-    const int sum = group8_sum_i(sdot4((int)c, 0x01010101, 0));
-    if (s == 0) {
-      st.d[r * nb + j] = f16_bits_to_f32(ds[((size_t)r * nb + j) * 2]);
-      st.qsum[r * nb + j] = sum;
+// Quantize rows of fp32 X into the stage, pass after pass of XPre loads
+// (all threads of the workgroup call this; blockDim.x % 64 == 0).  `from`
+// skips tasks an earlier xpre_load / xpre_quantize pair already covered.
+constexpr int kStageMaxT = 8;
+__device__ __forceinline__ void stage_quantize(const float *__restrict__ X, int64_t ldx,
+                                               const int *rowmap, int nrows, int K,
+                                               XStage st, int from = 0, int nth = 0) {
+  const int total = nrows * (K >> 5) * 8;
+  if (nth == 0) nth = blockDim.x;
+  for (int base = from; base < total; base += kStageMaxT * nth) {
+    XPre<kStageMaxT> p;
+    xpre_load(X, ldx, rowmap, nrows, K, p, base, nth);
+    xpre_quantize(p, nrows, K, st, base, nth);
+  }
+}
+
+// The same two phases for a planar Q8_1 buffer (B rows of K codes, then
+// B * K/32 {d, s} fp16 pairs): a task is 16 code bytes (half a block), the
+// two halves of a block sit in adjacent lanes, and the block's integer code
+// sum is formed from both.
+template <int MAXC>
+struct XqPre {
+  i32x4 c[MAXC];
+  uint32_t ds[MAXC];
+};
+template <int MAXC>
+__device__ __forceinline__ void xq_pre_load(const uint8_t *__restrict__ Xq, int B, int nrows,
+                                            int K, XqPre<MAXC> &p, int base = 0, int nth = 0) {
+  const int nb = K >> 5, total = nrows * nb * 2;
+  const uint32_t *ds = reinterpret_cast<const uint32_t *>(Xq + (size_t)B * K);
+  if (nth == 0) nth = blockDim.x;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int t = min(base + (int)threadIdx.x + i * nth, total - 1);
+    p.c[i] = *reinterpret_cast<const i32x4 *>(Xq + (size_t)16 * t);
+    p.ds[i] = ds[t >> 1];
+  }
+}
+template <int MAXC>
+__device__ __forceinline__ void xq_pre_store(const XqPre<MAXC> &p, int nrows, int K, XStage st,
+                                             int base = 0, int nth = 0) {
+  const int nb = K >> 5, total = nrows * nb * 2;
+  if (nth == 0) nth = blockDim.x;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int t = base + (int)threadIdx.x + i * nth;
+    int sum = sdot4(p.c[i].x, 0x01010101, 0);
+    sum = sdot4(p.c[i].y, 0x01010101, sum);
+    sum = sdot4(p.c[i].z, 0x01010101, sum);
+    sum = sdot4(p.c[i].w, 0x01010101, sum);
+    sum += (int)dpp_u32<kDppQuadXor1>((uint32_t)sum);  // the block's other half
+    // an unconditional use keeps the scale load where it was issued
+    uint32_t dsv = p.ds[i];
+    asm volatile("" : "+v"(dsv));
+    if (t < total) {  // uniform over each lane pair: total is even
+      *reinterpret_cast<i32x4 *>(st.codes + xstage_chunk_off(t, K)) = p.c[i];
+      if ((t & 1) == 0) {
+        st.d[t >> 1] = f16_bits_to_f32((uint16_t)(dsv & 0xFFFFu));
+        st.qsum[t >> 1] = sum;
+      }
     }
+  }
+}
+constexpr int kStageMaxC = 8;
+__device__ __forceinline__ void stage_copy_q8(const uint8_t *__restrict__ Xq, int B, int nrows,
+                                              int K, XStage st, int from = 0, int nth = 0) {
+  const int total = nrows * (K >> 5) * 2;
+  if (nth == 0) nth = blockDim.x;
+  for (int base = from; base < total; base += kStageMaxC * nth) {
+    XqPre<kStageMaxC> p;
+    xq_pre_load(Xq, B, nrows, K, p, base, nth);
+    xq_pre_store(p, nrows, K, st, base, nth);
   }
 }
 

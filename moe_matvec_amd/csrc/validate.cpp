@@ -74,7 +74,7 @@ int check_quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B, const
 int check_gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,
                     int32_t B, const float *Y, int64_t ldy) {
   if (!W || !W->qs || !W->d || !Y) return MMV_E_NULL;
-  if ((X == nullptr) == (Xq == nullptr)) return MMV_E_ARG;
+  if (!X && !Xq) return MMV_E_NULL;
   if (bad_batch(B)) return MMV_E_BATCH;
   const int32_t N = W->N, K = W->K;
   if (N < 1 || K < 32 || K % 32 != 0 || ldy < N || ldy > kMaxLd) return MMV_E_SHAPE;
@@ -83,9 +83,17 @@ int check_gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *
   if (!aligned(W->qs, 16) || !aligned(W->d, 2) || !aligned(Y, 4)) return MMV_E_ALIGN;
   if (X && (!aligned(X, 16) || ldx % 4 != 0)) return MMV_E_ALIGN;
   if (Xq && !aligned(Xq, 16)) return MMV_E_ALIGN;
-  const Range outs[1] = {rng(Y, span(B, ldy, N, 4))};
-  const Range ins[3] = {q4_qs(W->qs, N, K), q4_d(W->d, N, K),
-                        X ? rng(X, span(B, ldx, K, 4)) : rng(Xq, q8_1_bytes(K, B))};
+  const Range y = rng(Y, span(B, ldy, N, 4));
+  const Range xq = rng(Xq, q8_1_bytes(K, B));
+  const Range w[2] = {q4_qs(W->qs, N, K), q4_d(W->d, N, K)};
+  if (X && Xq) {  // Xq is an output here
+    const Range outs[2] = {y, xq};
+    const Range ins[3] = {w[0], w[1], rng(X, span(B, ldx, K, 4))};
+    if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+    return MMV_OK;
+  }
+  const Range outs[1] = {y};
+  const Range ins[3] = {w[0], w[1], X ? rng(X, span(B, ldx, K, 4)) : xq};
   if (any_overlap(outs, ins)) return MMV_E_ALIAS;
   return MMV_OK;
 }

@@ -88,8 +88,11 @@ def test_gemv_q4_0_validation(L):
     g = L.gemv_q4_0
     W = _q4(A, Bp, 64, 256)
     assert g(None, Cp, 256, None, 1, Dp, 64, None) == E_NULL
-    assert g(C.byref(W), Cp, 256, Cp, 1, Dp, 64, None) == E_ARG      # both X and Xq
-    assert g(C.byref(W), None, 256, None, 1, Dp, 64, None) == E_ARG  # neither
+    assert g(C.byref(W), None, 256, None, 1, Dp, 64, None) == E_NULL  # neither X nor Xq
+    # X and Xq both given: Xq is an output and must not overlap X, Y or W
+    assert g(C.byref(W), Cp, 256, Cp + 512, 1, Dp, 64, None) == E_ALIAS
+    assert g(C.byref(W), Cp, 256, Dp + 128, 1, Dp, 64, None) == E_ALIAS
+    assert g(C.byref(W), Cp, 256, A + 256, 1, Dp, 64, None) == E_ALIAS
     assert g(C.byref(W), Cp, 256, None, 0, Dp, 64, None) == E_BATCH
     assert g(C.byref(_q4(A, Bp, 64, 200)), Cp, 256, None, 1, Dp, 64, None) == E_SHAPE
     assert g(C.byref(_q4(A, Bp, 64, 32 * 1600)), Cp, 51200, None, 8, Dp, 64, None) == E_SHAPE

@@ -156,6 +156,10 @@ def test_q4_0_parity(mm, orc, dev, N, K, B):
     torch.cuda.synchronize()
     # on-the-fly quantization inside the GEMV equals quantize_q8_1 + Xq bit for bit
     assert torch.equal(y_x, y_q)
+    # x and xq together: x is quantized into xq, then xq is read
+    buf = torch.full_like(xq, 0x5A)
+    y_b = mm.gemv_q4_0(W, x=X, xq=buf)
+    assert torch.equal(buf, xq) and torch.equal(y_b, y_x)
     q_ref, ds_ref = orc.quantize_q8_1(npc(X))
     ref = orc.gemv_q4_0(qs, d, q_ref, ds_ref)
     assert rel_l2_rows(npc(y_x), ref) <= Q4_TOL
