@@ -159,16 +159,23 @@ def q4_section(mm, dev, copies, B, steps, warmup):
     K = Q4_SHAPES[0][1]
     X = synth.activations(copies * B, K, 0, "q4bench-x", B, device=dev).view(copies, B, K)
     Ys = [[torch.empty((B, N), device=dev) for N, _ in Q4_SHAPES] for _ in range(copies)]
+    # B = 1: Q8_1 quantization inside every workgroup of the product (one
+    # launch); B >= 2: one quantization pass per product into a scratch
+    # buffer, then the product (two launches; each product quantizes its
+    # own activations, none is shared)
+    xq = torch.empty(mm.q8_1_bytes(K, B), dtype=torch.uint8, device=dev) if B > 1 else None
 
     def step():
         for c in range(copies):
             for i, W in enumerate(Ws[c]):
-                mm.gemv_q4_0(W, x=X[c], out=Ys[c][i])
+                mm.gemv_q4_0(W, x=X[c], xq=xq, out=Ys[c][i])
     g = capture(step)
     t = time_graph(g, steps, warmup)
     nbytes = copies * q4_bytes(B)
     del mats, Ws
-    return dict(B=B, copies=copies, stored_GB=copies * sum(N * K // 32 * 18 for N, K in Q4_SHAPES) / 1e9,
+    return dict(B=B, copies=copies, act_quant="in-kernel" if B == 1 else "separate pass",
+                launches_per_copy=len(Q4_SHAPES) * (1 if B == 1 else 2),
+                stored_GB=copies * sum(N * K // 32 * 18 for N, K in Q4_SHAPES) / 1e9,
                 s_per_step=t, us_per_copy=t / copies * 1e6, GBps=nbytes / t / 1e9,
                 frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS)
 

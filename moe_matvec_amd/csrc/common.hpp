@@ -173,6 +173,22 @@ __device__ __forceinline__ float dpp_rows_or_zero(float v) {
   return __int_as_float(
       __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
 }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_rows_or_zero_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+// maximum of a uint32 over the wave, returned wave-uniform (lane 63's value
+// after the row and row-broadcast steps)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuadXor1>(v));
+  v = max(v, dpp_u32<kDppQuadXor2>(v));
+  v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = max(v, dpp_u32<kDppRowMirror>(v));
+  v = max(v, dpp_rows_or_zero_u32<kDppRowBcast15, 0xA>(v));
+  v = max(v, dpp_rows_or_zero_u32<kDppRowBcast31, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 template <int G>
 __device__ __forceinline__ float gsum_last(float v) {
   v = row16_sum(v);

@@ -85,17 +85,24 @@ __device__ __forceinline__ void router_row(const float *__restrict__ row, int H,
 // ---------------------------------------------------------------------------
 // top-k of one row by one wave
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-  v = v + 0.0f;  // -0 and +0 compare equal: map both to +0
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
+// Order-preserving map of fp32 onto uint32 (larger float, larger key), with
+// -0 and +0 mapped to the same key so that they tie; and its inverse.
+__device__ __forceinline__ uint32_t topk_ord(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float topk_unord(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // Selects the k largest of l[0..E) (ties: lower index first), writes ids,
 // renormalised weights and the shared weight.  Whole wave, uniform control.
-// KPL = keys per lane (E <= 64 * KPL).  All loads are unconditional (clamped
-// in bounds) so they are in flight together.
+// KPL = keys per lane (E <= 64 * KPL); lane l holds experts l + 64 i.  Each
+// round takes the wave maximum of the keys (DPP), then the lowest expert
+// index holding it: the first slot i whose ballot is non-empty, then that
+// ballot's lowest lane.  Selected keys drop to 0, below every finite logit.
+// The selected logit is read back from the key itself.  All loads are
+// unconditional (clamped in bounds) so they are in flight together.
 template <int KPL>
 __device__ void topk_row(const float *__restrict__ l, int E, int k, int has_shared,
                          int32_t *__restrict__ ids, float *__restrict__ weights,
@@ -105,33 +112,29 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int has_shar
 #pragma unroll
   for (int i = 0; i < KPL; ++i) v[i] = l[min(lane + 64 * i, E - 1)];
   const float lsh = has_shared ? l[E] : 0.0f;
-  uint64_t key[KPL];
+  uint32_t key[KPL];
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? topk_key(v[i], e) : 0ull;  // 0 never wins: real keys are > 0
-  }
+  for (int i = 0; i < KPL; ++i) key[i] = lane + 64 * i < E ? topk_ord(v[i]) : 0u;
   int my_id = 0;
   float my_l = 0.0f;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    uint32_t m = key[0];
 #pragma unroll
-    for (int i = 1; i < KPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(~(uint32_t)best);
-    float le = 0.0f;
+    for (int i = 1; i < KPL; ++i) m = max(m, key[i]);
+    const uint32_t M = wave_max_u32(m);
+    int e = 64 * KPL;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const bool hit = (lane + 64 * i) == e;
-      key[i] = hit ? 0ull : key[i];
-      le = hit ? v[i] : le;
+    for (int i = KPL - 1; i >= 0; --i) {  // the lowest slot with a hit wins
+      const unsigned long long hit = __ballot(key[i] == M);
+      if (hit) e = 64 * i + __builtin_ctzll(hit);
     }
-    const float lsel = __shfl(le, e & 63, kWave);  // the owner lane's logit
-    if (lane == j) { my_id = e; my_l = lsel; }
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) key[i] = (lane + 64 * i == e) ? 0u : key[i];
+    if (lane == j) { my_id = e; my_l = topk_unord(M); }
   }
-  const float lmax = __shfl(my_l, 0, kWave);  // slot 0 holds the largest
+  const float lmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
   const float ex = lane < k ? expf(my_l - lmax) : 0.0f;
-  const float den = row16_sum(ex);            // k <= 16: lanes 0..15
+  const float den = row16_sum(ex);  // k <= 16: lanes 0..15
   if (lane < k) {
     ids[lane] = my_id;
     weights[lane] = ex / den;
@@ -225,47 +228,70 @@ hipError_t run_moe_route(const float *router, int E, int H, const float *X, int6
 // per-expert row lists, rebuilt in LDS by every routed expert workgroup
 // ---------------------------------------------------------------------------
 struct GatherLds {
-  int sid[kMaxPairs];      // ids, or -1 for an id outside [0, E)
-  int first[kMaxPairs];    // 1 if the first occurrence of its expert
-  int unique[kMaxPairs];   // sorted unique experts
+  __align__(16) uint32_t key[kMaxPairs];   // expert << 8 | pair, ~0 if unused
+  uint32_t skey[kMaxPairs];                // the valid keys in ascending order
+  int unique[kMaxPairs];                   // sorted unique experts
   int offsets[kMaxPairs + 1];
-  int pairs[kMaxPairs];    // b*k + j grouped by expert, then b, then j
+  int pairs[kMaxPairs];                    // b*k + j grouped by expert, then b, then j
   int U;
 };
 
-// blockDim.x >= Bk; contains __syncthreads (call from uniform control flow)
+// Sorting the keys (expert << 8 | pair index) ascending gives the pairs
+// grouped by expert, then by pair index (b, then j).  Each pair's rank is
+// the number of smaller keys (every thread reads all keys: LDS broadcast);
+// in sorted order an expert's first pair starts a group, and the groups are
+// numbered by a ballot prefix count.  Ids outside [0, E) take no part.
+// MAXP (compile time) bounds Bk; blockDim.x >= MAXP.  Contains
+// __syncthreads: call from uniform control flow.
+template <int MAXP>
 __device__ void build_gather(const int32_t *__restrict__ ids, int Bk, int E, GatherLds &g) {
+  static_assert(MAXP % 4 == 0 && MAXP <= kMaxPairs && MAXP <= 128, "pairs per lane");
   const int t = threadIdx.x;
-  if (t < Bk) {
-    const int e = ids[t];
-    g.sid[t] = (e >= 0 && e < E) ? e : -1;
-  }
-  __syncthreads();
-  if (t < Bk) {
-    const int e = g.sid[t];
-    int first = e >= 0;
-    for (int t2 = 0; t2 < t; ++t2) first &= (g.sid[t2] != e);
-    g.first[t] = first;
-  }
-  __syncthreads();
-  if (t < Bk) {
-    const int e = g.sid[t];
-    if (e >= 0) {
-      int urank = 0, nless = 0, before = 0;
-      for (int t2 = 0; t2 < Bk; ++t2) {
-        const int v = g.sid[t2];
-        if (v >= 0 && v < e) { ++nless; urank += g.first[t2]; }
-        before += (v == e && t2 < t);
-      }
-      g.pairs[nless + before] = t;
-      if (g.first[t]) { g.unique[urank] = e; g.offsets[urank] = nless; }
+  if (t < MAXP) {
+    uint32_t key = 0xFFFFFFFFu;
+    if (t < Bk) {
+      const int e = ids[t];
+      if (e >= 0 && e < E) key = ((uint32_t)e << 8) | (uint32_t)t;
     }
+    g.key[t] = key;
   }
-  if (t == 0) {
-    int U = 0, nv = 0;
-    for (int t2 = 0; t2 < Bk; ++t2) { U += g.first[t2]; nv += g.sid[t2] >= 0; }
-    g.U = U;
-    g.offsets[U] = nv;
+  __syncthreads();
+  int nv = 0;  // valid pairs (every thread counts all keys)
+  if (t < MAXP) {
+    const uint32_t mine = g.key[t];
+    int rank = 0;
+#pragma unroll
+    for (int c = 0; c < MAXP / 4; ++c) {
+      const uint4 q = reinterpret_cast<const uint4 *>(g.key)[c];
+      rank += (q.x < mine) + (q.y < mine) + (q.z < mine) + (q.w < mine);
+      nv += (q.x != 0xFFFFFFFFu) + (q.y != 0xFFFFFFFFu) + (q.z != 0xFFFFFFFFu) +
+            (q.w != 0xFFFFFFFFu);
+    }
+    if (mine != 0xFFFFFFFFu) g.skey[rank] = mine;
+  }
+  __syncthreads();
+  if (t < 64) {
+    int base = 0;
+#pragma unroll
+    for (int h = 0; h < (MAXP + 63) / 64; ++h) {
+      const int r = t + 64 * h;
+      const bool valid = r < nv;
+      const uint32_t sk = valid ? g.skey[r] : 0u;
+      const uint32_t prev = (valid && r > 0) ? g.skey[r - 1] : 0xFFFFFFFFu;
+      const bool first = valid && (sk >> 8) != (prev >> 8);
+      const unsigned long long bal = __ballot(first);
+      const int urank = base + __popcll(bal & ((1ull << t) - 1ull));
+      if (valid) g.pairs[r] = (int)(sk & 0xFFu);
+      if (first) {
+        g.unique[urank] = (int)(sk >> 8);
+        g.offsets[urank] = r;
+      }
+      base += __popcll(bal);
+    }
+    if (t == 0) {
+      g.U = base;
+      g.offsets[base] = nv;
+    }
   }
   __syncthreads();
 }
@@ -478,7 +504,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     }
     ids = s_ids;
   }
-  build_gather(ids, Bk, L.n_experts, g);
+  build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs)>(ids, Bk, L.n_experts, g);
   if (blockIdx.x == 0) {
     // publish the row lists for the down kernel (and the debug copies)
     const int t = threadIdx.x;
