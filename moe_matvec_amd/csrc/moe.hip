@@ -349,13 +349,20 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 // lane per row (compile time: all 4*T weight loads issued before x is
 // staged), or 0 for a runtime loop over any H % 32 == 0.
 // rowmap / pairmap (LDS) must be written before the call; the call begins
-// with the barrier that publishes them.
-template <int B, int T>
+// with the barrier that publishes them.  PRE > 0: the caller already loaded
+// the activations of all B rows into xall (PRE float4 tasks per thread,
+// issued before routing); they are quantized into stage rows 0..B-1 and
+// row r of the tile reads stage row rowmap[r].  PRE == 0: the nr rows
+// rowmap[0..nr) are loaded here, into stage rows 0..nr-1.
+// mid() runs once the weight loads are in flight, before the activations
+// are staged (uniform control flow; it may contain barriers).
+template <int B, int T, int PRE, typename Mid>
 __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq,
                                              const uint16_t *gd, const uint8_t *uq,
                                              const uint16_t *ud, int tile, int nr,
                                              const int *rowmap, const int *pairmap,
-                                             uint8_t *smem, float (*hbuf)[32]) {
+                                             uint8_t *smem, float (*hbuf)[32],
+                                             const XPre<(PRE > 0 ? PRE : 1)> &xall, Mid &&mid) {
   const int H = a.L.hidden, I = a.L.inter, nbh = H >> 5, ntiles = I >> 5;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int sub = lane & 15, q = lane >> 4;
@@ -366,10 +373,10 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
   constexpr int TT = T > 0 ? T : 1;
   // activations first (loads complete in issue order), then the weights
   // tasks of 4 values: nr * H / 4 <= B * 128 * T over 256 threads
-  constexpr int MAXT = T > 0 ? (B * T + 1) / 2 : 1;
+  constexpr int MAXT = (T > 0 && PRE == 0) ? cmax(1, cmin(B, 2) * T / 2) : 1;  // <= 2 rows
   XPre<MAXT> xp;
   __syncthreads();  // rowmap / pairmap visible
-  if constexpr (T > 0) xpre_load(a.X, a.ldx, rowmap, nr, H, xp);
+  if constexpr (T > 0 && PRE == 0) xpre_load(a.X, a.ldx, rowmap, nr, H, xp, 0, 256);
   u32x4 w[4][TT];
   float dw[4][TT];
   if constexpr (T > 0) {
@@ -385,10 +392,21 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
       }
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // every weight load issued before any wait
+  mid();
   const XStage st = xstage_at(smem, B, H);
-  if constexpr (T > 0) xpre_quantize(xp, nr, H, st);
-  else stage_quantize(a.X, a.ldx, rowmap, nr, H, st);
+  if constexpr (PRE > 0) {
+    xpre_quantize(xall, B, H, st, 0, 256);
+  } else if constexpr (T > 0) {
+    xpre_quantize(xp, nr, H, st, 0, 256);
+    stage_quantize(a.X, a.ldx, rowmap, nr, H, st, MAXT * 256, 256);
+  } else {
+    stage_quantize(a.X, a.ldx, rowmap, nr, H, st);
+  }
   __syncthreads();
+  int srow[B];  // stage row of tile row r
+#pragma unroll
+  for (int r = 0; r < B; ++r) srow[r] = PRE > 0 ? rowmap[min(r, nr - 1)] : r;
 
   float acc[4][B];
 #pragma unroll
@@ -399,10 +417,11 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
 #pragma unroll
     for (int r = 0; r < B; ++r) {
       if (r < nr) {
-        const i32x4 xa = xstage_lo(st, r, H, j);
-        const i32x4 xb = xstage_hi(st, r, H, j);
-        const int xs = st.qsum[r * nbh + j];
-        const float dx = st.d[r * nbh + j];
+        const int sr = srow[r];
+        const i32x4 xa = xstage_lo(st, sr, H, j);
+        const i32x4 xb = xstage_hi(st, sr, H, j);
+        const int xs = st.qsum[sr * nbh + j];
+        const float dx = st.d[sr * nbh + j];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int Iv = q4_block_isum(wb[p], xa, xb, xs);
@@ -489,12 +508,25 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
   const int k = L.top_k, H = L.hidden, I = L.inter;
   const int Bk = B * k;
   const int ntiles = I >> 5;
-  const int slot = blockIdx.x / ntiles, tile = blockIdx.x - slot * ntiles;
+  // slot 0 is the shared expert's when K2 runs it (dispatched first: its
+  // tiles carry every row), then one slot per routed expert
+  const int slot0 = blockIdx.x / ntiles, tile = blockIdx.x - slot0 * ntiles;
+  const bool shared_slot = a.routed_shared && slot0 == 0;
+  const int slot = slot0 - a.routed_shared;
+
+  // B <= 2: the activations of every row are loaded before routing (they do
+  // not depend on it) and stay in registers until the weights are in flight
+  constexpr int PRE = (B <= 2 && T > 0) ? B * T / 2 : 0;
+  XPre<(PRE > 0 ? PRE : 1)> xall;
+  if constexpr (PRE > 0) {
+    xpre_load(a.X, a.ldx, nullptr, B, H, xall, 0, 256);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   const int32_t *ids = a.ids;
+  const int E = L.n_experts;
   if (a.topk_in_k2) {
     // routing from the logits K1 wrote; block 0 publishes it for K3
-    const int E = L.n_experts;
     topk_any(a.logits, E + 1, E, B, k, L.shared_gate_row ? 1 : 0, s_ids, s_w, s_sw);
     __syncthreads();
     if (blockIdx.x == 0) {
@@ -504,9 +536,8 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     }
     ids = s_ids;
   }
-  build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs)>(ids, Bk, L.n_experts, g);
-  if (blockIdx.x == 0) {
-    // publish the row lists for the down kernel (and the debug copies)
+  // row lists for the down kernel (and the debug copies), from block 0
+  auto publish_gather = [&]() {
     const int t = threadIdx.x;
     int32_t *gl = a.gather;
     if (t == 0) gl[0] = g.U;
@@ -519,11 +550,44 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
       if (a.dbg.pairs && t < g.offsets[g.U]) a.dbg.pairs[t] = g.pairs[t];
       if (a.dbg.n_unique && t == 0) a.dbg.n_unique[0] = g.U;
     }
+  };
+  const int nbh = H >> 5;
+
+  if constexpr (B == 1) {
+    if (a.topk_in_k2) {
+      // One row and the ids this kernel selected (valid and distinct): slot
+      // j is the j-th selected expert, pair j.  The weights are requested at
+      // once; block 0 builds the row lists for the down kernel while its
+      // weights are in flight.
+      if (!shared_slot && slot >= k) return;  // uniform over the workgroup
+      const uint8_t *gq, *uq;
+      const uint16_t *gd, *ud;
+      if (shared_slot) {
+        gq = L.sh_gate_qs; gd = L.sh_gate_d; uq = L.sh_up_qs; ud = L.sh_up_d;
+      } else {
+        const int64_t eo = (int64_t)s_ids[slot] * I * nbh;
+        gq = L.gate_qs + eo * 16; gd = L.gate_d + eo;
+        uq = L.up_qs + eo * 16; ud = L.up_d + eo;
+      }
+      if (threadIdx.x == 0) {
+        rowmap[0] = 0;
+        pairmap[0] = shared_slot ? Bk : slot;
+      }
+      gate_up_tile<B, T, PRE>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem, hbuf, xall,
+                              [&]() {
+                                if (blockIdx.x == 0) {
+                                  build_gather<MMV_MAX_TOPK>(s_ids, Bk, E, g);
+                                  publish_gather();
+                                }
+                              });
+      return;
+    }
   }
-  const bool shared_slot = a.routed_shared && slot == Bk;
+
+  build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs)>(ids, Bk, E, g);
+  if (blockIdx.x == 0) publish_gather();
   if (!shared_slot && slot >= g.U) return;  // uniform over the workgroup
 
-  const int nbh = H >> 5;
   const uint8_t *gq, *uq;
   const uint16_t *gd, *ud;
   int nr;
@@ -544,49 +608,35 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     pairmap[r] = p;
     rowmap[r] = shared_slot ? r : p / k;
   }
-  gate_up_tile<B, T>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf);
+  gate_up_tile<B, T, PRE>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf, xall,
+                          []() {});
 }
 
 // ---------------------------------------------------------------------------
-// K1: router rows + shared expert gate/up tiles; last router workgroup: top-k
+// K1: router rows; with the ticket, the last router workgroup runs top-k
 // ---------------------------------------------------------------------------
-template <int B, int HC, int T>
+template <int B, int HC>
 __global__ __launch_bounds__(256) void k_moe_route_fused(MoeArgs a) {
-  __shared__ int rowmap[MMV_MAX_BATCH];
-  __shared__ int pairmap[MMV_MAX_BATCH];
-  __shared__ float hbuf[MMV_MAX_BATCH][32];
   __shared__ int is_last;
-  extern __shared__ __align__(16) uint8_t smem[];
   const mmv_moe_layer &L = a.L;
   const int E = L.n_experts, H = L.hidden, k = L.top_k;
   const bool has_sg = L.shared_gate_row != nullptr;
 
-  if ((int)blockIdx.x < a.router_wgs) {
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e < E + (has_sg ? 1 : 0)) {
-      const float *row = e < E ? L.router + (int64_t)e * H : L.shared_gate_row;
-      router_row<B, HC>(row, H, a.X, a.ldx, a.logits + e, E + 1);
-    }
-    if (a.topk_in_k2) return;  // the next kernel runs top-k
-    __threadfence();  // logits visible device-wide before the ticket
-    __syncthreads();
-    if (threadIdx.x == 0) is_last = atomicAdd(a.counter, 1) == a.router_wgs - 1;
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    topk_any(a.logits, E + 1, E, B, k, has_sg ? 1 : 0, a.ids_out, a.weights_out,
-             a.shared_w_out);
-    if (threadIdx.x == 0) atomicExch(a.counter, 0);  // ready for the next launch
-    return;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e < E + (has_sg ? 1 : 0)) {
+    const float *row = e < E ? L.router + (int64_t)e * H : L.shared_gate_row;
+    router_row<B, HC>(row, H, a.X, a.ldx, a.logits + e, E + 1);
   }
-  // shared expert tile (routing-independent)
-  const int tile = blockIdx.x - a.router_wgs;
-  if (threadIdx.x < (unsigned)B) {
-    rowmap[threadIdx.x] = threadIdx.x;
-    pairmap[threadIdx.x] = B * k + threadIdx.x;
-  }
-  gate_up_tile<B, T>(a, L.sh_gate_qs, L.sh_gate_d, L.sh_up_qs, L.sh_up_d, tile, B, rowmap,
-                     pairmap, smem, hbuf);
+  if (a.topk_in_k2) return;  // the next kernel runs top-k
+  __threadfence();  // logits visible device-wide before the ticket
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = atomicAdd(a.counter, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  topk_any(a.logits, E + 1, E, B, k, has_sg ? 1 : 0, a.ids_out, a.weights_out,
+           a.shared_w_out);
+  if (threadIdx.x == 0) atomicExch(a.counter, 0);  // ready for the next launch
 }
 
 // ---------------------------------------------------------------------------
@@ -595,14 +645,25 @@ __global__ __launch_bounds__(256) void k_moe_route_fused(MoeArgs a) {
 // 256 threads = 4 waves; the workgroup owns 4 output rows (lane group q of
 // every wave = row 4*blockIdx + q).  Wave w takes the experts with id % 4 == w
 // (ascending), wave 0 also the shared expert last.  Q8_1(h) of every pair is
-// staged in LDS (codes, fp32 d, integer sums).  Every prologue load is issued
-// before the first wait; expert weights go in chunks of kDownCH experts whose
-// loads are unconditional (a chunk slot past the wave's list re-reads its
-// last expert and is not used).  TI = I / 512 blocks per lane per row
-// (compile time) or 0 (runtime loop over I % 32 == 0).
+// staged in LDS (codes, fp32 d, integer sums).  Order of work, so that no
+// wait covers more than it needs (loads complete in issue order): the row
+// lists, then Q8_1(h), are requested; the lists go to LDS and each wave's
+// expert list is built; the wave's first chunk of expert weights is
+// requested; only then is Q8_1(h) stored to LDS.  Weight chunks (kDownCH
+// experts, TI blocks per lane each) are double-buffered: the next chunk is
+// requested before the current one is used.  Chunk loads are unconditional:
+// a slot past the end of the wave's list re-reads its last expert (or expert
+// 0 for an empty list) and is not used.  TI = I / 512 (compile time) or 0
+// (runtime loop over I % 32 == 0, one block at a time).
 constexpr int kDownCH = 4;
 constexpr int kDownStageChunks = kMaxDownStageElems / 16 / 256;  // 16-byte copies per thread
 constexpr int kDownStageBlocks = kMaxDownStageElems / 32 / 256 + 1;
+
+template <int TI>
+struct DownChunk {
+  u32x4 w[kDownCH][TI > 0 ? TI : 1];
+  float d[kDownCH][TI > 0 ? TI : 1];
+};
 
 template <int B, int TI>
 __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
@@ -622,7 +683,13 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
   const bool has_sh = L.sh_down_qs != nullptr;
   const int t = threadIdx.x;
 
-  // ---- prologue loads: row lists, pair weights, Q8_1(h) -- all in flight
+  // Q8_1(h) copies per thread: P <= B * (MMV_MAX_TOPK + 1) pairs of I codes
+  constexpr int CHK = TI > 0 ? cmin(kDownStageChunks, (B * (MMV_MAX_TOPK + 1) * 32 * TI + 255) / 256)
+                             : kDownStageChunks;
+  constexpr int BLK = TI > 0 ? cmin(kDownStageBlocks, (B * (MMV_MAX_TOPK + 1) * TI * 16 + 255) / 256)
+                             : kDownStageBlocks;
+
+  // ---- prologue loads: row lists and pair weights first, then Q8_1(h)
   const int gl_n = 3 * Bk + 2;
   const int g0 = a.gather[min(t, gl_n - 1)];
   const int g1 = a.gather[min(t + 256, gl_n - 1)];
@@ -630,17 +697,17 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
   const float pwv = pwi < Bk ? a.weights[pwi] : (a.shared_w ? a.shared_w[pwi - Bk] : 1.0f);
   const HqView hv = hq_view(a.hq, P, I);
   const int n16 = P * I / 16, nblk = P * nbi;
-  u32x4 cbuf[kDownStageChunks];
-  i32x2 dqbuf[kDownStageBlocks];
+  u32x4 cbuf[CHK];
+  i32x2 dqbuf[BLK];
+  // unconditional (clamped in bounds) so that they all issue back to back
 #pragma unroll
-  for (int m = 0; m < kDownStageBlocks; ++m)  // 8-byte records, clamped in bounds
-    dqbuf[m] = hv.dq[min(t + 256 * m, nblk - 1)];
+  for (int m = 0; m < BLK; ++m) dqbuf[m] = hv.dq[min(t + 256 * m, nblk - 1)];
 #pragma unroll
-  for (int m = 0; m < kDownStageChunks; ++m)
-    if (m * 256 < n16) cbuf[m] = reinterpret_cast<const u32x4 *>(hv.codes)[min(t + 256 * m, n16 - 1)];
-  // keep every load above in flight before the first store below uses one
-  asm volatile("" ::: "memory");
-  // ---- LDS stores
+  for (int m = 0; m < CHK; ++m)
+    cbuf[m] = reinterpret_cast<const u32x4 *>(hv.codes)[min(t + 256 * m, n16 - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- row lists to LDS, per-wave expert lists
   // gather region: [0] U, [1, 1+Bk) unique, [1+Bk, 2+2Bk) offsets, [2+2Bk, 2+3Bk) pairs
   auto put_gather = [&](int idx, int val) {
     if (idx == 0) s_U = val;
@@ -651,33 +718,29 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
   put_gather(t, g0);
   put_gather(t + 256, g1);
   if (t < Bk + B) s_pw[t] = pwv;
-  const XStage hs = xstage_at(smem, P, I);
-#pragma unroll
-  for (int m = 0; m < kDownStageChunks; ++m)
-    if (t + 256 * m < n16)
-      *reinterpret_cast<u32x4 *>(hs.codes + xstage_chunk_off(t + 256 * m, I)) = cbuf[m];
-#pragma unroll
-  for (int m = 0; m < kDownStageBlocks; ++m) {
-    if (t + 256 * m < nblk) {
-      hs.d[t + 256 * m] = __uint_as_float((uint32_t)dqbuf[m].x);
-      hs.qsum[t + 256 * m] = dqbuf[m].y;
-    }
-  }
   __syncthreads();
   const int U = s_U;
   // per-wave expert lists: class = id % 4, ascending; shared expert (index U)
   // appended to wave 0
-  if (t < U) {
-    const int e = s_unique[t], cls = e & 3;
-    int rank = 0;
-    for (int u = 0; u < t; ++u) rank += (s_unique[u] & 3) == cls;
-    s_wl[cls][rank] = t;
-  }
-  if (t < 4) {
-    int n = 0;
-    for (int u = 0; u < U; ++u) n += (s_unique[u] & 3) == t;
-    if (t == 0 && has_sh) s_wl[0][n++] = U;
-    s_wn[t] = n;
+  if (t < 64) {  // wave 0: list positions by ballot prefix counts
+    int base[4] = {0, 0, 0, 0};
+    const unsigned long long lt = (1ull << t) - 1ull;
+#pragma unroll
+    for (int h = 0; h < kMaxPairs / 64; ++h) {
+      const int u = t + 64 * h;
+      const int cls = u < U ? (s_unique[u] & 3) : -1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const unsigned long long bal = __ballot(cls == c);
+        if (cls == c) s_wl[c][base[c] + __popcll(bal & lt)] = u;
+        base[c] += __popcll(bal);
+      }
+    }
+    if (t == 0) {
+      if (has_sh) s_wl[0][base[0]++] = U;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s_wn[c] = base[c];
+    }
   }
   __syncthreads();
 
@@ -686,66 +749,114 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
   const int rowc = min(row, H - 1);
   const int n = s_wn[wv];
   const int *wl = s_wl[wv];
+
+  // list entry c of this wave -> weight planes of its expert (expert 0 for
+  // an empty list: a valid address whose data is never used)
+  auto expert_ptr = [&](int c, const uint8_t *&dq, const uint16_t *&dd) {
+    const int u = n > 0 ? wl[min(c, n - 1)] : -1;
+    if (u >= 0 && u < U) {
+      const int64_t eo = (int64_t)s_unique[u] * H * nbi;
+      dq = L.down_qs + eo * 16; dd = L.down_d + eo;
+    } else if (u == U) {
+      dq = L.sh_down_qs; dd = L.sh_down_d;
+    } else {
+      dq = L.down_qs; dd = L.down_d;
+    }
+  };
+  auto load_chunk = [&](int c0, DownChunk<TI> &ch) {
+#pragma unroll
+    for (int c = 0; c < kDownCH; ++c) {
+      const uint8_t *dq;
+      const uint16_t *dd;
+      expert_ptr(c0 + c, dq, dd);
+#pragma unroll
+      for (int ti = 0; ti < TI; ++ti) {
+        const int64_t blk = (int64_t)rowc * nbi + sub + 16 * ti;
+        ch.w[c][ti] = load_stream16(dq + blk * 16);
+        ch.d[c][ti] = f16_bits_to_f32(load_stream2(dd + blk));
+      }
+    }
+  };
+
+  DownChunk<TI> cha, chb;
+  if constexpr (TI > 0) load_chunk(0, cha);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- Q8_1(h) to LDS (its loads were issued before the weights)
+  const XStage hs = xstage_at(smem, P, I);
+#pragma unroll
+  for (int m = 0; m < CHK; ++m)
+    if (t + 256 * m < n16)
+      *reinterpret_cast<u32x4 *>(hs.codes + xstage_chunk_off(t + 256 * m, I)) = cbuf[m];
+#pragma unroll
+  for (int m = 0; m < BLK; ++m) {
+    if (t + 256 * m < nblk) {
+      hs.d[t + 256 * m] = __uint_as_float((uint32_t)dqbuf[m].x);
+      hs.qsum[t + 256 * m] = dqbuf[m].y;
+    }
+  }
+  __syncthreads();
+
   float acc[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-
-  auto expert_ptr = [&](int u, const uint8_t *&dq, const uint16_t *&dd) {
-    if (u < U) {
-      const int64_t eo = (int64_t)s_unique[u] * H * nbi;
-      dq = L.down_qs + eo * 16; dd = L.down_d + eo;
-    } else {
-      dq = L.sh_down_qs; dd = L.sh_down_d;
-    }
-  };
-  auto consume = [&](int u, const u32x4 wb, const float db, int j) {
-    const int pbeg = u < U ? s_off[u] : 0;
-    const int pend = u < U ? s_off[u + 1] : B;
-    for (int pi = pbeg; pi < pend; ++pi) {
-      const int p = u < U ? s_pairs[pi] : Bk + pi;
-      const int pb = u < U ? p / k : pi;
-      const i32x4 xa = xstage_lo(hs, p, I, j);
-      const i32x4 xb = xstage_hi(hs, p, I, j);
-      const int Iv = q4_block_isum(wb, xa, xb, hs.qsum[p * nbi + j]);
-      const float part_v = (db * hs.d[p * nbi + j]) * (float)Iv;
-      const float gw = s_pw[p];
+  // one (pair, block) product into its row's sum
+  auto pair_block = [&](int p, int pb, const u32x4 wb, const float db, int j) {
+    const i32x4 xa = xstage_lo(hs, p, I, j);
+    const i32x4 xb = xstage_hi(hs, p, I, j);
+    const int Iv = q4_block_isum(wb, xa, xb, hs.qsum[p * nbi + j]);
+    const float part_v = (db * hs.d[p * nbi + j]) * (float)Iv;
+    const float gw = s_pw[p];
 #pragma unroll
-      for (int b = 0; b < B; ++b)
-        if (b == pb) acc[b] = fmaf(gw, part_v, acc[b]);
+    for (int b = 0; b < B; ++b)
+      if (b == pb) acc[b] = fmaf(gw, part_v, acc[b]);
+  };
+  // every pair of list entry c0 + c, in pair order
+  auto consume_chunk = [&](const DownChunk<TI> &ch, int c0) {
+    int pbeg[kDownCH], pend[kDownCH], isu[kDownCH];
+#pragma unroll
+    for (int c = 0; c < kDownCH; ++c) {  // list metadata first: LDS reads in flight together
+      const int u = wl[min(c0 + c, max(n - 1, 0))];
+      isu[c] = u < U;
+      pbeg[c] = isu[c] ? s_off[u] : 0;
+      pend[c] = isu[c] ? s_off[u + 1] : B;
+    }
+#pragma unroll
+    for (int c = 0; c < kDownCH; ++c) {
+      if (c0 + c < n) {
+        for (int pi = pbeg[c]; pi < pend[c]; ++pi) {
+          const int p = isu[c] ? s_pairs[pi] : Bk + pi;
+          const int pb = isu[c] ? p / k : pi;
+#pragma unroll
+          for (int ti = 0; ti < TI; ++ti) pair_block(p, pb, ch.w[c][ti], ch.d[c][ti], sub + 16 * ti);
+        }
+      }
     }
   };
 
   if constexpr (TI > 0) {
-    for (int c0 = 0; c0 < n; c0 += kDownCH) {
-      u32x4 wbuf[kDownCH][TI];
-      float dbf[kDownCH][TI];
-#pragma unroll
-      for (int c = 0; c < kDownCH; ++c) {
-        const uint8_t *dq;
-        const uint16_t *dd;
-        expert_ptr(wl[min(c0 + c, n - 1)], dq, dd);
-#pragma unroll
-        for (int ti = 0; ti < TI; ++ti) {
-          const int64_t blk = (int64_t)rowc * nbi + sub + 16 * ti;
-          wbuf[c][ti] = load_stream16(dq + blk * 16);
-          dbf[c][ti] = f16_bits_to_f32(load_stream2(dd + blk));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < kDownCH; ++c)
-        if (c0 + c < n)
-#pragma unroll
-          for (int ti = 0; ti < TI; ++ti)
-            consume(wl[c0 + c], wbuf[c][ti], dbf[c][ti], sub + 16 * ti);
+    for (int c0 = 0; c0 < n; c0 += 2 * kDownCH) {
+      load_chunk(c0 + kDownCH, chb);  // re-reads the last expert past the end
+      consume_chunk(cha, c0);
+      load_chunk(c0 + 2 * kDownCH, cha);
+      if (c0 + kDownCH < n) consume_chunk(chb, c0 + kDownCH);
     }
   } else {
     for (int c = 0; c < n; ++c) {
       const uint8_t *dq;
       const uint16_t *dd;
-      expert_ptr(wl[c], dq, dd);
+      expert_ptr(c, dq, dd);
+      const int u = wl[c];
+      const bool su = u < U;
+      const int pb0 = su ? s_off[u] : 0, pe0 = su ? s_off[u + 1] : B;
       for (int j = sub; j < nbi; j += 16) {
         const int64_t blk = (int64_t)rowc * nbi + j;
-        consume(wl[c], load_stream16(dq + blk * 16), f16_bits_to_f32(load_stream2(dd + blk)), j);
+        const u32x4 wb = load_stream16(dq + blk * 16);
+        const float db = f16_bits_to_f32(load_stream2(dd + blk));
+        for (int pi = pb0; pi < pe0; ++pi) {
+          const int p = su ? s_pairs[pi] : Bk + pi;
+          pair_block(p, su ? p / k : pi, wb, db, j);
+        }
       }
     }
   }
@@ -827,12 +938,9 @@ void launch_down(const MoeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((k_moe_down<B, TI>), dim3((a.L.hidden + 3) / 4), dim3(256), lds, s, a);
 }
 
-template <int B, int HC, int T>
+template <int B, int HC>
 void launch_route_fused(const MoeArgs &a, hipStream_t s) {
-  const int shared_tiles = a.L.sh_gate_qs ? a.L.inter / 32 : 0;
-  const size_t lds = xstage_bytes(B, a.L.hidden);
-  hipLaunchKernelGGL((k_moe_route_fused<B, HC, T>), dim3(a.router_wgs + shared_tiles),
-                     dim3(256), lds, s, a);
+  hipLaunchKernelGGL((k_moe_route_fused<B, HC>), dim3(a.router_wgs), dim3(256), 0, s, a);
 }
 
 template <int B>
@@ -854,10 +962,10 @@ void launch_experts(const MoeArgs &a, hipStream_t s) {
 template <int B>
 void launch_route(const MoeArgs &a, hipStream_t s) {
   switch (a.L.hidden) {
-    case 1024: launch_route_fused<B, 4, 2>(a, s); break;
-    case 2048: launch_route_fused<B, 8, 4>(a, s); break;
-    case 4096: launch_route_fused<B, 16, 8>(a, s); break;
-    default: launch_route_fused<B, 0, 0>(a, s); break;
+    case 1024: launch_route_fused<B, 4>(a, s); break;
+    case 2048: launch_route_fused<B, 8>(a, s); break;
+    case 4096: launch_route_fused<B, 16>(a, s); break;
+    default: launch_route_fused<B, 0>(a, s); break;
   }
 }
 
@@ -897,12 +1005,10 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
   // the ticket (one top-k, then device-scope fences) costs less
   const int knob = moe_ticket_knob();
   a.topk_in_k2 = knob > 0 ? 0 : (knob < 0 ? 1 : (B <= 2 ? 1 : 0));
-  // K1 already runs the shared expert's gate/up tiles
   switch (B) {
 #define MMV_LAYER_CASE(BB)    \
   case BB:                    \
     launch_route<BB>(a, s);   \
-    a.routed_shared = 0;      \
     launch_experts<BB>(a, s); \
     break;
     MMV_LAYER_CASE(1) MMV_LAYER_CASE(2) MMV_LAYER_CASE(3) MMV_LAYER_CASE(4)

@@ -99,13 +99,16 @@ __device__ __forceinline__ void xpre_quantize(const XPre<MAXT> &p, int nrows, in
                                               int base = 0, int nth = 0) {
   const int nb = K >> 5, total = nrows * nb * 8;
   if (nth == 0) nth = blockDim.x;
+  // an unconditional use of every loaded value keeps each load where it was
+  // issued (ahead of any later weight loads) instead of letting the
+  // compiler sink it into the guarded block below
+#pragma unroll
+  for (int i = 0; i < MAXT; ++i) asm volatile("" ::"v"(p.v[i]));
 #pragma unroll
   for (int i = 0; i < MAXT; ++i) {
     const int t = base + (int)threadIdx.x + i * nth;
-    // quantized unconditionally: the cross-lane steps keep the loads that
-    // feed them in place (ahead of any later weight loads)
-    const Q8Block q = q8_1_quantize8(p.v[i]);
     if (t < total) {  // uniform over each 8-lane group: total % 8 == 0
+      const Q8Block q = q8_1_quantize8(p.v[i]);
       const int r = t / (nb * 8);
       const int rem = t - r * nb * 8;
       const int j = rem >> 3, s = rem & 7;
