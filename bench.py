@@ -207,7 +207,7 @@ def moe_section(mm, dev, E, k, layers, Bs, steps, warmup, H=2048, I=512):
         X = synth.activations(layers * B, H, 0, "moebench-x", E, B, device=dev).view(layers, B, H)
         Y = torch.empty((layers, B, H), device=dev)
         ids = torch.empty((layers, B, k), dtype=torch.int32, device=dev)
-        ws = torch.zeros((layers, mm.moe_workspace_bytes(lay[0], B)), dtype=torch.uint8,
+        ws = torch.empty((layers, mm.moe_workspace_bytes(lay[0], B)), dtype=torch.uint8,
                          device=dev)
 
         def step():
@@ -223,7 +223,7 @@ def moe_section(mm, dev, E, k, layers, Bs, steps, warmup, H=2048, I=512):
                             mean_unique_experts=sum(uniq) / layers,
                             MB_per_layer=nbytes / layers / 1e6, GBps=nbytes / t / 1e9,
                             frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS,
-                            launches_per_layer=3)
+                            launches_per_layer=3 if B <= 2 else 4)
         del X, Y, ids, ws, g
     if len(Bs) > 1:
         res["ratio_Bmax_B1_time"] = res[f"B{max(Bs)}"]["us_per_layer"] / res["B1"]["us_per_layer"]

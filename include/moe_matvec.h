@@ -230,14 +230,14 @@ int moe_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx,
                    const mmv_moe_debug *dbg, void *stream);
 
 /* --------------------------------------------------------------------------
- * moe_layer_decode -- the whole MoE layer in three launches: router rows
- *   and the shared expert's gate/up (routing-independent) in one grid whose
- *   last router workgroup runs top-k; the routed gate/up; the down
- *   projection with the combine.  Routing stays in device memory.
- *   ids / weights (B x k) may be NULL; when given they receive the routing
- *   decision.  The workspace must be zero-filled once before its first use
- *   (its synchronization word must start at zero); every call leaves it
- *   zero again.  Calls that share a workspace must not overlap.
+ * moe_layer_decode -- the whole MoE layer: the router rows; top-k with the
+ *   per-expert row lists (inside every gate/up workgroup for B <= 2, in a
+ *   one-workgroup kernel of its own for larger B); the gate/up of the
+ *   shared and the routed experts with the Q8_1 epilogue; the down
+ *   projection with the combine.  Three launches for B <= 2, four above.
+ *   Routing stays in device memory.  ids / weights (B x k) may be NULL;
+ *   when given they receive the routing decision.  The workspace needs no
+ *   initialisation; calls that share a workspace must not overlap.
  *   [STRATA: Pass 3 item 1, graph replay; FOURTEEN: launches below five
  *   microseconds cost more than they run; "The router with 257 rows"]
  * ------------------------------------------------------------------------ */

@@ -325,14 +325,13 @@ def moe_mul_mat_id(layer: MoeLayer, x: torch.Tensor, ids: torch.Tensor, weights:
 
 def moe_layer_decode(layer: MoeLayer, x: torch.Tensor, out=None, workspace=None, ids=None,
                      weights=None, stream=None):
-    """Whole MoE layer (route + experts) on device; returns out [B, H].
-    A workspace must be zero-filled before its first use (see moe_matvec.h)."""
+    """Whole MoE layer (route + experts) on device; returns out [B, H]."""
     x2 = x.unsqueeze(0) if x.dim() == 1 else x
     B = x2.shape[0]
     if out is None:
         out = torch.empty((B, layer.H), dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace = torch.zeros(moe_workspace_bytes(layer, B), dtype=torch.uint8,
+        workspace = torch.empty(moe_workspace_bytes(layer, B), dtype=torch.uint8,
                                 device=x.device)
     y2 = out.unsqueeze(0) if out.dim() == 1 else out
     _check("moe_layer_decode", lib().moe_layer_decode(

@@ -330,13 +330,23 @@ struct MoeArgs {
   int has_dbg;
   // fused routing (K1)
   float *logits;     // B x (E+1)
-  int32_t *counter;  // zero before the launch; K1's last workgroup re-zeroes it
+  int gather_ready;  // 1: a previous kernel published the row lists (K2 reads them)
   int32_t *ids_out;
   float *weights_out;
   float *shared_w_out;
   int router_wgs;
   int topk_in_k2;    // 1: every K2 workgroup runs top-k on the logits itself
 };
+
+// Published row lists (workspace): [0] U, [1, 1+Bk) unique experts,
+// [1+Bk, 2+2Bk) offsets, [2+2Bk, 2+3Bk) pairs.  Thread t of a 256-thread
+// workgroup holds entries t and t + 256 (gl_n = 3 Bk + 2 <= 386).
+__device__ __forceinline__ void put_gather_entry(int idx, int val, int Bk, GatherLds &g) {
+  if (idx == 0) g.U = val;
+  else if (idx < 1 + Bk) g.unique[idx - 1] = val;
+  else if (idx < 2 + 2 * Bk) g.offsets[idx - 1 - Bk] = val;
+  else if (idx < 2 + 3 * Bk) g.pairs[idx - 2 - 2 * Bk] = val;
+}
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
@@ -584,8 +594,16 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     }
   }
 
-  build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs)>(ids, Bk, E, g);
-  if (blockIdx.x == 0) publish_gather();
+  if (a.gather_ready) {  // the top-k kernel published the row lists
+    const int t = threadIdx.x, gl_n = 3 * Bk + 2;
+    const int g0 = a.gather[min(t, gl_n - 1)], g1 = a.gather[min(t + 256, gl_n - 1)];
+    if (t < gl_n) put_gather_entry(t, g0, Bk, g);
+    if (t + 256 < gl_n) put_gather_entry(t + 256, g1, Bk, g);
+    __syncthreads();
+  } else {
+    build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs)>(ids, Bk, E, g);
+    if (blockIdx.x == 0) publish_gather();
+  }
   if (!shared_slot && slot >= g.U) return;  // uniform over the workgroup
 
   const uint8_t *gq, *uq;
@@ -613,30 +631,41 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K1: router rows; with the ticket, the last router workgroup runs top-k
+// K1: router rows (one wave per row, logits to the workspace)
 // ---------------------------------------------------------------------------
 template <int B, int HC>
-__global__ __launch_bounds__(256) void k_moe_route_fused(MoeArgs a) {
-  __shared__ int is_last;
+__global__ __launch_bounds__(256) void k_moe_router(MoeArgs a) {
   const mmv_moe_layer &L = a.L;
-  const int E = L.n_experts, H = L.hidden, k = L.top_k;
-  const bool has_sg = L.shared_gate_row != nullptr;
-
+  const int E = L.n_experts, H = L.hidden;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e < E + (has_sg ? 1 : 0)) {
+  if (e < E + (L.shared_gate_row ? 1 : 0)) {
     const float *row = e < E ? L.router + (int64_t)e * H : L.shared_gate_row;
     router_row<B, HC>(row, H, a.X, a.ldx, a.logits + e, E + 1);
   }
-  if (a.topk_in_k2) return;  // the next kernel runs top-k
-  __threadfence();  // logits visible device-wide before the ticket
+}
+
+// ---------------------------------------------------------------------------
+// K1b (more rows): one workgroup runs top-k for every row, builds the row
+// lists and publishes both, so the gate/up workgroups only read them.
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ __launch_bounds__(256) void k_moe_topk_gather(MoeArgs a) {
+  __shared__ GatherLds g;
+  __shared__ int s_ids[kMaxPairs];
+  __shared__ float s_w[kMaxPairs];
+  __shared__ float s_sw[MMV_MAX_BATCH];
+  const mmv_moe_layer &L = a.L;
+  const int E = L.n_experts, k = L.top_k, Bk = B * k, t = threadIdx.x;
+  topk_any(a.logits, E + 1, E, B, k, L.shared_gate_row ? 1 : 0, s_ids, s_w, s_sw);
   __syncthreads();
-  if (threadIdx.x == 0) is_last = atomicAdd(a.counter, 1) == (int)gridDim.x - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  topk_any(a.logits, E + 1, E, B, k, has_sg ? 1 : 0, a.ids_out, a.weights_out,
-           a.shared_w_out);
-  if (threadIdx.x == 0) atomicExch(a.counter, 0);  // ready for the next launch
+  if (t < Bk) { a.ids_out[t] = s_ids[t]; a.weights_out[t] = s_w[t]; }
+  if (t < B) a.shared_w_out[t] = s_sw[t];
+  build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs)>(s_ids, Bk, E, g);
+  int32_t *gl = a.gather;
+  if (t == 0) gl[0] = g.U;
+  if (t < g.U) gl[1 + t] = g.unique[t];
+  if (t <= g.U) gl[1 + Bk + t] = g.offsets[t];
+  if (t < g.offsets[g.U]) gl[2 + 2 * Bk + t] = g.pairs[t];
 }
 
 // ---------------------------------------------------------------------------
@@ -880,15 +909,15 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 
-// MMV_MOE_TICKET=1: top-k by the last router workgroup (atomic ticket and
-// device-scope fences); =0: top-k in every gate/up workgroup; unset: by B.
-// Prints one line the first time it is read.  Returns 1, -1 or 0 (unset).
-int moe_ticket_knob() {
-  const char *v = getenv("MMV_MOE_TICKET");
+// MMV_MOE_TOPK_KERNEL=1: top-k and row lists in a kernel of their own;
+// =0: top-k in every gate/up workgroup; unset: by B.  Prints one line the
+// first time it is read.  Returns 1, -1 or 0 (unset).
+int moe_topk_knob() {
+  const char *v = getenv("MMV_MOE_TOPK_KERNEL");
   if (!v || !*v) return 0;
   static bool printed = false;
   if (!printed) {
-    fprintf(stderr, "[moe_matvec] MMV_MOE_TICKET=%s\n", v);
+    fprintf(stderr, "[moe_matvec] MMV_MOE_TOPK_KERNEL=%s\n", v);
     printed = true;
   }
   return atoi(v) ? 1 : -1;
@@ -915,7 +944,7 @@ MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
   a.has_dbg = dbg != nullptr;
   a.dbg = dbg ? *dbg : mmv_moe_debug{nullptr, nullptr, nullptr, nullptr, nullptr};
   a.logits = reinterpret_cast<float *>(ws + lay.logits);
-  a.counter = reinterpret_cast<int32_t *>(ws + lay.counter);
+  a.gather_ready = 0;
   a.ids_out = nullptr;
   a.weights_out = nullptr;
   a.shared_w_out = nullptr;
@@ -939,8 +968,8 @@ void launch_down(const MoeArgs &a, hipStream_t s) {
 }
 
 template <int B, int HC>
-void launch_route_fused(const MoeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((k_moe_route_fused<B, HC>), dim3(a.router_wgs), dim3(256), 0, s, a);
+void launch_router_k1(const MoeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((k_moe_router<B, HC>), dim3(a.router_wgs), dim3(256), 0, s, a);
 }
 
 template <int B>
@@ -962,10 +991,10 @@ void launch_experts(const MoeArgs &a, hipStream_t s) {
 template <int B>
 void launch_route(const MoeArgs &a, hipStream_t s) {
   switch (a.L.hidden) {
-    case 1024: launch_route_fused<B, 4>(a, s); break;
-    case 2048: launch_route_fused<B, 8>(a, s); break;
-    case 4096: launch_route_fused<B, 16>(a, s); break;
-    default: launch_route_fused<B, 0>(a, s); break;
+    case 1024: launch_router_k1<B, 4>(a, s); break;
+    case 2048: launch_router_k1<B, 8>(a, s); break;
+    case 4096: launch_router_k1<B, 16>(a, s); break;
+    default: launch_router_k1<B, 0>(a, s); break;
   }
 }
 
@@ -1001,15 +1030,19 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
   a.weights_out = weights;
   a.shared_w_out = sw;
   a.router_wgs = (L.n_experts + (L.shared_gate_row ? 1 : 0) + 3) / 4;
-  // top-k in every gate/up workgroup is cheapest for few rows; for more rows
-  // the ticket (one top-k, then device-scope fences) costs less
-  const int knob = moe_ticket_knob();
+  // Top-k in every gate/up workgroup costs no launch and is cheapest for
+  // one or two rows; for more rows it grows with B in every workgroup, and
+  // one workgroup of its own (plus a launch) costs less.  A grid-wide
+  // barrier or ticket inside one kernel measured slower than a launch.
+  const int knob = moe_topk_knob();
   a.topk_in_k2 = knob > 0 ? 0 : (knob < 0 ? 1 : (B <= 2 ? 1 : 0));
+  a.gather_ready = a.topk_in_k2 ? 0 : 1;
   switch (B) {
-#define MMV_LAYER_CASE(BB)    \
-  case BB:                    \
-    launch_route<BB>(a, s);   \
-    launch_experts<BB>(a, s); \
+#define MMV_LAYER_CASE(BB)                                                              \
+  case BB:                                                                              \
+    launch_route<BB>(a, s);                                                             \
+    if (!a.topk_in_k2) hipLaunchKernelGGL((k_moe_topk_gather<BB>), dim3(1), dim3(256), 0, s, a); \
+    launch_experts<BB>(a, s);                                                           \
     break;
     MMV_LAYER_CASE(1) MMV_LAYER_CASE(2) MMV_LAYER_CASE(3) MMV_LAYER_CASE(4)
     MMV_LAYER_CASE(5) MMV_LAYER_CASE(6) MMV_LAYER_CASE(7) MMV_LAYER_CASE(8)

@@ -84,18 +84,21 @@ def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
     assert rel_l2_rows(npc(y), y_ref) <= MOE_TOL
 
 
-@pytest.mark.parametrize("ticket", ["0", "1"])
+@pytest.mark.parametrize("topk_kernel", ["0", "1"])
 @pytest.mark.parametrize("E,H,I,k,B", [(256, 2048, 512, 8, 1), (512, 2048, 512, 10, 4),
-                                       (32, 512, 64, 4, 8), (20, 96, 64, 3, 2)])
-def test_moe_layer_decode(mm, orc, dev, monkeypatch, ticket, E, H, I, k, B):
-    # ticket "1": top-k by the last router workgroup; "0": in every gate/up workgroup
-    monkeypatch.setenv("MMV_MOE_TICKET", ticket)
+                                       (32, 512, 64, 4, 8), (20, 96, 64, 3, 2),
+                                       (512, 2048, 512, 10, 8)])
+def test_moe_layer_decode(mm, orc, dev, monkeypatch, topk_kernel, E, H, I, k, B):
+    # "1": top-k and row lists in a kernel of their own; "0": in every gate/up workgroup
+    monkeypatch.setenv("MMV_MOE_TOPK_KERNEL", topk_kernel)
     layer, ref = build_moe(mm, orc, E, H, I, k, 0, "dec", E, H, I, device=dev)
     X = synth.activations(B, H, 0, "dec", E, B, device=dev)
     ids = torch.empty((B, k), dtype=torch.int32, device=dev)
     w = torch.empty((B, k), dtype=torch.float32, device=dev)
-    y = mm.moe_layer_decode(layer, X, ids=ids, weights=w)
-    y2 = mm.moe_layer_decode(layer, X)
+    # the workspace needs no initialisation: start from garbage, reuse it
+    ws = torch.full((mm.moe_workspace_bytes(layer, B),), 0xA5, dtype=torch.uint8, device=dev)
+    y = mm.moe_layer_decode(layer, X, ids=ids, weights=w, workspace=ws)
+    y2 = mm.moe_layer_decode(layer, X, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
     out = ref.layer(npc(X))
