@@ -153,6 +153,57 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_bf16_ni(
   }
 }
 
+// LDS-x variant for B = 1 and K = 512 * NI: a workgroup of WPB waves (R
+// rows each) first requests x (K fp32, once for the workgroup instead of
+// once per wave), then every weight chunk of its rows; x goes to LDS while
+// the weights are in flight, and the FMAs read it from there.  Same per-row
+// order as k_gemv_bf16_ni (chunk ascending, 8 products per chunk, then the
+// lanes), so the two give identical bits.
+template <int NI, int WPB, int R>
+__global__ __launch_bounds__(WPB * 64) void k_gemv_bf16_xl(
+    const uint16_t *__restrict__ W, int N, int64_t ldw, const float *__restrict__ X,
+    float *__restrict__ Y) {
+  __shared__ __align__(16) float xs[NI * 512];
+  constexpr int NT = WPB * 64;
+  constexpr int XL = (NI * 128 + NT - 1) / NT;  // float4 loads of x per thread
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * WPB + (threadIdx.x >> 6)) * R;
+  f32x4 xv[XL];
+#pragma unroll
+  for (int m = 0; m < XL; ++m)
+    xv[m] = load_f4(X + 4 * min((int)threadIdx.x + NT * m, NI * 128 - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 w[R][NI];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint8_t *wr =
+        reinterpret_cast<const uint8_t *>(W + (int64_t)min(row0 + r, N - 1) * ldw);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) w[r][i] = load_stream16(wr + (int64_t)(lane + 64 * i) * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < XL; ++m)
+    if ((int)threadIdx.x + NT * m < NI * 128)
+      *reinterpret_cast<f32x4 *>(&xs[4 * (threadIdx.x + NT * m)]) = xv[m];
+  __syncthreads();
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const float *xp = xs + 8 * (lane + 64 * i);
+    const f32x4 xa = *reinterpret_cast<const f32x4 *>(xp);
+    const f32x4 xb = *reinterpret_cast<const f32x4 *>(xp + 4);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = dot8_bf16(w[r][i], xa, xb, acc[r]);
+  }
+  gsum_last_n<64>(acc);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (lane == 63 && row0 + r < N) Y[row0 + r] = acc[r];
+}
+
 // B >= 2: the x rows form a small dense operand, and 8 fp32 FMAs per weight
 // would make the VALU, not HBM, the bound.  v_mfma_f32_16x16x32_bf16 takes a
 // 16-row x 32-k tile of W (one 128-bit load per lane: row l%16, k 8*(l/16)..)
@@ -266,12 +317,13 @@ hipError_t launch_ni(const Bf16Args &a) {
 }
 
 // tuning knobs for experiments: MMV_BF16_R (rows per wave), MMV_BF16_WPB
-// (waves per workgroup); each prints one line the first time it is used
+// (waves per workgroup), MMV_BF16_XL (waves per workgroup of the LDS-x
+// kernel; -1: off); each prints one line the first time it is used
 int env_knob(const char *name) {
   const char *v = getenv(name);
   if (!v || !*v) return 0;
-  static thread_local bool printed[2] = {false, false};
-  const int idx = name[9] == 'R' ? 0 : 1;
+  static thread_local bool printed[3] = {false, false, false};
+  const int idx = name[9] == 'R' ? 0 : (name[9] == 'W' ? 1 : 2);  // R, WPB, XL
   if (!printed[idx]) {
     fprintf(stderr, "[moe_matvec] %s=%s\n", name, v);
     printed[idx] = true;
@@ -299,6 +351,21 @@ hipError_t launch_mfma(const Bf16Args &a) {
   return hipGetLastError();
 }
 
+template <int NI, int WPB>
+hipError_t launch_xl(const Bf16Args &a) {
+  hipLaunchKernelGGL((k_gemv_bf16_xl<NI, WPB, 1>), dim3((a.N + WPB - 1) / WPB), dim3(WPB * 64),
+                     0, a.s, a.W, a.N, a.ldw, a.X, a.Y);
+  return hipGetLastError();
+}
+
+template <int NI>
+hipError_t dispatch_xl(const Bf16Args &a, int WPB) {
+  if (WPB >= 16) return launch_xl<NI, 16>(a);
+  if (WPB >= 8) return launch_xl<NI, 8>(a);
+  if (WPB >= 4) return launch_xl<NI, 4>(a);
+  return launch_xl<NI, 2>(a);
+}
+
 template <int B>
 hipError_t dispatch_b(const Bf16Args &a) {
   if constexpr (B >= 2) {
@@ -311,6 +378,24 @@ hipError_t dispatch_b(const Bf16Args &a) {
     return launch_mfma<B, 4, 8>(a);
   } else {
     const int kr = env_knob("MMV_BF16_R"), kw = env_knob("MMV_BF16_WPB");
+    const int kx = env_knob("MMV_BF16_XL");
+    if (a.K % 512 == 0) {
+      // x staged once per workgroup in LDS: measured faster for long rows
+      // (2560 x 9728: 4 waves per workgroup) and for many rows (19456 x 2560:
+      // 8); for 2560 x 2560 the per-wave kernel is as fast
+      const int NI = a.K / 512;
+      const int xl = kx != 0 ? kx : (NI >= 8 ? 4 : (NI >= 4 && a.N >= 8192 ? 8 : -1));
+      if (xl > 0) {
+        switch (NI) {
+          case 4: return dispatch_xl<4>(a, xl);
+          case 5: return dispatch_xl<5>(a, xl);
+          case 8: return dispatch_xl<8>(a, xl);
+          case 16: return dispatch_xl<16>(a, xl);
+          case 19: return dispatch_xl<19>(a, xl);
+          default: break;
+        }
+      }
+    }
     if (a.K % 512 == 0) {
       const int NI = a.K / 512;
       // enough rows per wave that a wave streams >= ~8 KiB; one-wave

@@ -63,13 +63,15 @@ def test_bf16_batch_invariance_and_determinism(mm, dev):
         assert torch.equal(mm.gemv_bf16(W, X[:B].contiguous()), y8[:B])
 
 
-@pytest.mark.parametrize("knobs", [dict(MMV_BF16_R="1", MMV_BF16_WPB="1"),
-                                   dict(MMV_BF16_R="2", MMV_BF16_WPB="4"),
-                                   dict(MMV_BF16_R="4", MMV_BF16_WPB="1")])
+@pytest.mark.parametrize("knobs", [dict(MMV_BF16_XL="-1", MMV_BF16_R="1", MMV_BF16_WPB="1"),
+                                   dict(MMV_BF16_XL="-1", MMV_BF16_R="2", MMV_BF16_WPB="4"),
+                                   dict(MMV_BF16_XL="-1", MMV_BF16_R="4", MMV_BF16_WPB="1"),
+                                   dict(MMV_BF16_XL="2"), dict(MMV_BF16_XL="16")])
 def test_bf16_b1_variants_identical(mm, dev, monkeypatch, knobs):
-    # every B = 1 variant (rows per wave, waves per workgroup) sums each row in
-    # the same order, so all give the same bits as the default choice
-    for N, K in ((1000, 2560), (2560, 9728), (333, 1016)):
+    # every B = 1 variant (x from L1/L2 or staged in LDS, rows per wave, waves
+    # per workgroup) sums each row in the same order: all give the same bits
+    for N, K in ((1000, 2560), (2560, 9728), (333, 1016), (300, 2048), (257, 4096),
+                 (100, 8192), (9000, 2560)):
         W = synth.bf16_weights(N, K, 0, "var", N, K, device=dev)
         x = synth.activations(1, K, 0, "var", N, K, device=dev)
         y0 = mm.gemv_bf16(W, x)
