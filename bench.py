@@ -129,7 +129,7 @@ def dominant_kernel(mm, dev, W, layers, steps, warmup):
     g = capture(step)
     t = time_graph(g, steps, warmup) / layers
     per_launch = 2 * N * K + 4 * K + 4 * N
-    return dict(kernel="k_gemv_bf16_ni<1, 2, 5, 1> (gate+up 19456x2560, B=1)", s_per_launch=t,
+    return dict(kernel="k_gemv_bf16_xl<5, 8, 1> (gate+up 19456x2560, B=1)", s_per_launch=t,
                 bytes_per_launch=per_launch, GBps=per_launch / t / 1e9)
 
 
