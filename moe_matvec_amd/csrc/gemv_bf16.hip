@@ -153,25 +153,50 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_bf16_ni(
   }
 }
 
-// LDS-x variant for B = 1 and K = 512 * NI: a workgroup of WPB waves (R
-// rows each) first requests x (K fp32, once for the workgroup instead of
-// once per wave), then every weight chunk of its rows; x goes to LDS while
-// the weights are in flight, and the FMAs read it from there.  Same per-row
-// order as k_gemv_bf16_ni (chunk ascending, 8 products per chunk, then the
-// lanes), so the two give identical bits.
-template <int NI, int WPB, int R>
+// LDS-x variant for K = 512 * NI and B rows of x: a workgroup of WPB waves
+// (R rows each) requests x (once for the workgroup instead of once per
+// wave), then every weight chunk of its rows; x goes to LDS while the
+// weights are in flight, and the FMAs read it from there, each x chunk once
+// for the R rows.  x is staged in slabs of SL chunks (B * SL * 2 KiB of LDS),
+// slab after slab when K is longer, the next slab's loads in flight while
+// the current one is used.  Every (row, b) sum has the order of
+// k_gemv_bf16_ni (chunk ascending, 8 products per chunk, then the lanes),
+// whatever B, R, WPB and SL: all give the bits of the B = 1 kernel, row by
+// row.
+template <int B, int NI, int WPB, int R, int SL>
 __global__ __launch_bounds__(WPB * 64) void k_gemv_bf16_xl(
     const uint16_t *__restrict__ W, int N, int64_t ldw, const float *__restrict__ X,
-    float *__restrict__ Y) {
-  __shared__ __align__(16) float xs[NI * 512];
+    int64_t ldx, float *__restrict__ Y, int64_t ldy) {
+  extern __shared__ __align__(16) float xs[];  // [B][SL * 512]
   constexpr int NT = WPB * 64;
-  constexpr int XL = (NI * 128 + NT - 1) / NT;  // float4 loads of x per thread
+  constexpr int NSL = (NI + SL - 1) / SL;     // slabs
   const int lane = threadIdx.x & 63;
   const int row0 = (blockIdx.x * WPB + (threadIdx.x >> 6)) * R;
-  f32x4 xv[XL];
+
+  // float4 task t of slab sl: row b = t / (nc * 128), chunk c0 + (t % ...)
+  auto slab_load = [&](int sl, f32x4 (&xv)[(B * SL * 128 + NT - 1) / NT]) {
+    const int c0 = sl * SL, nc = min(SL, NI - c0), tot = B * nc * 128;
 #pragma unroll
-  for (int m = 0; m < XL; ++m)
-    xv[m] = load_f4(X + 4 * min((int)threadIdx.x + NT * m, NI * 128 - 1));
+    for (int m = 0; m < (B * SL * 128 + NT - 1) / NT; ++m) {
+      const int t = min((int)threadIdx.x + NT * m, tot - 1);
+      const int b = t / (nc * 128), q = t - b * nc * 128;
+      xv[m] = load_f4(X + (int64_t)b * ldx + 4 * (c0 * 128 + q));
+    }
+  };
+  auto slab_store = [&](int sl, const f32x4 (&xv)[(B * SL * 128 + NT - 1) / NT]) {
+    const int nc = min(SL, NI - sl * SL), tot = B * nc * 128;
+#pragma unroll
+    for (int m = 0; m < (B * SL * 128 + NT - 1) / NT; ++m) {
+      const int t = (int)threadIdx.x + NT * m;
+      if (t < tot) {
+        const int b = t / (nc * 128), q = t - b * nc * 128;
+        *reinterpret_cast<f32x4 *>(&xs[b * SL * 512 + 4 * q]) = xv[m];
+      }
+    }
+  };
+
+  f32x4 xv[(B * SL * 128 + NT - 1) / NT];
+  slab_load(0, xv);
   __builtin_amdgcn_sched_barrier(0);
   u32x4 w[R][NI];
 #pragma unroll
@@ -182,26 +207,35 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_bf16_xl(
     for (int i = 0; i < NI; ++i) w[r][i] = load_stream16(wr + (int64_t)(lane + 64 * i) * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
+  float acc[R * B];
 #pragma unroll
-  for (int m = 0; m < XL; ++m)
-    if ((int)threadIdx.x + NT * m < NI * 128)
-      *reinterpret_cast<f32x4 *>(&xs[4 * (threadIdx.x + NT * m)]) = xv[m];
-  __syncthreads();
-  float acc[R];
+  for (int j = 0; j < R * B; ++j) acc[j] = 0.0f;
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int sl = 0; sl < NSL; ++sl) {
+    if (sl > 0) __syncthreads();  // the previous slab is consumed
+    slab_store(sl, xv);
+    __syncthreads();
+    if (sl + 1 < NSL) slab_load(sl + 1, xv);  // in flight while this slab is used
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const float *xp = xs + 8 * (lane + 64 * i);
-    const f32x4 xa = *reinterpret_cast<const f32x4 *>(xp);
-    const f32x4 xb = *reinterpret_cast<const f32x4 *>(xp + 4);
+    for (int i = sl * SL; i < (sl + 1) * SL && i < NI; ++i) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = dot8_bf16(w[r][i], xa, xb, acc[r]);
+      for (int b = 0; b < B; ++b) {
+        const float *xp = xs + b * SL * 512 + 8 * (lane + 64 * (i - sl * SL));
+        const f32x4 xa = *reinterpret_cast<const f32x4 *>(xp);
+        const f32x4 xb = *reinterpret_cast<const f32x4 *>(xp + 4);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r * B + b] = dot8_bf16(w[r][i], xa, xb, acc[r * B + b]);
+      }
+    }
   }
   gsum_last_n<64>(acc);
+  if (lane == 63) {
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (lane == 63 && row0 + r < N) Y[row0 + r] = acc[r];
+    for (int r = 0; r < R; ++r)
+      if (row0 + r < N)
+#pragma unroll
+        for (int b = 0; b < B; ++b) Y[(int64_t)b * ldy + row0 + r] = acc[r * B + b];
+  }
 }
 
 // B >= 2: the x rows form a small dense operand, and 8 fp32 FMAs per weight
@@ -351,19 +385,54 @@ hipError_t launch_mfma(const Bf16Args &a) {
   return hipGetLastError();
 }
 
-template <int NI, int WPB>
+// slab length: x of B rows in at most 80 KiB of LDS (SL chunks of 512)
+template <int B, int NI>
+constexpr int xl_slab() { return cmin(NI, 40 / B); }
+
+template <int B, int NI, int WPB, int R>
 hipError_t launch_xl(const Bf16Args &a) {
-  hipLaunchKernelGGL((k_gemv_bf16_xl<NI, WPB, 1>), dim3((a.N + WPB - 1) / WPB), dim3(WPB * 64),
-                     0, a.s, a.W, a.N, a.ldw, a.X, a.Y);
+  constexpr int RPB = WPB * R, SL = xl_slab<B, NI>();
+  const size_t lds = (size_t)B * SL * 512 * 4;
+  hipLaunchKernelGGL((k_gemv_bf16_xl<B, NI, WPB, R, SL>), dim3((a.N + RPB - 1) / RPB),
+                     dim3(WPB * 64), lds, a.s, a.W, a.N, a.ldw, a.X, a.ldx, a.Y, a.ldy);
   return hipGetLastError();
 }
 
 template <int NI>
 hipError_t dispatch_xl(const Bf16Args &a, int WPB) {
-  if (WPB >= 16) return launch_xl<NI, 16>(a);
-  if (WPB >= 8) return launch_xl<NI, 8>(a);
-  if (WPB >= 4) return launch_xl<NI, 4>(a);
-  return launch_xl<NI, 2>(a);
+  if (WPB >= 16) return launch_xl<1, NI, 16, 1>(a);
+  if (WPB >= 8) return launch_xl<1, NI, 8, 1>(a);
+  if (WPB >= 4) return launch_xl<1, NI, 4, 1>(a);
+  return launch_xl<1, NI, 2, 1>(a);
+}
+
+// B >= 2 with x in LDS, K = 512 * NI: two rows per wave share each x read;
+// MMV_BF16_XL = 100 * R + WPB overrides (-1: off).  Returns
+// hipErrorNotSupported for other K.
+template <int B>
+hipError_t dispatch_xl_b(const Bf16Args &a, int knob) {
+  if (a.K % 512 != 0) return hipErrorNotSupported;
+  const int NI = a.K / 512;
+  // long rows at B > 2: two rows' weights do not fit in registers, and with
+  // one row per wave the LDS reads of x (2 B per weight chunk) bound the
+  // kernel; the MFMA kernel is faster there (2560 x 9728, B = 8: 27.7 us
+  // against 35 us)
+  if (knob == 0 && NI > 8 && B > 2) return hipErrorNotSupported;
+  const int R = knob >= 100 ? knob / 100 : 2;
+  const int WPB = knob ? knob % 100 : 8;
+#define MMV_XLB(NIV)                                                                 \
+  if (NI == NIV) {                                                                   \
+    if constexpr (NIV * 4 <= 24) {                                                   \
+      if (R >= 4) return WPB >= 8 ? launch_xl<B, NIV, 8, 4>(a) : launch_xl<B, NIV, 4, 4>(a); \
+    }                                                                                \
+    if constexpr (NIV * 2 <= 40) {                                                   \
+      if (R >= 2) return WPB >= 8 ? launch_xl<B, NIV, 8, 2>(a) : launch_xl<B, NIV, 4, 2>(a); \
+    }                                                                                \
+    return WPB >= 8 ? launch_xl<B, NIV, 8, 1>(a) : launch_xl<B, NIV, 4, 1>(a);        \
+  }
+  MMV_XLB(1) MMV_XLB(2) MMV_XLB(4) MMV_XLB(5) MMV_XLB(8) MMV_XLB(16) MMV_XLB(19)
+#undef MMV_XLB
+  return hipErrorNotSupported;
 }
 
 template <int B>
@@ -371,8 +440,13 @@ hipError_t dispatch_b(const Bf16Args &a) {
   if constexpr (B >= 2) {
     // few 16-row tiles: more waves per tile keep enough loads in flight
     const int kw = env_knob("MMV_BF16_WPB");
+    const int kx = env_knob("MMV_BF16_XL");  // experiments: 100 * R + WPB; -1: off
+    if (kx >= 0) {
+      const hipError_t e = dispatch_xl_b<B>(a, kx);
+      if (e != hipErrorNotSupported) return e;
+    }
     const int tiles = (a.N + 15) / 16;
-    const int KS = kw ? kw : (tiles < 1024 ? 16 : 8);
+    const int KS = kw ? kw : 8;
     if (KS >= 16) return launch_mfma<B, 16, 8>(a);
     if (KS >= 8) return launch_mfma<B, 8, 8>(a);
     return launch_mfma<B, 4, 8>(a);

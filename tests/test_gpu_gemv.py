@@ -46,21 +46,42 @@ def test_bf16_integer_pin_bit_exact(mm, orc, dev):
 
 
 def test_bf16_batch_invariance_and_determinism(mm, dev):
-    # B = 1 runs fp32 FMAs on the VALU; B >= 2 runs the bf16 MFMA with x split
-    # into hi + lo.  Rows agree bit for bit among all B >= 2 calls, and with
-    # the B = 1 call within rounding.
-    N, K = 3000, 2560
-    W = synth.bf16_weights(N, K, 0, "inv", device=dev)
-    X = synth.activations(8, K, 0, "inv", device=dev)
-    y8 = mm.gemv_bf16(W, X)
-    assert torch.equal(y8, mm.gemv_bf16(W, X))
-    for b in range(8):
-        pair = X[[b, (b + 3) % 8]].contiguous()
-        assert torch.equal(mm.gemv_bf16(W, pair)[0], y8[b])
-        y1 = mm.gemv_bf16(W, X[b].clone())
-        assert rel_l2_rows(npc(y1)[None], npc(y8[b])[None]) <= 1e-5
-    for B in (3, 4, 5, 6, 7):
-        assert torch.equal(mm.gemv_bf16(W, X[:B].contiguous()), y8[:B])
+    # K = 512 * NI with x in LDS: every B sums each (row, b) in the B = 1
+    # kernel's order, so every row equals its 1-row call bit for bit.  For
+    # long rows at B > 2 the MFMA kernel (x split into bf16 hi + lo) takes
+    # over: rows agree bit for bit among those B, and with B = 1 within
+    # rounding.
+    for N, K, bit_b in ((3000, 2560, 8), (700, 9728, 2)):
+        W = synth.bf16_weights(N, K, 0, "inv", K, device=dev)
+        X = synth.activations(8, K, 0, "inv", K, device=dev)
+        y8 = mm.gemv_bf16(W, X)
+        assert torch.equal(y8, mm.gemv_bf16(W, X))
+        for b in range(8):
+            y1 = mm.gemv_bf16(W, X[b].clone())
+            pair = mm.gemv_bf16(W, X[[b, (b + 3) % 8]].contiguous())[0]
+            assert torch.equal(pair, y1)
+            if bit_b == 8:
+                assert torch.equal(y1, y8[b])
+            else:
+                assert rel_l2_rows(npc(y1)[None], npc(y8[b])[None]) <= 1e-5
+        for B in (3, 4, 5, 6, 7):
+            assert torch.equal(mm.gemv_bf16(W, X[:B].contiguous()), y8[:B])
+
+
+@pytest.mark.parametrize("knob", ["104", "108", "204", "404", "408"])
+def test_bf16_lds_x_variants_identical(mm, dev, monkeypatch, knob):
+    # B >= 2 with x in LDS, any rows per wave and waves per workgroup, and x
+    # slabs (K = 9728 at B = 8 stages x in four slabs): the bits of the
+    # 1-row calls
+    for N, K, B in ((1000, 2560, 8), (300, 2048, 5), (257, 4096, 3), (130, 9728, 8),
+                    (90, 9728, 2)):
+        W = synth.bf16_weights(N, K, 0, "xlb", N, K, device=dev)
+        X = synth.activations(B, K, 0, "xlb", N, K, device=dev)
+        monkeypatch.setenv("MMV_BF16_XL", knob)
+        y = mm.gemv_bf16(W, X)
+        monkeypatch.delenv("MMV_BF16_XL")
+        for b in range(B):
+            assert torch.equal(y[b], mm.gemv_bf16(W, X[b].clone()))
 
 
 @pytest.mark.parametrize("knobs", [dict(MMV_BF16_XL="-1", MMV_BF16_R="1", MMV_BF16_WPB="1"),
