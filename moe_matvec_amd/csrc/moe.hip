@@ -10,24 +10,28 @@
 // quantized to Q8 in the producing kernel, the K <= 512 down projection uses
 // four rows per wave.  "Flash-Next on Strix Halo" (Expert GEMMs) builds
 // per-expert row lists so each expert's weights are read once for all rows
-// that chose it.  Here, on gfx950, one layer is three launches:
-//  K1 router rows (one wave per row, all loads issued up front) and, in the
-//     same grid, the shared expert's gate/up tiles (they do not depend on
-//     routing); the last router workgroup to finish (atomic ticket) runs
-//     top-k: order-preserving 64-bit keys (value, ~index) so equal logits
-//     rank by lower index, DPP wave maxima, weights exp(l - l_max)
-//     renormalised over the selected k (the full-E denominator cancels);
-//  K2 routed gate/up: a workgroup owns 32 rows of one unique expert's gate
-//     and up (16 lanes per row, every weight load issued before x is staged
-//     as Q8_1 in LDS), silu(g)*u in registers, and the tile's 32 h values
-//     are exactly one Q8_1 block of the down input, quantized in the
-//     epilogue; the per-expert row lists are rebuilt in LDS from ids;
+// that chose it.  Here, on gfx950, one layer is three launches for B <= 2
+// and four above:
+//  K1 router rows (one wave per row, all loads issued up front), logits to
+//     the workspace;
+//  (B > 2) K1b one workgroup, a wave per row: top-k with order-preserving
+//     32-bit keys (equal logits rank by lower index), weights exp(l - l_max)
+//     renormalised over the selected k (the full-E denominator cancels), and
+//     the per-expert row lists, published for K2 and K3;
+//  K2 gate/up: a workgroup owns 32 rows of one expert's gate and up (the
+//     shared expert first, then the unique routed experts; 16 lanes per row,
+//     every weight load issued before x is staged as Q8_1 in LDS); for B <= 2
+//     every workgroup runs top-k on the logits itself (no extra launch);
+//     silu(g)*u in registers; the tile's 32 h values are exactly one Q8_1
+//     block of the down input, quantized in the epilogue;
 //  K3 down + combine: a workgroup owns 4 output rows (16 lanes per row, one
 //     Q4_0 block per lane at I = 512); its 4 waves split the experts by
 //     expert id mod 4, each walking its experts in ascending id (the shared
 //     expert last, in wave 0), and the 4 wave partials are added in wave
 //     order: every row's sum has the same order whatever the other rows
 //     chose, no atomics, one store per output.
+// A grid-wide barrier inside one kernel measured slower than a launch
+// boundary on this GPU, so the phases stay separate launches.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -147,7 +151,7 @@ __device__ __forceinline__ void topk_rows(const float *__restrict__ L, int64_t l
                                           int k, int has_shared, int32_t *__restrict__ ids,
                                           float *__restrict__ weights,
                                           float *__restrict__ shared_w) {
-  for (int b = threadIdx.x >> 6; b < B; b += 4)
+  for (int b = threadIdx.x >> 6; b < B; b += blockDim.x >> 6)
     topk_row<KPL>(L + (int64_t)b * ldl, E, k, has_shared, ids + (int64_t)b * k,
                   weights + (int64_t)b * k, shared_w ? shared_w + b : nullptr);
 }
@@ -645,11 +649,12 @@ __global__ __launch_bounds__(256) void k_moe_router(MoeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K1b (more rows): one workgroup runs top-k for every row, builds the row
-// lists and publishes both, so the gate/up workgroups only read them.
+// K1b (more rows): one workgroup, a wave per row, runs top-k for every
+// row, builds the row lists and publishes both, so the gate/up workgroups
+// only read them.
 // ---------------------------------------------------------------------------
 template <int B>
-__global__ __launch_bounds__(256) void k_moe_topk_gather(MoeArgs a) {
+__global__ __launch_bounds__(512) void k_moe_topk_gather(MoeArgs a) {
   __shared__ GatherLds g;
   __shared__ int s_ids[kMaxPairs];
   __shared__ float s_w[kMaxPairs];
@@ -684,7 +689,7 @@ __global__ __launch_bounds__(256) void k_moe_topk_gather(MoeArgs a) {
 // a slot past the end of the wave's list re-reads its last expert (or expert
 // 0 for an empty list) and is not used.  TI = I / 512 (compile time) or 0
 // (runtime loop over I % 32 == 0, one block at a time).
-constexpr int kDownCH = 4;
+constexpr int kDownCH = 4;  // experts per weight chunk (8 measured no faster at B = 8)
 constexpr int kDownStageChunks = kMaxDownStageElems / 16 / 256;  // 16-byte copies per thread
 constexpr int kDownStageBlocks = kMaxDownStageElems / 32 / 256 + 1;
 
@@ -1041,7 +1046,7 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
 #define MMV_LAYER_CASE(BB)                                                              \
   case BB:                                                                              \
     launch_route<BB>(a, s);                                                             \
-    if (!a.topk_in_k2) hipLaunchKernelGGL((k_moe_topk_gather<BB>), dim3(1), dim3(256), 0, s, a); \
+    if (!a.topk_in_k2) hipLaunchKernelGGL((k_moe_topk_gather<BB>), dim3(1), dim3(64 * BB), 0, s, a); \
     launch_experts<BB>(a, s);                                                           \
     break;
     MMV_LAYER_CASE(1) MMV_LAYER_CASE(2) MMV_LAYER_CASE(3) MMV_LAYER_CASE(4)
