@@ -65,6 +65,8 @@ def lib():
             "orc_quantize_q8_1": (None, [_P, _I, _L, _I, _P, _P]),
             "orc_q4_0_block_sums": (None, [_P, _I, _I, _P, _I, _P]),
             "orc_gemv_q4_0": (None, [_P, _P, _I, _I, _P, _P, _I, _P]),
+            "orc_gemv_q4_0_f32": (None, [_P, _P, _I, _I, _P, _L, _I, _P]),
+            "orc_argmax": (None, [_P, _L, _I, _I, _P]),
             "orc_router_logits": (None, [_P, _I, _I, _P, _L, _I, _P]),
             "orc_topk": (None, [_P, _I, _L, _I, _I, _P]),
             "orc_gate_weights": (None, [_P, _L, _P, _I, _I, _P]),
@@ -172,6 +174,28 @@ def gemv_q4_0(qs, dw, xq, xds):
     Y = np.empty((B, N), np.float64)
     lib().orc_gemv_q4_0(_p(qs), _p(dw), N, K, _p(xq), _p(xds), B, _p(Y))
     return Y
+
+
+def gemv_q4_0_f32(qs, dw, X):
+    """W4A16: qs uint8 [N, nb, 16], dw uint16 [N, nb], X float32 [B, K] -> float64 [B, N]."""
+    qs = _c(qs, np.uint8)
+    dw = _c(dw, np.uint16)
+    X = _c(np.atleast_2d(X), np.float32)
+    N, nb, _ = qs.shape
+    B, K = X.shape
+    assert K == nb * 32 and dw.shape == (N, nb)
+    Y = np.empty((B, N), np.float64)
+    lib().orc_gemv_q4_0_f32(_p(qs), _p(dw), N, K, _p(X), K, B, _p(Y))
+    return Y
+
+
+def argmax(Y):
+    """Y float32 [B, N] -> int32 [B]: largest value, lowest index on ties."""
+    Y = _c(np.atleast_2d(Y), np.float32)
+    B, N = Y.shape
+    ids = np.empty(B, np.int32)
+    lib().orc_argmax(_p(Y), N, N, B, _p(ids))
+    return ids
 
 
 # ---- routing ---------------------------------------------------------------

@@ -216,6 +216,33 @@ void orc_router_logits(const float *R, int E, int H, const float *X, long ldx,
     }
 }
 
+void orc_gemv_q4_0_f32(const uint8_t *qs, const uint16_t *dw, int N, int K,
+                       const float *X, long ldx, int B, double *Y) {
+  int nb = K / 32;
+  for (int b = 0; b < B; b++)
+    for (int n = 0; n < N; n++) {
+      double acc = 0.0;
+      for (int j = 0; j < nb; j++) {
+        const uint8_t *blk = qs + ((long)n * nb + j) * 16;
+        const float *xb = X + (long)b * ldx + 32L * j;
+        double s = 0.0;
+        for (int i = 0; i < 32; i++) s += (double)(q4_code(blk, i) - 8) * (double)xb[i];
+        acc += (double)orc_f16_to_f32(dw[(long)n * nb + j]) * s;
+      }
+      Y[(long)b * N + n] = acc;
+    }
+}
+
+void orc_argmax(const float *Y, long ldy, int N, int B, int32_t *ids) {
+  for (int b = 0; b < B; b++) {
+    const float *y = Y + (long)b * ldy;
+    int best = 0;
+    for (int n = 1; n < N; n++)          /* ascending scan, strict '>' */
+      if (y[n] > y[best]) best = n;
+    ids[b] = best;
+  }
+}
+
 void orc_topk(const float *L, int E, long ldl, int B, int k, int32_t *ids) {
   char *taken = (char *)calloc((size_t)E, 1);
   for (int b = 0; b < B; b++) {

@@ -81,6 +81,19 @@ void orc_q4_0_block_sums(const uint8_t *qs, int N, int K,
 void orc_gemv_q4_0(const uint8_t *qs, const uint16_t *dw, int N, int K,
                    const int8_t *xq, const uint16_t *xds, int B, double *Y);
 
+/* ---- Q4_0 weights x fp32 activations (W4A16: no Q8_1 step) -------------
+ * Y[b*N + n] = sum_j f16(d_w[n][j]) * sum_i (code_i - 8) * X[b*ldx + 32j + i],
+ * in float64.  [STRATA: "BF16 vs Quantization" (W4A16 INT4), and the
+ * dequant-gemv kernels its closing paragraph announces] */
+void orc_gemv_q4_0_f32(const uint8_t *qs, const uint16_t *dw, int N, int K,
+                       const float *X, long ldx, int B, double *Y);
+
+/* ---- argmax of rows (the top-1 case of orc_topk) ------------------------
+ * ids[b] = the index of the largest Y[b*ldy + n], n < N (fp32 compare, so
+ * -0 == +0); among equal values the lowest index.  [STRATA: The
+ * Optimization Passes, Pass 3 item 3: on-device argmax over the logits] */
+void orc_argmax(const float *Y, long ldy, int N, int B, int32_t *ids);
+
 /* ---- F32 router, top-k, renormalised gate weights ----------------------- */
 /* logits[b*E + e] = sum_h R[e*H + h] * X[b*ldx + h], in float64 */
 void orc_router_logits(const float *R, int E, int H, const float *X, long ldx,
