@@ -69,6 +69,7 @@ extern "C" {
 #define MMV_MAX_EXPERTS 1024  /* router rows E                              */
 #define MMV_MAX_TOPK    16    /* experts per row k                          */
 #define MMV_Q4_MAX_XK   49152 /* B*K limit of gemv_q4_0 (x staged in LDS)   */
+#define MMV_Q4F32_MAX_XK 16384 /* B*K limit of gemv_q4_0_f32 (fp32 x in LDS) */
 
 typedef enum {
   MMV_OK = 0,
@@ -143,6 +144,34 @@ int quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B,
  * ------------------------------------------------------------------------ */
 int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,
               int32_t B, float *Y, int64_t ldy, void *stream);
+
+/* --------------------------------------------------------------------------
+ * gemv_q4_0_f32 -- Q4_0 weights x fp32 activations (W4A16: no Q8_1 step).
+ *   [STRATA: "BF16 vs Quantization" (W4A16 INT4 with on-the-fly
+ *    dequantization) and the dequant-gemv kernels its closing paragraph
+ *    announces]
+ *   Y[b*ldy + n] = sum_j d_w[n][j] * sum_i (code_i - 8) * X[b*ldx + 32j + i],
+ *   fp32 arithmetic: per block s = sum_i code_i * x_i, then d_w * (s - 8 *
+ *   sum_i x_i).  K / 32 in {16, 32, 64, 128, 256}; B * K <=
+ *   MMV_Q4F32_MAX_XK (x of every row is staged in on-chip memory).
+ *   X: B x K fp32, 16-byte aligned, ldx % 4 == 0.  Y: B x N fp32, ldy >= N.
+ * ------------------------------------------------------------------------ */
+int gemv_q4_0_f32(const mmv_q4_0 *W, const float *X, int64_t ldx, int32_t B,
+                  float *Y, int64_t ldy, void *stream);
+
+/* --------------------------------------------------------------------------
+ * argmax_rows -- per row, the index of the largest value, on the device.
+ *   [STRATA: The Optimization Passes, Pass 3 item 3: argmax of the
+ *    248,320 logits on the device, 4 bytes per token to the host]
+ *   ids[b] = index of the largest Y[b*ldy + n], n < N; equal values rank
+ *   by lower index and -0 equals +0 (the ordering of moe_route_topk).
+ *   vals[b] (optional, may be NULL) = that value.  Y finite, 4-byte
+ *   aligned, ldy >= N.  workspace: mmv_argmax_workspace_bytes(N, B) bytes,
+ *   8-byte aligned, no initialisation needed.  Two launches.
+ * ------------------------------------------------------------------------ */
+size_t mmv_argmax_workspace_bytes(int32_t N, int32_t B);
+int argmax_rows(const float *Y, int64_t ldy, int32_t N, int32_t B, int32_t *ids,
+                float *vals, void *workspace, size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
  * moe_route_topk -- F32 router, softmax, top-k, renormalised gate weights.

@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "MatvecError", "Q4_0", "MoeLayer", "library_path", "lib",
-    "gemv_bf16", "quantize_q8_1", "q8_1_bytes", "gemv_q4_0",
+    "gemv_bf16", "quantize_q8_1", "q8_1_bytes", "gemv_q4_0", "gemv_q4_0_f32",
+    "argmax_rows", "argmax_workspace_bytes", "Q4F32_MAX_XK",
     "moe_route_topk", "moe_mul_mat_id", "moe_layer_decode", "moe_workspace_bytes",
     "MAX_BATCH", "MAX_EXPERTS", "MAX_TOPK", "Q4_MAX_XK", "stream_read", "split_q8_1",
 ]
@@ -25,6 +26,7 @@ MAX_BATCH = 8
 MAX_EXPERTS = 1024
 MAX_TOPK = 16
 Q4_MAX_XK = 49152
+Q4F32_MAX_XK = 16384
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmoe_matvec.so")
@@ -78,6 +80,9 @@ def lib():
             "gemv_bf16": (C.c_int, [_P, _i32, _i32, _i64, _P, _i64, _i32, _P, _i64, _P]),
             "quantize_q8_1": (C.c_int, [_P, _i32, _i64, _i32, _P, _P]),
             "gemv_q4_0": (C.c_int, [C.POINTER(_Q4), _P, _i64, _P, _i32, _P, _i64, _P]),
+            "gemv_q4_0_f32": (C.c_int, [C.POINTER(_Q4), _P, _i64, _i32, _P, _i64, _P]),
+            "mmv_argmax_workspace_bytes": (C.c_size_t, [_i32, _i32]),
+            "argmax_rows": (C.c_int, [_P, _i64, _i32, _i32, _P, _P, _P, C.c_size_t, _P]),
             "moe_route_topk": (C.c_int, [_P, _i32, _i32, _P, _i64, _i32, _i32, _P, _P, _P,
                                          _P, _P, _P]),
             "moe_workspace_bytes": (C.c_size_t, [C.POINTER(_Layer), _i32]),
@@ -214,6 +219,45 @@ def gemv_q4_0(W: Q4_0, x: torch.Tensor | None = None, xq: torch.Tensor | None = 
     _check("gemv_q4_0", lib().gemv_q4_0(C.byref(W._s), xp, ldx, _ptr(xq), B,
                                         y2.data_ptr(), _ld(y2), _stream(stream)))
     return out
+
+
+def gemv_q4_0_f32(W: Q4_0, x: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """W4A16: y = W x with Q4_0 weights and fp32 activations (no Q8_1 step);
+    x fp32 [B, K] or [K]."""
+    x2, squeeze = (x.unsqueeze(0), True) if x.dim() == 1 else (x, False)
+    if x2.dtype != torch.float32 or x2.stride(-1) != 1:
+        raise TypeError("x must be float32 with unit inner stride")
+    B = x2.shape[0]
+    if out is None:
+        out = torch.empty((B, W.N), dtype=torch.float32, device=x.device)
+    y2 = out.unsqueeze(0) if out.dim() == 1 else out
+    _check("gemv_q4_0_f32", lib().gemv_q4_0_f32(C.byref(W._s), x2.data_ptr(), _ld(x2), B,
+                                                y2.data_ptr(), _ld(y2), _stream(stream)))
+    return out[0] if (squeeze and out.dim() == 2) else out
+
+
+def argmax_workspace_bytes(N: int, B: int) -> int:
+    return int(lib().mmv_argmax_workspace_bytes(N, B))
+
+
+def argmax_rows(y: torch.Tensor, ids: torch.Tensor | None = None, vals: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None):
+    """Per row of fp32 y [B, N]: index (int32 [B]) of the largest value, lowest
+    index on ties; returns (ids, vals)."""
+    y2 = y.unsqueeze(0) if y.dim() == 1 else y
+    if y2.dtype != torch.float32 or y2.stride(-1) != 1:
+        raise TypeError("y must be float32 with unit inner stride")
+    B, N = y2.shape
+    if ids is None:
+        ids = torch.empty(B, dtype=torch.int32, device=y.device)
+    if vals is None:
+        vals = torch.empty(B, dtype=torch.float32, device=y.device)
+    if workspace is None:
+        workspace = torch.empty(argmax_workspace_bytes(N, B), dtype=torch.uint8, device=y.device)
+    _check("argmax_rows", lib().argmax_rows(y2.data_ptr(), _ld(y2), N, B, ids.data_ptr(),
+                                            _ptr(vals), workspace.data_ptr(), workspace.numel(),
+                                            _stream(stream)))
+    return ids, vals
 
 
 # ---------------------------------------------------------------------------

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libmoe_matvec.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "validate.cpp", "gemv_bf16.hip", "gemv_q4_0.hip", "moe.hip", "probe.hip"]
+SOURCES = ["api.hip", "validate.cpp", "gemv_bf16.hip", "gemv_q4_0.hip", "moe.hip", "probe.hip", "argmax.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -68,6 +68,24 @@ int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq, in
                                        as_stream(stream)));
 }
 
+int gemv_q4_0_f32(const mmv_q4_0 *W, const float *X, int64_t ldx, int32_t B, float *Y,
+                  int64_t ldy, void *stream) {
+  const int st = mmv::check_gemv_q4_0_f32(W, X, ldx, B, Y, ldy);
+  if (st != MMV_OK) return st;
+  return hip_status(mmv::run_gemv_q4_0_f32(W->qs, W->d, W->N, W->K, X, ldx, B, Y, ldy,
+                                           as_stream(stream)));
+}
+
+size_t mmv_argmax_workspace_bytes(int32_t N, int32_t B) { return mmv::argmax_ws_bytes(N, B); }
+
+int argmax_rows(const float *Y, int64_t ldy, int32_t N, int32_t B, int32_t *ids, float *vals,
+                void *workspace, size_t ws_bytes, void *stream) {
+  const int st = mmv::check_argmax(Y, ldy, N, B, ids, vals, workspace, ws_bytes);
+  if (st != MMV_OK) return st;
+  return hip_status(mmv::run_argmax(Y, ldy, N, B, ids, vals, static_cast<uint64_t *>(workspace),
+                                    as_stream(stream)));
+}
+
 int moe_route_topk(const float *router, int32_t E, int32_t H, const float *X, int64_t ldx,
                    int32_t B, int32_t k, const float *shared_gate_row, float *logits,
                    int32_t *ids, float *weights, float *shared_w, void *stream) {

@@ -126,6 +126,12 @@ __device__ __forceinline__ float group8_max(float v) {
   v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
   return v;
 }
+__device__ __forceinline__ float group8_sum(float v) {  // same value in all 8 lanes
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowHalfMirror>(v);
+  return v;
+}
 __device__ __forceinline__ int group8_sum_i(int v) {
   v += (int)dpp_u32<kDppQuadXor1>((uint32_t)v);
   v += (int)dpp_u32<kDppQuadXor2>((uint32_t)v);
@@ -220,6 +226,17 @@ __device__ __forceinline__ void gsum_last_n(float (&v)[N]) {
 #pragma unroll
     for (int i = 0; i < N; ++i) v[i] += dpp_rows_or_zero<kDppRowBcast31, 0xC>(v[i]);
   }
+}
+
+// Order-preserving map of fp32 onto uint32 (larger float, larger key), with
+// -0 and +0 mapped to the same key so that they tie; and its inverse.
+// Finite inputs map to keys > 0.
+__device__ __forceinline__ uint32_t topk_ord(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float topk_unord(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) {

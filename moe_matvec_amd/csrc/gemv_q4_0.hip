@@ -251,6 +251,127 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
   }
 }
 
+// ---- W4A16: Q4_0 weights x fp32 activations, no Q8_1 step ---------------
+// "Beating llama.cpp from Scratch on Consumer AMD" ("BF16 vs Quantization")
+// names W4A16 INT4 weights with on-the-fly dequantization as the variant
+// that trades integer unpacking for activation precision.  Same row layout
+// as k_gemv_q4_0_t (G lanes per row, RP rows per lane group, every weight
+// load issued after the first activation loads).  x is staged in LDS as
+// fp32 in a block-transposed layout ([b][q][j] float4, q = 0..7 within a
+// block, so lanes reading consecutive blocks read consecutive 16-byte
+// words), with each block's sum sx = sum_i x_i (fixed order).  Per block:
+// s1 = sum_i code_i * x_i (codes converted from bytes, k ascending through
+// the low then the high nibbles), value d_w * (s1 - 8 sx).  Every (row, b)
+// sum has one order for every B.
+constexpr int kF32Pass = 8;  // float4 staging tasks per thread per pass
+
+template <int B, int G, int RP, int T>
+__global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int /*K*/,
+    const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int K = 32 * G * T, nb = G * T;
+  constexpr int RPP = 64 / G, ROWS_WAVE = RP * RPP, ROWS_WG = 4 * ROWS_WAVE;
+  constexpr int TOT = B * K / 4;                          // float4 staging tasks
+  constexpr int NPASS = (TOT + 256 * kF32Pass - 1) / (256 * kF32Pass);
+  constexpr int P0 = cmin(kF32Pass, (TOT + 255) / 256);   // first pass per thread
+  f32x4 *xs = reinterpret_cast<f32x4 *>(smem);            // [B][8][nb]
+  float *sx = reinterpret_cast<float *>(smem + (size_t)B * K * 4);  // [B][nb]
+  const int lane = threadIdx.x & 63, sub = lane % G, grp = lane / G, wv = threadIdx.x >> 6;
+
+  auto load_pass = [&](int base, f32x4 (&v)[kF32Pass]) {
+#pragma unroll
+    for (int m = 0; m < kF32Pass; ++m) {
+      const int t = min(base + (int)threadIdx.x + 256 * m, TOT - 1);
+      const int b = t / (K / 4), r = t - b * (K / 4);
+      v[m] = load_f4(X + (int64_t)b * ldx + 4 * r);
+    }
+  };
+  auto store_pass = [&](int base, const f32x4 (&v)[kF32Pass], int np) {
+#pragma unroll
+    for (int m = 0; m < kF32Pass; ++m) {
+      if (m >= np) break;
+      asm volatile("" ::"v"(v[m]));
+      const int t = base + threadIdx.x + 256 * m;
+      const float s = group8_sum((v[m].x + v[m].y) + (v[m].z + v[m].w));
+      if (t < TOT) {  // uniform over each 8-lane group: TOT % 8 == 0
+        const int b = t / (K / 4), r = t - b * (K / 4), j = r >> 3, q = r & 7;
+        xs[(b * 8 + q) * nb + j] = v[m];
+        if (q == 0) sx[b * nb + j] = s;
+      }
+    }
+  };
+
+  f32x4 xv[kF32Pass];
+  load_pass(0, xv);
+  __builtin_amdgcn_sched_barrier(0);
+  const int rbase = blockIdx.x * ROWS_WG + wv * ROWS_WAVE + grp;
+  u32x4 w[RP][T];
+  float d[RP][T];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int64_t rowblk = (int64_t)min(rbase + p * RPP, N - 1) * nb;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t blk = rowblk + sub + G * t;
+      w[p][t] = load_stream16(qs + blk * 16);
+      d[p][t] = f16_bits_to_f32(load_stream2(dw + blk));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  store_pass(0, xv, P0);
+#pragma unroll
+  for (int ps = 1; ps < NPASS; ++ps) {
+    load_pass(256 * kF32Pass * ps, xv);
+    store_pass(256 * kF32Pass * ps, xv, kF32Pass);
+  }
+  __syncthreads();
+
+  float acc[RP][B];
+#pragma unroll
+  for (int p = 0; p < RP; ++p)
+#pragma unroll
+    for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int j = sub + G * t;
+#pragma unroll
+    for (int r = 0; r < B; ++r) {
+      f32x4 xq[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xq[q] = xs[(r * 8 + q) * nb + j];
+      const float sxr = sx[r * nb + j];
+#pragma unroll
+      for (int p = 0; p < RP; ++p) {
+        const uint32_t wd[4] = {w[p][t].x, w[p][t].y, w[p][t].z, w[p][t].w};
+        float s1 = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {      // low nibbles: codes 0..15; high: 16..31
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) {
+            const uint32_t c = (wd[dd] >> (4 * h)) & 0x0F0F0F0Fu;
+            const f32x4 xv4 = xq[4 * h + dd];
+            s1 = fmaf((float)(c & 0xFFu), xv4.x, s1);
+            s1 = fmaf((float)((c >> 8) & 0xFFu), xv4.y, s1);
+            s1 = fmaf((float)((c >> 16) & 0xFFu), xv4.z, s1);
+            s1 = fmaf((float)(c >> 24), xv4.w, s1);
+          }
+        }
+        acc[p][r] = fmaf(d[p][t], fmaf(-8.0f, sxr, s1), acc[p][r]);
+      }
+    }
+  }
+  float (&flat)[RP * B] = *reinterpret_cast<float(*)[RP * B]>(&acc[0][0]);
+  gsum_last_n<G>(flat);
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int row = rbase + p * RPP;
+#pragma unroll
+    for (int r = 0; r < B; ++r)
+      if (sub == G - 1 && row < N) Y[(int64_t)r * ldy + row] = acc[p][r];
+  }
+}
+
 namespace {
 
 int cu_count() {
@@ -351,6 +472,56 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
   if (nb <= 16) return launch_q4<B, 16, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   if (nb <= 32) return launch_q4<B, 32, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   return launch_q4<B, 64, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+}
+
+namespace {
+
+template <int B, int G, int T>
+hipError_t launch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                         int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+  constexpr int RP = T >= 4 ? 2 : 4;
+  constexpr int rows_wg = 4 * RP * (64 / G);
+  const size_t lds = (size_t)B * K * 4 + (size_t)B * (K / 32) * 4;
+  if (lds > 65536) {  // above the default dynamic-LDS limit: raise it once per kernel
+    static const hipError_t raised = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_gemv_q4_0_f32<B, G, RP, T>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 32 * G * T * B * 4 + G * T * B * 4);
+    if (raised != hipSuccess) return raised;
+  }
+  hipLaunchKernelGGL((k_gemv_q4_0_f32<B, G, RP, T>), dim3((N + rows_wg - 1) / rows_wg),
+                     dim3(256), lds, s, qs, d, N, K, X, ldx, Y, ldy);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t dispatch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                           int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+  switch (K / 32) {
+    case 16: return launch_q4_f32<B, 16, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 32: return launch_q4_f32<B, 32, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 64: return launch_q4_f32<B, 64, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 128: return launch_q4_f32<B, 64, 2>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 256: return launch_q4_f32<B, 64, 4>(qs, d, N, K, X, ldx, Y, ldy, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t run_gemv_q4_0_f32(const uint8_t *qs, const uint16_t *d, int N, int K,
+                             const float *X, int64_t ldx, int B, float *Y, int64_t ldy,
+                             hipStream_t s) {
+  switch (B) {
+    case 1: return dispatch_q4_f32<1>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 2: return dispatch_q4_f32<2>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 3: return dispatch_q4_f32<3>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 4: return dispatch_q4_f32<4>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 5: return dispatch_q4_f32<5>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 6: return dispatch_q4_f32<6>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 7: return dispatch_q4_f32<7>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 8: return dispatch_q4_f32<8>(qs, d, N, K, X, ldx, Y, ldy, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t run_gemv_q4_0(const uint8_t *qs, const uint16_t *d, int N, int K,

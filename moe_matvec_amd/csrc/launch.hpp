@@ -21,6 +21,15 @@ hipError_t run_gemv_q4_0(const uint8_t *qs, const uint16_t *d, int N, int K,
                          const float *X, int64_t ldx, const uint8_t *Xq, int B,
                          float *Y, int64_t ldy, hipStream_t s);
 
+hipError_t run_gemv_q4_0_f32(const uint8_t *qs, const uint16_t *d, int N, int K,
+                             const float *X, int64_t ldx, int B, float *Y, int64_t ldy,
+                             hipStream_t s);
+
+// per-row argmax in two passes; part: B * argmax_parts(N) 64-bit keys
+int argmax_parts(int N);
+hipError_t run_argmax(const float *Y, int64_t ldy, int N, int B, int32_t *ids, float *vals,
+                      uint64_t *part, hipStream_t s);
+
 // router logits (+ shared-gate logit in column E), then top-k and weights
 hipError_t run_moe_route(const float *router, int E, int H, const float *X,
                          int64_t ldx, int B, int k, const float *shared_gate_row,

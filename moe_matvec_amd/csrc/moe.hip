@@ -89,16 +89,6 @@ __device__ __forceinline__ void router_row(const float *__restrict__ row, int H,
 // ---------------------------------------------------------------------------
 // top-k of one row by one wave
 // ---------------------------------------------------------------------------
-// Order-preserving map of fp32 onto uint32 (larger float, larger key), with
-// -0 and +0 mapped to the same key so that they tie; and its inverse.
-__device__ __forceinline__ uint32_t topk_ord(float v) {
-  const uint32_t u = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float topk_unord(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
 // Selects the k largest of l[0..E) (ties: lower index first), writes ids,
 // renormalised weights and the shared weight.  Whole wave, uniform control.
 // KPL = keys per lane (E <= 64 * KPL); lane l holds experts l + 64 i.  Each

@@ -98,6 +98,45 @@ int check_gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *
   return MMV_OK;
 }
 
+int check_gemv_q4_0_f32(const mmv_q4_0 *W, const float *X, int64_t ldx, int32_t B,
+                        const float *Y, int64_t ldy) {
+  if (!W || !W->qs || !W->d || !X || !Y) return MMV_E_NULL;
+  if (bad_batch(B)) return MMV_E_BATCH;
+  const int32_t N = W->N, K = W->K;
+  if (N < 1 || K % 32 != 0 || ldx < K || ldy < N || ldx > kMaxLd || ldy > kMaxLd)
+    return MMV_E_SHAPE;
+  const int nb = K / 32;
+  if (nb != 16 && nb != 32 && nb != 64 && nb != 128 && nb != 256) return MMV_E_SHAPE;
+  if ((int64_t)B * K > MMV_Q4F32_MAX_XK) return MMV_E_SHAPE;
+  if (!aligned(W->qs, 16) || !aligned(W->d, 2) || !aligned(Y, 4)) return MMV_E_ALIGN;
+  if (!aligned(X, 16) || ldx % 4 != 0) return MMV_E_ALIGN;
+  const Range outs[1] = {rng(Y, span(B, ldy, N, 4))};
+  const Range ins[3] = {q4_qs(W->qs, N, K), q4_d(W->d, N, K), rng(X, span(B, ldx, K, 4))};
+  if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+  return MMV_OK;
+}
+
+size_t argmax_ws_bytes(int32_t N, int32_t B) {
+  if (N < 1 || B < 1) return 0;
+  return (size_t)B * (size_t)((N + 4095) / 4096) * 8;
+}
+
+int check_argmax(const float *Y, int64_t ldy, int32_t N, int32_t B, const int32_t *ids,
+                 const float *vals, const void *ws, size_t ws_bytes) {
+  if (!Y || !ids || !ws) return MMV_E_NULL;
+  if (bad_batch(B)) return MMV_E_BATCH;
+  if (N < 1 || ldy < N || ldy > kMaxLd) return MMV_E_SHAPE;
+  if (!aligned(Y, 4) || !aligned(ids, 4) || !aligned(vals, 4) || !aligned(ws, 8))
+    return MMV_E_ALIGN;
+  const size_t need = argmax_ws_bytes(N, B);
+  if (ws_bytes < need) return MMV_E_WORKSPACE;
+  const Range outs[3] = {rng(ids, 4 * (size_t)B), vals ? rng(vals, 4 * (size_t)B) : none(),
+                         rng(ws, need)};
+  const Range ins[1] = {rng(Y, span(B, ldy, N, 4))};
+  if (any_overlap(outs, ins)) return MMV_E_ALIAS;
+  return MMV_OK;
+}
+
 int check_route(const float *router, int32_t E, int32_t H, const float *X, int64_t ldx,
                 int32_t B, int32_t k, const float *shg, const float *logits,
                 const int32_t *ids, const float *weights, const float *shared_w) {

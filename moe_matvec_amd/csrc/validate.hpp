@@ -15,6 +15,11 @@ int check_gemv_bf16(const uint16_t *W, int32_t N, int32_t K, int64_t ldw, const 
 int check_quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B, const void *Xq);
 int check_gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,
                     int32_t B, const float *Y, int64_t ldy);
+int check_gemv_q4_0_f32(const mmv_q4_0 *W, const float *X, int64_t ldx, int32_t B,
+                        const float *Y, int64_t ldy);
+size_t argmax_ws_bytes(int32_t N, int32_t B);
+int check_argmax(const float *Y, int64_t ldy, int32_t N, int32_t B, const int32_t *ids,
+                 const float *vals, const void *ws, size_t ws_bytes);
 int check_route(const float *router, int32_t E, int32_t H, const float *X, int64_t ldx,
                 int32_t B, int32_t k, const float *shg, const float *logits,
                 const int32_t *ids, const float *weights, const float *shared_w);

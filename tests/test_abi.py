@@ -180,3 +180,37 @@ def test_layer_decode_validation(L):
     assert f(C.byref(lay), None, 2048, 2, Cp, 2048, None, None, Dp, need, None) == E_NULL
     assert f(C.byref(lay), A, 2048, 2, Cp, 2048, A + 8, None, Dp, need, None) == E_ALIAS
     assert f(C.byref(lay), A, 2048, 2, Cp, 2048, Dp + 64, None, Dp, need, None) == E_ALIAS
+
+
+def test_gemv_q4_0_f32_validation(L):
+    g = L.gemv_q4_0_f32
+    W = _q4(A, Bp, 64, 512)
+    assert g(None, Cp, 512, 1, Dp, 64, None) == E_NULL
+    assert g(C.byref(W), None, 512, 1, Dp, 64, None) == E_NULL
+    assert g(C.byref(W), Cp, 512, 0, Dp, 64, None) == E_BATCH
+    assert g(C.byref(_q4(A, Bp, 64, 96)), Cp, 96, 1, Dp, 64, None) == E_SHAPE   # K/32 = 3
+    assert g(C.byref(_q4(A, Bp, 64, 4096)), Cp, 4096, 5, Dp, 64, None) == E_SHAPE  # B*K
+    assert g(C.byref(W), Cp, 500, 1, Dp, 64, None) == E_SHAPE                  # ldx < K
+    assert g(C.byref(W), Cp + 4, 512, 1, Dp, 64, None) == E_ALIGN
+    assert g(C.byref(W), Cp, 514, 2, Dp, 64, None) == E_ALIGN                  # ldx % 4
+    assert g(C.byref(W), Cp, 512, 1, A + 64, 64, None) == E_ALIAS
+    assert g(C.byref(W), Cp, 512, 1, Cp + 16, 64, None) == E_ALIAS
+
+
+def test_argmax_validation(L):
+    a = L.argmax_rows
+    assert L.mmv_argmax_workspace_bytes(248320, 8) == 8 * 61 * 8
+    assert L.mmv_argmax_workspace_bytes(0, 1) == 0
+    ws = L.mmv_argmax_workspace_bytes(5000, 2)
+    assert a(None, 5000, 5000, 2, Bp, Cp, Dp, ws, None) == E_NULL
+    assert a(A, 5000, 5000, 2, None, Cp, Dp, ws, None) == E_NULL
+    assert a(A, 5000, 5000, 2, Bp, None, None, ws, None) == E_NULL             # workspace
+    assert a(A, 5000, 5000, 9, Bp, Cp, Dp, ws, None) == E_BATCH
+    assert a(A, 4000, 5000, 2, Bp, Cp, Dp, ws, None) == E_SHAPE                # ldy < N
+    assert a(A, 5000, 0, 2, Bp, Cp, Dp, ws, None) == E_SHAPE
+    assert a(A + 2, 5000, 5000, 2, Bp, Cp, Dp, ws, None) == E_ALIGN
+    assert a(A, 5000, 5000, 2, Bp, Cp, Dp + 4, ws, None) == E_ALIGN
+    assert a(A, 5000, 5000, 2, Bp, Cp, Dp, ws - 8, None) == E_WS
+    assert a(A, 5000, 5000, 2, A + 40, Cp, Dp, ws, None) == E_ALIAS            # ids inside Y
+    assert a(A, 5000, 5000, 2, Bp, Bp + 4, Dp, ws, None) == E_ALIAS            # vals on ids
+    assert a(A, 5000, 5000, 2, Bp, Cp, A + 1024, ws, None) == E_ALIAS          # ws inside Y

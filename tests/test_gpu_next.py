@@ -1,0 +1,166 @@
+"""GPU parity of the LM-head pieces (on-device argmax, the 248,320-row BF16
+GEMV feeding it) and of the W4A16 Q4_0 GEMV, against the oracle, through
+the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests._util import np16, npc, rel_l2_rows
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 1e-3   # rel-L2 per output row, BF16 GEMV
+Q4_TOL = 2e-3     # rel-L2 per output row, Q4_0 weight products
+
+VOCAB, HID = 248320, 2560   # LM head of the 2560-wide model
+
+
+# ---------------------------------------------------------------------------
+# argmax_rows
+# ---------------------------------------------------------------------------
+
+def _argmax_check(mm, orc, Y: torch.Tensor, N=None):
+    """Y fp32 [B, ldy] on the device; argmax over the first N columns."""
+    N = Y.shape[1] if N is None else N
+    ids, vals = mm.argmax_rows(Y[:, :N])
+    torch.cuda.synchronize()
+    Yh = npc(Y[:, :N])
+    want = orc.argmax(Yh)
+    assert np.array_equal(npc(ids), want)
+    got_v = npc(vals)
+    ref_v = Yh[np.arange(Yh.shape[0]), want]
+    # the value returned is the element itself (a -0 maximum comes back as +0)
+    assert np.array_equal(got_v, ref_v + np.float32(0.0))
+
+
+@pytest.mark.parametrize("N,B", [
+    (1, 1), (3, 2), (4095, 1), (4096, 3), (4097, 8), (50001, 5), (VOCAB, 1), (VOCAB, 8),
+])
+def test_argmax_random(mm, orc, dev, N, B):
+    Y = synth.normal((B, N), 1.0, 0, "argmax", N, B, device=dev)
+    _argmax_check(mm, orc, Y)
+
+
+def test_argmax_ties_lowest_index(mm, orc, dev):
+    # the maximum planted at several positions, in different slices of 4096
+    N, B = 3 * 4096 + 17, 4
+    Y = synth.normal((B, N), 1.0, 0, "ties", device=dev)
+    spots = [[9000, 4100, N - 1], [N - 1, 12287], [5, 4095, 4096], [0, 1, 2]]
+    for b, s in enumerate(spots):
+        Y[b, s] = 7.5
+    _argmax_check(mm, orc, Y)
+    ids, _ = mm.argmax_rows(Y)
+    assert npc(ids).tolist() == [min(s) for s in spots]
+
+
+def test_argmax_signed_zero_and_negative_rows(mm, orc, dev):
+    N = 9000
+    Y = -1.0 - synth.normal((4, N), 1.0, 0, "neg", device=dev).abs()
+    Y[0, 7] = -0.0          # -0 before +0: equal values, the lower index wins
+    Y[0, 8000] = 0.0
+    Y[1, 3] = 0.0           # +0 before -0
+    Y[1, 6000] = -0.0
+    Y[2].fill_(-0.0)        # all -0: index 0, value +0
+    Y[3, N - 1] = -0.5      # every value negative: the largest at the tail
+    _argmax_check(mm, orc, Y)
+    ids, vals = mm.argmax_rows(Y)
+    assert npc(ids).tolist() == [7, 3, 0, N - 1]
+    assert npc(vals).tolist() == [0.0, 0.0, 0.0, -0.5]
+
+
+def test_argmax_strided_rows_and_stale_workspace(mm, orc, dev):
+    B, N, ld = 6, 20000, 20480
+    Y = synth.normal((B, ld), 1.0, 0, "stride", device=dev)
+    Y[:, N:] = 100.0        # beyond N: must not be seen
+    ws = torch.full((mm.argmax_workspace_bytes(N, B),), 0xFF, dtype=torch.uint8, device=dev)
+    ids, vals = mm.argmax_rows(Y[:, :N], workspace=ws)
+    torch.cuda.synchronize()
+    want = orc.argmax(npc(Y[:, :N]))
+    assert np.array_equal(npc(ids), want)
+    assert np.array_equal(npc(vals), npc(Y)[np.arange(B), want])
+
+
+# ---------------------------------------------------------------------------
+# LM head: BF16 GEMV over the vocabulary, then argmax on the device
+# ---------------------------------------------------------------------------
+
+def test_lm_head_gemv_argmax(mm, orc, dev):
+    W = synth.bf16_weights(VOCAB, HID, 0, "lm_head", device=dev)
+    for B in (1, 8):
+        X = synth.activations(B, HID, 0, "lm_head", B, device=dev)
+        y = mm.gemv_bf16(W, X)
+        ids, vals = mm.argmax_rows(y)
+        torch.cuda.synchronize()
+        Yg = npc(y)
+        ref = orc.gemv_bf16(np16(W), npc(X))
+        assert rel_l2_rows(Yg, ref) <= BF16_TOL
+        # the decision is taken on the fp32 logits the GEMV produced
+        assert np.array_equal(npc(ids), orc.argmax(Yg))
+        assert np.array_equal(npc(vals), Yg[np.arange(B), npc(ids)])
+        # and it is the exact argmax unless the top two are within rounding
+        top = np.argmax(ref, axis=1)
+        gap = np.abs(ref[np.arange(B), top] - ref[np.arange(B), npc(ids)])
+        assert np.all(gap <= 1e-4 * np.abs(ref).max(axis=1))
+
+
+# ---------------------------------------------------------------------------
+# W4A16: Q4_0 weights x fp32 activations
+# ---------------------------------------------------------------------------
+
+def _q4(mm, N, K, dev, *tags):
+    qs, d = synth.q4_0_weights(N, K, 0, "w4a16", N, K, *tags, device=dev)
+    return mm.Q4_0(qs, d), npc(qs), np16(d)
+
+
+@pytest.mark.parametrize("N,K,B", [
+    (4096, 4096, 1), (11008, 4096, 1), (4096, 4096, 4), (1000, 512, 8), (515, 1024, 3),
+    (4097, 2048, 8), (300, 8192, 2), (9, 4096, 4), (1, 512, 1), (2560, 8192, 1),
+])
+def test_w4a16_parity(mm, orc, dev, N, K, B):
+    W, qs, d = _q4(mm, N, K, dev)
+    X = synth.activations(B, K, 0, "w4a16", N, K, device=dev)
+    y = mm.gemv_q4_0_f32(W, X)
+    torch.cuda.synchronize()
+    ref = orc.gemv_q4_0_f32(qs, d, npc(X))
+    assert rel_l2_rows(npc(y), ref) <= Q4_TOL
+
+
+def test_w4a16_integer_pin_bit_exact(mm, orc, dev):
+    # power-of-two scales and integer activations: every partial sum is an
+    # exact fp32 value, so the product must match the float64 oracle exactly
+    g = torch.Generator().manual_seed(3)
+    N, K, B = 777, 2048, 8
+    qs = torch.randint(0, 256, (N, K // 32, 16), generator=g, dtype=torch.uint8)
+    scales = torch.tensor([1.0, 0.5, 2.0, 0.25], dtype=torch.float16)
+    d = scales[torch.randint(0, 4, (N, K // 32), generator=g)]
+    X = torch.randint(-16, 17, (B, K), generator=g).float()
+    y = mm.gemv_q4_0_f32(mm.Q4_0(qs.to(dev), d.to(dev)), X.to(dev))
+    torch.cuda.synchronize()
+    want = orc.gemv_q4_0_f32(qs.numpy(), np16(d), X.numpy())
+    assert np.array_equal(npc(y).astype(np.float64), want)
+
+
+def test_w4a16_batch_invariance(mm, dev):
+    # every (row, b) sum is taken in one order for every B
+    for N, K in ((2000, 2048), (700, 8192)):
+        W, _, _ = _q4(mm, N, K, dev, "inv")
+        Bmax = min(8, 16384 // K)
+        X = synth.activations(Bmax, K, 0, "w4a16inv", K, device=dev)
+        yB = mm.gemv_q4_0_f32(W, X)
+        assert torch.equal(yB, mm.gemv_q4_0_f32(W, X))
+        for b in range(Bmax):
+            assert torch.equal(yB[b], mm.gemv_q4_0_f32(W, X[b].clone()))
+
+
+def test_w4a16_strided_x_and_y(mm, orc, dev):
+    N, K, B = 1200, 1024, 5
+    W, qs, d = _q4(mm, N, K, dev, "stride")
+    Xb = synth.activations(B, K + 64, 0, "w4a16s", device=dev)
+    X = Xb[:, 32:32 + K]
+    Yb = torch.full((B, N + 7), 123.0, device=dev)
+    mm.gemv_q4_0_f32(W, X, out=Yb[:, :N])
+    torch.cuda.synchronize()
+    ref = orc.gemv_q4_0_f32(qs, d, npc(X))
+    assert rel_l2_rows(npc(Yb[:, :N]), ref) <= Q4_TOL
+    assert torch.all(Yb[:, N:] == 123.0)
