@@ -2,7 +2,7 @@
 """Benchmark of the decode matrix-vector path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
-                    [--only dense,q4,moe256,moe512] [--profile-kernel]
+                    [--only dense,q4,w4a16,lmhead,moe256,moe512] [--profile-kernel]
 
 The headline step is one pass over the dense BF16 decode matvec set: 36 layer
 copies (5.85 GB, far past the 256 MB Infinity Cache) of attn-out 2560x2560,
@@ -10,6 +10,7 @@ fused gate+up 2 x 9728x2560 and down 2560x9728, batch 1, each matrix with
 its own synthetic N(0,1) activation row, captured in one HIP graph and
 replayed K times.  `value` is algorithmic bytes / time in GB/s.  The same
 JSON line carries the other workloads (B = 8 dense, Q4_0 x Q8_1 GEMV, the
+W4A16 Q4_0 GEMV, the 248320 x 2560 LM head with its on-device argmax, the
 256- and 512-expert MoE layers) under "sections", the roofline of the
 dominant kernel and the CPU oracle's throughput on a bounded sample.
 """
@@ -180,6 +181,76 @@ def q4_section(mm, dev, copies, B, steps, warmup):
                 frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS)
 
 
+def w4a16_section(mm, dev, copies, B, steps, warmup):
+    """The Q4_0 shapes with fp32 activations (no Q8_1 step): one launch per
+    product at every B."""
+    import torch
+    import synth
+    mats = []
+    for N, K in Q4_SHAPES:
+        qs1, d1 = synth.q4_0_weights(N, K, 0, "q4bench", N, device=dev)
+        qs = torch.empty((copies,) + tuple(qs1.shape), dtype=torch.uint8, device=dev)
+        d = torch.empty((copies,) + tuple(d1.shape), dtype=torch.float16, device=dev)
+        qs[:] = qs1
+        d[:] = d1
+        mats.append((qs, d))
+    Ws = [[mm.Q4_0(qs[c], d[c]) for (qs, d) in mats] for c in range(copies)]
+    K = Q4_SHAPES[0][1]
+    X = synth.activations(copies * B, K, 0, "w4a16bench-x", B, device=dev).view(copies, B, K)
+    Ys = [[torch.empty((B, N), device=dev) for N, _ in Q4_SHAPES] for _ in range(copies)]
+
+    def step():
+        for c in range(copies):
+            for i, W in enumerate(Ws[c]):
+                mm.gemv_q4_0_f32(W, X[c], out=Ys[c][i])
+    g = capture(step)
+    t = time_graph(g, steps, warmup)
+    nbytes = copies * q4_bytes(B)
+    del mats, Ws
+    return dict(B=B, copies=copies, launches_per_copy=len(Q4_SHAPES), s_per_step=t,
+                us_per_copy=t / copies * 1e6, GBps=nbytes / t / 1e9,
+                frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS)
+
+
+# ---------------------------------------------------------------------------
+# LM head: BF16 GEMV over the vocabulary, then argmax on the device
+# ---------------------------------------------------------------------------
+
+LM_VOCAB, LM_HID = 248320, 2560
+
+
+def lm_head_section(mm, dev, Bs, steps, warmup):
+    import torch
+    import synth
+    W = synth.bf16_weights(LM_VOCAB, LM_HID, 0, "lm_head", device=dev)   # 1.27 GB
+    res = dict(vocab=LM_VOCAB, hidden=LM_HID, weight_GB=W.numel() * 2 / 1e9)
+    for B in Bs:
+        X = synth.activations(B, LM_HID, 0, "lm_head", B, device=dev)
+        Y = torch.empty((B, LM_VOCAB), device=dev)
+        ids = torch.empty(B, dtype=torch.int32, device=dev)
+        vals = torch.empty(B, device=dev)
+        ws = torch.empty(mm.argmax_workspace_bytes(LM_VOCAB, B), dtype=torch.uint8, device=dev)
+        gemv = lambda: mm.gemv_bf16(W, X, out=Y)
+        amax = lambda: mm.argmax_rows(Y, ids=ids, vals=vals, workspace=ws)
+
+        def both():
+            gemv()
+            amax()
+        t_g = time_graph(capture(gemv), steps, warmup)
+        t_a = time_graph(capture(amax), steps, warmup)
+        t_b = time_graph(capture(both), steps, warmup)
+        gbytes = 2 * LM_VOCAB * LM_HID + 4 * B * LM_HID + 4 * B * LM_VOCAB
+        res[f"B{B}"] = dict(us_gemv=t_g * 1e6, us_argmax=t_a * 1e6, us_gemv_argmax=t_b * 1e6,
+                            gemv_GBps=gbytes / t_g / 1e9,
+                            gemv_frac_of_peak=gbytes / t_g / 1e9 / PEAK_HBM_GBPS,
+                            argmax_GBps=4 * B * LM_VOCAB / t_a / 1e9,
+                            bytes_to_host_per_token=4)
+        del X, Y, ids, vals, ws
+    del W
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------
 # MoE layers
 # ---------------------------------------------------------------------------
@@ -328,7 +399,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="dense,q4,moe256,moe512")
+    ap.add_argument("--only", default="dense,q4,w4a16,lmhead,moe256,moe512")
     ap.add_argument("--quick", action="store_true", help="fewer layer copies (smoke timing)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-kernel", action="store_true",
@@ -377,6 +448,20 @@ def main():
             log(f"q4_0 copies={copies} B={B}: {r['GBps']:.0f} GB/s, {r['us_per_copy']:.2f} us/copy")
             torch.cuda.empty_cache()
         sections["q4_0"] = q
+    if "w4a16" in only:
+        q = {}
+        for copies, B in ((8 if args.quick else 32, 1), (8 if args.quick else 32, 4)):
+            r = w4a16_section(mm, dev, copies, B, steps, warmup)
+            q[f"copies{copies}_B{B}"] = r
+            log(f"w4a16 copies={copies} B={B}: {r['GBps']:.0f} GB/s, {r['us_per_copy']:.2f} us/copy")
+            torch.cuda.empty_cache()
+        sections["q4_0_w4a16"] = q
+    if "lmhead" in only:
+        r = lm_head_section(mm, dev, [1, 8], steps, warmup)
+        sections["lm_head"] = r
+        log("lm head: " + ", ".join(
+            f"B{b} gemv {r[f'B{b}']['us_gemv']:.1f} us ({r[f'B{b}']['gemv_GBps']:.0f} GB/s), "
+            f"argmax {r[f'B{b}']['us_argmax']:.2f} us" for b in (1, 8)))
     if "moe256" in only:
         r = moe_section(mm, dev, 256, 8, 4 if args.quick else 40, [1], steps, warmup)
         sections["moe_e256_top8"] = r

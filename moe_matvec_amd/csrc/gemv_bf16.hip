@@ -4,17 +4,18 @@
 // Pass 3 item 2) replaces GEMM tiles, which use their tiles poorly at M = 1,
 // with a matrix-vector kernel whose vector loads stream the weights; its
 // Act 6 shows that decode then sits on the memory-bandwidth wall.  On gfx950
-// the same bound applies at ~8 TB/s of HBM3E, so the kernel is shaped only
+// the same bound applies at ~8 TB/s of HBM3E, so the kernels are shaped
 // around the weight stream:
-//  - one wave64 owns R whole rows; lane l reads 16-byte chunks l, l+64, ...
-//    of every row (8 bf16 per 128-bit load, 1 KiB per wave instruction,
-//    fully coalesced), non-temporal so x stays cached;
-//  - x is read through the L1/L2 (a few KiB, shared by every wave); each
-//    x chunk is loaded once and reused for the R rows of the wave;
-//  - no LDS and no MFMA: at B <= 8 the work is a matvec, bound by HBM;
-//  - each (row, b) sum runs over the same lanes and the same chunk order for
-//    every B, R and unroll, so a B-row call reproduces the 1-row call bit for
-//    bit; the 64 lane partials are combined by a fixed xor butterfly.
+//  - B = 1: one wave64 owns R whole rows; lane l reads 16-byte chunks l,
+//    l+64, ... of every row (8 bf16 per 128-bit load, 1 KiB per wave
+//    instruction, fully coalesced), non-temporal so x stays cached; x comes
+//    through L1/L2 or is staged once per workgroup in LDS; fp32 FMAs, no
+//    MFMA (a matvec); every variant sums a row in one order (chunk
+//    ascending, then a fixed lane butterfly), so all give the same bits.
+//  - B >= 2: 8 FMAs per weight would make the VALU the bound, so the x rows
+//    become one bf16 hi/lo matrix-core operand; the weights still arrive in
+//    contiguous 1 KiB wave loads and are re-laid out through LDS.  Rows
+//    agree bit for bit for every B >= 2, and with B = 1 within ~1e-6.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -238,8 +239,7 @@ __global__ __launch_bounds__(WPB * 64) void k_gemv_bf16_xl(
   }
 }
 
-// B >= 2: the x rows form a small dense operand, and 8 fp32 FMAs per weight
-// would make the VALU, not HBM, the bound.  v_mfma_f32_16x16x32_bf16 takes a
+// B >= 2 when K % 512 != 0: v_mfma_f32_16x16x32_bf16 takes a
 // 16-row x 32-k tile of W (one 128-bit load per lane: row l%16, k 8*(l/16)..)
 // against x^T (column l%16 = activation row b, zero for b >= B).  fp32 x is
 // split exactly into bf16 hi + lo (x - hi is exact in fp32; lo keeps the next
@@ -321,6 +321,159 @@ __global__ __launch_bounds__(KS * 64) void k_gemv_bf16_mfma(
   }
 }
 
+// x as one matrix-core operand for B >= 2: 16 columns made from the B rows
+// of x, column c < 8 holding bf16(x_c) (round to nearest even) and column
+// 8 + c the rounded remainder bf16(x_c - bf16(x_c)) (the subtraction is
+// exact in fp32), zero for c >= B; y[n][c] = D[n][c] + D[n][c + 8] keeps
+// ~2^-17 relative accuracy per product with one MFMA per step.  Each lane
+// loads only half of its 8 x values and takes the other half from the lane
+// 8 places along its 16-lane row (DPP row_ror:8).
+constexpr int kDppRowRor8 = 0x128;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t bf16_pair_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
+}
+
+// 8 consecutive x values -> this lane's 8 B-operand entries (hi or lo half)
+__device__ __forceinline__ bf16x8 x_operand(f32x4 p, f32x4 q, bool lo, uint32_t keep) {
+  const float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h = bf16_pair_bits(v[2 * i], v[2 * i + 1]);
+    const uint32_t l = bf16_pair_bits(v[2 * i] - bf16_lo(h), v[2 * i + 1] - bf16_hi(h));
+    out[i] = (lo ? l : h) & keep;
+  }
+  return __builtin_bit_cast(bf16x8, out);
+}
+
+// B >= 2 through LDS: the workgroup streams RT rows in chunks of 1 KiB per
+// row with contiguous 1 KiB wave loads (the pattern HBM serves best; loads
+// in the operand layout itself, 16 rows x 64 B per instruction, ran ~30%
+// slower), stores each chunk to LDS, and reads it back in the operand
+// layout of v_mfma_f32_16x16x32_bf16 (A = 16 weight rows x 32 k, lane l:
+// row l % 16, k 8 * (l / 16) ..).  Chunk i + PD is in flight while chunk i
+// is multiplied.  The NW waves split each chunk's 16 k-steps (wave w: steps
+// w, w + NW, ...) and make their own x operands for every row tile of the
+// workgroup; partial tiles are summed in LDS in wave order at the end, so a
+// row's bits depend on NW only (not on RT, PD, TH or B).  TH = 8: tiles of
+// 8 rows (operand rows 8..15 repeat rows 0..7).  NCH > 0 fixes the chunk
+// count (K = 512 NCH) and unrolls every chunk: a loop would carry the
+// prefetch registers around its back edge, and the copies that makes wait
+// for the loads still filling them.  Needs K % 512 == 0.
+constexpr int kMlChunk = 1024;             // bytes of a row per chunk
+constexpr int kMlPitch = kMlChunk + 16;    // LDS row pitch: 16-B skew between rows
+
+template <int B, int RT, int NW>
+constexpr size_t ml_lds_bytes() {
+  return (size_t)2 * RT * kMlPitch + (size_t)NW * RT * B * 4;
+}
+
+template <int B, int RT, int NW, int PD, int TH, int NCH = 0>
+__global__ __launch_bounds__(NW * 64) void k_gemv_bf16_ml(
+    const uint16_t *__restrict__ W, int N, int K, int64_t ldw, const float *__restrict__ X,
+    int64_t ldx, float *__restrict__ Y, int64_t ldy) {
+  constexpr int LPC = RT / NW;    // weight loads per lane per chunk (one row each)
+  constexpr int SPW = 16 / NW;    // k-steps per wave per chunk
+  constexpr int TILES = (RT + 15) / 16;
+  static_assert(RT % NW == 0 && 16 % NW == 0 && (TH == 16 || RT == 8), "shape");
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t *abuf = smem;                                                  // [2][RT][pitch]
+  float *part = reinterpret_cast<float *>(smem + (size_t)2 * RT * kMlPitch);  // [NW][RT][B]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4, c = n & 7;
+  const bool lo = n >= 8;
+  const int rb = blockIdx.x * RT;
+  const int nch = NCH ? NCH : K >> 9;
+  const uint8_t *wsrc[LPC];
+#pragma unroll
+  for (int j = 0; j < LPC; ++j)
+    wsrc[j] = reinterpret_cast<const uint8_t *>(W + (int64_t)min(rb + w + NW * j, N - 1) * ldw) +
+              16 * lane;
+  const float *xr = X + (int64_t)min(c, B - 1) * ldx + (lo ? 4 : 0) + 8 * g + 32 * w;
+  const uint32_t keep = c < B ? 0xFFFFFFFFu : 0u;
+
+  u32x4 wreg[PD][LPC];
+  f32x4 xreg[PD][SPW];
+  // x first, then weights: loads complete in order, so chunk i's x and
+  // weights arrive without waiting for later chunks
+  auto issue = [&](int ch, u32x4(&wr)[LPC], f32x4(&xg)[SPW]) {
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) xg[s] = load_f4(xr + 512 * ch + 32 * NW * s);
+#pragma unroll
+    for (int j = 0; j < LPC; ++j) wr[j] = load_stream16(wsrc[j] + (int64_t)kMlChunk * ch);
+  };
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+    if (p < nch) issue(p, wreg[p], xreg[p]);
+
+  f32x4v acc[TILES];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  // NCH > 0: every chunk unrolled, so no register is carried around a loop
+  // (a copy of a register that a load is still filling would wait for it)
+#pragma unroll
+  for (int i0 = 0; i0 < (NCH ? NCH : nch); i0 += PD) {
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+      const int i = i0 + p;
+      if (i < nch) {
+        uint8_t *buf = abuf + (size_t)(i & 1) * RT * kMlPitch;
+#pragma unroll
+        for (int j = 0; j < LPC; ++j)
+          *reinterpret_cast<u32x4 *>(buf + (w + NW * j) * kMlPitch + 16 * lane) = wreg[p][j];
+        bf16x8 xb[SPW];
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+          f32x4 o;
+          o.x = dpp_f32<kDppRowRor8>(xreg[p][s].x);
+          o.y = dpp_f32<kDppRowRor8>(xreg[p][s].y);
+          o.z = dpp_f32<kDppRowRor8>(xreg[p][s].z);
+          o.w = dpp_f32<kDppRowRor8>(xreg[p][s].w);
+          xb[s] = x_operand(lo ? o : xreg[p][s], lo ? xreg[p][s] : o, lo, keep);
+        }
+        __syncthreads();
+        if (i + PD < nch) issue(i + PD, wreg[p], xreg[p]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+          const int st = w + NW * s;
+#pragma unroll
+          for (int t = 0; t < TILES; ++t) {
+            const int row = t * 16 + (TH == 16 ? n : c);
+            const u32x4 av = *reinterpret_cast<const u32x4 *>(buf + row * kMlPitch + 64 * st + 16 * g);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), xb[s],
+                                                             acc[t], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = acc[t][i] + dpp_f32<kDppRowRor8>(acc[t][i]);
+      const int m = 4 * g + i;
+      if (!lo && c < B && m < TH) part[(w * RT + t * 16 + m) * B + c] = v;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < RT * B; idx += NW * 64) {
+    const int r = idx / B, cc = idx - r * B;
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) v += part[(q * RT + r) * B + cc];
+    if (rb + r < N) Y[(int64_t)cc * ldy + rb + r] = v;
+  }
+}
+
 namespace {
 
 struct Bf16Args {
@@ -352,12 +505,13 @@ hipError_t launch_ni(const Bf16Args &a) {
 
 // tuning knobs for experiments: MMV_BF16_R (rows per wave), MMV_BF16_WPB
 // (waves per workgroup), MMV_BF16_XL (waves per workgroup of the LDS-x
-// kernel; -1: off); each prints one line the first time it is used
+// kernel; -1: off), MMV_BF16_ML (matrix-core kernel shape); each prints one
+// line the first time it is used
 int env_knob(const char *name) {
   const char *v = getenv(name);
   if (!v || !*v) return 0;
-  static thread_local bool printed[3] = {false, false, false};
-  const int idx = name[9] == 'R' ? 0 : (name[9] == 'W' ? 1 : 2);  // R, WPB, XL
+  static thread_local bool printed[4] = {false, false, false, false};
+  const int idx = name[9] == 'R' ? 0 : (name[9] == 'W' ? 1 : (name[9] == 'X' ? 2 : 3));
   if (!printed[idx]) {
     fprintf(stderr, "[moe_matvec] %s=%s\n", name, v);
     printed[idx] = true;
@@ -385,6 +539,50 @@ hipError_t launch_mfma(const Bf16Args &a) {
   return hipGetLastError();
 }
 
+template <int B, int RT, int NW, int PD, int TH, int NCH = 0>
+hipError_t launch_ml(const Bf16Args &a) {
+  constexpr size_t lds = ml_lds_bytes<B, RT, NW>();
+  if (lds > 65536) {
+    static const hipError_t raised = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_gemv_bf16_ml<B, RT, NW, PD, TH, NCH>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (raised != hipSuccess) return raised;
+  }
+  hipLaunchKernelGGL((k_gemv_bf16_ml<B, RT, NW, PD, TH, NCH>), dim3((a.N + RT - 1) / RT),
+                     dim3(NW * 64), lds, a.s, a.W, a.N, a.K, a.ldw, a.X, a.ldx, a.Y, a.ldy);
+  return hipGetLastError();
+}
+
+template <int B, int RT, int NW, int PD, int TH>
+hipError_t launch_mlu(const Bf16Args &a) {
+  switch (a.K >> 9) {
+    case 4: return launch_ml<B, RT, NW, PD, TH, 4>(a);
+    case 5: return launch_ml<B, RT, NW, PD, TH, 5>(a);
+    case 8: return launch_ml<B, RT, NW, PD, TH, 8>(a);
+    case 19: return launch_ml<B, RT, NW, PD, TH, 19>(a);
+  }
+  return launch_ml<B, RT, NW, PD, TH>(a);
+}
+
+// B >= 2 and K % 512 == 0.  MMV_BF16_ML (experiments) = 10000 * RT +
+// 1000 * NW + 100 * PD + TH, + 1000000 for the chunk loop instead of the
+// unrolled chunks.  Default: 16-row workgroups of 8 waves, two chunks in
+// flight (2560 x 2560 / 19456 x 2560 / 2560 x 9728 at B = 8: 6.0 / 21 /
+// 15.7 us against 8.2 / 26 / 27.7 us for FMAs with x in LDS or the operand-
+// layout loads).
+template <int B>
+hipError_t dispatch_ml(const Bf16Args &a, int knob) {
+  switch (knob) {
+    case 0: return launch_mlu<B, 16, 8, 2, 16>(a);
+    case 1168216: return launch_ml<B, 16, 8, 2, 16>(a);
+    case 1328216: return launch_ml<B, 32, 8, 2, 16>(a);
+    case 1168316: return launch_ml<B, 16, 8, 3, 16>(a);
+    case 1088208: return launch_ml<B, 8, 8, 2, 8>(a);
+    case 1164216: return launch_ml<B, 16, 4, 2, 16>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
 // slab length: x of B rows in at most 80 KiB of LDS (SL chunks of 512)
 template <int B, int NI>
 constexpr int xl_slab() { return cmin(NI, 40 / B); }
@@ -406,46 +604,12 @@ hipError_t dispatch_xl(const Bf16Args &a, int WPB) {
   return launch_xl<1, NI, 2, 1>(a);
 }
 
-// B >= 2 with x in LDS, K = 512 * NI: two rows per wave share each x read;
-// MMV_BF16_XL = 100 * R + WPB overrides (-1: off).  Returns
-// hipErrorNotSupported for other K.
-template <int B>
-hipError_t dispatch_xl_b(const Bf16Args &a, int knob) {
-  if (a.K % 512 != 0) return hipErrorNotSupported;
-  const int NI = a.K / 512;
-  // long rows at B > 2: two rows' weights do not fit in registers, and with
-  // one row per wave the LDS reads of x (2 B per weight chunk) bound the
-  // kernel; the MFMA kernel is faster there (2560 x 9728, B = 8: 27.7 us
-  // against 35 us)
-  if (knob == 0 && NI > 8 && B > 2) return hipErrorNotSupported;
-  const int R = knob >= 100 ? knob / 100 : 2;
-  const int WPB = knob ? knob % 100 : 8;
-#define MMV_XLB(NIV)                                                                 \
-  if (NI == NIV) {                                                                   \
-    if constexpr (NIV * 4 <= 24) {                                                   \
-      if (R >= 4) return WPB >= 8 ? launch_xl<B, NIV, 8, 4>(a) : launch_xl<B, NIV, 4, 4>(a); \
-    }                                                                                \
-    if constexpr (NIV * 2 <= 40) {                                                   \
-      if (R >= 2) return WPB >= 8 ? launch_xl<B, NIV, 8, 2>(a) : launch_xl<B, NIV, 4, 2>(a); \
-    }                                                                                \
-    return WPB >= 8 ? launch_xl<B, NIV, 8, 1>(a) : launch_xl<B, NIV, 4, 1>(a);        \
-  }
-  MMV_XLB(1) MMV_XLB(2) MMV_XLB(4) MMV_XLB(5) MMV_XLB(8) MMV_XLB(16) MMV_XLB(19)
-#undef MMV_XLB
-  return hipErrorNotSupported;
-}
-
 template <int B>
 hipError_t dispatch_b(const Bf16Args &a) {
   if constexpr (B >= 2) {
-    // few 16-row tiles: more waves per tile keep enough loads in flight
+    if (a.K % 512 == 0) return dispatch_ml<B>(a, env_knob("MMV_BF16_ML"));
+    // other K: operand-layout loads, KS = MMV_BF16_WPB waves per 16-row tile
     const int kw = env_knob("MMV_BF16_WPB");
-    const int kx = env_knob("MMV_BF16_XL");  // experiments: 100 * R + WPB; -1: off
-    if (kx >= 0) {
-      const hipError_t e = dispatch_xl_b<B>(a, kx);
-      if (e != hipErrorNotSupported) return e;
-    }
-    const int tiles = (a.N + 15) / 16;
     const int KS = kw ? kw : 8;
     if (KS >= 16) return launch_mfma<B, 16, 8>(a);
     if (KS >= 8) return launch_mfma<B, 8, 8>(a);

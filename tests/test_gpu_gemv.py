@@ -35,9 +35,11 @@ def test_bf16_parity(mm, orc, dev, N, K, B):
     assert rel_l2_rows(npc(y), ref) <= BF16_TOL
 
 
-def test_bf16_integer_pin_bit_exact(mm, orc, dev):
+@pytest.mark.parametrize("N,K,B", [(777, 1032, 8), (777, 1032, 1), (300, 2560, 8), (35, 9728, 3)])
+def test_bf16_integer_pin_bit_exact(mm, orc, dev, N, K, B):
+    # small integers: every product and partial sum is exact in fp32 (and x
+    # is exact in bf16, so its hi/lo split has lo = 0 on the B >= 2 path)
     g = torch.Generator().manual_seed(1)
-    N, K, B = 777, 1032, 8
     Wf = torch.randint(-8, 9, (N, K), generator=g).float()
     Xf = torch.randint(-16, 17, (B, K), generator=g).float()
     y = mm.gemv_bf16(Wf.to(torch.bfloat16).to(dev), Xf.to(dev))
@@ -45,13 +47,23 @@ def test_bf16_integer_pin_bit_exact(mm, orc, dev):
     assert np.array_equal(npc(y).astype(np.float64), want)
 
 
+@pytest.mark.parametrize("N,K", [(2560, 2560), (19456, 2560), (2560, 9728)])
+@pytest.mark.parametrize("B", [1, 8])
+def test_bf16_full_size_decode_shapes(mm, orc, dev, N, K, B):
+    # the dense decode set at full size (attn-out, fused gate+up, down), in
+    # the configuration the benchmark times
+    W = synth.bf16_weights(N, K, 0, "full", N, K, device=dev)
+    X = synth.activations(B, K, 0, "full", N, K, B, device=dev)
+    y = mm.gemv_bf16(W, X)
+    torch.cuda.synchronize()
+    assert rel_l2_rows(npc(y), orc.gemv_bf16(np16(W), npc(X))) <= BF16_TOL
+
+
 def test_bf16_batch_invariance_and_determinism(mm, dev):
-    # K = 512 * NI with x in LDS: every B sums each (row, b) in the B = 1
-    # kernel's order, so every row equals its 1-row call bit for bit.  For
-    # long rows at B > 2 the MFMA kernel (x split into bf16 hi + lo) takes
-    # over: rows agree bit for bit among those B, and with B = 1 within
-    # rounding.
-    for N, K, bit_b in ((3000, 2560, 8), (700, 9728, 2)):
+    # B >= 2 runs on the matrix cores with x split into bf16 hi + lo: column b
+    # of the product depends on x row b alone, so every B >= 2 gives the same
+    # bits for a row, and the B = 1 kernel (fp32 FMAs) agrees within rounding
+    for N, K in ((3000, 2560), (700, 9728), (300, 1016), (129, 3072)):
         W = synth.bf16_weights(N, K, 0, "inv", K, device=dev)
         X = synth.activations(8, K, 0, "inv", K, device=dev)
         y8 = mm.gemv_bf16(W, X)
@@ -59,29 +71,31 @@ def test_bf16_batch_invariance_and_determinism(mm, dev):
         for b in range(8):
             y1 = mm.gemv_bf16(W, X[b].clone())
             pair = mm.gemv_bf16(W, X[[b, (b + 3) % 8]].contiguous())[0]
-            assert torch.equal(pair, y1)
-            if bit_b == 8:
-                assert torch.equal(y1, y8[b])
-            else:
-                assert rel_l2_rows(npc(y1)[None], npc(y8[b])[None]) <= 1e-5
+            assert torch.equal(pair, y8[b])
+            assert rel_l2_rows(npc(y1)[None], npc(y8[b])[None]) <= 1e-5
         for B in (3, 4, 5, 6, 7):
             assert torch.equal(mm.gemv_bf16(W, X[:B].contiguous()), y8[:B])
 
 
-@pytest.mark.parametrize("knob", ["104", "108", "204", "404", "408"])
-def test_bf16_lds_x_variants_identical(mm, dev, monkeypatch, knob):
-    # B >= 2 with x in LDS, any rows per wave and waves per workgroup, and x
-    # slabs (K = 9728 at B = 8 stages x in four slabs): the bits of the
-    # 1-row calls
+@pytest.mark.parametrize("knob", ["1168216", "1328216", "1168316", "1088208", "1164216"])
+def test_bf16_lds_mfma_variants(mm, orc, dev, monkeypatch, knob):
+    # B >= 2, K % 512 == 0: the chunk loop instead of unrolled chunks, 32-row
+    # workgroups, three chunks in flight and 8-row tiles give the default's
+    # bits (a row's order depends on the waves per workgroup only); 4 waves
+    # per workgroup sum the k-steps in another grouping: within rounding
     for N, K, B in ((1000, 2560, 8), (300, 2048, 5), (257, 4096, 3), (130, 9728, 8),
-                    (90, 9728, 2)):
-        W = synth.bf16_weights(N, K, 0, "xlb", N, K, device=dev)
-        X = synth.activations(B, K, 0, "xlb", N, K, device=dev)
-        monkeypatch.setenv("MMV_BF16_XL", knob)
+                    (90, 9728, 2), (17, 3072, 4), (1, 512, 2)):
+        W = synth.bf16_weights(N, K, 0, "mlb", N, K, device=dev)
+        X = synth.activations(B, K, 0, "mlb", N, K, device=dev)
+        y0 = mm.gemv_bf16(W, X)
+        monkeypatch.setenv("MMV_BF16_ML", knob)
         y = mm.gemv_bf16(W, X)
-        monkeypatch.delenv("MMV_BF16_XL")
-        for b in range(B):
-            assert torch.equal(y[b], mm.gemv_bf16(W, X[b].clone()))
+        monkeypatch.delenv("MMV_BF16_ML")
+        if knob == "1164216":
+            assert rel_l2_rows(npc(y), npc(y0)) <= 1e-6
+            assert rel_l2_rows(npc(y), orc.gemv_bf16(np16(W), npc(X))) <= BF16_TOL
+        else:
+            assert torch.equal(y, y0)
 
 
 @pytest.mark.parametrize("knobs", [dict(MMV_BF16_XL="-1", MMV_BF16_R="1", MMV_BF16_WPB="1"),
@@ -186,6 +200,21 @@ def test_q4_0_parity(mm, orc, dev, N, K, B):
     q_ref, ds_ref = orc.quantize_q8_1(npc(X))
     ref = orc.gemv_q4_0(qs, d, q_ref, ds_ref)
     assert rel_l2_rows(npc(y_x), ref) <= Q4_TOL
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096)])
+@pytest.mark.parametrize("B", [1, 8])
+def test_q4_0_full_size(mm, orc, dev, N, K, B):
+    # the Q4_0 decode shapes at full size; B = 8 as the benchmark runs it
+    # (quantize into a buffer, then the product)
+    W, qs, d = _q4(mm, N, K, dev, "full")
+    X = synth.activations(B, K, 0, "q4full", N, K, B, device=dev)
+    xq = torch.empty(mm.q8_1_bytes(K, B), dtype=torch.uint8, device=dev) if B > 1 else None
+    y = mm.gemv_q4_0(W, x=X, xq=xq)
+    torch.cuda.synchronize()
+    xq_ref, xds_ref = orc.quantize_q8_1(npc(X))
+    ref = orc.gemv_q4_0(qs, d, xq_ref, xds_ref)
+    assert rel_l2_rows(npc(y), ref) <= Q4_TOL
 
 
 def test_q4_0_unit_scale_pin_bit_exact(mm, dev):
