@@ -130,7 +130,7 @@ def dominant_kernel(mm, dev, W, layers, steps, warmup):
     g = capture(step)
     t = time_graph(g, steps, warmup) / layers
     per_launch = 2 * N * K + 4 * K + 4 * N
-    return dict(kernel="k_gemv_bf16_xl<5, 8, 1> (gate+up 19456x2560, B=1)", s_per_launch=t,
+    return dict(kernel="k_gemv_bf16_xl<1, 5, 8, 1, 5> (gate+up 19456x2560, B=1)", s_per_launch=t,
                 bytes_per_launch=per_launch, GBps=per_launch / t / 1e9)
 
 
@@ -224,20 +224,25 @@ def lm_head_section(mm, dev, Bs, steps, warmup):
     import synth
     W = synth.bf16_weights(LM_VOCAB, LM_HID, 0, "lm_head", device=dev)   # 1.27 GB
     res = dict(vocab=LM_VOCAB, hidden=LM_HID, weight_GB=W.numel() * 2 / 1e9)
+    reps = 16  # argmax alone: this many calls per graph, so the replay is not host-bound
     for B in Bs:
         X = synth.activations(B, LM_HID, 0, "lm_head", B, device=dev)
         Y = torch.empty((B, LM_VOCAB), device=dev)
+        Ys = synth.normal((reps, B, LM_VOCAB), 1.0, 0, "lm_logits", B, device=dev)
         ids = torch.empty(B, dtype=torch.int32, device=dev)
         vals = torch.empty(B, device=dev)
         ws = torch.empty(mm.argmax_workspace_bytes(LM_VOCAB, B), dtype=torch.uint8, device=dev)
         gemv = lambda: mm.gemv_bf16(W, X, out=Y)
-        amax = lambda: mm.argmax_rows(Y, ids=ids, vals=vals, workspace=ws)
+
+        def amax():
+            for r in range(reps):
+                mm.argmax_rows(Ys[r], ids=ids, vals=vals, workspace=ws)
 
         def both():
             gemv()
-            amax()
+            mm.argmax_rows(Y, ids=ids, vals=vals, workspace=ws)
         t_g = time_graph(capture(gemv), steps, warmup)
-        t_a = time_graph(capture(amax), steps, warmup)
+        t_a = time_graph(capture(amax), steps, warmup) / reps
         t_b = time_graph(capture(both), steps, warmup)
         gbytes = 2 * LM_VOCAB * LM_HID + 4 * B * LM_HID + 4 * B * LM_VOCAB
         res[f"B{B}"] = dict(us_gemv=t_g * 1e6, us_argmax=t_a * 1e6, us_gemv_argmax=t_b * 1e6,
@@ -245,7 +250,7 @@ def lm_head_section(mm, dev, Bs, steps, warmup):
                             gemv_frac_of_peak=gbytes / t_g / 1e9 / PEAK_HBM_GBPS,
                             argmax_GBps=4 * B * LM_VOCAB / t_a / 1e9,
                             bytes_to_host_per_token=4)
-        del X, Y, ids, vals, ws
+        del X, Y, Ys, ids, vals, ws
     del W
     torch.cuda.empty_cache()
     return res
