@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import synth
-from tests._util import build_moe, check_route, npc, rel_l2_rows
+from tests._util import build_moe, check_route, np16, npc, rel_l2_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,41 @@ def test_moe_layer_decode(mm, orc, dev, monkeypatch, topk_kernel, E, H, I, k, B)
     same = [b for b in range(B) if np.array_equal(npc(ids)[b], out["ids"][b])]
     assert len(same) >= B - 1            # near ties in float64 logits are rare
     assert rel_l2_rows(npc(y)[same], out["y"][same]) <= MOE_TOL
+
+
+@pytest.mark.parametrize("topk_kernel", ["0", "1"])
+@pytest.mark.parametrize("B", [1, 2, 5])
+def test_moe_layer_decode_tied_router_rows(mm, orc, dev, monkeypatch, topk_kernel, B):
+    # identical router rows give bit-identical logits: the selected experts and
+    # their slot order must follow the lower index among equal logits, in the
+    # per-workgroup rank selection (one row) as in the full top-k
+    monkeypatch.setenv("MMV_MOE_TOPK_KERNEL", topk_kernel)
+    E, H, I, k = 64, 512, 64, 8
+    t = synth.moe_layer_tensors(E, H, I, 0, "ties", E, device=dev)
+    X = synth.activations(B, H, 0, "ties", B, device=dev)
+    R = t["router"]
+    for b in range(B):  # a strong expert per row, copied to higher and lower indices
+        src = 20 + b
+        R[src] = 0.3 * X[b] / X[b].norm()
+        for dst in (40 + 2 * b, 41 + 2 * b, b):
+            R[dst] = R[src]
+    sh = t["shared"]
+    layer = mm.MoeLayer(R, t["gate_qs"], t["gate_d"], t["up_qs"], t["up_d"], t["down_qs"],
+                        t["down_d"], k, shared=sh)
+    ref = orc.MoE(npc(R), npc(t["gate_qs"]), np16(t["gate_d"]), npc(t["up_qs"]),
+                  np16(t["up_d"]), npc(t["down_qs"]), np16(t["down_d"]), k,
+                  shared=tuple(npc(sh[n]) if n.endswith("qs") else np16(sh[n])
+                               for n in ("gate_qs", "gate_d", "up_qs", "up_d", "down_qs",
+                                         "down_d")))
+    ids = torch.empty((B, k), dtype=torch.int32, device=dev)
+    y = mm.moe_layer_decode(layer, X, ids=ids)
+    torch.cuda.synchronize()
+    out = ref.layer(npc(X))
+    assert np.array_equal(npc(ids), out["ids"])
+    for b in range(B):
+        tied = [b, 20 + b, 40 + 2 * b, 41 + 2 * b]
+        assert npc(ids)[b, :4].tolist() == tied
+    assert rel_l2_rows(npc(y), out["y"]) <= MOE_TOL
 
 
 def test_topk_exact_ties_from_logits(mm, orc, dev):
