@@ -196,7 +196,7 @@ def test_q4_0_parity(mm, orc, dev, N, K, B):
     # x and xq together: x is quantized into xq, then xq is read
     buf = torch.full_like(xq, 0x5A)
     y_b = mm.gemv_q4_0(W, x=X, xq=buf)
-    assert torch.equal(buf, xq) and torch.equal(y_b, y_x)
+    assert torch.equal(buf, xq) and torch.equal(y_b, y_q)
     q_ref, ds_ref = orc.quantize_q8_1(npc(X))
     ref = orc.gemv_q4_0(qs, d, q_ref, ds_ref)
     assert rel_l2_rows(npc(y_x), ref) <= Q4_TOL
@@ -230,6 +230,47 @@ def test_q4_0_unit_scale_pin_bit_exact(mm, dev):
     y = mm.gemv_q4_0(W, x=x.to(dev))
     want = x.double() @ (codes.reshape(N, K).double() - 8).T
     assert np.array_equal(npc(y).astype(np.float64), want.numpy())
+
+
+@pytest.mark.parametrize("B", [8, 3])
+def test_q4_0_unit_scale_pin_matrix_cores(mm, dev, monkeypatch, B):
+    # the same exact case through a caller Q8_1 buffer on the int8 matrix
+    # cores (MMV_Q4_MF=1: exact int32 block dots, unit scales)
+    monkeypatch.setenv("MMV_Q4_MF", "1")
+    g = torch.Generator().manual_seed(4)
+    N, K = 333, 4096
+    codes = torch.randint(0, 16, (N, K // 32, 32), generator=g, dtype=torch.uint8)
+    qs = (codes[..., :16] | (codes[..., 16:] << 4)).contiguous()
+    d = torch.ones((N, K // 32), dtype=torch.float16)
+    x = torch.randint(-127, 128, (B, K), generator=g).float()
+    x.view(B, -1, 32)[:, :, 7] = -127.0
+    W = mm.Q4_0(qs.to(dev), d.to(dev))
+    xq = torch.empty(mm.q8_1_bytes(K, B), dtype=torch.uint8, device=dev)
+    y = mm.gemv_q4_0(W, x=x.to(dev), xq=xq)
+    want = x.double() @ (codes.reshape(N, K).double() - 8).T
+    assert np.array_equal(npc(y).astype(np.float64), want.numpy())
+
+
+@pytest.mark.parametrize("N,K,B", [(1000, 4096, 3), (17, 2048, 8), (4097, 4096, 2),
+                                   (33, 4096, 8), (2048, 2048, 5)])
+def test_q4_0_matrix_core_path(mm, orc, dev, monkeypatch, N, K, B):
+    monkeypatch.setenv("MMV_Q4_MF", "1")
+    W, qs, d = _q4(mm, N, K, dev, "mf")
+    X = synth.activations(B, K, 0, "q4mf", N, K, B, device=dev)
+    xq = mm.quantize_q8_1(X)
+    y = mm.gemv_q4_0(W, xq=xq, B=B)
+    torch.cuda.synchronize()
+    q_ref, ds_ref = orc.quantize_q8_1(npc(X))
+    assert rel_l2_rows(npc(y), orc.gemv_q4_0(qs, d, q_ref, ds_ref)) <= Q4_TOL
+    # every B >= 2 gives a row the same bits; the vector-ALU kernel (dot4)
+    # sums the same exact block products in another order
+    for b in range(B):
+        other = X[[b, (b + 1) % B]].contiguous()
+        y2 = mm.gemv_q4_0(W, xq=mm.quantize_q8_1(other), B=2)
+        assert torch.equal(y2[0], y[b])
+    monkeypatch.delenv("MMV_Q4_MF")
+    y_v = mm.gemv_q4_0(W, xq=xq, B=B)
+    assert rel_l2_rows(npc(y_v), npc(y)) <= 1e-6
 
 
 def test_q4_0_batch_invariance(mm, dev):
