@@ -254,7 +254,7 @@ __device__ void build_gather(const int32_t *__restrict__ ids, int Bk, int E, Gat
   if (t < MAXP) {
     const uint32_t mine = g.key[t];
     int rank = 0;
-#pragma unroll
+#pragma unroll 4  // (fully unrolled, all MAXP keys would sit in registers at once)
     for (int c = 0; c < MAXP / 4; ++c) {
       const uint4 q = reinterpret_cast<const uint4 *>(g.key)[c];
       rank += (q.x < mine) + (q.y < mine) + (q.z < mine) + (q.w < mine);
@@ -403,74 +403,82 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
     xpre_quantize(xall, B, H, st, 0, 256);
   } else if constexpr (T > 0) {
     xpre_quantize(xp, nr, H, st, 0, 256);
-    stage_quantize(a.X, a.ldx, rowmap, nr, H, st, MAXT * 256, 256);
+    // rows past the preloaded ones (B > 2), in passes of MAXT tasks: the
+    // weights are in flight meanwhile, so registers are short here
+    stage_quantize<MAXT>(a.X, a.ldx, rowmap, nr, H, st, MAXT * 256, 256);
   } else {
     stage_quantize(a.X, a.ldx, rowmap, nr, H, st);
   }
   __syncthreads();
-  int srow[B];  // stage row of tile row r
+  // gate row n and up row n of one activation row -> h (lanes sub == 0)
+  auto put_h = [&](int r, const float (&a4)[4]) {
 #pragma unroll
-  for (int r = 0; r < B; ++r) srow[r] = PRE > 0 ? rowmap[min(r, nr - 1)] : r;
-
-  float acc[4][B];
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-#pragma unroll
-    for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
-  auto block = [&](const u32x4 (&wb)[4], const float (&db)[4], int j) {
-#pragma unroll
-    for (int r = 0; r < B; ++r) {
-      if (r < nr) {
-        const int sr = srow[r];
-        const i32x4 xa = xstage_lo(st, sr, H, j);
-        const i32x4 xb = xstage_hi(st, sr, H, j);
-        const int xs = st.qsum[sr * nbh + j];
-        const float dx = st.d[sr * nbh + j];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int Iv = q4_block_isum(wb[p], xa, xb, xs);
-          acc[p][r] = fmaf(db[p] * dx, (float)Iv, acc[p][r]);
-        }
+    for (int hh = 0; hh < 2; ++hh) {
+      const float gv = row16_sum(a4[hh]);
+      const float uv = row16_sum(a4[2 + hh]);
+      const float h = silu_f(gv) * uv;
+      const int nl = 8 * wv + 4 * hh + q;
+      if (sub == 0) {
+        hbuf[r][nl] = h;
+        if (a.has_dbg && a.dbg.h) a.dbg.h[(int64_t)pairmap[r] * I + tile * 32 + nl] = h;
       }
     }
   };
-  if constexpr (T > 0) {
+  {
+    int srow[B];  // stage row of tile row r
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      u32x4 wb[4];
-      float db[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) { wb[p] = w[p][t]; db[p] = dw[p][t]; }
-      block(wb, db, sub + 16 * t);
-    }
-  } else {
-    for (int j = sub; j < nbh; j += 16) {
-      u32x4 wb[4];
-      float db[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint8_t *wq = p < 2 ? gq : uq;
-        const uint16_t *wd = p < 2 ? gd : ud;
-        wb[p] = load_stream16(wq + (rowoff[p] + j) * 16);
-        db[p] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
-      }
-      block(wb, db, j);
-    }
-  }
+    for (int r = 0; r < B; ++r) srow[r] = PRE > 0 ? rowmap[min(r, nr - 1)] : r;
 
+    float acc[4][B];
 #pragma unroll
-  for (int r = 0; r < B; ++r) {
-    if (r < nr) {
+    for (int p = 0; p < 4; ++p)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float gv = row16_sum(acc[hh][r]);
-        const float uv = row16_sum(acc[2 + hh][r]);
-        const float h = silu_f(gv) * uv;
-        const int nl = 8 * wv + 4 * hh + q;
-        if (sub == 0) {
-          hbuf[r][nl] = h;
-          if (a.has_dbg && a.dbg.h) a.dbg.h[(int64_t)pairmap[r] * I + tile * 32 + nl] = h;
+      for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
+    auto block = [&](const u32x4 (&wb)[4], const float (&db)[4], int j) {
+#pragma unroll
+      for (int r = 0; r < B; ++r) {
+        if (r < nr) {
+          const int sr = srow[r];
+          const i32x4 xa = xstage_lo(st, sr, H, j);
+          const i32x4 xb = xstage_hi(st, sr, H, j);
+          const int xs = st.qsum[sr * nbh + j];
+          const float dx = st.d[sr * nbh + j];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int Iv = q4_block_isum(wb[p], xa, xb, xs);
+            acc[p][r] = fmaf(db[p] * dx, (float)Iv, acc[p][r]);
+          }
         }
+      }
+    };
+    if constexpr (T > 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        u32x4 wb[4];
+        float db[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) { wb[p] = w[p][t]; db[p] = dw[p][t]; }
+        block(wb, db, sub + 16 * t);
+      }
+    } else {
+      for (int j = sub; j < nbh; j += 16) {
+        u32x4 wb[4];
+        float db[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint8_t *wq = p < 2 ? gq : uq;
+          const uint16_t *wd = p < 2 ? gd : ud;
+          wb[p] = load_stream16(wq + (rowoff[p] + j) * 16);
+          db[p] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
+        }
+        block(wb, db, j);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < B; ++r) {
+      if (r < nr) {
+        const float a4[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+        put_h(r, a4);
       }
     }
   }

@@ -125,13 +125,14 @@ __device__ __forceinline__ void xpre_quantize(const XPre<MAXT> &p, int nrows, in
 // (all threads of the workgroup call this; blockDim.x % 64 == 0).  `from`
 // skips tasks an earlier xpre_load / xpre_quantize pair already covered.
 constexpr int kStageMaxT = 8;
+template <int PASS = kStageMaxT>  // tasks per thread per pass (registers held: 4 * PASS)
 __device__ __forceinline__ void stage_quantize(const float *__restrict__ X, int64_t ldx,
                                                const int *rowmap, int nrows, int K,
                                                XStage st, int from = 0, int nth = 0) {
   const int total = nrows * (K >> 5) * 8;
   if (nth == 0) nth = blockDim.x;
-  for (int base = from; base < total; base += kStageMaxT * nth) {
-    XPre<kStageMaxT> p;
+  for (int base = from; base < total; base += PASS * nth) {
+    XPre<PASS> p;
     xpre_load(X, ldx, rowmap, nrows, K, p, base, nth);
     xpre_quantize(p, nrows, K, st, base, nth);
   }
