@@ -332,33 +332,58 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
   for (int p = 0; p < RP; ++p)
 #pragma unroll
     for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
+  // Per block: the codes of a (row, group of 4 bytes) are converted to fp32
+  // once and used for every x row; x of all B rows for those positions is
+  // read from LDS once and used for the RP rows.  For each (row, x row) the
+  // FMAs run low nibbles then high nibbles, bytes ascending: one order for
+  // every B.
+  constexpr int DG = B > 4 ? 2 : 4;  // code dwords per step (registers: x of B rows)
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int j = sub + G * t;
+    float s1[RP][B];
+#pragma unroll
+    for (int p = 0; p < RP; ++p)
+#pragma unroll
+      for (int r = 0; r < B; ++r) s1[p][r] = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {        // low nibbles: codes 0..15; high: 16..31
+#pragma unroll
+      for (int d0 = 0; d0 < 4; d0 += DG) {
+        f32x4 xq[B][DG];
+#pragma unroll
+        for (int r = 0; r < B; ++r)
+#pragma unroll
+          for (int dd = 0; dd < DG; ++dd) xq[r][dd] = xs[(r * 8 + 4 * h + d0 + dd) * nb + j];
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+          const uint32_t wd[4] = {w[p][t].x, w[p][t].y, w[p][t].z, w[p][t].w};
+          float cf[DG][4];
+#pragma unroll
+          for (int dd = 0; dd < DG; ++dd) {
+            const uint32_t c = (wd[d0 + dd] >> (4 * h)) & 0x0F0F0F0Fu;
+            cf[dd][0] = (float)(c & 0xFFu);
+            cf[dd][1] = (float)((c >> 8) & 0xFFu);
+            cf[dd][2] = (float)((c >> 16) & 0xFFu);
+            cf[dd][3] = (float)(c >> 24);
+          }
+#pragma unroll
+          for (int r = 0; r < B; ++r)
+#pragma unroll
+            for (int dd = 0; dd < DG; ++dd) {
+              s1[p][r] = fmaf(cf[dd][0], xq[r][dd].x, s1[p][r]);
+              s1[p][r] = fmaf(cf[dd][1], xq[r][dd].y, s1[p][r]);
+              s1[p][r] = fmaf(cf[dd][2], xq[r][dd].z, s1[p][r]);
+              s1[p][r] = fmaf(cf[dd][3], xq[r][dd].w, s1[p][r]);
+            }
+        }
+      }
+    }
 #pragma unroll
     for (int r = 0; r < B; ++r) {
-      f32x4 xq[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) xq[q] = xs[(r * 8 + q) * nb + j];
       const float sxr = sx[r * nb + j];
 #pragma unroll
-      for (int p = 0; p < RP; ++p) {
-        const uint32_t wd[4] = {w[p][t].x, w[p][t].y, w[p][t].z, w[p][t].w};
-        float s1 = 0.0f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {      // low nibbles: codes 0..15; high: 16..31
-#pragma unroll
-          for (int dd = 0; dd < 4; ++dd) {
-            const uint32_t c = (wd[dd] >> (4 * h)) & 0x0F0F0F0Fu;
-            const f32x4 xv4 = xq[4 * h + dd];
-            s1 = fmaf((float)(c & 0xFFu), xv4.x, s1);
-            s1 = fmaf((float)((c >> 8) & 0xFFu), xv4.y, s1);
-            s1 = fmaf((float)((c >> 16) & 0xFFu), xv4.z, s1);
-            s1 = fmaf((float)(c >> 24), xv4.w, s1);
-          }
-        }
-        acc[p][r] = fmaf(d[p][t], fmaf(-8.0f, sxr, s1), acc[p][r]);
-      }
+      for (int p = 0; p < RP; ++p) acc[p][r] = fmaf(d[p][t], fmaf(-8.0f, sxr, s1[p][r]), acc[p][r]);
     }
   }
   float (&flat)[RP * B] = *reinterpret_cast<float(*)[RP * B]>(&acc[0][0]);
