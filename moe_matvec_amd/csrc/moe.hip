@@ -91,12 +91,75 @@ __device__ __forceinline__ void router_row(const float *__restrict__ row, int H,
 // ---------------------------------------------------------------------------
 // Selects the k largest of l[0..E) (ties: lower index first), writes ids,
 // renormalised weights and the shared weight.  Whole wave, uniform control.
-// KPL = keys per lane (E <= 64 * KPL); lane l holds experts l + 64 i.  Each
-// round takes the wave maximum of the keys (DPP), then the lowest expert
-// index holding it: the first slot i whose ballot is non-empty, then that
-// ballot's lowest lane.  Selected keys drop to 0, below every finite logit.
-// The selected logit is read back from the key itself.  All loads are
-// unconditional (clamped in bounds) so they are in flight together.
+// KPL = keys per lane (E <= 64 * KPL); lane l holds experts l + 64 i, as
+// order-preserving keys (-0 = +0; padding lanes hold 0, below every logit).
+// Each lane first sorts its own keys, largest first (a min/max network), so
+// that a round needs only the lanes' leading keys: the wave maximum M of
+// them (DPP), the lane holding it (one ballot; when several lanes hold M,
+// the lowest expert index among their leading elements wins), and that lane
+// drops its leading key.  Which of a lane's elements a pick was is settled
+// after the rounds from the lane's unsorted keys: the lowest index holding M
+// that earlier picks of the same lane and value have not taken.  With one
+// wave per row the rounds are bound by instruction issue, so what counts is
+// a round's instruction count: about 30 + KPL here against about 12 * KPL
+// for rescanning every key each round.
+
+// Batcher's odd-even merge sort networks (comparator pairs a[c] < b[c]),
+// applied largest first; N a power of two.
+template <int N> struct SortNet {
+  static constexpr int n = 0;
+  static constexpr unsigned char a[1] = {0};
+  static constexpr unsigned char b[1] = {0};
+};
+template <> struct SortNet<2> {
+  static constexpr int n = 1;
+  static constexpr unsigned char a[1] = {0};
+  static constexpr unsigned char b[1] = {1};
+};
+template <> struct SortNet<4> {
+  static constexpr int n = 5;
+  static constexpr unsigned char a[5] = {0, 2, 0, 1, 1};
+  static constexpr unsigned char b[5] = {1, 3, 2, 3, 2};
+};
+template <> struct SortNet<8> {
+  static constexpr int n = 19;
+  static constexpr unsigned char a[19] = {0, 2, 4, 6, 0, 1, 4, 5, 1, 5, 0, 1, 2, 3, 2, 3, 1, 3, 5};
+  static constexpr unsigned char b[19] = {1, 3, 5, 7, 2, 3, 6, 7, 2, 6, 4, 5, 6, 7, 4, 5, 2, 4, 6};
+};
+template <> struct SortNet<16> {
+  static constexpr int n = 63;
+  static constexpr unsigned char a[63] = {0, 2, 4, 6, 8, 10, 12, 14, 0, 1, 4, 5, 8, 9, 12, 13, 1, 5, 9, 13, 0, 1, 2, 3, 8, 9, 10, 11, 2, 3, 10, 11, 1, 3, 5, 9, 11, 13, 0, 1, 2, 3, 4, 5, 6, 7, 4, 5, 6, 7, 2, 3, 6, 7, 10, 11, 1, 3, 5, 7, 9, 11, 13};
+  static constexpr unsigned char b[63] = {1, 3, 5, 7, 9, 11, 13, 15, 2, 3, 6, 7, 10, 11, 14, 15, 2, 6, 10, 14, 4, 5, 6, 7, 12, 13, 14, 15, 4, 5, 12, 13, 2, 4, 6, 10, 12, 14, 8, 9, 10, 11, 12, 13, 14, 15, 8, 9, 10, 11, 4, 5, 8, 9, 12, 13, 2, 4, 6, 8, 10, 12, 14};
+};
+
+template <int N>
+__device__ __forceinline__ void sort_desc_u32(uint32_t (&v)[N]) {
+#pragma unroll
+  for (int c = 0; c < SortNet<N>::n; ++c) {
+    const uint32_t x = v[SortNet<N>::a[c]], y = v[SortNet<N>::b[c]];
+    v[SortNet<N>::a[c]] = max(x, y);
+    v[SortNet<N>::b[c]] = min(x, y);
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// Slot (0..KPL) of this lane's element that a pick of value M takes: earlier
+// picks of this lane with value M took the lowest such slots, and their
+// number is the count of M among the unsorted keys minus the count of M
+// still in the sorted list.
+template <int KPL>
+__device__ __forceinline__ int slot_of_value(const uint32_t (&orig)[KPL], int taken, uint32_t M) {
+  int seen = 0, s = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const bool m = orig[i] == M;
+    s = (m && seen == taken) ? i : s;
+    seen += m ? 1 : 0;
+  }
+  return s;
+}
+
 template <int KPL>
 __device__ void topk_row(const float *__restrict__ l, int E, int k, int has_shared,
                          int32_t *__restrict__ ids, float *__restrict__ weights,
@@ -106,26 +169,63 @@ __device__ void topk_row(const float *__restrict__ l, int E, int k, int has_shar
 #pragma unroll
   for (int i = 0; i < KPL; ++i) v[i] = l[min(lane + 64 * i, E - 1)];
   const float lsh = has_shared ? l[E] : 0.0f;
-  uint32_t key[KPL];
+  uint32_t orig[KPL], key[KPL];
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) key[i] = lane + 64 * i < E ? topk_ord(v[i]) : 0u;
-  int my_id = 0;
-  float my_l = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint32_t m = key[0];
-#pragma unroll
-    for (int i = 1; i < KPL; ++i) m = max(m, key[i]);
-    const uint32_t M = wave_max_u32(m);
-    int e = 64 * KPL;
-#pragma unroll
-    for (int i = KPL - 1; i >= 0; --i) {  // the lowest slot with a hit wins
-      const unsigned long long hit = __ballot(key[i] == M);
-      if (hit) e = 64 * i + __builtin_ctzll(hit);
-    }
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) key[i] = (lane + 64 * i == e) ? 0u : key[i];
-    if (lane == j) { my_id = e; my_l = topk_unord(M); }
+  for (int i = 0; i < KPL; ++i) {
+    orig[i] = lane + 64 * i < E ? topk_ord(v[i]) : 0u;
+    key[i] = orig[i];
   }
+  sort_desc_u32<KPL>(key);
+  // equal keys within a lane (rare): picks then count earlier picks
+  bool dup = false;
+#pragma unroll
+  for (int i = 0; i + 1 < KPL; ++i) dup = dup || (key[i] == key[i + 1] && key[i] != 0u);
+  const bool any_dup = __ballot(dup) != 0ull;
+
+  uint32_t pick_lane = 0, pick_key = 0;  // round j's pick, held by lane j
+  for (int j = 0; j < k; ++j) {
+    const uint32_t M = wave_max_u32(key[0]);
+    const unsigned long long hit = __ballot(key[0] == M);
+    uint32_t L;
+    if (__popcll(hit) == 1) {
+      L = (uint32_t)__builtin_ctzll(hit);
+    } else {  // the lowest index among the lanes' leading elements equal to M
+      int cnt_o = 0, cnt_r = 0;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        cnt_o += orig[i] == M ? 1 : 0;
+        cnt_r += key[i] == M ? 1 : 0;
+      }
+      const int s = slot_of_value<KPL>(orig, cnt_o - cnt_r, M);
+      L = wave_min_u32(key[0] == M ? ((uint32_t)s << 6) | (uint32_t)lane : 0xFFFFFFFFu) & 63u;
+    }
+    // the winning lane shifts its list by one (bit-select with an opaque
+    // mask: written as a select, the compiler rebuilds it as a dynamically
+    // indexed vector read)
+    uint32_t m = (uint32_t)lane == L ? ~0u : 0u;
+    asm volatile("" : "+v"(m));
+#pragma unroll
+    for (int i = 0; i + 1 < KPL; ++i) key[i] = (key[i + 1] & m) | (key[i] & ~m);
+    key[KPL - 1] &= ~m;
+    pick_lane = lane == j ? L : pick_lane;
+    pick_key = lane == j ? M : pick_key;
+  }
+  // which element of lane pick_lane each pick was (lanes j < k)
+  int taken = 0;
+  if (any_dup) {
+    for (int j = 0; j < k; ++j) {
+      const uint32_t Lj = (uint32_t)__builtin_amdgcn_readlane((int)pick_lane, j);
+      const uint32_t Mj = (uint32_t)__builtin_amdgcn_readlane((int)pick_key, j);
+      taken += (j < lane && Lj == pick_lane && Mj == pick_key) ? 1 : 0;
+    }
+  }
+  uint32_t theirs[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i)
+    theirs[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(pick_lane << 2), (int)orig[i]);
+  const int my_id = 64 * slot_of_value<KPL>(theirs, taken, pick_key) + (int)pick_lane;
+  const float my_l = lane < k ? topk_unord(pick_key) : 0.0f;
+
   const float lmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
   const float ex = lane < k ? expf(my_l - lmax) : 0.0f;
   const float den = row16_sum(ex);  // k <= 16: lanes 0..15
