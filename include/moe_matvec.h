@@ -229,8 +229,9 @@ typedef struct {
  * Layout: bytes [0, mmv_q8_1_bytes(I, P)) hold Q8_1(h) for the P pairs
  * (P = B*k routed pairs p = b*k + j, then B shared pairs p = B*k + b),
  * followed by the integer code sums of those blocks, the per-expert row
- * lists, and the routing buffers and one synchronization word that
- * moe_layer_decode uses.  256-byte aligned workspace required.
+ * lists, the routing buffers that moe_layer_decode uses, and P x H fp32
+ * per-pair down products (the by-expert down projection for B >= 3).
+ * 256-byte aligned workspace required.
  * The down projection stages Q8_1(h) of all P pairs in LDS:
  * P * I <= MMV_MOE_MAX_PI (else MMV_E_SHAPE). */
 #define MMV_MOE_MAX_PI 49152
@@ -263,7 +264,10 @@ int moe_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx,
  *   per-expert row lists (inside every gate/up workgroup for B <= 2, in a
  *   one-workgroup kernel of its own for larger B); the gate/up of the
  *   shared and the routed experts with the Q8_1 epilogue; the down
- *   projection with the combine.  Three launches for B <= 2, four above.
+ *   projection with the combine (one kernel for B <= 2; for B >= 3 one
+ *   workgroup per (expert, 64 output rows), then a combine kernel).  Three
+ *   launches for B <= 2, five above.  Every row's result is the same bits
+ *   whatever the other rows of the batch are.
  *   Routing stays in device memory.  ids / weights (B x k) may be NULL;
  *   when given they receive the routing decision.  The workspace needs no
  *   initialisation; calls that share a workspace must not overlap.

@@ -118,7 +118,8 @@ int moe_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_
   if (st != MMV_OK) return st;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   const mmv::MoeWsLayout lay =
-      mmv::moe_ws_layout(L->n_experts, L->inter, L->top_k, B, L->sh_gate_qs != nullptr);
+      mmv::moe_ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, B,
+                         L->sh_gate_qs != nullptr);
   int32_t *id = ids ? ids : reinterpret_cast<int32_t *>(ws + lay.ids);
   float *w = weights ? weights : reinterpret_cast<float *>(ws + lay.weights);
   return hip_status(mmv::run_moe_layer(*L, X, ldx, B, id, w, Y, ldy, ws, as_stream(stream)));

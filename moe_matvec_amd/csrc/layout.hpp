@@ -25,11 +25,11 @@ MMV_HD size_t q8_1_bytes(int K, int B) { return (size_t)B * K + (size_t)4 * B * 
 MMV_HD size_t hq_bytes(int P, int I) { return q8_1_bytes(I, P) + (size_t)8 * P * (I / 32); }
 
 // moe workspace: [hq][gather lists][logits B x (E+1)][ids B x k]
-// [weights B x k][shared_w B]
+// [weights B x k][shared_w B][per-pair down products P x H fp32]
 struct MoeWsLayout {
-  size_t hq, gather, logits, ids, weights, shared_w, total;
+  size_t hq, gather, logits, ids, weights, shared_w, dpart, total;
 };
-MMV_HD MoeWsLayout moe_ws_layout(int E, int I, int k, int B, bool has_shared) {
+MMV_HD MoeWsLayout moe_ws_layout(int E, int H, int I, int k, int B, bool has_shared) {
   MoeWsLayout l;
   const int P = B * k + (has_shared ? B : 0);
   l.hq = 0;
@@ -38,7 +38,8 @@ MMV_HD MoeWsLayout moe_ws_layout(int E, int I, int k, int B, bool has_shared) {
   l.ids = align_up(l.logits + (size_t)4 * B * (E + 1), kWsAlign);
   l.weights = align_up(l.ids + (size_t)4 * B * k, kWsAlign);
   l.shared_w = align_up(l.weights + (size_t)4 * B * k, kWsAlign);
-  l.total = align_up(l.shared_w + (size_t)4 * B, kWsAlign);
+  l.dpart = align_up(l.shared_w + (size_t)4 * B, kWsAlign);
+  l.total = align_up(l.dpart + (size_t)4 * P * H, kWsAlign);
   return l;
 }
 

@@ -11,7 +11,7 @@
 // four rows per wave.  "Flash-Next on Strix Halo" (Expert GEMMs) builds
 // per-expert row lists so each expert's weights are read once for all rows
 // that chose it.  Here, on gfx950, one layer is three launches for B <= 2
-// and four above:
+// and five above:
 //  K1 router rows (one wave per row, all loads issued up front), logits to
 //     the workspace;
 //  (B > 2) K1b one workgroup, a wave per row: top-k with order-preserving
@@ -24,12 +24,16 @@
 //     every workgroup runs top-k on the logits itself (no extra launch);
 //     silu(g)*u in registers; the tile's 32 h values are exactly one Q8_1
 //     block of the down input, quantized in the epilogue;
-//  K3 down + combine: a workgroup owns 4 output rows (16 lanes per row, one
-//     Q4_0 block per lane at I = 512); its 4 waves split the experts by
-//     expert id mod 4, each walking its experts in ascending id (the shared
-//     expert last, in wave 0), and the 4 wave partials are added in wave
-//     order: every row's sum has the same order whatever the other rows
-//     chose, no atomics, one store per output.
+//  K3 down + combine (B <= 2): a workgroup owns 4 output rows (16 lanes per
+//     row, one Q4_0 block per lane at I = 512); its waves split the experts
+//     by expert id; each (row, pair) product is formed whole (per lane its
+//     blocks, then the 16-lane sum) and a row's pairs are added by a fixed
+//     tree over its slots, then the shared expert's term: no atomics, one
+//     store per output;
+//  K3 by expert + K4 combine (B >= 3): a workgroup owns one expert and 64
+//     output rows and writes each of its pairs' products (the same values,
+//     bit for bit) to the workspace; K4 adds them with the same tree.
+//  Every row's result is thus the same bits for every B.
 // A grid-wide barrier inside one kernel measured slower than a launch
 // boundary on this GPU, so the phases stay separate launches.
 #include <stdio.h>
@@ -430,6 +434,7 @@ struct MoeArgs {
   float *shared_w_out;
   int router_wgs;
   int topk_in_k2;    // 1: every K2 workgroup runs top-k on the logits itself
+  float *dpart;      // P x H per-pair down products (the by-expert down path)
 };
 
 // Published row lists (workspace): [0] U, [1, 1+Bk) unique experts,
@@ -772,31 +777,53 @@ __global__ __launch_bounds__(512) void k_moe_topk_gather(MoeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K3: down + weighted combine + shared expert
+// K3: down + weighted combine + shared expert (one kernel)
 // ---------------------------------------------------------------------------
 // NWV waves (8 for B = 3, 4; else 4); the workgroup owns 4 output rows (lane
 // group q of every wave = row 4*blockIdx + q).  Wave w takes the experts with
-// id % NWV == w (ascending: a row's order depends on its own experts only),
-// wave 0 also the shared expert last.  Q8_1(h) of every pair is
-// staged in LDS (codes, fp32 d, integer sums).  Order of work, so that no
-// wait covers more than it needs (loads complete in issue order): the row
-// lists, then Q8_1(h), are requested; the lists go to LDS and each wave's
-// expert list is built; the wave's first chunk of expert weights is
-// requested; only then is Q8_1(h) stored to LDS.  The first chunk covers
-// every expert of the wave for typical batches (one load latency for all of
-// them); experts beyond it follow in double-buffered chunks of kDownCH (the
-// next requested before the current one is used).  Loads within a chunk are
-// unconditional: a slot past the end of the wave's list re-reads its last
-// expert (or expert 0 for an empty list) and is not used.  TI = I / 512 (compile time) or 0
-// (runtime loop over I % 32 == 0, one block at a time).
+// id % NWV == w, wave 0 also the shared expert last; each (row, pair)
+// product goes to LDS, and after the expert loop a row's pairs are added
+// by the slot tree (down_combine_tree), so which wave held an expert does
+// not change any bit.  Q8_1(h) of every pair is staged in LDS (codes, fp32
+// d, integer sums).  Order of work, so that no wait covers more than it
+// needs (loads complete in issue order): the row lists are requested and go
+// to LDS, and each wave's expert list is built; the wave's first chunk of
+// expert weights is requested, then Q8_1(h) goes straight into LDS.  The
+// first chunk covers every expert of the wave for typical batches (one load
+// latency for all of them); experts beyond it follow in double-buffered
+// chunks of kDownCH (the next requested before the current one is used).
+// Loads within a chunk are unconditional: a slot past the end of the
+// wave's list re-reads its last expert (or expert 0 for an empty list) and
+// is not used.  TI = I / 512 (compile time) or 0 (runtime loop over
+// I % 32 == 0, one block at a time).
 constexpr int kDownCH = 4;  // experts per weight chunk after the first
 
+// one (pair, block) term of a down product: d_w d_h sum_i (q_i - 8) c_i
+__device__ __forceinline__ float down_block_value(u32x4 wb, float db, i32x4 xa, i32x4 xb,
+                                                  float dx, int qs) {
+  return (db * dx) * (float)q4_block_isum(wb, xa, xb, qs);
+}
+
+// The sum over a row's slots: the pairwise tree row16_sum forms over 16
+// lanes (lane j = slot j, zero past k), written out for one thread; float
+// addition commutes, so every lane of the DPP tree and this code agree.
+__device__ __forceinline__ float down_combine_tree(const float (&p)[16]) {
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = (p[4 * i] + p[4 * i + 1]) + (p[4 * i + 2] + p[4 * i + 3]);
+  return (q[0] + q[1]) + (q[2] + q[3]);
+}
+
+// Scales stay fp16 bits until the products: converted where they are
+// loaded, they make the compiler wait for the weight loads before anything
+// requested after them (Q8_1(h)).
 template <int TI, int CH = kDownCH>
 struct DownChunk {
   static constexpr int kCH = CH;
   u32x4 w[CH][TI > 0 ? TI : 1];
-  float d[CH][TI > 0 ? TI : 1];
+  uint16_t d[CH][TI > 0 ? TI : 1];
 };
+
 
 // experts in a wave's first chunk: every expert of the wave for typical
 // batches (experts are split over the 4 waves by id % 4, so about U / 4 each;
@@ -815,7 +842,7 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
   __shared__ int s_wn[NWV];
   __shared__ int s_U;
   __shared__ float s_pw[kMaxPairs + MMV_MAX_BATCH];
-  __shared__ float part[NWV][4][B];
+  __shared__ float s_dot[4][kMaxPairs + MMV_MAX_BATCH];  // per output row, per pair
   extern __shared__ __align__(16) uint8_t smem[];
 
   const mmv_moe_layer &L = a.L;
@@ -847,6 +874,8 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
   put_gather(t, g0);
   put_gather(t + 256, g1);
   if (t < Bk + B) s_pw[t] = pwv;
+  // pairs that no expert list holds (ids outside [0, E)) add zero
+  for (int i = t; i < 4 * (kMaxPairs + MMV_MAX_BATCH); i += 64 * NWV) (&s_dot[0][0])[i] = 0.0f;
   __syncthreads();
   const int U = s_U;
   // per-wave expert lists: class = id % NWV, ascending; shared expert (index
@@ -905,7 +934,7 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
       for (int ti = 0; ti < TI; ++ti) {
         const int64_t blk = (int64_t)rowc * nbi + sub + 16 * ti;
         ch.w[c][ti] = load_stream16(dq + blk * 16);
-        ch.d[c][ti] = f16_bits_to_f32(load_stream2(dd + blk));
+        ch.d[c][ti] = load_stream2(dd + blk);
       }
     }
   };
@@ -954,47 +983,39 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS writes done; the barrier publishes them
   __syncthreads();
 
-  float acc[B];
-#pragma unroll
-  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-  // one (pair, block) product into its row's sum
-  // one (pair, block) product into its row's sum: the LDS reads, then the math
+  // Each pair's product with its expert is formed whole, in one order for
+  // every B and whichever wave holds the expert: per lane the blocks it owns
+  // (ascending), then the 16-lane sum; a row's pairs are added after the
+  // expert loop by a fixed tree over its slots, as k_moe_combine adds them.
   struct PairData {
     i32x4 xa, xb;
     int qs;
-    float dx, gw;
+    float dx;
   };
   auto pair_load = [&](int p, int j, PairData &pd) {
     pd.xa = xstage_lo(hs, p, I, j);
     pd.xb = xstage_hi(hs, p, I, j);
     pd.qs = hs.qsum[p * nbi + j];
     pd.dx = hs.d[p * nbi + j];
-    pd.gw = s_pw[p];
   };
-  auto pair_apply = [&](const PairData &pd, int pb, const u32x4 wb, const float db) {
-    const int Iv = q4_block_isum(wb, pd.xa, pd.xb, pd.qs);
-    const float part_v = (db * pd.dx) * (float)Iv;
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-      if (b == pb) acc[b] = fmaf(pd.gw, part_v, acc[b]);
+  auto pair_value = [&](const PairData &pd, const u32x4 wb, const float db) {
+    return down_block_value(wb, db, pd.xa, pd.xb, pd.dx, pd.qs);
   };
-  auto pair_block = [&](int p, int pb, const u32x4 wb, const float db, int j) {
-    PairData pd;
-    pair_load(p, j, pd);
-    pair_apply(pd, pb, wb, db);
+  auto put_dot = [&](int p, float v) {
+    v = row16_sum(v);
+    if (sub == 0) s_dot[q][p] = v;
   };
-  // every pair of list entries c0 .. c0 + CH - 1, expert by expert, pairs in
-  // order (a row meets each expert once, so its sum runs in list order).  In
-  // groups of 4 experts, the list metadata, then the first pair's LDS data
-  // of each expert are read together (independent reads in flight), so most
-  // experts (one pair each when rows share few experts) cost no dependent
-  // LDS round trip of their own.
+  // every pair of list entries c0 .. c0 + CH - 1.  In groups of 4 experts,
+  // the list metadata, then the first pair's LDS data of each expert are
+  // read together (independent reads in flight), so most experts (one pair
+  // each when rows share few experts) cost no dependent LDS round trip of
+  // their own, and their 16-lane sums run interleaved.
   auto consume_chunk = [&](const auto &ch, int c0) {
     constexpr int CH = std::remove_reference_t<decltype(ch)>::kCH;
     constexpr int MG = cmin(CH, 4);
 #pragma unroll
     for (int c4 = 0; c4 < CH; c4 += MG) {
-      int pbeg[MG], pend[MG], isu[MG], p0[MG], b0[MG];
+      int pbeg[MG], pend[MG], isu[MG], p0[MG];
       bool val[MG];
 #pragma unroll
       for (int c = 0; c < MG; ++c) {
@@ -1002,30 +1023,40 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
         val[c] = c0 + c4 + c < n;
         isu[c] = u < U;
         pbeg[c] = isu[c] ? s_off[u] : 0;
-        pend[c] = isu[c] ? s_off[u + 1] : B;
+        pend[c] = isu[c] ? min(s_off[u + 1], s_off[u] + B) : B;
       }
 #pragma unroll
-      for (int c = 0; c < MG; ++c) {
-        p0[c] = isu[c] ? s_pairs[pbeg[c]] : Bk;
-        b0[c] = isu[c] ? s_prow[pbeg[c]] : 0;
-      }
+      for (int c = 0; c < MG; ++c) p0[c] = isu[c] ? s_pairs[pbeg[c]] : Bk;
       PairData pd[MG][TI];
 #pragma unroll
       for (int c = 0; c < MG; ++c)
 #pragma unroll
         for (int ti = 0; ti < TI; ++ti) pair_load(p0[c], sub + 16 * ti, pd[c][ti]);
+      float v0[MG];
+#pragma unroll
+      for (int c = 0; c < MG; ++c) {
+        v0[c] = 0.0f;
+#pragma unroll
+        for (int ti = 0; ti < TI; ++ti)
+          v0[c] += pair_value(pd[c][ti], ch.w[c4 + c][ti], f16_bits_to_f32(ch.d[c4 + c][ti]));
+      }
+      gsum_last_n<16, MG>(v0);  // the same sums as row16_sum, interleaved
+#pragma unroll
+      for (int c = 0; c < MG; ++c)
+        if (val[c] && sub == 0) s_dot[q][p0[c]] = v0[c];
 #pragma unroll
       for (int c = 0; c < MG; ++c) {
         if (val[c]) {
-#pragma unroll
-          for (int ti = 0; ti < TI; ++ti)
-            pair_apply(pd[c][ti], b0[c], ch.w[c4 + c][ti], ch.d[c4 + c][ti]);
           for (int pi = pbeg[c] + 1; pi < pend[c]; ++pi) {
             const int p = isu[c] ? s_pairs[pi] : Bk + pi;
-            const int pb = isu[c] ? s_prow[pi] : pi;
+            float v = 0.0f;
 #pragma unroll
-            for (int ti = 0; ti < TI; ++ti)
-              pair_block(p, pb, ch.w[c4 + c][ti], ch.d[c4 + c][ti], sub + 16 * ti);
+            for (int ti = 0; ti < TI; ++ti) {
+              PairData pdx;
+              pair_load(p, sub + 16 * ti, pdx);
+              v += pair_value(pdx, ch.w[c4 + c][ti], f16_bits_to_f32(ch.d[c4 + c][ti]));
+            }
+            put_dot(p, v);
           }
         }
       }
@@ -1048,38 +1079,228 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
       expert_ptr(c, dq, dd);
       const int u = wl[c];
       const bool su = u < U;
-      const int pb0 = su ? s_off[u] : 0, pe0 = su ? s_off[u + 1] : B;
+      const int pb0 = su ? s_off[u] : 0;
+      const int np = su ? min(s_off[u + 1] - pb0, B) : B;
+      float vp[B];
+#pragma unroll
+      for (int r = 0; r < B; ++r) vp[r] = 0.0f;
       for (int j = sub; j < nbi; j += 16) {
         const int64_t blk = (int64_t)rowc * nbi + j;
         const u32x4 wb = load_stream16(dq + blk * 16);
         const float db = f16_bits_to_f32(load_stream2(dd + blk));
-        for (int pi = pb0; pi < pe0; ++pi) {
-          const int p = su ? s_pairs[pi] : Bk + pi;
-          pair_block(p, su ? s_prow[pi] : pi, wb, db, j);
+#pragma unroll
+        for (int r = 0; r < B; ++r) {
+          if (r < np) {
+            PairData pd;
+            pair_load(su ? s_pairs[pb0 + r] : Bk + r, j, pd);
+            vp[r] += pair_value(pd, wb, db);
+          }
         }
       }
+#pragma unroll
+      for (int r = 0; r < B; ++r)
+        if (r < np) put_dot(su ? s_pairs[pb0 + r] : Bk + r, vp[r]);
     }
   }
 
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    const float v = row16_sum(acc[b]);
-    if (sub == 0) part[wv][q][b] = v;
-  }
   __syncthreads();
-  if (t < 4 * B) {
-    const int qq = t / B, b = t - qq * B;
-    float v = part[0][qq][b];
-#pragma unroll
-    for (int w = 1; w < NWV; ++w) v += part[w][qq][b];
-    const int r = blockIdx.x * 4 + qq;
-    if (r < H) a.Y[(int64_t)b * a.ldy + r] = v;
+  // each row's pairs: lane j of a 16-lane group takes slot j (zero past k),
+  // the products w * dot summed by the 16-lane tree, then the shared term
+  // (down_combine_tree is the same sum, written out)
+  for (int b = wv; b < B; b += NWV) {  // uniform over the wave
+    const int j = sub;
+    const int p = b * k + min(j, k - 1);
+    const float prod = j < k ? s_pw[p] * s_dot[q][p] : 0.0f;
+    float v = row16_sum(prod);
+    if (has_sh) v = fmaf(s_pw[Bk + b], s_dot[q][Bk + b], v);
+    const int r = blockIdx.x * 4 + q;
+    if (sub == 0 && r < H) a.Y[(int64_t)b * a.ldy + r] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// K3 by expert (more rows) + combine
+// ---------------------------------------------------------------------------
+// With many rows the one-kernel down projection walks every unique expert
+// in every output-row workgroup and stages Q8_1(h) of all pairs in each of
+// them.  Here a workgroup owns one expert slot (the shared expert first,
+// then the unique routed experts) and 64 output rows: it reads that
+// 64 x I block of the expert's Down once, Q8_1(h) of the slot's pairs
+// straight from the workspace (at most 4 pairs in flight), and writes each
+// pair's product to the workspace (dpart[p * H + n]), formed as in K3
+// (per lane its blocks ascending, then the 16-lane sum), so the result is
+// the same bit for bit.  k_moe_combine then adds each row's pairs in slot
+// order.  A slot's expert and pair range come from the published row lists;
+// slots past the number of unique experts exit.
+constexpr int kDownPartRows = 64;
+
+template <int B, int TI>
+__global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
+  constexpr int RP = kDownPartRows / 16;   // rows per 16-lane group
+  constexpr int NP = B < 4 ? B : 4;        // pairs whose Q8_1(h) is in flight together
+  constexpr int TT = TI > 0 ? TI : 1;
+  const mmv_moe_layer &L = a.L;
+  const int k = L.top_k, H = L.hidden, I = L.inter;
+  const int Bk = B * k, nbi = I >> 5;
+  const int has_sh = L.sh_down_qs != nullptr ? 1 : 0;
+  const int ntile = (H + kDownPartRows - 1) / kDownPartRows;
+  const int slot0 = blockIdx.x / ntile, tile = blockIdx.x - slot0 * ntile;
+  const bool shared_slot = has_sh && slot0 == 0;
+  const int u = slot0 - has_sh;  // < Bk: every list entry read below is in bounds
+  const int32_t *gl = a.gather;
+  const uint8_t *dq;
+  const uint16_t *dd;
+  int np, pbase;
+  if (shared_slot) {
+    dq = L.sh_down_qs; dd = L.sh_down_d;
+    np = B; pbase = 0;
+  } else {
+    const int U = gl[0], e = gl[1 + u], o0 = gl[1 + Bk + u], o1 = gl[2 + Bk + u];
+    if (u >= U) return;  // uniform over the workgroup
+    const int64_t eo = (int64_t)e * H * nbi;
+    dq = L.down_qs + eo * 16; dd = L.down_d + eo;
+    np = min(o1 - o0, B);
+    pbase = o0;
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, sub = lane & 15, q = lane >> 4;
+  const int row0 = tile * kDownPartRows + 16 * wv + q;  // + 4 rp
+  // the slot's pair indices, lane r holding the r-th, requested before the
+  // weights (loads complete in issue order: waiting for these does not wait
+  // for the weights)
+  const int pl_r = gl[2 + 2 * Bk + pbase + min(lane, max(np - 1, 0))];
+  const int pl = shared_slot ? Bk + min(lane, B - 1) : pl_r;
+  u32x4 w[RP][TT];
+  uint16_t dw[RP][TT];  // fp16 bits until use (see DownChunk)
+  if constexpr (TI > 0) {
+#pragma unroll
+    for (int rp = 0; rp < RP; ++rp) {
+      const int rowc = min(row0 + 4 * rp, H - 1);
+#pragma unroll
+      for (int ti = 0; ti < TI; ++ti) {
+        const int64_t blk = (int64_t)rowc * nbi + sub + 16 * ti;
+        w[rp][ti] = load_stream16(dq + blk * 16);
+        dw[rp][ti] = load_stream2(dd + blk);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const HqView hv = hq_view(a.hq, a.P, I);
+  auto store_dots = [&](int p, float (&v)[RP]) {
+    gsum_last_n<16, RP>(v);  // the same sums as row16_sum, interleaved
+    if (sub == 0) {
+#pragma unroll
+      for (int rp = 0; rp < RP; ++rp)
+        if (row0 + 4 * rp < H) a.dpart[(int64_t)p * H + row0 + 4 * rp] = v[rp];
+    }
+  };
+  // NP pairs at a time: the Q8_1(h) loads of the group, then its products.
+  // The first group is straight-line code, so that nothing working on the
+  // weights (scale conversion, nibble masks) is hoisted above its loads;
+  // more groups (the shared expert for B > 4, or an expert that more than 4
+  // rows chose) follow in a loop.
+  auto pair_group = [&](int r0) {
+    int pp[NP];
+#pragma unroll
+    for (int c = 0; c < NP; ++c) {
+      pp[c] = __builtin_amdgcn_readlane(pl, min(r0 + c, np - 1));
+    }
+    if constexpr (TI > 0) {
+      i32x4 xa[NP][TT], xb[NP][TT];
+      int xd[NP][TT], xs[NP][TT];
+#pragma unroll
+      for (int c = 0; c < NP; ++c)
+#pragma unroll
+        for (int ti = 0; ti < TI; ++ti) {
+          const int j = sub + 16 * ti;
+          const int8_t *cb = reinterpret_cast<const int8_t *>(hv.codes) + (size_t)pp[c] * I + 32 * j;
+          xa[c][ti] = *reinterpret_cast<const i32x4 *>(cb);
+          xb[c][ti] = *reinterpret_cast<const i32x4 *>(cb + 16);
+          const int *rec = reinterpret_cast<const int *>(hv.dq + (size_t)pp[c] * nbi + j);
+          xd[c][ti] = rec[0];
+          xs[c][ti] = rec[1];
+        }
+      __builtin_amdgcn_sched_barrier(0);  // the loads above go out before any product
+#pragma unroll
+      for (int c = 0; c < NP; ++c) {
+        if (r0 + c < np) {  // uniform
+          float v[RP];
+#pragma unroll
+          for (int rp = 0; rp < RP; ++rp) {
+            v[rp] = 0.0f;
+#pragma unroll
+            for (int ti = 0; ti < TI; ++ti) {
+              v[rp] += down_block_value(w[rp][ti], f16_bits_to_f32(dw[rp][ti]), xa[c][ti],
+                                        xb[c][ti], __int_as_float(xd[c][ti]), xs[c][ti]);
+            }
+          }
+          store_dots(pp[c], v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NP; ++c) {
+        if (r0 + c < np) {  // uniform
+          float v[RP];
+#pragma unroll
+          for (int rp = 0; rp < RP; ++rp) v[rp] = 0.0f;
+          for (int j = sub; j < nbi; j += 16) {
+            const int8_t *cb = reinterpret_cast<const int8_t *>(hv.codes) + (size_t)pp[c] * I + 32 * j;
+            const i32x4 xa = *reinterpret_cast<const i32x4 *>(cb);
+            const i32x4 xb = *reinterpret_cast<const i32x4 *>(cb + 16);
+            const int *rec = reinterpret_cast<const int *>(hv.dq + (size_t)pp[c] * nbi + j);
+            const float dx = __int_as_float(rec[0]);
+            const int qs = rec[1];
+#pragma unroll
+            for (int rp = 0; rp < RP; ++rp) {
+              const int64_t blk = (int64_t)min(row0 + 4 * rp, H - 1) * nbi + j;
+              const u32x4 wb = load_stream16(dq + blk * 16);
+              const float db = f16_bits_to_f32(load_stream2(dd + blk));
+              v[rp] += down_block_value(wb, db, xa, xb, dx, qs);
+            }
+          }
+          store_dots(pp[c], v);
+        }
+      }
+    }
+  };
+  pair_group(0);
+  for (int r0 = NP; r0 < np; r0 += NP) pair_group(r0);  // uniform
+}
+
+// Y[b][n] = tree_j (w[b k + j] dot_{b k + j}[n]) + s_b dot_{Bk + b}[n] with
+// the sum K3 forms (down_combine_tree); pairs with ids outside [0, E) add
+// zero.  grid = (ceil(H / 256), B).
+template <int B>
+__global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
+  const mmv_moe_layer &L = a.L;
+  const int H = L.hidden, k = L.top_k, E = L.n_experts, Bk = B * k;
+  const int b = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  const int nc = min(n, H - 1);
+  const bool has_sh = L.sh_down_qs != nullptr;
+  static_assert(MMV_MAX_TOPK <= 16, "slots per row");
+  float d[16], pr[16];
+  // every load first, unconditionally (pinned in registers, so that the
+  // selects below cannot pull them into branches one round trip each)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) d[j] = a.dpart[(int64_t)(b * k + min(j, k - 1)) * H + nc];
+  float dsh = a.dpart[(int64_t)(has_sh ? Bk + b : 0) * H + nc];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(d[j]));
+  asm volatile("" : "+v"(dsh));
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int p = b * k + min(j, k - 1);
+    const int e = a.ids[p];
+    pr[j] = j < k ? a.weights[p] * ((e >= 0 && e < E) ? d[j] : 0.0f) : 0.0f;
+  }
+  float v = down_combine_tree(pr);
+  if (has_sh) v = fmaf(a.shared_w ? a.shared_w[b] : 1.0f, dsh, v);
+  if (n < H) a.Y[(int64_t)b * a.ldy + n] = v;
+}
+
 namespace {
 
 // MMV_MOE_TOPK_KERNEL=1: top-k and row lists in a kernel of their own;
@@ -1096,6 +1317,19 @@ int moe_topk_knob() {
   return atoi(v) ? 1 : -1;
 }
 
+// MMV_MOE_DOWN=1: the one-kernel down projection at every B; =2: by expert
+// at every B; unset: by B.  Prints one line the first time it is read.
+int moe_down_knob() {
+  const char *v = getenv("MMV_MOE_DOWN");
+  if (!v || !*v) return 0;
+  static bool printed = false;
+  if (!printed) {
+    fprintf(stderr, "[moe_matvec] MMV_MOE_DOWN=%s\n", v);
+    printed = true;
+  }
+  return atoi(v);
+}
+
 MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
                   const int32_t *ids, const float *weights, const float *shared_w, float *Y,
                   int64_t ldy, uint8_t *ws, const mmv_moe_debug *dbg) {
@@ -1109,7 +1343,7 @@ MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
   a.Y = Y;
   a.ldy = ldy;
   const bool has_sh = L.sh_gate_qs != nullptr;
-  const MoeWsLayout lay = moe_ws_layout(L.n_experts, L.inter, L.top_k, B, has_sh);
+  const MoeWsLayout lay = moe_ws_layout(L.n_experts, L.hidden, L.inter, L.top_k, B, has_sh);
   a.hq = ws + lay.hq;
   a.gather = reinterpret_cast<int32_t *>(ws + lay.gather);
   a.P = B * L.top_k + (has_sh ? B : 0);
@@ -1117,6 +1351,7 @@ MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
   a.has_dbg = dbg != nullptr;
   a.dbg = dbg ? *dbg : mmv_moe_debug{nullptr, nullptr, nullptr, nullptr, nullptr};
   a.logits = reinterpret_cast<float *>(ws + lay.logits);
+  a.dpart = reinterpret_cast<float *>(ws + lay.dpart);
   a.gather_ready = 0;
   a.ids_out = nullptr;
   a.weights_out = nullptr;
@@ -1140,8 +1375,20 @@ void launch_gate_up(const MoeArgs &a, hipStream_t s) {
 template <int B>
 constexpr int down_waves() { return (B == 3 || B == 4) ? 8 : 4; }
 
+// rows from which the down projection runs by expert (two launches: the
+// per-pair products, then the combine)
+constexpr int kDownSplitMinB = 3;
+
 template <int B, int TI>
 void launch_down(const MoeArgs &a, hipStream_t s) {
+  const int knob = moe_down_knob();
+  if (knob == 2 || (knob != 1 && B >= kDownSplitMinB)) {
+    const int slots = B * a.L.top_k + (a.L.sh_down_qs ? 1 : 0);
+    const int ntile = (a.L.hidden + kDownPartRows - 1) / kDownPartRows;
+    hipLaunchKernelGGL((k_moe_down_part<B, TI>), dim3(slots * ntile), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_moe_combine<B>), dim3((a.L.hidden + 255) / 256, B), dim3(256), 0, s, a);
+    return;
+  }
   const size_t lds = xstage_bytes(a.P, a.L.inter);
   constexpr int NWV = down_waves<B>();
   hipLaunchKernelGGL((k_moe_down<B, TI, NWV>), dim3((a.L.hidden + 3) / 4), dim3(64 * NWV), lds, s,
@@ -1204,7 +1451,7 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
                          int32_t *ids, float *weights, float *Y, int64_t ldy, uint8_t *ws,
                          hipStream_t s) {
   const bool has_sh = L.sh_gate_qs != nullptr;
-  const MoeWsLayout lay = moe_ws_layout(L.n_experts, L.inter, L.top_k, B, has_sh);
+  const MoeWsLayout lay = moe_ws_layout(L.n_experts, L.hidden, L.inter, L.top_k, B, has_sh);
   float *sw = reinterpret_cast<float *>(ws + lay.shared_w);
   MoeArgs a = make_args(L, X, ldx, B, ids, weights, sw, Y, ldy, ws, nullptr);
   a.ids_out = ids;

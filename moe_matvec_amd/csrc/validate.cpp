@@ -194,7 +194,8 @@ int check_moe_layer(const mmv_moe_layer *L) {
 
 size_t moe_ws_bytes(const mmv_moe_layer *L, int32_t B) {
   if (check_moe_layer(L) != MMV_OK || bad_batch(B)) return 0;
-  return moe_ws_layout(L->n_experts, L->inter, L->top_k, B, L->sh_gate_qs != nullptr).total;
+  return moe_ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, B,
+                       L->sh_gate_qs != nullptr).total;
 }
 
 namespace {

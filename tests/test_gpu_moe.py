@@ -158,9 +158,12 @@ def test_topk_exact_ties_from_logits(mm, orc, dev):
     np.testing.assert_allclose(npc(w), w_ref, rtol=2e-6, atol=1e-7)
 
 
-def test_moe_batch_invariance(mm, orc, dev):
-    E, H, I, k, B = 64, 1024, 128, 6, 8
-    layer, _ = build_moe(mm, orc, E, H, I, k, 0, "binv", device=dev)
+@pytest.mark.parametrize("I,B", [(128, 8), (512, 3), (512, 4), (512, 8)])
+def test_moe_batch_invariance(mm, orc, dev, I, B):
+    # every row's result has one order whatever the other rows chose: B = 1
+    # takes the one-kernel down projection, B >= 3 the by-expert one
+    E, H, k = 64, 1024, 6
+    layer, _ = build_moe(mm, orc, E, H, I, k, 0, "binv", I, device=dev)
     X = synth.activations(B, H, 0, "binv", device=dev)
     ids, w, sw, _ = mm.moe_route_topk(layer.router, X, k)
     y8 = mm.moe_mul_mat_id(layer, X, ids, w, sw)
@@ -184,3 +187,32 @@ def test_moe_single_expert_and_no_shared(mm, orc, dev):
     for b, e in enumerate((3, 6)):
         want = orc.gemv_q4_0(ref.down_qs[e], ref.down_d[e], hq[b:b + 1], hds[b:b + 1])
         assert rel_l2_rows(npc(y)[b:b + 1], want) <= MOE_TOL
+
+
+@pytest.mark.parametrize("E,H,I,k,shared", [
+    (64, 1024, 512, 6, True),     # I = 512: one block per lane
+    (32, 512, 1024, 4, True),     # I = 1024: two blocks per lane
+    (40, 256, 96, 5, False),      # I = 96: the runtime block loop, no shared expert
+    (16, 224, 64, 3, True),       # H not a multiple of 64: a ragged last row tile
+])
+def test_moe_down_paths_bit_identical(mm, orc, dev, monkeypatch, E, H, I, k, shared):
+    # the by-expert down projection (+ combine) and the one-kernel one form
+    # each pair's product and each row's sum in the same order: same bits
+    layer, ref = build_moe(mm, orc, E, H, I, k, 0, "dpath", E, H, I, shared=shared, device=dev)
+    for B in (1, 2, 3, 8):
+        X = synth.activations(B, H, 0, "dpath", E, B, device=dev)
+        ids, w, sw, _ = mm.moe_route_topk(layer.router, X, k,
+                                          shared_gate_row=layer.shared_gate_row)
+        ys = []
+        for mode in ("1", "2"):
+            monkeypatch.setenv("MMV_MOE_DOWN", mode)
+            ws = torch.full((mm.moe_workspace_bytes(layer, B),), 0x5A, dtype=torch.uint8,
+                            device=dev)
+            ys.append(mm.moe_mul_mat_id(layer, X, ids, w, sw if shared else None, workspace=ws))
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0], ys[1]), B
+        ids_np = npc(ids)
+        hq, hds = orc.quantize_q8_1(ref.gate_up(npc(X), ids_np))
+        s64 = npc(sw).astype(np.float64) if shared else np.ones(B)
+        want = ref.down(hq, hds, ids_np, npc(w).astype(np.float64), s64)
+        assert rel_l2_rows(npc(ys[1]), want) <= MOE_TOL
