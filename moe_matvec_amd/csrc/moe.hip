@@ -336,14 +336,22 @@ struct GatherLds {
 
 // Sorting the keys (expert << 8 | pair index) ascending gives the pairs
 // grouped by expert, then by pair index (b, then j).  Each pair's rank is
-// the number of smaller keys (every thread reads all keys: LDS broadcast);
-// in sorted order an expert's first pair starts a group, and the groups are
-// numbered by a ballot prefix count.  Ids outside [0, E) take no part.
-// MAXP (compile time) bounds Bk; blockDim.x >= MAXP.  Contains
-// __syncthreads: call from uniform control flow.
-template <int MAXP>
+// the number of smaller keys: the key range is split over PARTS thread
+// groups (every thread of a group reads its part of the keys: LDS
+// broadcast), whose counts are then added.  In sorted order an expert's
+// first pair starts a group, and the groups are numbered by a ballot prefix
+// count.  Ids outside [0, E) take no part.  MAXP (compile time) bounds Bk;
+// NT = blockDim.x >= MAXP.  Contains __syncthreads: call from uniform
+// control flow.
+template <int MAXP, int NT>
 __device__ void build_gather(const int32_t *__restrict__ ids, int Bk, int E, GatherLds &g) {
   static_assert(MAXP % 4 == 0 && MAXP <= kMaxPairs && MAXP <= 128, "pairs per lane");
+  static_assert(NT >= MAXP && NT % 64 == 0, "threads");
+  // key groups scanned in parallel (MAXP is a multiple of 16)
+  constexpr int PARTS = NT / MAXP >= 4 ? 4 : (NT / MAXP >= 2 ? 2 : 1);
+  constexpr int PK = MAXP / PARTS;  // keys per group
+  static_assert(MAXP % 16 == 0 && PK % 4 == 0, "keys per group");
+  __shared__ int s_rank[PARTS][MAXP], s_nv[PARTS][MAXP];
   const int t = threadIdx.x;
   if (t < MAXP) {
     uint32_t key = 0xFFFFFFFFu;
@@ -354,16 +362,29 @@ __device__ void build_gather(const int32_t *__restrict__ ids, int Bk, int E, Gat
     g.key[t] = key;
   }
   __syncthreads();
-  int nv = 0;  // valid pairs (every thread counts all keys)
-  if (t < MAXP) {
-    const uint32_t mine = g.key[t];
-    int rank = 0;
-#pragma unroll 4  // (fully unrolled, all MAXP keys would sit in registers at once)
-    for (int c = 0; c < MAXP / 4; ++c) {
-      const uint4 q = reinterpret_cast<const uint4 *>(g.key)[c];
+  if (t < PARTS * MAXP) {
+    const int mi = t % MAXP, part = t / MAXP;
+    const uint32_t mine = g.key[mi];
+    int rank = 0, nv = 0;
+#pragma unroll
+    for (int c = 0; c < PK / 4; ++c) {
+      const uint4 q = reinterpret_cast<const uint4 *>(g.key)[part * (PK / 4) + c];
       rank += (q.x < mine) + (q.y < mine) + (q.z < mine) + (q.w < mine);
       nv += (q.x != 0xFFFFFFFFu) + (q.y != 0xFFFFFFFFu) + (q.z != 0xFFFFFFFFu) +
             (q.w != 0xFFFFFFFFu);
+    }
+    s_rank[part][mi] = rank;
+    s_nv[part][mi] = nv;
+  }
+  __syncthreads();
+  int nv = 0;  // valid pairs (every thread of the first wave adds the groups)
+  if (t < MAXP) {
+    const uint32_t mine = g.key[t];
+    int rank = 0;
+#pragma unroll
+    for (int part = 0; part < PARTS; ++part) {
+      rank += s_rank[part][t];
+      nv += s_nv[part][t];
     }
     if (mine != 0xFFFFFFFFu) g.skey[rank] = mine;
   }
@@ -693,7 +714,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
       gate_up_tile<B, T, PRE>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem, hbuf, xall,
                               [&]() {
                                 if (blockIdx.x == 0) {
-                                  build_gather<MMV_MAX_TOPK>(s_ids, Bk, E, g);
+                                  build_gather<MMV_MAX_TOPK, 256>(s_ids, Bk, E, g);
                                   publish_gather();
                                 }
                               });
@@ -708,7 +729,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     if (t + 256 < gl_n) put_gather_entry(t + 256, g1, Bk, g);
     __syncthreads();
   } else {
-    build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs)>(ids, Bk, E, g);
+    build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs), 256>(ids, Bk, E, g);
     if (blockIdx.x == 0) publish_gather();
   }
   if (!shared_slot && slot >= g.U) return;  // uniform over the workgroup
@@ -768,7 +789,7 @@ __global__ __launch_bounds__(512) void k_moe_topk_gather(MoeArgs a) {
   __syncthreads();
   if (t < Bk) { a.ids_out[t] = s_ids[t]; a.weights_out[t] = s_w[t]; }
   if (t < B) a.shared_w_out[t] = s_sw[t];
-  build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs)>(s_ids, Bk, E, g);
+  build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs), 64 * B>(s_ids, Bk, E, g);
   int32_t *gl = a.gather;
   if (t == 0) gl[0] = g.U;
   if (t < g.U) gl[1 + t] = g.unique[t];
