@@ -486,7 +486,7 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 // rowmap[0..nr) are loaded here, into stage rows 0..nr-1.
 // mid() runs once the weight loads are in flight, before the activations
 // are staged (uniform control flow; it may contain barriers).
-template <int B, int T, int PRE, typename Mid>
+template <int B, int T, int PRE, bool SC, typename Mid>
 __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq,
                                              const uint16_t *gd, const uint8_t *uq,
                                              const uint16_t *ud, int tile, int nr,
@@ -507,6 +507,27 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
   XPre<MAXT> xp;
   __syncthreads();  // rowmap / pairmap visible
   if constexpr (T > 0 && PRE == 0) xpre_load(a.X, a.ldx, rowmap, nr, H, xp, 0, 256);
+  // SC (T > 0, 16-byte aligned scale planes): a wave's 8 gate rows and 8 up
+  // rows hold 2 x 8 x 32T bytes of fp16 scales, fetched as 16-byte chunks
+  // (2T per row) by SCL loads per lane instead of one 2-byte load per (row,
+  // block): a load instruction costs issue time whatever its width, and
+  // with one workgroup per CU the weights' issue is on the critical path
+  // (traced: 1.65 -> 1.0 us without the 2-byte loads).  The chunks go to this
+  // wave's LDS rows while the weights are in flight.
+  static_assert(!SC || T > 0, "chunked scales need compile-time T");
+  constexpr int SCH = 16 * TT;              // chunks per matrix and wave
+  constexpr int SCL = (2 * SCH + 63) / 64;  // chunk loads per lane
+  __shared__ __align__(16) uint16_t s_sc[SC ? 4 : 1][2][8][16 * TT];  // [wave][gate, up][row][block]
+  u32x4 scv[SCL];
+  if constexpr (SC) {  // requested before the weights (loads complete in order)
+#pragma unroll
+    for (int i = 0; i < SCL; ++i) {
+      const int c = min(lane + 64 * i, 2 * SCH - 1);
+      const int m = c >= SCH ? 1 : 0, cc = c - m * SCH;
+      const int rl = cc / (2 * TT), part = cc - rl * 2 * TT;
+      scv[i] = load_stream16((m ? ud : gd) + (int64_t)(tile * 32 + 8 * wv + rl) * nbh + 8 * part);
+    }
+  }
   u32x4 w[4][TT];
   float dw[4][TT];
   if constexpr (T > 0) {
@@ -518,7 +539,7 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
         const uint8_t *wq = p < 2 ? gq : uq;
         const uint16_t *wd = p < 2 ? gd : ud;
         w[p][t] = load_stream16(wq + (rowoff[p] + j) * 16);
-        dw[p][t] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
+        if constexpr (!SC) dw[p][t] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
       }
     }
   }
@@ -534,6 +555,17 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
     stage_quantize<MAXT>(a.X, a.ldx, rowmap, nr, H, st, MAXT * 256, 256);
   } else {
     stage_quantize(a.X, a.ldx, rowmap, nr, H, st);
+  }
+  if constexpr (SC) {  // the scale chunks (in before the weights) to this wave's LDS rows
+#pragma unroll
+    for (int i = 0; i < SCL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < 2 * SCH) {
+        const int m = c >= SCH ? 1 : 0, cc = c - m * SCH;
+        const int rl = cc / (2 * TT), part = cc - rl * 2 * TT;
+        *reinterpret_cast<u32x4 *>(&s_sc[wv][m][rl][8 * part]) = scv[i];
+      }
+    }
   }
   __syncthreads();
   // gate row n and up row n of one activation row -> h (lanes sub == 0)
@@ -583,7 +615,13 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
         u32x4 wb[4];
         float db[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) { wb[p] = w[p][t]; db[p] = dw[p][t]; }
+        for (int p = 0; p < 4; ++p) {
+          wb[p] = w[p][t];
+          if constexpr (SC)
+            db[p] = f16_bits_to_f32(s_sc[wv][p >> 1][4 * (p & 1) + q][sub + 16 * t]);
+          else
+            db[p] = dw[p][t];
+        }
         block(wb, db, sub + 16 * t);
       }
     } else {
@@ -625,6 +663,11 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
       hv.dq[bi] = i32x2{(int32_t)__float_as_uint(f16_bits_to_f32(qb.d16)), qb.qsum};
     }
   }
+}
+
+// both scale planes 16-byte aligned (the chunked scale loads)
+__device__ __forceinline__ bool scales16(const uint16_t *gd, const uint16_t *ud) {
+  return ((reinterpret_cast<uintptr_t>(gd) | reinterpret_cast<uintptr_t>(ud)) & 15) == 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -711,13 +754,18 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
         rowmap[0] = 0;
         pairmap[0] = shared_slot ? Bk : slot;
       }
-      gate_up_tile<B, T, PRE>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem, hbuf, xall,
-                              [&]() {
-                                if (blockIdx.x == 0) {
-                                  build_gather<MMV_MAX_TOPK, 256>(s_ids, Bk, E, g);
-                                  publish_gather();
-                                }
-                              });
+      auto mid = [&]() {
+        if (blockIdx.x == 0) {
+          build_gather<MMV_MAX_TOPK, 256>(s_ids, Bk, E, g);
+          publish_gather();
+        }
+      };
+      if (T > 0 && scales16(gd, ud))  // uniform
+        gate_up_tile<B, T, PRE, (T > 0 && B <= 2)>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem,
+                                         hbuf, xall, mid);
+      else
+        gate_up_tile<B, T, PRE, false>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem, hbuf,
+                                       xall, mid);
       return;
     }
   }
@@ -754,8 +802,15 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     pairmap[r] = p;
     rowmap[r] = shared_slot ? r : p / k;
   }
-  gate_up_tile<B, T, PRE>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf, xall,
-                          []() {});
+  // chunked scales for one or two rows (at one workgroup per CU the issue
+  // time counts); more rows keep more workgroups per CU, and there the
+  // extra registers cost more than the issue time saved (B = 8: +0.3 us)
+  if (T > 0 && B <= 2 && scales16(gd, ud))  // uniform
+    gate_up_tile<B, T, PRE, (T > 0 && B <= 2)>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf,
+                                     xall, []() {});
+  else
+    gate_up_tile<B, T, PRE, false>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf,
+                                   xall, []() {});
 }
 
 // ---------------------------------------------------------------------------
