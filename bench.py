@@ -2,7 +2,7 @@
 """Benchmark of the decode matrix-vector path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
-                    [--only dense,q4,w4a16,lmhead,moe256,moe512] [--profile-kernel]
+                    [--only dense,q4,w4a16,lmhead,moe256,moe512,moe512v] [--profile-kernel]
 
 The headline step is one pass over the dense BF16 decode matvec set: 36 layer
 copies (5.85 GB, far past the 256 MB Infinity Cache) of attn-out 2560x2560,
@@ -299,9 +299,10 @@ def moe_section(mm, dev, E, k, layers, Bs, steps, warmup, H=2048, I=512):
                             mean_unique_experts=sum(uniq) / layers,
                             MB_per_layer=nbytes / layers / 1e6, GBps=nbytes / t / 1e9,
                             frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS,
-                            launches_per_layer=3 if B <= 2 else 5)
+                            launches_per_layer=(3 if B <= 2 else 5) if B <= 8
+                            else 5 + (B + 7) // 8)
         del X, Y, ids, ws, g
-    if len(Bs) > 1:
+    if len(Bs) > 1 and 1 in Bs:
         res["ratio_Bmax_B1_time"] = res[f"B{max(Bs)}"]["us_per_layer"] / res["B1"]["us_per_layer"]
     del lay, big, sh
     torch.cuda.empty_cache()
@@ -404,7 +405,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="dense,q4,w4a16,lmhead,moe256,moe512")
+    ap.add_argument("--only", default="dense,q4,w4a16,lmhead,moe256,moe512,moe512v")
     ap.add_argument("--quick", action="store_true", help="fewer layer copies (smoke timing)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-kernel", action="store_true",
@@ -476,6 +477,12 @@ def main():
         sections["moe_e512_top10"] = r
         log("moe E=512: " + ", ".join(f"B{b} {r[f'B{b}']['us_per_layer']:.2f} us"
                                       for b in (1, 4, 8)))
+    if "moe512v" in only:  # verify / prefill batches: the row-list path (B > 8)
+        r = moe_section(mm, dev, 512, 10, 4 if args.quick else 48, [16, 32, 64], steps, warmup)
+        sections["moe_e512_top10_verify"] = r
+        log("moe E=512 verify: " + ", ".join(
+            f"B{b} {r[f'B{b}']['us_per_layer']:.1f} us ({r[f'B{b}']['us_per_layer_per_token']:.2f}"
+            f" us/token, {r[f'B{b}']['GBps']:.0f} GB/s)" for b in (16, 32, 64)))
     sections["bw_probe"] = bw_probe(mm, dev)
 
     cpu = None if args.no_cpu else cpu_baseline()

@@ -66,6 +66,7 @@ extern "C" {
 #endif
 
 #define MMV_MAX_BATCH   8     /* rows per call                              */
+#define MMV_MOE_MAX_BATCH 64  /* rows per MoE call (verify / prefill batches) */
 #define MMV_MAX_EXPERTS 1024  /* router rows E                              */
 #define MMV_MAX_TOPK    16    /* experts per row k                          */
 #define MMV_Q4_MAX_XK   49152 /* B*K limit of gemv_q4_0 (x staged in LDS)   */
@@ -76,7 +77,7 @@ typedef enum {
   MMV_E_NULL = -1,      /* a required pointer is NULL                       */
   MMV_E_SHAPE = -2,     /* a size is out of range or not a block multiple   */
   MMV_E_ALIGN = -3,     /* a pointer or leading dimension is misaligned     */
-  MMV_E_BATCH = -4,     /* B outside 1..MMV_MAX_BATCH                        */
+  MMV_E_BATCH = -4,     /* B outside 1..MMV_MAX_BATCH (MoE: MMV_MOE_MAX_BATCH) */
   MMV_E_TOPK = -5,      /* k outside 1..min(E, MMV_MAX_TOPK)                 */
   MMV_E_WORKSPACE = -6, /* workspace NULL or smaller than required          */
   MMV_E_ALIAS = -7,     /* an output overlaps an input                      */
@@ -189,7 +190,8 @@ int argmax_rows(const float *Y, int64_t ldy, int32_t N, int32_t B, int32_t *ids,
  *           k, i.e. exp(l_j - l_max) / sum over selected.
  *   shared_w: B fp32 (may be NULL): sigmoid(shared_gate_row . x_b), or 1
  *           when shared_gate_row is NULL.
- *   1 <= k <= min(E, MMV_MAX_TOPK), E <= MMV_MAX_EXPERTS.
+ *   1 <= k <= min(E, MMV_MAX_TOPK), E <= MMV_MAX_EXPERTS,
+ *   1 <= B <= MMV_MOE_MAX_BATCH.
  * ------------------------------------------------------------------------ */
 int moe_route_topk(const float *router, int32_t E, int32_t H,
                    const float *X, int64_t ldx, int32_t B, int32_t k,
@@ -232,8 +234,8 @@ typedef struct {
  * lists, the routing buffers that moe_layer_decode uses, and P x H fp32
  * per-pair down products (the by-expert down projection for B >= 3).
  * 256-byte aligned workspace required.
- * The down projection stages Q8_1(h) of all P pairs in LDS:
- * P * I <= MMV_MOE_MAX_PI (else MMV_E_SHAPE). */
+ * For B <= 8 the down projection may stage Q8_1(h) of all P pairs in LDS:
+ * P * I <= MMV_MOE_MAX_PI (else MMV_E_SHAPE); larger batches do not. */
 #define MMV_MOE_MAX_PI 49152
 size_t moe_workspace_bytes(const mmv_moe_layer *L, int32_t B);
 
@@ -252,6 +254,11 @@ size_t moe_workspace_bytes(const mmv_moe_layer *L, int32_t B);
  *   ids: B x k int32 in [0, E), distinct within a row; weights: B x k fp32;
  *   shared_w: B fp32 or NULL (weight 1).  X: B x H fp32, ldx % 4 == 0.
  *   Y: B x H fp32.  workspace: moe_workspace_bytes(L, B) bytes.
+ *   1 <= B <= MMV_MOE_MAX_BATCH.  Verify / prefill batches (B > 8) take a
+ *   row-list pass over all B*k pairs [STRIX: Expert GEMMs: per-expert row
+ *   lists, then compact (expert, tile) work]; each (expert, 32-row tile)
+ *   workgroup walks its rows eight at a time with the weights re-read from
+ *   cache, and every row's result is the same bits as in a call of B <= 8.
  * ------------------------------------------------------------------------ */
 int moe_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx,
                    int32_t B, const int32_t *ids, const float *weights,

@@ -19,10 +19,11 @@ __all__ = [
     "gemv_bf16", "quantize_q8_1", "q8_1_bytes", "gemv_q4_0", "gemv_q4_0_f32",
     "argmax_rows", "argmax_workspace_bytes", "Q4F32_MAX_XK",
     "moe_route_topk", "moe_mul_mat_id", "moe_layer_decode", "moe_workspace_bytes",
-    "MAX_BATCH", "MAX_EXPERTS", "MAX_TOPK", "Q4_MAX_XK", "stream_read", "split_q8_1",
+    "MAX_BATCH", "MOE_MAX_BATCH", "MAX_EXPERTS", "MAX_TOPK", "Q4_MAX_XK", "stream_read", "split_q8_1",
 ]
 
 MAX_BATCH = 8
+MOE_MAX_BATCH = 64  # MoE calls: verify / prefill batches
 MAX_EXPERTS = 1024
 MAX_TOPK = 16
 Q4_MAX_XK = 49152

@@ -276,12 +276,15 @@ __global__ __launch_bounds__(256) void k_router(const float *__restrict__ R, int
   router_row<B, HC>(row, H, X, ldx, logits + e, E + 1);
 }
 
+// a workgroup per 4 rows (a wave per row)
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int64_t ldl, int E,
                                               int B, int k, int has_shared,
                                               int32_t *__restrict__ ids,
                                               float *__restrict__ weights,
                                               float *__restrict__ shared_w) {
-  topk_any(L, ldl, E, B, k, has_shared, ids, weights, shared_w);
+  const int b0 = blockIdx.x * 4;
+  topk_any(L + (int64_t)b0 * ldl, ldl, E, min(4, B - b0), k, has_shared, ids + (int64_t)b0 * k,
+           weights + (int64_t)b0 * k, shared_w ? shared_w + b0 : nullptr);
 }
 
 template <int B>
@@ -303,21 +306,25 @@ hipError_t run_moe_route(const float *router, int E, int H, const float *X, int6
   const float *L = X;
   int64_t ldl = ldx;
   if (router) {
-    switch (B) {
-      case 1: launch_router<1>(router, E, H, shg, X, ldx, logits, s); break;
-      case 2: launch_router<2>(router, E, H, shg, X, ldx, logits, s); break;
-      case 3: launch_router<3>(router, E, H, shg, X, ldx, logits, s); break;
-      case 4: launch_router<4>(router, E, H, shg, X, ldx, logits, s); break;
-      case 5: launch_router<5>(router, E, H, shg, X, ldx, logits, s); break;
-      case 6: launch_router<6>(router, E, H, shg, X, ldx, logits, s); break;
-      case 7: launch_router<7>(router, E, H, shg, X, ldx, logits, s); break;
-      case 8: launch_router<8>(router, E, H, shg, X, ldx, logits, s); break;
-      default: return hipErrorInvalidValue;
+    for (int b0 = 0; b0 < B; b0 += MMV_MAX_BATCH) {  // router rows 8 activation rows at a time
+      const float *Xc = X + (int64_t)b0 * ldx;
+      float *lc = logits + (int64_t)b0 * (E + 1);
+      switch (min(B - b0, MMV_MAX_BATCH)) {
+        case 1: launch_router<1>(router, E, H, shg, Xc, ldx, lc, s); break;
+        case 2: launch_router<2>(router, E, H, shg, Xc, ldx, lc, s); break;
+        case 3: launch_router<3>(router, E, H, shg, Xc, ldx, lc, s); break;
+        case 4: launch_router<4>(router, E, H, shg, Xc, ldx, lc, s); break;
+        case 5: launch_router<5>(router, E, H, shg, Xc, ldx, lc, s); break;
+        case 6: launch_router<6>(router, E, H, shg, Xc, ldx, lc, s); break;
+        case 7: launch_router<7>(router, E, H, shg, Xc, ldx, lc, s); break;
+        case 8: launch_router<8>(router, E, H, shg, Xc, ldx, lc, s); break;
+        default: return hipErrorInvalidValue;
+      }
     }
     L = logits;
     ldl = E + 1;
   }
-  hipLaunchKernelGGL(k_topk, dim3(1), dim3(256), 0, s, L, ldl, E, B, k,
+  hipLaunchKernelGGL(k_topk, dim3((B + 3) / 4), dim3(256), 0, s, L, ldl, E, B, k,
                      (router && shg) ? 1 : 0, ids, weights, shared_w);
   return hipGetLastError();
 }
@@ -456,6 +463,8 @@ struct MoeArgs {
   int router_wgs;
   int topk_in_k2;    // 1: every K2 workgroup runs top-k on the logits itself
   float *dpart;      // P x H per-pair down products (the by-expert down path)
+  int nrows;         // B (the kernels for more than 8 rows take it at run time)
+  int32_t *work;     // B > 8: [0] count, then (slot << 4 | row group) gate/up items
 };
 
 // Published row lists (workspace): [0] U, [1, 1+Bk) unique experts,
@@ -1213,14 +1222,15 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
 // slots past the number of unique experts exit.
 constexpr int kDownPartRows = 64;
 
-template <int B, int TI>
+template <int B, int TI>  // B = 0: rows at run time (a.nrows <= 64)
 __global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
-  constexpr int RP = kDownPartRows / 16;   // rows per 16-lane group
-  constexpr int NP = B < 4 ? B : 4;        // pairs whose Q8_1(h) is in flight together
+  constexpr int RP = kDownPartRows / 16;             // rows per 16-lane group
+  constexpr int NP = (B > 0 && B < 4) ? B : 4;       // pairs whose Q8_1(h) is in flight together
   constexpr int TT = TI > 0 ? TI : 1;
   const mmv_moe_layer &L = a.L;
+  const int Bv = B > 0 ? B : a.nrows;
   const int k = L.top_k, H = L.hidden, I = L.inter;
-  const int Bk = B * k, nbi = I >> 5;
+  const int Bk = Bv * k, nbi = I >> 5;
   const int has_sh = L.sh_down_qs != nullptr ? 1 : 0;
   const int ntile = (H + kDownPartRows - 1) / kDownPartRows;
   const int slot0 = blockIdx.x / ntile, tile = blockIdx.x - slot0 * ntile;
@@ -1232,13 +1242,13 @@ __global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
   int np, pbase;
   if (shared_slot) {
     dq = L.sh_down_qs; dd = L.sh_down_d;
-    np = B; pbase = 0;
+    np = Bv; pbase = 0;
   } else {
     const int U = gl[0], e = gl[1 + u], o0 = gl[1 + Bk + u], o1 = gl[2 + Bk + u];
     if (u >= U) return;  // uniform over the workgroup
     const int64_t eo = (int64_t)e * H * nbi;
     dq = L.down_qs + eo * 16; dd = L.down_d + eo;
-    np = min(o1 - o0, B);
+    np = min(o1 - o0, Bv);  // a row meets an expert once: at most one pair per row
     pbase = o0;
   }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, sub = lane & 15, q = lane >> 4;
@@ -1247,7 +1257,7 @@ __global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
   // weights (loads complete in issue order: waiting for these does not wait
   // for the weights)
   const int pl_r = gl[2 + 2 * Bk + pbase + min(lane, max(np - 1, 0))];
-  const int pl = shared_slot ? Bk + min(lane, B - 1) : pl_r;
+  const int pl = shared_slot ? Bk + min(lane, Bv - 1) : pl_r;
   u32x4 w[RP][TT];
   uint16_t dw[RP][TT];  // fp16 bits until use (see DownChunk)
   if constexpr (TI > 0) {
@@ -1349,10 +1359,10 @@ __global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
 // Y[b][n] = tree_j (w[b k + j] dot_{b k + j}[n]) + s_b dot_{Bk + b}[n] with
 // the sum K3 forms (down_combine_tree); pairs with ids outside [0, E) add
 // zero.  grid = (ceil(H / 256), B).
-template <int B>
+template <int B>  // B = 0: rows at run time
 __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
   const mmv_moe_layer &L = a.L;
-  const int H = L.hidden, k = L.top_k, E = L.n_experts, Bk = B * k;
+  const int H = L.hidden, k = L.top_k, E = L.n_experts, Bk = (B > 0 ? B : a.nrows) * k;
   const int b = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
   const int nc = min(n, H - 1);
   const bool has_sh = L.sh_down_qs != nullptr;
@@ -1375,6 +1385,157 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
   float v = down_combine_tree(pr);
   if (has_sh) v = fmaf(a.shared_w ? a.shared_w[b] : 1.0f, dsh, v);
   if (n < H) a.Y[(int64_t)b * a.ldy + n] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Verify / prefill batches: 8 < B <= 64 rows
+// ---------------------------------------------------------------------------
+// "Flash-Next on Strix Halo" (Expert GEMMs) builds per-expert row lists in a
+// prepass and dispatches compact (expert, tile) work, so that each expert's
+// weights are read once for all the rows that chose it.  Here: the router in
+// 8-row chunks, top-k a wave per row, the row lists by one workgroup
+// (k_moe_gather_rows), gate/up by (expert, 32-row tile) workgroups that walk
+// their rows eight at a time (the same tile code as B <= 8, the weights
+// re-read from cache for each further 8 rows), then the by-expert down
+// projection and the combine with the row count at run time.  Every row is
+// formed by the same arithmetic as for B <= 8, so it is the same bits.
+
+// top-k for every row (layer decode): a workgroup per 4 rows, a wave per row
+__global__ __launch_bounds__(256) void k_moe_topk_rows(MoeArgs a) {
+  const mmv_moe_layer &L = a.L;
+  const int E = L.n_experts, k = L.top_k, b0 = blockIdx.x * 4;
+  topk_any(a.logits + (int64_t)b0 * (E + 1), E + 1, E, min(4, a.nrows - b0), k,
+           L.shared_gate_row ? 1 : 0, a.ids_out + (int64_t)b0 * k,
+           a.weights_out + (int64_t)b0 * k, a.shared_w_out + b0);
+}
+
+// Row lists for B <= 64 (B * k <= 1024 pairs, E <= 1024) by counting over
+// the experts: each expert's 64-bit mask of the rows that chose it (LDS
+// atomics), then prefix sums over the experts (a thread per expert) give
+// its first list position and its group number, and pair (b, j) of expert
+// e goes to start[e] + (rows below b in mask[e]): grouped by expert, then
+// by row, as the rank sort of build_gather orders them (a valid row meets
+// an expert once).  Ids outside [0, E) take no part; a row naming one
+// expert twice (invalid) keeps one of the two pairs.  One workgroup of
+// 1024 threads.
+__global__ __launch_bounds__(1024) void k_moe_gather_rows(MoeArgs a) {
+  __shared__ unsigned long long s_mask[MMV_MAX_EXPERTS];
+  __shared__ int s_start[MMV_MAX_EXPERTS];
+  __shared__ int s_wc[16], s_wp[16], s_wg[16];
+  const mmv_moe_layer &L = a.L;
+  const int t = threadIdx.x, E = L.n_experts, k = L.top_k, Bk = a.nrows * k;
+  const int lane = t & 63, wv = t >> 6;
+  if (t < E) s_mask[t] = 0ull;
+  __syncthreads();
+  if (t < Bk) {
+    const int e = a.ids[t];
+    if (e >= 0 && e < E) atomicOr(&s_mask[e], 1ull << (t / k));
+  }
+  __syncthreads();
+  const unsigned long long m = t < E ? s_mask[t] : 0ull;
+  const int c = __popcll(m), pr = c > 0 ? 1 : 0;
+  const int g = (c + MMV_MAX_BATCH - 1) / MMV_MAX_BATCH;  // gate/up row groups
+  int ic = c, ip = pr, ig = g;  // inclusive prefix sums within the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int oc = __shfl_up(ic, d), op = __shfl_up(ip, d), og = __shfl_up(ig, d);
+    if (lane >= d) { ic += oc; ip += op; ig += og; }
+  }
+  if (lane == 63) { s_wc[wv] = ic; s_wp[wv] = ip; s_wg[wv] = ig; }
+  __syncthreads();
+  int bc = 0, bp = 0, bg = 0, tc = 0, tp = 0, tg = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int wc = s_wc[w], wp = s_wp[w], wg = s_wg[w];
+    bc += w < wv ? wc : 0;
+    bp += w < wv ? wp : 0;
+    bg += w < wv ? wg : 0;
+    tc += wc;
+    tp += wp;
+    tg += wg;
+  }
+  const int start = bc + ic - c, urank = bp + ip - pr, gstart = bg + ig - g;  // exclusive
+  // work items: the shared expert's row groups, then each routed expert's
+  const int nsh = a.routed_shared ? (a.nrows + MMV_MAX_BATCH - 1) / MMV_MAX_BATCH : 0;
+  if (t < nsh) a.work[1 + t] = t;  // slot 0, row group t
+  if (t < E && pr)
+    for (int q = 0; q < g; ++q) a.work[1 + nsh + gstart + q] = ((a.routed_shared + urank) << 4) | q;
+  if (t == 0) a.work[0] = nsh + tg;
+  int32_t *gl = a.gather;
+  const bool dbg = a.has_dbg != 0;
+  if (t < E) {
+    s_start[t] = start;
+    if (pr) {
+      gl[1 + urank] = t;
+      gl[1 + Bk + urank] = start;
+      if (dbg && a.dbg.unique) a.dbg.unique[urank] = t;
+      if (dbg && a.dbg.offsets) a.dbg.offsets[urank] = start;
+    }
+  }
+  if (t == 0) {
+    gl[0] = tp;
+    gl[1 + Bk + tp] = tc;
+    if (dbg && a.dbg.offsets) a.dbg.offsets[tp] = tc;
+    if (dbg && a.dbg.n_unique) a.dbg.n_unique[0] = tp;
+  }
+  __syncthreads();
+  if (t < Bk) {
+    const int e = a.ids[t];
+    if (e >= 0 && e < E) {
+      const int pos = s_start[e] + __popcll(s_mask[e] & ((1ull << (t / k)) - 1ull));
+      gl[2 + 2 * Bk + pos] = t;
+      if (dbg && a.dbg.pairs) a.dbg.pairs[pos] = t;
+    }
+  }
+}
+
+// gate/up for B <= 64: one workgroup per (work item, 32-row tile), a work
+// item being up to eight rows of one expert (k_moe_gather_rows lists them:
+// the shared expert's row groups first, then each routed expert's); items
+// past the published count exit.  The B <= 8 tile code does the rows.
+template <int T>
+__global__ __launch_bounds__(256) void k_moe_gate_up_rows(MoeArgs a) {
+  __shared__ int rowmap[MMV_MAX_BATCH];
+  __shared__ int pairmap[MMV_MAX_BATCH];
+  __shared__ float hbuf[MMV_MAX_BATCH][32];
+  extern __shared__ __align__(16) uint8_t smem[];
+  const mmv_moe_layer &L = a.L;
+  const int k = L.top_k, H = L.hidden, I = L.inter, B = a.nrows, Bk = B * k;
+  const int ntiles = I >> 5, nbh = H >> 5;
+  const int wi = blockIdx.x / ntiles, tile = blockIdx.x - wi * ntiles;
+  const int32_t *gl = a.gather;
+  const int W = a.work[0];
+  if (wi >= W) return;  // uniform over the workgroup
+  const int item = a.work[1 + wi], slot0 = item >> 4, r0 = MMV_MAX_BATCH * (item & 15);
+  const bool shared_slot = a.routed_shared && slot0 == 0;
+  const int slot = slot0 - a.routed_shared;
+  const uint8_t *gq, *uq;
+  const uint16_t *gd, *ud;
+  int nr, pbase = 0;
+  if (shared_slot) {
+    gq = L.sh_gate_qs; gd = L.sh_gate_d; uq = L.sh_up_qs; ud = L.sh_up_d;
+    nr = B;
+  } else {
+    const int e = gl[1 + slot], o0 = gl[1 + Bk + slot], o1 = gl[2 + Bk + slot];
+    const int64_t eo = (int64_t)e * I * nbh;
+    gq = L.gate_qs + eo * 16; gd = L.gate_d + eo;
+    uq = L.up_qs + eo * 16; ud = L.up_d + eo;
+    nr = min(o1 - o0, B);
+    pbase = o0;
+  }
+  const int nc = min(MMV_MAX_BATCH, nr - r0);
+  if (nc <= 0) return;  // uniform; never for a published item
+  int ncv = nc;  // opaque: with its range known the compiler unrolls per row count
+  asm volatile("" : "+s"(ncv));
+  if (threadIdx.x < (unsigned)nc) {
+    const int r = r0 + threadIdx.x;
+    const int p = shared_slot ? Bk + r : gl[2 + 2 * Bk + pbase + r];
+    pairmap[threadIdx.x] = p;
+    rowmap[threadIdx.x] = shared_slot ? r : p / k;
+  }
+  const XPre<1> none{};
+  gate_up_tile<MMV_MAX_BATCH, T, 0, false>(a, gq, gd, uq, ud, tile, ncv, rowmap, pairmap, smem,
+                                           hbuf, none, []() {});
 }
 
 namespace {
@@ -1428,6 +1589,8 @@ MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
   a.dbg = dbg ? *dbg : mmv_moe_debug{nullptr, nullptr, nullptr, nullptr, nullptr};
   a.logits = reinterpret_cast<float *>(ws + lay.logits);
   a.dpart = reinterpret_cast<float *>(ws + lay.dpart);
+  a.nrows = B;
+  a.work = reinterpret_cast<int32_t *>(ws + lay.work);
   a.gather_ready = 0;
   a.ids_out = nullptr;
   a.weights_out = nullptr;
@@ -1492,6 +1655,45 @@ void launch_experts(const MoeArgs &a, hipStream_t s) {
   }
 }
 
+// work items: at most (shared row groups) + U + B*k/8, U <= min(E, B*k)
+int rows_work_max(const MoeArgs &a) {
+  const int Bk = a.nrows * a.L.top_k;
+  return (a.routed_shared ? (a.nrows + MMV_MAX_BATCH - 1) / MMV_MAX_BATCH : 0) +
+         min(a.L.n_experts, Bk) + Bk / MMV_MAX_BATCH;
+}
+
+template <int T>
+void launch_gate_up_rows(const MoeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((k_moe_gate_up_rows<T>), dim3(rows_work_max(a) * (a.L.inter / 32)),
+                     dim3(256), xstage_bytes(MMV_MAX_BATCH, a.L.hidden), s, a);
+}
+
+template <int TI>
+void launch_down_rows(const MoeArgs &a, hipStream_t s) {
+  const int slots = a.nrows * a.L.top_k + (a.L.sh_down_qs ? 1 : 0);
+  const int ntile = (a.L.hidden + kDownPartRows - 1) / kDownPartRows;
+  hipLaunchKernelGGL((k_moe_down_part<0, TI>), dim3(slots * ntile), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_moe_combine<0>), dim3((a.L.hidden + 255) / 256, a.nrows), dim3(256), 0,
+                     s, a);
+}
+
+// B > 8: the row lists (unless published), gate/up, down by expert, combine
+void launch_experts_rows(const MoeArgs &a, hipStream_t s) {
+  if (!a.gather_ready) hipLaunchKernelGGL(k_moe_gather_rows, dim3(1), dim3(1024), 0, s, a);
+  switch (a.L.hidden) {
+    case 512: launch_gate_up_rows<1>(a, s); break;
+    case 1024: launch_gate_up_rows<2>(a, s); break;
+    case 2048: launch_gate_up_rows<4>(a, s); break;
+    case 4096: launch_gate_up_rows<8>(a, s); break;
+    default: launch_gate_up_rows<0>(a, s); break;
+  }
+  switch (a.L.inter) {
+    case 512: launch_down_rows<1>(a, s); break;
+    case 1024: launch_down_rows<2>(a, s); break;
+    default: launch_down_rows<0>(a, s); break;
+  }
+}
+
 template <int B>
 void launch_route(const MoeArgs &a, hipStream_t s) {
   switch (a.L.hidden) {
@@ -1509,6 +1711,10 @@ hipError_t run_moe_experts(const mmv_moe_layer &L, const float *X, int64_t ldx, 
                            float *Y, int64_t ldy, uint8_t *ws, const mmv_moe_debug *dbg,
                            hipStream_t s) {
   const MoeArgs a = make_args(L, X, ldx, B, ids, weights, shared_w, Y, ldy, ws, dbg);
+  if (B > MMV_MAX_BATCH) {
+    launch_experts_rows(a, s);
+    return hipGetLastError();
+  }
   switch (B) {
     case 1: launch_experts<1>(a, s); break;
     case 2: launch_experts<2>(a, s); break;
@@ -1538,6 +1744,29 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
   // one or two rows; for more rows it grows with B in every workgroup, and
   // one workgroup of its own (plus a launch) costs less.  A grid-wide
   // barrier or ticket inside one kernel measured slower than a launch.
+  if (B > MMV_MAX_BATCH) {
+    // router rows 8 activation rows at a time, top-k a wave per row, then
+    // the row lists and the experts
+    const int E = L.n_experts;
+    for (int b0 = 0; b0 < B; b0 += MMV_MAX_BATCH) {
+      MoeArgs ac = a;
+      ac.X = X + (int64_t)b0 * ldx;
+      ac.logits = a.logits + (int64_t)b0 * (E + 1);
+      switch (min(B - b0, MMV_MAX_BATCH)) {
+        case 1: launch_route<1>(ac, s); break;
+        case 2: launch_route<2>(ac, s); break;
+        case 3: launch_route<3>(ac, s); break;
+        case 4: launch_route<4>(ac, s); break;
+        case 5: launch_route<5>(ac, s); break;
+        case 6: launch_route<6>(ac, s); break;
+        case 7: launch_route<7>(ac, s); break;
+        default: launch_route<8>(ac, s); break;
+      }
+    }
+    hipLaunchKernelGGL(k_moe_topk_rows, dim3((B + 3) / 4), dim3(256), 0, s, a);
+    launch_experts_rows(a, s);
+    return hipGetLastError();
+  }
   const int knob = moe_topk_knob();
   a.topk_in_k2 = knob > 0 ? 0 : (knob < 0 ? 1 : (B <= 2 ? 1 : 0));
   a.gather_ready = a.topk_in_k2 ? 0 : 1;

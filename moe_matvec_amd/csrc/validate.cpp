@@ -1,4 +1,5 @@
 // validate.cpp -- host-side argument checks of the C ABI (pure C++).
+#include <algorithm>
 #include "validate.hpp"
 
 #include "layout.hpp"
@@ -26,6 +27,7 @@ size_t span(int64_t rows, int64_t ld, int64_t cols, size_t elem) {
   return (size_t)(((rows - 1) * ld + cols) * (int64_t)elem);
 }
 bool bad_batch(int32_t B) { return B < 1 || B > MMV_MAX_BATCH; }
+bool bad_moe_batch(int32_t B) { return B < 1 || B > MMV_MOE_MAX_BATCH; }
 int64_t moe_pairs(const mmv_moe_layer *L, int32_t B) {
   return (int64_t)B * L->top_k + (L->sh_gate_qs ? B : 0);
 }
@@ -142,7 +144,7 @@ int check_route(const float *router, int32_t E, int32_t H, const float *X, int64
                 const int32_t *ids, const float *weights, const float *shared_w) {
   if (!X || !ids || !weights) return MMV_E_NULL;
   if (router && !logits) return MMV_E_NULL;
-  if (bad_batch(B)) return MMV_E_BATCH;
+  if (bad_moe_batch(B)) return MMV_E_BATCH;
   if (E < 1 || E > MMV_MAX_EXPERTS) return MMV_E_SHAPE;
   if (k < 1 || k > E || k > MMV_MAX_TOPK) return MMV_E_TOPK;
   if (!router && shg) return MMV_E_ARG;
@@ -193,7 +195,7 @@ int check_moe_layer(const mmv_moe_layer *L) {
 }
 
 size_t moe_ws_bytes(const mmv_moe_layer *L, int32_t B) {
-  if (check_moe_layer(L) != MMV_OK || bad_batch(B)) return 0;
+  if (check_moe_layer(L) != MMV_OK || bad_moe_batch(B)) return 0;
   return moe_ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, B,
                        L->sh_gate_qs != nullptr).total;
 }
@@ -238,11 +240,14 @@ int check_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_
   const int st = check_moe_layer(L);
   if (st != MMV_OK) return st;
   if (!X || !ids || !weights || !Y) return MMV_E_NULL;
-  if (bad_batch(B)) return MMV_E_BATCH;
+  if (bad_moe_batch(B)) return MMV_E_BATCH;
   const int32_t H = L->hidden, k = L->top_k;
   if (ldx < H || ldy < H || ldx > kMaxLd || ldy > kMaxLd) return MMV_E_SHAPE;
-  if ((int64_t)B * H > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
-  if (moe_pairs(L, B) * (int64_t)L->inter > kMaxDownStageElems) return MMV_E_SHAPE;
+  // x of at most 8 rows is staged per gate/up workgroup; only B <= 8 may
+  // stage Q8_1(h) of every pair in the down projection's LDS
+  if ((int64_t)std::min<int32_t>(B, MMV_MAX_BATCH) * H > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
+  if (B <= MMV_MAX_BATCH && moe_pairs(L, B) * (int64_t)L->inter > kMaxDownStageElems)
+    return MMV_E_SHAPE;
   if (!aligned(X, 16) || ldx % 4 != 0 || !aligned(ids, 4) || !aligned(weights, 4) ||
       !aligned(shared_w, 4) || !aligned(Y, 4))
     return MMV_E_ALIGN;
@@ -263,11 +268,14 @@ int check_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx, int3
   const int st = check_moe_layer(L);
   if (st != MMV_OK) return st;
   if (!X || !Y) return MMV_E_NULL;
-  if (bad_batch(B)) return MMV_E_BATCH;
+  if (bad_moe_batch(B)) return MMV_E_BATCH;
   const int32_t H = L->hidden, k = L->top_k;
   if (ldx < H || ldy < H || ldx > kMaxLd || ldy > kMaxLd) return MMV_E_SHAPE;
-  if ((int64_t)B * H > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
-  if (moe_pairs(L, B) * (int64_t)L->inter > kMaxDownStageElems) return MMV_E_SHAPE;
+  // x of at most 8 rows is staged per gate/up workgroup; only B <= 8 may
+  // stage Q8_1(h) of every pair in the down projection's LDS
+  if ((int64_t)std::min<int32_t>(B, MMV_MAX_BATCH) * H > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
+  if (B <= MMV_MAX_BATCH && moe_pairs(L, B) * (int64_t)L->inter > kMaxDownStageElems)
+    return MMV_E_SHAPE;
   if (!aligned(X, 16) || ldx % 4 != 0 || !aligned(ids, 4) || !aligned(weights, 4) ||
       !aligned(Y, 4))
     return MMV_E_ALIGN;

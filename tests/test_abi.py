@@ -114,7 +114,8 @@ def test_route_validation(L):
                  a["logits"], a["ids"], a["weights"], a["sw"], None)
     assert call(ids=None) == E_NULL
     assert call(logits=None) == E_NULL
-    assert call(B=9) == E_BATCH
+    assert call(B=0) == E_BATCH
+    assert call(B=65) == E_BATCH                      # MMV_MOE_MAX_BATCH = 64
     assert call(E=0) == E_SHAPE
     assert call(E=1025) == E_SHAPE
     assert call(k=0) == E_TOPK
@@ -158,8 +159,9 @@ def test_mul_mat_id_validation(L):
     assert call(ws_bytes=need - 1) == E_WS
     assert call(ws=None) == E_WS
     assert call(ws=Dp + 16) == E_ALIGN
-    assert call(B=9) == E_BATCH
+    assert call(B=65) == E_BATCH
     assert call(B=8) == E_WS                               # workspace sized for B = 1
+    assert call(B=64) == E_WS                              # verify / prefill batches
     assert call(ids=None) == E_NULL
     assert call(layer=_layer(top_k=17)) == E_TOPK
     assert call(layer=_layer(inter=500)) == E_SHAPE

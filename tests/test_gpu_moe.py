@@ -36,6 +36,11 @@ def _route_and_check(mm, orc, layer, ref, X):
     (40, 256, 32, 16, 8, True, True),
     (256, 2048, 512, 8, 1, True, False),     # the 256-expert decode layer
     (512, 2048, 512, 10, 8, True, False),    # the 512-expert verify batch
+    # verify / prefill batches (B > 8): row lists by the counting pass
+    (64, 512, 64, 4, 16, True, False),
+    (40, 256, 96, 5, 33, False, False),
+    (16, 256, 64, 4, 64, True, True),        # every expert chosen by many rows
+    (512, 2048, 512, 10, 32, True, False),
 ])
 def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
     layer, ref = build_moe(mm, orc, E, H, I, k, 0, "moe", E, H, I, shared=shared,
@@ -87,7 +92,8 @@ def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
 @pytest.mark.parametrize("topk_kernel", ["0", "1"])
 @pytest.mark.parametrize("E,H,I,k,B", [(256, 2048, 512, 8, 1), (512, 2048, 512, 10, 4),
                                        (32, 512, 64, 4, 8), (20, 96, 64, 3, 2),
-                                       (512, 2048, 512, 10, 8)])
+                                       (512, 2048, 512, 10, 8), (512, 2048, 512, 10, 16),
+                                       (64, 512, 64, 6, 64)])
 def test_moe_layer_decode(mm, orc, dev, monkeypatch, topk_kernel, E, H, I, k, B):
     # "1": top-k and row lists in a kernel of their own; "0": in every gate/up workgroup
     monkeypatch.setenv("MMV_MOE_TOPK_KERNEL", topk_kernel)
@@ -108,7 +114,7 @@ def test_moe_layer_decode(mm, orc, dev, monkeypatch, topk_kernel, E, H, I, k, B)
 
 
 @pytest.mark.parametrize("topk_kernel", ["0", "1"])
-@pytest.mark.parametrize("B", [1, 2, 5])
+@pytest.mark.parametrize("B", [1, 2, 5, 12])
 def test_moe_layer_decode_tied_router_rows(mm, orc, dev, monkeypatch, topk_kernel, B):
     # identical router rows give bit-identical logits: the selected experts and
     # their slot order must follow the lower index among equal logits, in the
@@ -158,10 +164,12 @@ def test_topk_exact_ties_from_logits(mm, orc, dev):
     np.testing.assert_allclose(npc(w), w_ref, rtol=2e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("I,B", [(128, 8), (512, 3), (512, 4), (512, 8)])
+@pytest.mark.parametrize("I,B", [(128, 8), (512, 3), (512, 4), (512, 8), (128, 24),
+                                 (512, 40)])
 def test_moe_batch_invariance(mm, orc, dev, I, B):
     # every row's result has one order whatever the other rows chose: B = 1
-    # takes the one-kernel down projection, B >= 3 the by-expert one
+    # takes the one-kernel down projection, B >= 3 the by-expert one, B > 8
+    # the row-list pass and row groups of eight
     E, H, k = 64, 1024, 6
     layer, _ = build_moe(mm, orc, E, H, I, k, 0, "binv", I, device=dev)
     X = synth.activations(B, H, 0, "binv", device=dev)
