@@ -273,8 +273,10 @@ int moe_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx,
  *   shared and the routed experts with the Q8_1 epilogue; the down
  *   projection with the combine (one kernel for B <= 2; for B >= 3 one
  *   workgroup per (expert, 64 output rows), then a combine kernel).  Three
- *   launches for B <= 2, five above.  Every row's result is the same bits
- *   whatever the other rows of the batch are.
+ *   launches for B <= 2, five for B <= 8, 5 + ceil(B/8) above (the router
+ *   per 8 rows, top-k, the row-list pass, gate/up per 8-row group of an
+ *   expert, down, combine).  Every row's result is the same bits whatever
+ *   the other rows of the batch are.  1 <= B <= MMV_MOE_MAX_BATCH.
  *   Routing stays in device memory.  ids / weights (B x k) may be NULL;
  *   when given they receive the routing decision.  The workspace needs no
  *   initialisation; calls that share a workspace must not overlap.
