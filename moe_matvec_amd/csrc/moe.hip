@@ -276,6 +276,62 @@ __global__ __launch_bounds__(256) void k_router(const float *__restrict__ R, int
   router_row<B, HC>(row, H, X, ldx, logits + e, E + 1);
 }
 
+// Router rows for B >= 4 (any B <= 64 in one launch): x is staged in LDS
+// eight activation rows at a time and every wave reads it there, instead of
+// each wave holding all B rows of x in registers (at B = 8 that spills and
+// leaves one wave per SIMD).  A wave owns one router row, held in registers
+// across the row groups.  Per lane the same fused multiply-adds in the same
+// order as router_row, then the same wave sum: the same logits, bit for bit.
+// Dynamic LDS: 8 * H * 4 bytes.  HC = H / 256 > 0.
+template <int HC>
+__global__ __launch_bounds__(256) void k_router_lds(const float *__restrict__ R, int E,
+                                                    const float *__restrict__ shg,
+                                                    const float *__restrict__ X, int64_t ldx,
+                                                    int B, float *__restrict__ logits) {
+  extern __shared__ __align__(16) f32x4 xs4[];  // [8][H / 4]
+  constexpr int H4 = 64 * HC;                    // float4 per row
+  constexpr int PER = 8 * H4 / 256;              // staging float4 per thread
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rows = E + (shg ? 1 : 0);
+  const float *row = e < E ? R + (int64_t)e * 4 * H4 : (shg ? shg : R);
+  f32x4 r[HC];
+#pragma unroll
+  for (int i = 0; i < HC; ++i)
+    r[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row) + lane + 64 * i);
+  for (int b0 = 0; b0 < B; b0 += 8) {  // uniform
+    const int nb = min(8, B - b0);
+    f32x4 xv[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int t = threadIdx.x + 256 * m, bb = min(t / H4, nb - 1), c = t - (t / H4) * H4;
+      xv[m] = load_f4(X + (int64_t)(b0 + bb) * ldx + 4 * c);
+    }
+    if (b0 > 0) __syncthreads();  // the previous rows are consumed
+#pragma unroll
+    for (int m = 0; m < PER; ++m) xs4[threadIdx.x + 256 * m] = xv[m];
+    __syncthreads();
+    if (e < rows) {
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) {
+        if (bb < nb) {  // uniform
+          float acc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < HC; ++i) {
+            const f32x4 x = xs4[bb * H4 + lane + 64 * i];
+            acc = fmaf(r[i].x, x.x, acc);
+            acc = fmaf(r[i].y, x.y, acc);
+            acc = fmaf(r[i].z, x.z, acc);
+            acc = fmaf(r[i].w, x.w, acc);
+          }
+          const float v = wave_sum_last(acc);
+          if (lane == 63) logits[(int64_t)(b0 + bb) * (E + 1) + e] = v;
+        }
+      }
+    }
+  }
+}
+
 // a workgroup per 4 rows (a wave per row)
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int64_t ldl, int E,
                                               int B, int k, int has_shared,
@@ -300,12 +356,26 @@ static void launch_router(const float *router, int E, int H, const float *shg, c
   }
 }
 
+// B >= 4 with H of 1024 or 2048: every row in one launch of the LDS-staged
+// router (same logits as router_row); returns false when it does not apply
+static bool launch_router_lds(const float *router, int E, int H, const float *shg,
+                              const float *X, int64_t ldx, int B, float *logits, hipStream_t s) {
+  if (B < 4 || (H != 1024 && H != 2048)) return false;
+  const dim3 grid((E + (shg ? 1 : 0) + 3) / 4), block(256);
+  const size_t lds = (size_t)8 * H * 4;
+  if (H == 1024)
+    hipLaunchKernelGGL((k_router_lds<4>), grid, block, lds, s, router, E, shg, X, ldx, B, logits);
+  else
+    hipLaunchKernelGGL((k_router_lds<8>), grid, block, lds, s, router, E, shg, X, ldx, B, logits);
+  return true;
+}
+
 hipError_t run_moe_route(const float *router, int E, int H, const float *X, int64_t ldx,
                          int B, int k, const float *shg, float *logits, int32_t *ids,
                          float *weights, float *shared_w, hipStream_t s) {
   const float *L = X;
   int64_t ldl = ldx;
-  if (router) {
+  if (router && !launch_router_lds(router, E, H, shg, X, ldx, B, logits, s)) {
     for (int b0 = 0; b0 < B; b0 += MMV_MAX_BATCH) {  // router rows 8 activation rows at a time
       const float *Xc = X + (int64_t)b0 * ldx;
       float *lc = logits + (int64_t)b0 * (E + 1);
@@ -321,6 +391,8 @@ hipError_t run_moe_route(const float *router, int E, int H, const float *X, int6
         default: return hipErrorInvalidValue;
       }
     }
+  }
+  if (router) {
     L = logits;
     ldl = E + 1;
   }
@@ -1748,7 +1820,9 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
     // router rows 8 activation rows at a time, top-k a wave per row, then
     // the row lists and the experts
     const int E = L.n_experts;
-    for (int b0 = 0; b0 < B; b0 += MMV_MAX_BATCH) {
+    const bool one = launch_router_lds(L.router, E, L.hidden, L.shared_gate_row, X, ldx, B,
+                                       a.logits, s);
+    for (int b0 = one ? B : 0; b0 < B; b0 += MMV_MAX_BATCH) {
       MoeArgs ac = a;
       ac.X = X + (int64_t)b0 * ldx;
       ac.logits = a.logits + (int64_t)b0 * (E + 1);
@@ -1773,7 +1847,9 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
   switch (B) {
 #define MMV_LAYER_CASE(BB)                                                              \
   case BB:                                                                              \
-    launch_route<BB>(a, s);                                                             \
+    if (!launch_router_lds(L.router, L.n_experts, L.hidden, L.shared_gate_row, X, ldx, BB, \
+                           a.logits, s))                                                \
+      launch_route<BB>(a, s);                                                           \
     if (!a.topk_in_k2) hipLaunchKernelGGL((k_moe_topk_gather<BB>), dim3(1), dim3(64 * BB), 0, s, a); \
     launch_experts<BB>(a, s);                                                           \
     break;

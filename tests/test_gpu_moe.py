@@ -224,3 +224,23 @@ def test_moe_down_paths_bit_identical(mm, orc, dev, monkeypatch, E, H, I, k, sha
         s64 = npc(sw).astype(np.float64) if shared else np.ones(B)
         want = ref.down(hq, hds, ids_np, npc(w).astype(np.float64), s64)
         assert rel_l2_rows(npc(ys[1]), want) <= MOE_TOL
+
+
+@pytest.mark.parametrize("E,H,B", [(256, 2048, 8), (512, 2048, 40), (64, 1024, 5), (96, 512, 12)])
+def test_router_logits_same_bits_for_every_batch(mm, orc, dev, E, H, B):
+    # B >= 4 stages x in LDS (H of 1024 or 2048), B < 4 holds it in registers,
+    # other H runs the router 8 rows at a time: one fused multiply-add order
+    # per lane and one wave sum in every case, so every row's logits are the
+    # same bits as the 1-row call's
+    t = synth.moe_layer_tensors(E, H, 64, 0, "rbits", E, H, device=dev)
+    R, shg = t["router"], synth.normal((H,), 0.02, 0, "rbits-g", E, H, device=dev)
+    X = synth.activations(B, H, 0, "rbits", E, B, device=dev)
+    k = 4
+    _, _, _, lg = mm.moe_route_topk(R, X, k, shared_gate_row=shg)
+    for b in range(B):
+        _, _, _, lb = mm.moe_route_topk(R, X[b:b + 1].clone(), k, shared_gate_row=shg)
+        assert torch.equal(lb[0], lg[b]), b
+    torch.cuda.synchronize()
+    ref = orc.router_logits(npc(R), npc(X))
+    got = npc(lg)[:, :E].astype(np.float64)
+    assert np.abs(got - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6
