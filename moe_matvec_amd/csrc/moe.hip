@@ -39,6 +39,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "layout.hpp"
@@ -276,14 +278,16 @@ __global__ __launch_bounds__(256) void k_router(const float *__restrict__ R, int
   router_row<B, HC>(row, H, X, ldx, logits + e, E + 1);
 }
 
-// Router rows for B >= 4 (any B <= 64 in one launch): x is staged in LDS
-// eight activation rows at a time and every wave reads it there, instead of
-// each wave holding all B rows of x in registers (at B = 8 that spills and
-// leaves one wave per SIMD).  A wave owns one router row, held in registers
-// across the row groups.  Per lane the same fused multiply-adds in the same
-// order as router_row, then the same wave sum: the same logits, bit for bit.
-// Dynamic LDS: 8 * H * 4 bytes.  HC = H / 256 > 0.
-template <int HC>
+// Router rows for B >= 4 (any B <= 64 in one launch): a workgroup per (4 * RW
+// router rows, 8 activation rows).  The workgroup stages its 8 rows of x in
+// LDS once (each wave holding all B rows of x in registers spills at B = 8
+// and leaves one wave per SIMD); a wave owns RW router rows, held in
+// registers.  Groups of 8 (or 4) rows run as 8 * RW (4 * RW) independent
+// chains side by side (their wave sums too), so no chain waits on its
+// predecessor; each x value read from LDS serves RW router rows.  Per lane the same fused
+// multiply-adds in the same order as router_row, then the same wave sum:
+// the same logits, bit for bit.  Dynamic LDS: 8 * H * 4 bytes.  HC = H / 256.
+template <int HC, int RW>
 __global__ __launch_bounds__(256) void k_router_lds(const float *__restrict__ R, int E,
                                                     const float *__restrict__ shg,
                                                     const float *__restrict__ X, int64_t ldx,
@@ -292,43 +296,106 @@ __global__ __launch_bounds__(256) void k_router_lds(const float *__restrict__ R,
   constexpr int H4 = 64 * HC;                    // float4 per row
   constexpr int PER = 8 * H4 / 256;              // staging float4 per thread
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int e0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RW;
   const int rows = E + (shg ? 1 : 0);
-  const float *row = e < E ? R + (int64_t)e * 4 * H4 : (shg ? shg : R);
-  f32x4 r[HC];
+  const int b0 = blockIdx.y * 8, nb = min(8, B - b0);
+  f32x4 r[RW][HC];
 #pragma unroll
-  for (int i = 0; i < HC; ++i)
-    r[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row) + lane + 64 * i);
-  for (int b0 = 0; b0 < B; b0 += 8) {  // uniform
-    const int nb = min(8, B - b0);
-    f32x4 xv[PER];
+  for (int j = 0; j < RW; ++j) {
+    const int e = e0 + j;  // rows past the end read row 0 and store nothing
+    const float *row = e < E ? R + (int64_t)e * 4 * H4 : (e == E && shg ? shg : R);
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int t = threadIdx.x + 256 * m, bb = min(t / H4, nb - 1), c = t - (t / H4) * H4;
-      xv[m] = load_f4(X + (int64_t)(b0 + bb) * ldx + 4 * c);
-    }
-    if (b0 > 0) __syncthreads();  // the previous rows are consumed
+    for (int i = 0; i < HC; ++i)
+      r[j][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row) + lane + 64 * i);
+  }
+  f32x4 xv[PER];
 #pragma unroll
-    for (int m = 0; m < PER; ++m) xs4[threadIdx.x + 256 * m] = xv[m];
-    __syncthreads();
-    if (e < rows) {
+  for (int m = 0; m < PER; ++m) {
+    const int t = threadIdx.x + 256 * m, bb = min(t / H4, nb - 1), c = t - (t / H4) * H4;
+    xv[m] = load_f4(X + (int64_t)(b0 + bb) * ldx + 4 * c);
+  }
 #pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        if (bb < nb) {  // uniform
-          float acc = 0.0f;
+  for (int m = 0; m < PER; ++m) xs4[threadIdx.x + 256 * m] = xv[m];
+  __syncthreads();
+  if (e0 >= rows) return;  // uniform over the wave; no barrier follows
+  auto chain = [&](float &acc, const f32x4 &w, const f32x4 &x) {
+    acc = fmaf(w.x, x.x, acc);
+    acc = fmaf(w.y, x.y, acc);
+    acc = fmaf(w.z, x.z, acc);
+    acc = fmaf(w.w, x.w, acc);
+  };
+  auto put = [&](int bb, int j, float v) {
+    if (lane == 63 && e0 + j < rows) logits[(int64_t)(b0 + bb) * (E + 1) + e0 + j] = v;
+  };
+  // NB rows from g0 as NB * RW chains side by side.  x chunk i + 1 is read
+  // while chunk i is used; the scheduling barriers and the opaque
+  // accumulators keep the compiler from hoisting every LDS read and running
+  // one chain after another (which needs 256 registers of x).
+  auto group = [&](auto nbc, int g0) {
+    constexpr int NB = decltype(nbc)::value;
+    float acc[RW][NB];
 #pragma unroll
-          for (int i = 0; i < HC; ++i) {
-            const f32x4 x = xs4[bb * H4 + lane + 64 * i];
-            acc = fmaf(r[i].x, x.x, acc);
-            acc = fmaf(r[i].y, x.y, acc);
-            acc = fmaf(r[i].z, x.z, acc);
-            acc = fmaf(r[i].w, x.w, acc);
-          }
-          const float v = wave_sum_last(acc);
-          if (lane == 63) logits[(int64_t)(b0 + bb) * (E + 1) + e] = v;
+    for (int j = 0; j < RW; ++j)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) acc[j][bb] = 0.0f;
+    f32x4 xa[NB], xb[NB];
+    auto ld = [&](f32x4(&x)[NB], int i) {
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) x[bb] = xs4[(g0 + bb) * H4 + lane + 64 * i];
+    };
+    auto mac = [&](const f32x4(&x)[NB], int i) {
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+          chain(acc[j][bb], r[j][i], x[bb]);
+          asm volatile("" : "+v"(acc[j][bb]));  // the products of chunk i happen here
         }
-      }
+    };
+    static_assert(HC % 2 == 0, "chunks go in pairs");
+    ld(xa, 0);
+#pragma unroll
+    for (int i = 0; i < HC; i += 2) {
+      ld(xb, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mac(xa, i);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < HC) ld(xa, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mac(xb, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    float v[RW][NB];  // every wave sum first, side by side, then the stores
+#pragma unroll
+    for (int j = 0; j < RW; ++j)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) v[j][bb] = wave_sum_last(acc[j][bb]);
+#pragma unroll
+    for (int j = 0; j < RW; ++j)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) put(g0 + bb, j, v[j][bb]);
+  };
+  if (nb == 8) {  // uniform
+    group(std::integral_constant<int, 8>{}, 0);
+    return;
+  }
+  int g = 0;
+  if (nb >= 4) {
+    group(std::integral_constant<int, 4>{}, 0);
+    g = 4;
+  }
+  for (int bb = g; bb < nb; ++bb) {  // uniform
+    float acc[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < HC; ++i) {
+      const f32x4 x = xs4[bb * H4 + lane + 64 * i];
+#pragma unroll
+      for (int j = 0; j < RW; ++j) chain(acc[j], r[j][i], x);
+    }
+#pragma unroll
+    for (int j = 0; j < RW; ++j) put(bb, j, wave_sum_last(acc[j]));
   }
 }
 
@@ -356,17 +423,32 @@ static void launch_router(const float *router, int E, int H, const float *shg, c
   }
 }
 
+// two router rows per wave from 32 activation rows (E = 512, H = 2048: at 16
+// rows one per wave measured 68.2 against 69.4 us per layer; at 64 rows two
+// per wave 158.5 against 160.4)
+constexpr int kRouterTwoRowsMinB = 32;
+
 // B >= 4 with H of 1024 or 2048: every row in one launch of the LDS-staged
 // router (same logits as router_row); returns false when it does not apply
 static bool launch_router_lds(const float *router, int E, int H, const float *shg,
                               const float *X, int64_t ldx, int B, float *logits, hipStream_t s) {
   if (B < 4 || (H != 1024 && H != 2048)) return false;
-  const dim3 grid((E + (shg ? 1 : 0) + 3) / 4), block(256);
+  const int rows = E + (shg ? 1 : 0), gy = (B + 7) / 8;
+  const dim3 block(256), grid1((rows + 3) / 4, gy), grid2((rows + 7) / 8, gy);
   const size_t lds = (size_t)8 * H * 4;
-  if (H == 1024)
-    hipLaunchKernelGGL((k_router_lds<4>), grid, block, lds, s, router, E, shg, X, ldx, B, logits);
-  else
-    hipLaunchKernelGGL((k_router_lds<8>), grid, block, lds, s, router, E, shg, X, ldx, B, logits);
+  // two router rows per wave once there are workgroups enough for the chip
+  const bool two = B >= kRouterTwoRowsMinB;
+  if (H == 1024) {
+    if (two)
+      hipLaunchKernelGGL((k_router_lds<4, 2>), grid2, block, lds, s, router, E, shg, X, ldx, B, logits);
+    else
+      hipLaunchKernelGGL((k_router_lds<4, 1>), grid1, block, lds, s, router, E, shg, X, ldx, B, logits);
+  } else {
+    if (two)
+      hipLaunchKernelGGL((k_router_lds<8, 2>), grid2, block, lds, s, router, E, shg, X, ldx, B, logits);
+    else
+      hipLaunchKernelGGL((k_router_lds<8, 1>), grid1, block, lds, s, router, E, shg, X, ldx, B, logits);
+  }
   return true;
 }
 
