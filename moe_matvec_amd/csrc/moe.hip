@@ -1646,8 +1646,10 @@ __global__ __launch_bounds__(1024) void k_moe_gather_rows(MoeArgs a) {
 // gate/up for B <= 64: one workgroup per (work item, 32-row tile), a work
 // item being up to eight rows of one expert (k_moe_gather_rows lists them:
 // the shared expert's row groups first, then each routed expert's); items
-// past the published count exit.  The B <= 8 tile code does the rows.
-template <int T>
+// past the published count exit.  The B <= 8 tile code does the rows; SC:
+// every scale plane 16-byte aligned (checked on the host), the scales fetched
+// as 16-byte chunks.
+template <int T, bool SC>
 __global__ __launch_bounds__(256) void k_moe_gate_up_rows(MoeArgs a) {
   __shared__ int rowmap[MMV_MAX_BATCH];
   __shared__ int pairmap[MMV_MAX_BATCH];
@@ -1688,8 +1690,8 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_rows(MoeArgs a) {
     rowmap[threadIdx.x] = shared_slot ? r : p / k;
   }
   const XPre<1> none{};
-  gate_up_tile<MMV_MAX_BATCH, T, 0, false>(a, gq, gd, uq, ud, tile, ncv, rowmap, pairmap, smem,
-                                           hbuf, none, []() {});
+  gate_up_tile<MMV_MAX_BATCH, T, 0, SC>(a, gq, gd, uq, ud, tile, ncv, rowmap, pairmap, smem,
+                                        hbuf, none, []() {});
 }
 
 namespace {
@@ -1816,10 +1818,23 @@ int rows_work_max(const MoeArgs &a) {
          min(a.L.n_experts, Bk) + Bk / MMV_MAX_BATCH;
 }
 
+// every gate / up scale plane 16-byte aligned: the experts' planes start
+// at multiples of I * H / 32 * 2 bytes from the layer's
+bool rows_scales16(const MoeArgs &a) {
+  const mmv_moe_layer &L = a.L;
+  auto al = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool sh = !a.routed_shared || (al(L.sh_gate_d) && al(L.sh_up_d));
+  return al(L.gate_d) && al(L.up_d) && sh && ((int64_t)L.inter * (L.hidden / 32) * 2) % 16 == 0;
+}
+
 template <int T>
 void launch_gate_up_rows(const MoeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((k_moe_gate_up_rows<T>), dim3(rows_work_max(a) * (a.L.inter / 32)),
-                     dim3(256), xstage_bytes(MMV_MAX_BATCH, a.L.hidden), s, a);
+  const dim3 grid(rows_work_max(a) * (a.L.inter / 32)), block(256);
+  const size_t lds = xstage_bytes(MMV_MAX_BATCH, a.L.hidden);
+  if (T > 0 && rows_scales16(a))
+    hipLaunchKernelGGL((k_moe_gate_up_rows<T, T != 0>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((k_moe_gate_up_rows<T, false>), grid, block, lds, s, a);
 }
 
 template <int TI>

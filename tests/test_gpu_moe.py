@@ -245,3 +245,42 @@ def test_router_logits_same_bits_for_every_batch(mm, orc, dev, E, H, B):
     ref = orc.router_logits(npc(R), npc(X))
     got = npc(lg)[:, :E].astype(np.float64)
     assert np.abs(got - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6
+
+
+def _off2(t):
+    # the same values at an address 2 bytes past a 16-byte boundary
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    v = buf[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_moe_scale_planes_any_alignment(mm, orc, dev, shared):
+    # fp16 scale planes 16-byte aligned are read as 16-byte chunks where that
+    # pays; planes only 2-byte aligned take per-block loads: the same values,
+    # so the same bits
+    E, H, I, k = 64, 2048, 512, 6
+    layer, ref = build_moe(mm, orc, E, H, I, k, 0, "salign", shared=shared, device=dev)
+    t = layer.t
+    sh = None
+    if shared:
+        sh = dict(layer.shared)
+        for n in ("gate_d", "up_d", "down_d"):
+            sh[n] = _off2(sh[n])
+    odd = mm.MoeLayer(layer.router, t["gate_qs"], _off2(t["gate_d"]), t["up_qs"],
+                      _off2(t["up_d"]), t["down_qs"], _off2(t["down_d"]), k, shared=sh)
+    assert odd.t["gate_d"].data_ptr() % 16 == 2
+    for B in (1, 2, 5, 12):
+        X = synth.activations(B, H, 0, "salign", B, device=dev)
+        ids, w, sw, _ = mm.moe_route_topk(layer.router, X, k)
+        sw = sw if shared else None
+        y0 = mm.moe_mul_mat_id(layer, X, ids, w, sw)
+        y1 = mm.moe_mul_mat_id(odd, X, ids, w, sw)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1), B
+        ids_np = npc(ids)
+        hq, hds = orc.quantize_q8_1(ref.gate_up(npc(X), ids_np))
+        s64 = npc(sw).astype(np.float64) if shared else np.ones(B)
+        want = ref.down(hq, hds, ids_np, npc(w).astype(np.float64), s64)
+        assert rel_l2_rows(npc(y1), want) <= MOE_TOL
