@@ -1778,7 +1778,7 @@ template <int B, int TI>
 void launch_down(const MoeArgs &a, hipStream_t s) {
   const int knob = moe_down_knob();
   if (knob == 2 || (knob != 1 && B >= kDownSplitMinB)) {
-    const int slots = B * a.L.top_k + (a.L.sh_down_qs ? 1 : 0);
+    const int slots = min(a.L.n_experts, B * a.L.top_k) + (a.L.sh_down_qs ? 1 : 0);
     const int ntile = (a.L.hidden + kDownPartRows - 1) / kDownPartRows;
     hipLaunchKernelGGL((k_moe_down_part<B, TI>), dim3(slots * ntile), dim3(256), 0, s, a);
     hipLaunchKernelGGL((k_moe_combine<B>), dim3((a.L.hidden + 255) / 256, B), dim3(256), 0, s, a);
@@ -1811,11 +1811,13 @@ void launch_experts(const MoeArgs &a, hipStream_t s) {
   }
 }
 
-// work items: at most (shared row groups) + U + B*k/8, U <= min(E, B*k)
+// work items: (shared row groups) + U + sum over experts of (ceil(c_e / 8) - 1)
+// <= (shared row groups) + U + (B*k - U) / 8 (c_e rows chose expert e, the
+// c_e sum to B*k), which does not fall as U grows: bounded at U = min(E, B*k)
 int rows_work_max(const MoeArgs &a) {
-  const int Bk = a.nrows * a.L.top_k;
-  return (a.routed_shared ? (a.nrows + MMV_MAX_BATCH - 1) / MMV_MAX_BATCH : 0) +
-         min(a.L.n_experts, Bk) + Bk / MMV_MAX_BATCH;
+  const int Bk = a.nrows * a.L.top_k, Umax = min(a.L.n_experts, Bk);
+  return (a.routed_shared ? (a.nrows + MMV_MAX_BATCH - 1) / MMV_MAX_BATCH : 0) + Umax +
+         (Bk - Umax) / MMV_MAX_BATCH;
 }
 
 // every gate / up scale plane 16-byte aligned: the experts' planes start
@@ -1839,7 +1841,7 @@ void launch_gate_up_rows(const MoeArgs &a, hipStream_t s) {
 
 template <int TI>
 void launch_down_rows(const MoeArgs &a, hipStream_t s) {
-  const int slots = a.nrows * a.L.top_k + (a.L.sh_down_qs ? 1 : 0);
+  const int slots = min(a.L.n_experts, a.nrows * a.L.top_k) + (a.L.sh_down_qs ? 1 : 0);
   const int ntile = (a.L.hidden + kDownPartRows - 1) / kDownPartRows;
   hipLaunchKernelGGL((k_moe_down_part<0, TI>), dim3(slots * ntile), dim3(256), 0, s, a);
   hipLaunchKernelGGL((k_moe_combine<0>), dim3((a.L.hidden + 255) / 256, a.nrows), dim3(256), 0,
