@@ -26,7 +26,9 @@ MMV_HD size_t hq_bytes(int P, int I) { return q8_1_bytes(I, P) + (size_t)8 * P *
 
 // moe workspace: [hq][gather lists][logits B x (E+1)][ids B x k]
 // [weights B x k][shared_w B][per-pair down products P x H fp32]
-// [gate/up work items (B > 8): count + at most B*k + B/8 + 1]
+// [gate/up work items (B > 8): a 32-byte count slot, then at most
+//  B*k + B/8 + 1 records of 32 bytes (kWorkRecInts int32 each)]
+constexpr int kWorkRecInts = 8;  // one gate/up work record: 32 bytes
 struct MoeWsLayout {
   size_t hq, gather, logits, ids, weights, shared_w, dpart, work, total;
 };
@@ -41,7 +43,7 @@ MMV_HD MoeWsLayout moe_ws_layout(int E, int H, int I, int k, int B, bool has_sha
   l.shared_w = align_up(l.weights + (size_t)4 * B * k, kWsAlign);
   l.dpart = align_up(l.shared_w + (size_t)4 * B, kWsAlign);
   l.work = align_up(l.dpart + (size_t)4 * P * H, kWsAlign);
-  l.total = align_up(l.work + (size_t)4 * (B * k + B / 8 + 2), kWsAlign);
+  l.total = align_up(l.work + (size_t)4 * kWorkRecInts * (B * k + B / 8 + 2), kWsAlign);
   return l;
 }
 

@@ -1575,6 +1575,7 @@ __global__ __launch_bounds__(256) void k_moe_topk_rows(MoeArgs a) {
 __global__ __launch_bounds__(1024) void k_moe_gather_rows(MoeArgs a) {
   __shared__ unsigned long long s_mask[MMV_MAX_EXPERTS];
   __shared__ int s_start[MMV_MAX_EXPERTS];
+  __shared__ int s_item[MMV_MAX_EXPERTS];  // the expert's first work record
   __shared__ int s_wc[16], s_wp[16], s_wg[16];
   const mmv_moe_layer &L = a.L;
   const int t = threadIdx.x, E = L.n_experts, k = L.top_k, Bk = a.nrows * k;
@@ -1609,11 +1610,31 @@ __global__ __launch_bounds__(1024) void k_moe_gather_rows(MoeArgs a) {
     tg += wg;
   }
   const int start = bc + ic - c, urank = bp + ip - pr, gstart = bg + ig - g;  // exclusive
-  // work items: the shared expert's row groups, then each routed expert's
+  // work records: the shared expert's row groups, then each routed expert's
+  // (record = expert, or -1 for the shared one; rows; up to 8 pair indices
+  // as int16 pairs).  Gate/up reads one record, with nothing before it.
   const int nsh = a.routed_shared ? (a.nrows + MMV_MAX_BATCH - 1) / MMV_MAX_BATCH : 0;
-  if (t < nsh) a.work[1 + t] = t;  // slot 0, row group t
-  if (t < E && pr)
-    for (int q = 0; q < g; ++q) a.work[1 + nsh + gstart + q] = ((a.routed_shared + urank) << 4) | q;
+  int32_t *rec0 = a.work + kWorkRecInts;
+  if (t < nsh) {
+    int32_t *rec = rec0 + kWorkRecInts * t;
+    const int r0 = MMV_MAX_BATCH * t, nr = min(MMV_MAX_BATCH, a.nrows - r0);
+    rec[0] = -1;
+    rec[1] = nr;
+#pragma unroll
+    for (int i = 0; i < MMV_MAX_BATCH / 2; ++i) {  // pair of row r: Bk + r
+      const int pa = Bk + r0 + min(2 * i, nr - 1), pb = Bk + r0 + min(2 * i + 1, nr - 1);
+      rec[2 + i] = (pa & 0xFFFF) | (pb << 16);
+    }
+  }
+  if (t < E) {
+    s_item[t] = nsh + gstart;
+    if (pr)
+      for (int q = 0; q < g; ++q) {
+        int32_t *rec = rec0 + kWorkRecInts * (nsh + gstart + q);
+        rec[0] = t;
+        rec[1] = min(MMV_MAX_BATCH, c - MMV_MAX_BATCH * q);
+      }
+  }
   if (t == 0) a.work[0] = nsh + tg;
   int32_t *gl = a.gather;
   const bool dbg = a.has_dbg != 0;
@@ -1636,17 +1657,21 @@ __global__ __launch_bounds__(1024) void k_moe_gather_rows(MoeArgs a) {
   if (t < Bk) {
     const int e = a.ids[t];
     if (e >= 0 && e < E) {
-      const int pos = s_start[e] + __popcll(s_mask[e] & ((1ull << (t / k)) - 1ull));
+      const int rank = __popcll(s_mask[e] & ((1ull << (t / k)) - 1ull)), pos = s_start[e] + rank;
       gl[2 + 2 * Bk + pos] = t;
+      int16_t *rp = reinterpret_cast<int16_t *>(rec0 + kWorkRecInts * (s_item[e] + rank / MMV_MAX_BATCH) + 2);
+      rp[rank % MMV_MAX_BATCH] = (int16_t)t;
       if (dbg && a.dbg.pairs) a.dbg.pairs[pos] = t;
     }
   }
 }
 
 // gate/up for B <= 64: one workgroup per (work item, 32-row tile), a work
-// item being up to eight rows of one expert (k_moe_gather_rows lists them:
-// the shared expert's row groups first, then each routed expert's); items
-// past the published count exit.  The B <= 8 tile code does the rows; SC:
+// item being up to eight rows of one expert (k_moe_gather_rows writes one
+// record per item, the shared expert's row groups first, then each routed
+// expert's: the expert, the row count and the rows' pair indices, so that
+// the weights go out after one round trip); items past the published count
+// exit.  The B <= 8 tile code does the rows; SC:
 // every scale plane 16-byte aligned (checked on the host), the scales fetched
 // as 16-byte chunks.
 template <int T, bool SC>
@@ -1659,35 +1684,35 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_rows(MoeArgs a) {
   const int k = L.top_k, H = L.hidden, I = L.inter, B = a.nrows, Bk = B * k;
   const int ntiles = I >> 5, nbh = H >> 5;
   const int wi = blockIdx.x / ntiles, tile = blockIdx.x - wi * ntiles;
-  const int32_t *gl = a.gather;
+  // the count and this item's record in one round trip (wi is below the
+  // record capacity, so the record is in bounds even past the count)
+  const int32_t *rec = a.work + kWorkRecInts * (1 + wi);
   const int W = a.work[0];
-  if (wi >= W) return;  // uniform over the workgroup
-  const int item = a.work[1 + wi], slot0 = item >> 4, r0 = MMV_MAX_BATCH * (item & 15);
-  const bool shared_slot = a.routed_shared && slot0 == 0;
-  const int slot = slot0 - a.routed_shared;
+  const int e = rec[0], nc = rec[1];
+  int32_t pw[MMV_MAX_BATCH / 2];
+#pragma unroll
+  for (int i = 0; i < MMV_MAX_BATCH / 2; ++i) pw[i] = rec[2 + i];
+  if (wi >= W || nc <= 0 || nc > MMV_MAX_BATCH) return;  // uniform; never for a published item
+  const bool shared_slot = e < 0;
   const uint8_t *gq, *uq;
   const uint16_t *gd, *ud;
-  int nr, pbase = 0;
   if (shared_slot) {
     gq = L.sh_gate_qs; gd = L.sh_gate_d; uq = L.sh_up_qs; ud = L.sh_up_d;
-    nr = B;
   } else {
-    const int e = gl[1 + slot], o0 = gl[1 + Bk + slot], o1 = gl[2 + Bk + slot];
     const int64_t eo = (int64_t)e * I * nbh;
     gq = L.gate_qs + eo * 16; gd = L.gate_d + eo;
     uq = L.up_qs + eo * 16; ud = L.up_d + eo;
-    nr = min(o1 - o0, B);
-    pbase = o0;
   }
-  const int nc = min(MMV_MAX_BATCH, nr - r0);
-  if (nc <= 0) return;  // uniform; never for a published item
   int ncv = nc;  // opaque: with its range known the compiler unrolls per row count
   asm volatile("" : "+s"(ncv));
   if (threadIdx.x < (unsigned)nc) {
-    const int r = r0 + threadIdx.x;
-    const int p = shared_slot ? Bk + r : gl[2 + 2 * Bk + pbase + r];
-    pairmap[threadIdx.x] = p;
-    rowmap[threadIdx.x] = shared_slot ? r : p / k;
+    const int tr = threadIdx.x;
+    int32_t two = pw[0];
+#pragma unroll
+    for (int i = 1; i < MMV_MAX_BATCH / 2; ++i) two = (tr >> 1) == i ? pw[i] : two;
+    const int p = (tr & 1) ? (two >> 16) : (int)(int16_t)(two & 0xFFFF);
+    pairmap[tr] = p;
+    rowmap[tr] = shared_slot ? p - Bk : p / k;
   }
   const XPre<1> none{};
   gate_up_tile<MMV_MAX_BATCH, T, 0, SC>(a, gq, gd, uq, ud, tile, ncv, rowmap, pairmap, smem,
