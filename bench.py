@@ -300,7 +300,7 @@ def moe_section(mm, dev, E, k, layers, Bs, steps, warmup, H=2048, I=512):
                             MB_per_layer=nbytes / layers / 1e6, GBps=nbytes / t / 1e9,
                             frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS,
                             launches_per_layer=(3 if B <= 2 else 5) if B <= 8
-                            else 5 + (B + 7) // 8)
+                            else (6 if H in (1024, 2048) else 5 + (B + 7) // 8))
         del X, Y, ids, ws, g
     if len(Bs) > 1 and 1 in Bs:
         res["ratio_Bmax_B1_time"] = res[f"B{max(Bs)}"]["us_per_layer"] / res["B1"]["us_per_layer"]

@@ -273,9 +273,11 @@ int moe_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx,
  *   shared and the routed experts with the Q8_1 epilogue; the down
  *   projection with the combine (one kernel for B <= 2; for B >= 3 one
  *   workgroup per (expert, 64 output rows), then a combine kernel).  Three
- *   launches for B <= 2, five for B <= 8, 5 + ceil(B/8) above (the router
- *   per 8 rows, top-k, the row-list pass, gate/up per 8-row group of an
- *   expert, down, combine).  Every row's result is the same bits whatever
+ *   launches for B <= 2, five for B <= 8, six above (the router, top-k,
+ *   the row-list pass, gate/up per 8-row group of an expert, down,
+ *   combine); with H other than 1024 or 2048 the router takes a launch per
+ *   8 rows (5 + ceil(B/8) launches above B = 8).  Every row's
+ *   result is the same bits whatever
  *   the other rows of the batch are.  1 <= B <= MMV_MOE_MAX_BATCH.
  *   Routing stays in device memory.  ids / weights (B x k) may be NULL;
  *   when given they receive the routing decision.  The workspace needs no
