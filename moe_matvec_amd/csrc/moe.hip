@@ -10,10 +10,13 @@
 // quantized to Q8 in the producing kernel, the K <= 512 down projection uses
 // four rows per wave.  "Flash-Next on Strix Halo" (Expert GEMMs) builds
 // per-expert row lists so each expert's weights are read once for all rows
-// that chose it.  Here, on gfx950, one layer is three launches for B <= 2
-// and five above:
-//  K1 router rows (one wave per row, all loads issued up front), logits to
-//     the workspace;
+// that chose it.  Here, on gfx950, one layer is three launches for B <= 2,
+// five up to B = 8 and six for the verify / prefill batches above (see the
+// section on those):
+//  K1 router rows, logits to the workspace (B <= 3: one wave per router row
+//     with every activation row in registers, all loads issued up front;
+//     B >= 4 with H of 1024 or 2048: workgroups per 8 activation rows, x
+//     staged in LDS; the same per-lane order and wave sum either way);
 //  (B > 2) K1b one workgroup, a wave per row: top-k with order-preserving
 //     32-bit keys (equal logits rank by lower index), weights exp(l - l_max)
 //     renormalised over the selected k (the full-E denominator cancels), and
@@ -1546,13 +1549,14 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
 // ---------------------------------------------------------------------------
 // "Flash-Next on Strix Halo" (Expert GEMMs) builds per-expert row lists in a
 // prepass and dispatches compact (expert, tile) work, so that each expert's
-// weights are read once for all the rows that chose it.  Here: the router in
-// 8-row chunks, top-k a wave per row, the row lists by one workgroup
-// (k_moe_gather_rows), gate/up by (expert, 32-row tile) workgroups that walk
-// their rows eight at a time (the same tile code as B <= 8, the weights
-// re-read from cache for each further 8 rows), then the by-expert down
-// projection and the combine with the row count at run time.  Every row is
-// formed by the same arithmetic as for B <= 8, so it is the same bits.
+// weights are read once for all the rows that chose it.  Here: the router
+// (every row in one launch for H of 1024 or 2048, else 8 rows per launch),
+// top-k a wave per row, the row lists and one work record per (expert,
+// 8-row group) by one workgroup (k_moe_gather_rows), gate/up by (record,
+// 32-row tile) workgroups (the same tile code as B <= 8, an expert's
+// weights re-read from cache for each further 8 rows), then the by-expert
+// down projection and the combine with the row count at run time.  Every
+// row is formed by the same arithmetic as for B <= 8, so it is the same bits.
 
 // top-k for every row (layer decode): a workgroup per 4 rows, a wave per row
 __global__ __launch_bounds__(256) void k_moe_topk_rows(MoeArgs a) {
