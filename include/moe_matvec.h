@@ -231,8 +231,9 @@ typedef struct {
  * Layout: bytes [0, mmv_q8_1_bytes(I, P)) hold Q8_1(h) for the P pairs
  * (P = B*k routed pairs p = b*k + j, then B shared pairs p = B*k + b),
  * followed by the integer code sums of those blocks, the per-expert row
- * lists, the routing buffers that moe_layer_decode uses, and P x H fp32
- * per-pair down products (the by-expert down projection for B >= 3).
+ * lists, the routing buffers that moe_layer_decode uses, P x H fp32
+ * per-pair down products (the by-expert down projection for B >= 3), and
+ * for B > 8 the gate/up work records (32 bytes per expert and 8-row group).
  * 256-byte aligned workspace required.
  * For B <= 8 the down projection may stage Q8_1(h) of all P pairs in LDS:
  * P * I <= MMV_MOE_MAX_PI (else MMV_E_SHAPE); larger batches do not. */
