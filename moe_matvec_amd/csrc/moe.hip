@@ -287,9 +287,10 @@ __global__ __launch_bounds__(256) void k_router(const float *__restrict__ R, int
 // and leaves one wave per SIMD); a wave owns RW router rows, held in
 // registers.  Groups of 8 (or 4) rows run as 8 * RW (4 * RW) independent
 // chains side by side (their wave sums too), so no chain waits on its
-// predecessor; each x value read from LDS serves RW router rows.  Per lane the same fused
-// multiply-adds in the same order as router_row, then the same wave sum:
-// the same logits, bit for bit.  Dynamic LDS: 8 * H * 4 bytes.  HC = H / 256.
+// predecessor; each x value read from LDS serves RW router rows.  Per lane
+// the same fused multiply-adds in the same order as router_row, then the
+// same wave sum: the same logits, bit for bit.  Dynamic LDS: 8 * H * 4
+// bytes.  HC = H / 256.
 template <int HC, int RW>
 __global__ __launch_bounds__(256) void k_router_lds(const float *__restrict__ R, int E,
                                                     const float *__restrict__ shg,
