@@ -413,7 +413,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
-              "(the matvec shards by rows or experts with no exchange; see DESIGN.md)",
+              "(the matvec would shard by output rows or by experts, with no exchange "
+              "inside a layer)",
               file=sys.stderr)
         sys.exit(2)
 
