@@ -252,7 +252,9 @@ size_t moe_workspace_bytes(const mmv_moe_layer *L, int32_t B);
  *     Y[b*ldy + n] = sum_j weights[b*k+j] * (Down_e (x) Q8_1(h))[n]
  *                    + shared_w[b] * (Down_sh (x) Q8_1(h_sh))[n].
  *   Each unique expert's weights are read once for all rows that chose it.
- *   ids: B x k int32 in [0, E), distinct within a row; weights: B x k fp32;
+ *   ids: B x k int32 in [0, E), distinct within a row (an id outside
+ *   [0, E) adds nothing; a row naming one expert twice gets an unspecified
+ *   result, every access staying in bounds); weights: B x k fp32;
  *   shared_w: B fp32 or NULL (weight 1).  X: B x H fp32, ldx % 4 == 0.
  *   Y: B x H fp32.  workspace: moe_workspace_bytes(L, B) bytes.
  *   1 <= B <= MMV_MOE_MAX_BATCH.  Verify / prefill batches (B > 8) take a
