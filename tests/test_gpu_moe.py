@@ -284,3 +284,22 @@ def test_moe_scale_planes_any_alignment(mm, orc, dev, shared):
         s64 = npc(sw).astype(np.float64) if shared else np.ones(B)
         want = ref.down(hq, hds, ids_np, npc(w).astype(np.float64), s64)
         assert rel_l2_rows(npc(y1), want) <= MOE_TOL
+
+
+@pytest.mark.parametrize("B", [1, 4, 12])
+def test_moe_ids_outside_range_add_nothing(mm, orc, dev, B):
+    # a pair whose id lies outside [0, E) takes part in no expert list and
+    # adds nothing: the same result as its expert kept with weight 0
+    E, H, I, k = 64, 1024, 128, 6
+    layer, _ = build_moe(mm, orc, E, H, I, k, 0, "badid", B, device=dev)
+    X = synth.activations(B, H, 0, "badid", B, device=dev)
+    ids, w, sw, _ = mm.moe_route_topk(layer.router, X, k)
+    bad, w0 = ids.clone(), w.clone()
+    for b in range(B):
+        bad[b, 1] = -1 if b % 2 == 0 else E
+        w0[b, 1] = 0.0
+    y_bad = mm.moe_mul_mat_id(layer, X, bad, w, sw)
+    y_ref = mm.moe_mul_mat_id(layer, X, ids, w0, sw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y_bad).all()
+    assert torch.equal(y_bad, y_ref)
