@@ -93,7 +93,7 @@ def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
 @pytest.mark.parametrize("E,H,I,k,B", [(256, 2048, 512, 8, 1), (512, 2048, 512, 10, 4),
                                        (32, 512, 64, 4, 8), (20, 96, 64, 3, 2),
                                        (512, 2048, 512, 10, 8), (512, 2048, 512, 10, 16),
-                                       (64, 512, 64, 6, 64)])
+                                       (64, 512, 64, 6, 64), (96, 1024, 128, 6, 40)])
 def test_moe_layer_decode(mm, orc, dev, monkeypatch, topk_kernel, E, H, I, k, B):
     # "1": top-k and row lists in a kernel of their own; "0": in every gate/up workgroup
     monkeypatch.setenv("MMV_MOE_TOPK_KERNEL", topk_kernel)
