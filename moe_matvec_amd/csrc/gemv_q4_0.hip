@@ -469,8 +469,12 @@ static hipError_t launch_q4_rp(const uint8_t *qs, const uint16_t *d, int N, int 
                                int64_t ldy, hipStream_t s) {
   constexpr int kMaxLoads = B <= 2 ? 16 : 8;
   constexpr int kMaxRp = cmin(8, (kMaxLoads / T) & ~1);
+  // rows per lane group: 4, or 2 from B = 5 (more, smaller workgroups;
+  // 4096^2 + 11008 x 4096 with a Q8_1 buffer, us per pair, RP 4 -> 2:
+  // B = 5 18.7 -> 18.4, B = 6 20.2 -> 19.3, B = 8 22.7 -> 22.1; B = 4 level;
+  // RP 8 at B = 8: 26.1)
   int rp = q4_knob("MMV_Q4_RP");
-  if (rp == 0) rp = cmin(4, kMaxRp);
+  if (rp == 0) rp = B >= 5 ? 2 : cmin(4, kMaxRp);
   if constexpr (kMaxRp >= 8)
     if (rp > 6) return launch_q4_t<B, G, 8, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   if constexpr (kMaxRp >= 6)
