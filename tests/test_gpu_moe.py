@@ -227,7 +227,8 @@ def test_moe_down_paths_bit_identical(mm, orc, dev, monkeypatch, E, H, I, k, sha
 
 
 @pytest.mark.parametrize("E,H,B", [(256, 2048, 8), (512, 2048, 40), (64, 1024, 5), (96, 512, 12),
-                                   (512, 2048, 31), (160, 1024, 64), (256, 2048, 4)])
+                                   (512, 2048, 31), (160, 1024, 64), (256, 2048, 4),
+                                   (512, 2048, 37)])
 def test_router_logits_same_bits_for_every_batch(mm, orc, dev, E, H, B):
     # B >= 4 stages x in LDS (H of 1024 or 2048), B < 4 holds it in registers,
     # other H runs the router 8 rows at a time: one fused multiply-add order
