@@ -33,8 +33,12 @@
  *    (see mmv_last_hip_error).  Faults inside a kernel surface at the
  *    caller's next synchronization.
  *  - Results are deterministic: no floating-point atomics; repeated calls
- *    on the same inputs give bit-identical outputs, and each row of a
- *    B-row call equals the 1-row call on that row, bit for bit.
+ *    on the same inputs give bit-identical outputs.  Each row of a B-row
+ *    call equals the 1-row call on that row, bit for bit, for every entry
+ *    point except gemv_bf16: there rows are bit-identical across every
+ *    B >= 2, and the B = 1 result (fp32 fused multiply-adds) agrees with the
+ *    B >= 2 result (matrix cores on x split into bf16 high + low parts)
+ *    within rounding, not bit for bit.
  *  - Outputs must not overlap inputs (MMV_E_ALIAS).
  *
  * Data formats
@@ -218,13 +222,25 @@ typedef struct {
   const uint16_t *sh_gate_d, *sh_up_d, *sh_down_d;
 } mmv_moe_layer;
 
-/* Optional staged outputs of moe_mul_mat_id, for tests (each may be NULL). */
+/* Optional staged outputs of moe_mul_mat_id, for tests: device buffers the
+ * caller owns, each may be NULL.  P = B*k routed pairs (p = b*k + j) plus B
+ * shared pairs (p = B*k + b) when the layer has a shared expert.  The Q8_1
+ * buffers use the planar layout of the header (codes, then {d, s} pairs).
+ * [FOURTEEN: "Two bugs nobody was looking for": quantized activations as
+ *  explicit buffers, so each stage can be compared on its own] */
 typedef struct {
   float *h;            /* P x I fp32: silu(gate) * up for each pair          */
   int32_t *unique;     /* [B*k]: sorted unique routed experts               */
   int32_t *offsets;    /* [B*k + 1]: pair ranges per unique expert          */
   int32_t *pairs;      /* [B*k]: b*k + j grouped by expert, then b, then j  */
   int32_t *n_unique;   /* [1]                                               */
+  void *x_q8;          /* mmv_q8_1_bytes(H, B): Q8_1 of the B rows of x, as
+                          the gate/up workgroups stage it (same routine)     */
+  float *gate_out;     /* P x I fp32: gate product of each pair             */
+  float *up_out;       /* P x I fp32: up product of each pair               */
+  void *h_q8;          /* mmv_q8_1_bytes(I, P): Q8_1(h), the down input      */
+  float *down_out;     /* P x H fp32: each pair's down product, before the
+                          weight (0 for a pair whose id is outside [0, E))   */
 } mmv_moe_debug;
 
 /* Workspace bytes for moe_mul_mat_id / moe_layer_decode at B rows.
@@ -234,10 +250,7 @@ typedef struct {
  * lists, the routing buffers that moe_layer_decode uses, P x H fp32
  * per-pair down products (the by-expert down projection for B >= 3), and
  * for B > 8 the gate/up work records (32 bytes per expert and 8-row group).
- * 256-byte aligned workspace required.
- * For B <= 8 the down projection may stage Q8_1(h) of all P pairs in LDS:
- * P * I <= MMV_MOE_MAX_PI (else MMV_E_SHAPE); larger batches do not. */
-#define MMV_MOE_MAX_PI 49152
+ * 256-byte aligned workspace required. */
 size_t moe_workspace_bytes(const mmv_moe_layer *L, int32_t B);
 
 /* --------------------------------------------------------------------------

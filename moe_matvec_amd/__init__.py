@@ -20,6 +20,7 @@ __all__ = [
     "argmax_rows", "argmax_workspace_bytes", "Q4F32_MAX_XK",
     "moe_route_topk", "moe_mul_mat_id", "moe_layer_decode", "moe_workspace_bytes",
     "MAX_BATCH", "MOE_MAX_BATCH", "MAX_EXPERTS", "MAX_TOPK", "Q4_MAX_XK", "stream_read", "split_q8_1",
+    "PATH", "set_path", "get_path",
 ]
 
 MAX_BATCH = 8
@@ -61,7 +62,15 @@ class _Layer(C.Structure):
 
 
 class _Debug(C.Structure):
-    _fields_ = [("h", _P), ("unique", _P), ("offsets", _P), ("pairs", _P), ("n_unique", _P)]
+    _fields_ = [("h", _P), ("unique", _P), ("offsets", _P), ("pairs", _P), ("n_unique", _P),
+                ("x_q8", _P), ("gate_out", _P), ("up_out", _P), ("h_q8", _P), ("down_out", _P)]
+
+
+_DEBUG_FIELDS = [f for f, _ in _Debug._fields_]
+
+# kernel-variant switches of include/moe_matvec_testing.h (tests and measurements only)
+PATH = dict(BF16_ROWS=0, BF16_WAVES=1, BF16_XL=2, BF16_ML=3, Q4_RP=4, Q4_GENERIC=5,
+            Q4_WG_PER_CU=6, MOE_TOPK=7, MOE_DOWN=8)
 
 
 _lib = None
@@ -91,6 +100,8 @@ def lib():
                                          _i64, _P, C.c_size_t, C.POINTER(_Debug), _P]),
             "moe_layer_decode": (C.c_int, [C.POINTER(_Layer), _P, _i64, _i32, _P, _i64, _P,
                                            _P, _P, C.c_size_t, _P]),
+            "mmv_set_path": (C.c_int, [C.c_int, C.c_int]),
+            "mmv_get_path": (C.c_int, [C.c_int]),
             "mmv_probe_slots": (C.c_int, []),
             "mmv_stream_read": (C.c_int, [_P, C.c_size_t, _P, _P]),
         }
@@ -108,6 +119,17 @@ def lib():
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def set_path(name: str, value: int) -> int:
+    """Force a kernel variant (include/moe_matvec_testing.h; tests and
+    measurements only); 0 restores the automatic choice.  Returns the previous
+    value."""
+    return int(lib().mmv_set_path(PATH[name], int(value)))
+
+
+def get_path(name: str) -> int:
+    return int(lib().mmv_get_path(PATH[name]))
 
 
 def _stream(stream):
@@ -347,8 +369,11 @@ def moe_workspace_bytes(layer: MoeLayer, B: int) -> int:
 def moe_mul_mat_id(layer: MoeLayer, x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor,
                    shared_w: torch.Tensor | None = None, out=None, workspace=None,
                    debug: dict | None = None, stream=None):
-    """Routed + shared expert FFN.  debug may hold tensors h [P, I] f32, unique,
-    offsets, pairs, n_unique (int32) to receive staged results."""
+    """Routed + shared expert FFN.  debug may hold device tensors that receive
+    staged results (P = B*k + B with a shared expert, else B*k): h, gate_out,
+    up_out [P, I] f32; down_out [P, H] f32; x_q8 (q8_1_bytes(H, B) bytes) and
+    h_q8 (q8_1_bytes(I, P) bytes) planar Q8_1; unique, offsets, pairs,
+    n_unique int32."""
     x2 = x.unsqueeze(0) if x.dim() == 1 else x
     B = x2.shape[0]
     if out is None:
@@ -358,8 +383,10 @@ def moe_mul_mat_id(layer: MoeLayer, x: torch.Tensor, ids: torch.Tensor, weights:
                                 device=x.device)
     dbg = None
     if debug is not None:
-        dbg = _Debug(*(_ptr(debug.get(n)) for n in ("h", "unique", "offsets", "pairs",
-                                                    "n_unique")))
+        unknown = set(debug) - set(_DEBUG_FIELDS)
+        if unknown:
+            raise ValueError(f"unknown debug fields {sorted(unknown)}")
+        dbg = _Debug(*(_ptr(debug.get(n)) for n in _DEBUG_FIELDS))
     y2 = out.unsqueeze(0) if out.dim() == 1 else out
     _check("moe_mul_mat_id", lib().moe_mul_mat_id(
         C.byref(layer._s), x2.data_ptr(), _ld(x2), B, ids.data_ptr(), weights.data_ptr(),

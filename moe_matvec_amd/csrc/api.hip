@@ -1,7 +1,10 @@
 // api.hip -- the extern "C" entry points of moe_matvec.h: validate on the
 // host (validate.cpp, no device access), then enqueue on the caller's
 // stream.  No allocation, no synchronization, no host reads of device data.
+#include <atomic>
+
 #include "../../include/moe_matvec.h"
+#include "../../include/moe_matvec_testing.h"
 #include "launch.hpp"
 #include "layout.hpp"
 #include "validate.hpp"
@@ -18,7 +21,17 @@ int hip_status(hipError_t e) {
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// kernel-variant switches (moe_matvec_testing.h): 0 = automatic
+std::atomic<int> g_path[MMV_PATH_COUNT];
+
 }  // namespace
+
+namespace mmv {
+int path_switch(int which) {
+  if (which < 0 || which >= MMV_PATH_COUNT) return 0;
+  return g_path[which].load(std::memory_order_relaxed);
+}
+}  // namespace mmv
 
 extern "C" {
 
@@ -28,7 +41,7 @@ const char *mmv_status_str(int status) {
     case MMV_E_NULL: return "a required pointer is NULL";
     case MMV_E_SHAPE: return "a size is out of range or not a multiple of the block size";
     case MMV_E_ALIGN: return "a pointer or leading dimension is misaligned";
-    case MMV_E_BATCH: return "batch rows outside 1..8";
+    case MMV_E_BATCH: return "batch rows outside 1..8 (MoE entry points: 1..64)";
     case MMV_E_TOPK: return "top_k outside 1..min(E, 16)";
     case MMV_E_WORKSPACE: return "workspace missing or too small";
     case MMV_E_ALIAS: return "an output overlaps an input";
@@ -39,6 +52,13 @@ const char *mmv_status_str(int status) {
 }
 
 int mmv_last_hip_error(void) { return g_last_hip; }
+
+int mmv_set_path(int which, int value) {
+  if (which < 0 || which >= MMV_PATH_COUNT) return MMV_E_ARG;
+  return g_path[which].exchange(value, std::memory_order_relaxed);
+}
+
+int mmv_get_path(int which) { return mmv::path_switch(which); }
 
 size_t mmv_q8_1_bytes(int32_t K, int32_t B) {
   if (K < 32 || K % 32 != 0 || B < 1) return 0;

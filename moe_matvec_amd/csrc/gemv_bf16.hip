@@ -16,9 +16,6 @@
 //    become one bf16 hi/lo matrix-core operand; the weights still arrive in
 //    contiguous 1 KiB wave loads and are re-laid out through LDS.  Rows
 //    agree bit for bit for every B >= 2, and with B = 1 within ~1e-6.
-#include <stdio.h>
-#include <stdlib.h>
-
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -417,8 +414,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemv_bf16_ml(
 #pragma unroll
   for (int t = 0; t < TILES; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
   // NCH > 0: every chunk unrolled, so no register is carried around a loop
-  // (a copy of a register that a load is still filling would wait for it)
-#pragma unroll
+  // (a copy of a register that a load is still filling would wait for it);
+  // NCH == 0: a loop over the run-time chunk count
+  constexpr int kChunkUnroll = NCH > 0 ? NCH : 1;
+#pragma unroll kChunkUnroll
   for (int i0 = 0; i0 < (NCH ? NCH : nch); i0 += PD) {
 #pragma unroll
     for (int p = 0; p < PD; ++p) {
@@ -503,22 +502,6 @@ hipError_t launch_ni(const Bf16Args &a) {
   return hipGetLastError();
 }
 
-// tuning knobs for experiments: MMV_BF16_R (rows per wave), MMV_BF16_WPB
-// (waves per workgroup), MMV_BF16_XL (waves per workgroup of the LDS-x
-// kernel; -1: off), MMV_BF16_ML (matrix-core kernel shape); each prints one
-// line the first time it is used
-int env_knob(const char *name) {
-  const char *v = getenv(name);
-  if (!v || !*v) return 0;
-  static thread_local bool printed[4] = {false, false, false, false};
-  const int idx = name[9] == 'R' ? 0 : (name[9] == 'W' ? 1 : (name[9] == 'X' ? 2 : 3));
-  if (!printed[idx]) {
-    fprintf(stderr, "[moe_matvec] %s=%s\n", name, v);
-    printed[idx] = true;
-  }
-  return atoi(v);
-}
-
 template <int B, int NI>
 hipError_t dispatch_ni(const Bf16Args &a, int R, int WPB) {
   // all R * NI weight loads of a lane sit in registers (4 VGPRs each):
@@ -564,8 +547,8 @@ hipError_t launch_mlu(const Bf16Args &a) {
   return launch_ml<B, RT, NW, PD, TH>(a);
 }
 
-// B >= 2 and K % 512 == 0.  MMV_BF16_ML (experiments) = 10000 * RT +
-// 1000 * NW + 100 * PD + TH, + 1000000 for the chunk loop instead of the
+// B >= 2 and K % 512 == 0.  The MMV_PATH_BF16_ML switch (tests) = 10000 * RT
+// + 1000 * NW + 100 * PD + TH, + 1000000 for the chunk loop instead of the
 // unrolled chunks.  Default: 16-row workgroups of 8 waves, two chunks in
 // flight (2560 x 2560 / 19456 x 2560 / 2560 x 9728 at B = 8: 6.0 / 21 /
 // 15.7 us against 8.2 / 26 / 27.7 us for FMAs with x in LDS or the operand-
@@ -580,7 +563,7 @@ hipError_t dispatch_ml(const Bf16Args &a, int knob) {
     case 1088208: return launch_ml<B, 8, 8, 2, 8>(a);
     case 1164216: return launch_ml<B, 16, 4, 2, 16>(a);
   }
-  return hipErrorInvalidValue;
+  return launch_mlu<B, 16, 8, 2, 16>(a);  // an unknown shape code: the default
 }
 
 // slab length: x of B rows in at most 80 KiB of LDS (SL chunks of 512)
@@ -607,16 +590,16 @@ hipError_t dispatch_xl(const Bf16Args &a, int WPB) {
 template <int B>
 hipError_t dispatch_b(const Bf16Args &a) {
   if constexpr (B >= 2) {
-    if (a.K % 512 == 0) return dispatch_ml<B>(a, env_knob("MMV_BF16_ML"));
-    // other K: operand-layout loads, KS = MMV_BF16_WPB waves per 16-row tile
-    const int kw = env_knob("MMV_BF16_WPB");
+    if (a.K % 512 == 0) return dispatch_ml<B>(a, path_switch(MMV_PATH_BF16_ML));
+    // other K: operand-layout loads, KS waves per 16-row tile
+    const int kw = path_switch(MMV_PATH_BF16_WAVES);
     const int KS = kw ? kw : 8;
     if (KS >= 16) return launch_mfma<B, 16, 8>(a);
     if (KS >= 8) return launch_mfma<B, 8, 8>(a);
     return launch_mfma<B, 4, 8>(a);
   } else {
-    const int kr = env_knob("MMV_BF16_R"), kw = env_knob("MMV_BF16_WPB");
-    const int kx = env_knob("MMV_BF16_XL");
+    const int kr = path_switch(MMV_PATH_BF16_ROWS), kw = path_switch(MMV_PATH_BF16_WAVES);
+    const int kx = path_switch(MMV_PATH_BF16_XL);
     if (a.K % 512 == 0) {
       // x staged once per workgroup in LDS: measured faster for long rows
       // (2560 x 9728: 4 waves per workgroup) and for many rows (19456 x 2560:

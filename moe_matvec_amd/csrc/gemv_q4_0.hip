@@ -18,8 +18,7 @@
 //  - group partials are combined by a fixed xor butterfly; the per-row
 //    arithmetic is the same for every B, so rows of a batched call match
 //    single-row calls bit for bit.
-#include <stdio.h>
-#include <stdlib.h>
+#include <atomic>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -399,29 +398,20 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
 
 namespace {
 
+// compute units of the current device, queried once per device (a data
+// race between first calls only writes the same value twice)
 int cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cache[dev]) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
-}
-
-int q4_knob(const char *name) {
-  const char *v = getenv(name);
-  if (!v || !*v) return 0;
-  static thread_local bool printed = false;
-  if (!printed) {
-    fprintf(stderr, "[moe_matvec] %s=%s\n", name, v);
-    printed = true;
-  }
-  return atoi(v);
+  return n;
 }
 
 }  // namespace
@@ -433,7 +423,7 @@ static hipError_t launch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
   constexpr int rows_wg = 4 * RP * (64 / G);
   const int ngroups = (N + rows_wg - 1) / rows_wg;
   // workgroups per CU: each stages x once, so fewer when quantizing here
-  const int knob = q4_knob("MMV_Q4_WG_PER_CU");
+  const int knob = path_switch(MMV_PATH_Q4_WG_PER_CU);
   const int per_cu = knob ? knob : (X ? 2 : 4);
   const int blocks = min(ngroups, per_cu * cu_count());
   const size_t lds = xstage_bytes(B, K);
@@ -458,7 +448,8 @@ static hipError_t launch_q4_t(const uint8_t *qs, const uint16_t *d, int N, int K
   return hipGetLastError();
 }
 
-// Rows per lane group (2, 4, 6 or 8; MMV_Q4_RP overrides): 4 by default.
+// Rows per lane group (2, 4, 6 or 8; the MMV_PATH_Q4_RP switch overrides):
+// 4 by default.
 // Measured on the 4096 x 4096 and 11008 x 4096 shapes at B = 1, four rows
 // per lane group (16 per workgroup) beat both two (twice the workgroups,
 // each repeating the activation staging) and six or eight (fewer waves to
@@ -473,7 +464,7 @@ static hipError_t launch_q4_rp(const uint8_t *qs, const uint16_t *d, int N, int 
   // 4096^2 + 11008 x 4096 with a Q8_1 buffer, us per pair, RP 4 -> 2:
   // B = 5 18.7 -> 18.4, B = 6 20.2 -> 19.3, B = 8 22.7 -> 22.1; B = 4 level;
   // RP 8 at B = 8: 26.1)
-  int rp = q4_knob("MMV_Q4_RP");
+  int rp = path_switch(MMV_PATH_Q4_RP);
   if (rp == 0) rp = B >= 5 ? 2 : cmin(4, kMaxRp);
   if constexpr (kMaxRp >= 8)
     if (rp > 6) return launch_q4_t<B, G, 8, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
@@ -484,223 +475,14 @@ static hipError_t launch_q4_rp(const uint8_t *qs, const uint16_t *d, int N, int 
   return launch_q4_t<B, G, 2, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
 }
 
-// ---- B >= 2 on the int8 matrix cores ------------------------------------
-// At B = 8 eight v_dot4 per block and row for every x row make the VALU, not
-// HBM, the bound.  Here v_mfma_i32_16x16x32_i8 takes a 16-row x one-block
-// tile: A = the weight codes (lane l: row l % 16, dword l / 16 of the block:
-// its 4 low nibbles = codes 4g..4g+3 and 4 high nibbles = codes 16+4g..,
-// unpacked to 8 bytes), B = the Q8_1 codes of x at the same 8 positions
-// (column n = x row n, zero for n >= B).  The int32 result is the exact
-// dot(code, q) of every (row, x row) pair; I = dot - 8 * sum(q) and the
-// scales follow in fp32 (acc += d_w * d_x * I), block after block.  A
-// workgroup (8 waves) stages x once (codes in operand order, scales, integer
-// sums) and walks 16-row tiles blockIdx.x, + gridDim.x, ...: each tile's
-// codes and scales arrive in contiguous 1 KiB wave loads (the next tile's in
-// flight while this one is multiplied) and are re-laid out through LDS;
-// wave w takes blocks w, w + 8, ... of the row; partial tiles are summed in
-// LDS in wave order.  Column b depends on x row b alone: rows agree bit for
-// bit for every B >= 2.  K = 2048 or 4096, scale plane 16-byte aligned.
-constexpr int kQmRows = 16;
-constexpr int kQmChunk = 64;                     // blocks per chunk (1 KiB of codes per row)
-constexpr int kQmPitch = kQmChunk * 16 + 16;     // LDS row pitch of a code chunk
-
-template <int B, int NCH>
-constexpr size_t qm_lds_bytes() {
-  constexpr size_t nb = (size_t)NCH * kQmChunk;
-  return nb * B * 32 + nb * B * 8 + (size_t)NCH * kQmRows * kQmPitch +
-         (size_t)NCH * kQmChunk * kQmRows * 2 + (size_t)8 * kQmRows * B * 4;
-}
-
-typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
-
-template <int B, int NCH>
-__global__ __launch_bounds__(512) void k_gemv_q4_0_mf(const uint8_t *__restrict__ qs,
-                                                      const uint16_t *__restrict__ dw, int N,
-                                                      const uint8_t *__restrict__ Xq,
-                                                      float *__restrict__ Y, int64_t ldy) {
-  constexpr int nb = NCH * kQmChunk, K = nb * 32;
-  constexpr int XT = B * nb * 2;                 // 16-byte code chunks of x
-  constexpr int CPT = (XT + 511) / 512;
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t *ximg = reinterpret_cast<uint32_t *>(smem);           // [nb][B][4][2]
-  uint32_t *xsd = reinterpret_cast<uint32_t *>(smem + (size_t)nb * B * 32);  // [nb][B][2]
-  uint8_t *abuf = smem + (size_t)nb * B * 40;                    // [NCH][16][pitch]
-  uint16_t *dbuf = reinterpret_cast<uint16_t *>(abuf + NCH * kQmRows * kQmPitch);  // [NCH][64][16]
-  float *part = reinterpret_cast<float *>(dbuf + NCH * kQmChunk * kQmRows);        // [8][16][B]
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int ntiles = (N + kQmRows - 1) / kQmRows;
-
-  // x codes and {d, s} words first (loads complete in issue order)
-  const uint32_t *xds_g = reinterpret_cast<const uint32_t *>(Xq + (size_t)B * K);
-  i32x4 xc[CPT];
-  uint32_t xw[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = min(t + 512 * i, XT - 1);
-    xc[i] = *reinterpret_cast<const i32x4 *>(Xq + (size_t)16 * c);
-    xw[i] = xds_g[c >> 1];
-  }
-  // one tile's weights in flight: wave w rows w and w + 8 (1 KiB per chunk
-  // each), threads 0..127 the scales (row t / 8, 8 blocks each)
-  u32x4 wreg[NCH][2], dreg[NCH];
-  auto issue = [&](int tile) {
-    const int rb = tile * kQmRows;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t row = min(rb + w + 8 * j, N - 1);
-        wreg[c][j] = load_stream16(qs + (row * nb + c * kQmChunk) * 16 + 16 * lane);
-      }
-      const int64_t drow = min(rb + ((t & 127) >> 3), N - 1);
-      dreg[c] = load_stream16(dw + drow * nb + c * kQmChunk + 8 * (t & 7));
-    }
-  };
-  issue(blockIdx.x);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // x to LDS: chunk c = half h of block j of row b -> dwords (j, b, g, h);
-  // the block's integer code sum from the lane pair holding its two halves
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = t + 512 * i;
-    int sum = sdot4(xc[i].x, 0x01010101, 0);
-    sum = sdot4(xc[i].y, 0x01010101, sum);
-    sum = sdot4(xc[i].z, 0x01010101, sum);
-    sum = sdot4(xc[i].w, 0x01010101, sum);
-    sum += (int)dpp_u32<kDppQuadXor1>((uint32_t)sum);
-    uint32_t dsv = xw[i];
-    asm volatile("" : "+v"(dsv));
-    if (c < XT) {  // uniform over each lane pair: XT is even
-      const int b = c / (2 * nb), rem = c - b * 2 * nb, j = rem >> 1, h = rem & 1;
-      uint32_t *dst = ximg + ((size_t)(j * B + b) * 4) * 2 + h;
-      dst[0] = (uint32_t)xc[i].x;
-      dst[2] = (uint32_t)xc[i].y;
-      dst[4] = (uint32_t)xc[i].z;
-      dst[6] = (uint32_t)xc[i].w;
-      if (h == 0) {
-        xsd[(j * B + b) * 2 + 0] = __float_as_uint(f16_bits_to_f32((uint16_t)(dsv & 0xFFFFu)));
-        xsd[(j * B + b) * 2 + 1] = (uint32_t)sum;
-      }
-    }
-  }
-
-  const int bcol = min(n, B - 1);
-  const uint32_t keep = n < B ? 0xFFFFFFFFu : 0u;
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    // this tile's weights to LDS: codes row-major, scales to [block][row]
-    // (the previous tile's products are done: the barrier that ended it)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        *reinterpret_cast<u32x4 *>(abuf + (c * kQmRows + w + 8 * j) * kQmPitch + 16 * lane) =
-            wreg[c][j];
-      if (t < 128) {
-        const int r = t >> 3, b0 = 8 * (t & 7);
-        const uint32_t dv[4] = {dreg[c].x, dreg[c].y, dreg[c].z, dreg[c].w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          dbuf[(c * kQmChunk + b0 + q) * kQmRows + r] = (uint16_t)(dv[q >> 1] >> (16 * (q & 1)));
-      }
-    }
-    __syncthreads();
-    if (tile + (int)gridDim.x < ntiles) issue(tile + gridDim.x);
-    __builtin_amdgcn_sched_barrier(0);
-
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll 4  // (fully unrolled, every LDS read is hoisted: 220 VGPRs)
-      for (int s = 0; s < kQmChunk / 8; ++s) {
-        const int j = w + 8 * s, J = c * kQmChunk + j;
-        const uint32_t a32 = *reinterpret_cast<const uint32_t *>(
-            abuf + (c * kQmRows + n) * kQmPitch + 16 * j + 4 * g);
-        const uint64_t av =
-            (uint64_t)(a32 & 0x0F0F0F0Fu) | ((uint64_t)((a32 >> 4) & 0x0F0F0F0Fu) << 32);
-        const uint2 xv =
-            *reinterpret_cast<const uint2 *>(ximg + ((size_t)(J * B + bcol) * 4 + g) * 2);
-        const uint64_t bv = (uint64_t)(xv.x & keep) | ((uint64_t)(xv.y & keep) << 32);
-        const i32x4v z = {0, 0, 0, 0};
-        const i32x4v D = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)av, (long)bv, z, 0, 0, 0);
-        const uint2 dwv =
-            *reinterpret_cast<const uint2 *>(dbuf + (c * kQmChunk + j) * kQmRows + 4 * g);
-        const uint2 xs = *reinterpret_cast<const uint2 *>(xsd + (J * B + bcol) * 2);
-        const float dx = __uint_as_float(xs.x);
-        const int s8 = 8 * (int)xs.y;
-        acc.x = fmaf(f16_bits_to_f32((uint16_t)dwv.x) * dx, (float)(D.x - s8), acc.x);
-        acc.y = fmaf(f16_bits_to_f32((uint16_t)(dwv.x >> 16)) * dx, (float)(D.y - s8), acc.y);
-        acc.z = fmaf(f16_bits_to_f32((uint16_t)dwv.y) * dx, (float)(D.z - s8), acc.z);
-        acc.w = fmaf(f16_bits_to_f32((uint16_t)(dwv.y >> 16)) * dx, (float)(D.w - s8), acc.w);
-      }
-    }
-    if (n < B) {
-      part[(w * kQmRows + 4 * g + 0) * B + n] = acc.x;
-      part[(w * kQmRows + 4 * g + 1) * B + n] = acc.y;
-      part[(w * kQmRows + 4 * g + 2) * B + n] = acc.z;
-      part[(w * kQmRows + 4 * g + 3) * B + n] = acc.w;
-    }
-    __syncthreads();
-    if (t < kQmRows * B) {
-      const int r = t / B, b = t - r * B, row = tile * kQmRows + r;
-      float v = part[r * B + b];
-#pragma unroll
-      for (int q = 1; q < 8; ++q) v += part[(q * kQmRows + r) * B + b];
-      if (row < N) Y[(int64_t)b * ldy + row] = v;
-    }
-  }
-}
-
-int q4_mf_grid(int ntiles) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      cus = v > 0 ? v : 256;
-    else
-      cus = 256;
-  }
-  int per = q4_knob("MMV_Q4_MF_WPC");  // experiments: workgroups per CU
-  if (per <= 0) per = 1;                // measured best: ~2.7 tiles per workgroup at 11008 rows
-  return ntiles < per * cus ? ntiles : per * cus;
-}
-
-template <int B, int NCH>
-static hipError_t launch_q4_mf(const uint8_t *qs, const uint16_t *d, int N, const uint8_t *Xq,
-                               float *Y, int64_t ldy, hipStream_t s) {
-  constexpr size_t lds = qm_lds_bytes<B, NCH>();
-  if (lds > 65536) {
-    static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_gemv_q4_0_mf<B, NCH>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (raised != hipSuccess) return raised;
-  }
-  const int ntiles = (N + kQmRows - 1) / kQmRows;
-  hipLaunchKernelGGL((k_gemv_q4_0_mf<B, NCH>), dim3(q4_mf_grid(ntiles)), dim3(512), lds, s, qs,
-                     d, N, Xq, Y, ldy);
-  return hipGetLastError();
-}
-
 template <int B>
 static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
                               const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                               int64_t ldy, hipStream_t s) {
   const int nb = K / 32;
   constexpr int RP = B <= 2 ? 2 : 4;
-  if constexpr (B >= 2) {
-    // quantized x given, MMV_Q4_MF=1: the int8 matrix cores.  Off by
-    // default: at B = 8 they measured level with the dot4 kernel at 4096 x
-    // 4096 (6.4 us) and slower at 11008 x 4096 (13.1 against 12.1 us): both
-    // are bound by each workgroup's x staging and load latency, not the ALU
-    if (Xq && !X && (nb == 64 || nb == 128) && (reinterpret_cast<uintptr_t>(d) & 15) == 0 &&
-        q4_knob("MMV_Q4_MF") > 0)
-      return nb == 64 ? launch_q4_mf<B, 1>(qs, d, N, Xq, Y, ldy, s)
-                      : launch_q4_mf<B, 2>(qs, d, N, Xq, Y, ldy, s);
-  }
   // whole blocks per lane: every load of a row group in flight together
-  if (q4_knob("MMV_Q4_GENERIC") <= 0) {
+  if (path_switch(MMV_PATH_Q4_GENERIC) <= 0) {
     if (nb == 16) return launch_q4_rp<B, 16, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 32) return launch_q4_rp<B, 32, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 64) return launch_q4_rp<B, 64, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);

@@ -7,8 +7,12 @@
 #include <stdint.h>
 
 #include "../../include/moe_matvec.h"
+#include "../../include/moe_matvec_testing.h"
 
 namespace mmv {
+
+// value of a kernel-variant switch (moe_matvec_testing.h); 0 = automatic
+int path_switch(int which);
 
 hipError_t run_gemv_bf16(const uint16_t *W, int N, int K, int64_t ldw,
                          const float *X, int64_t ldx, int B, float *Y, int64_t ldy,

@@ -39,9 +39,6 @@
 //  Every row's result is thus the same bits for every B.
 // A grid-wide barrier inside one kernel measured slower than a launch
 // boundary on this GPU, so the phases stay separate launches.
-#include <stdio.h>
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "common.hpp"
@@ -745,7 +742,12 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
       const int nl = 8 * wv + 4 * hh + q;
       if (sub == 0) {
         hbuf[r][nl] = h;
-        if (a.has_dbg && a.dbg.h) a.dbg.h[(int64_t)pairmap[r] * I + tile * 32 + nl] = h;
+        if (a.has_dbg) {
+          const int64_t o = (int64_t)pairmap[r] * I + tile * 32 + nl;
+          if (a.dbg.h) a.dbg.h[o] = h;
+          if (a.dbg.gate_out) a.dbg.gate_out[o] = gv;
+          if (a.dbg.up_out) a.dbg.up_out[o] = uv;
+        }
       }
     }
   };
@@ -828,6 +830,16 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
       hv.ds[bi * 2 + 0] = qb.d16;
       hv.ds[bi * 2 + 1] = qb.s16;
       hv.dq[bi] = i32x2{(int32_t)__float_as_uint(f16_bits_to_f32(qb.d16)), qb.qsum};
+    }
+    if (a.has_dbg && a.dbg.h_q8) {  // the same planar layout as the workspace copy
+      uint8_t *dq8 = static_cast<uint8_t *>(a.dbg.h_q8);
+      *reinterpret_cast<uint32_t *>(dq8 + (size_t)p * I + tile * 32 + 4 * s) = qb.codes;
+      if (s == 0) {
+        uint16_t *dds = reinterpret_cast<uint16_t *>(dq8 + (size_t)a.P * I);
+        const size_t bi = (size_t)p * ntiles + tile;
+        dds[bi * 2 + 0] = qb.d16;
+        dds[bi * 2 + 1] = qb.s16;
+      }
     }
   }
 }
@@ -1347,6 +1359,12 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
   }
 
   __syncthreads();
+  if (a.has_dbg && a.dbg.down_out) {  // each (output row, pair) product, unweighted
+    for (int i = t; i < 4 * P; i += 64 * NWV) {
+      const int qq = i / P, p = i - qq * P, r = blockIdx.x * 4 + qq;
+      if (r < H) a.dbg.down_out[(int64_t)p * H + r] = s_dot[qq][p];
+    }
+  }
   // each row's pairs: lane j of a 16-lane group takes slot j (zero past k),
   // the products w * dot summed by the 16-lane tree, then the shared term
   // (down_combine_tree is the same sum, written out)
@@ -1543,6 +1561,13 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
   float v = down_combine_tree(pr);
   if (has_sh) v = fmaf(a.shared_w ? a.shared_w[b] : 1.0f, dsh, v);
   if (n < H) a.Y[(int64_t)b * a.ldy + n] = v;
+  if (a.has_dbg && a.dbg.down_out && n < H) {  // each pair's product, unweighted
+    for (int j = 0; j < k; ++j) {
+      const int e = a.ids[b * k + j];
+      a.dbg.down_out[(int64_t)(b * k + j) * H + n] = (e >= 0 && e < E) ? d[j] : 0.0f;
+    }
+    if (has_sh) a.dbg.down_out[(int64_t)(Bk + b) * H + n] = dsh;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1726,33 +1751,6 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_rows(MoeArgs a) {
 
 namespace {
 
-// MMV_MOE_TOPK_KERNEL=1: top-k and row lists in a kernel of their own;
-// =0: top-k in every gate/up workgroup; unset: by B.  Prints one line the
-// first time it is read.  Returns 1, -1 or 0 (unset).
-int moe_topk_knob() {
-  const char *v = getenv("MMV_MOE_TOPK_KERNEL");
-  if (!v || !*v) return 0;
-  static bool printed = false;
-  if (!printed) {
-    fprintf(stderr, "[moe_matvec] MMV_MOE_TOPK_KERNEL=%s\n", v);
-    printed = true;
-  }
-  return atoi(v) ? 1 : -1;
-}
-
-// MMV_MOE_DOWN=1: the one-kernel down projection at every B; =2: by expert
-// at every B; unset: by B.  Prints one line the first time it is read.
-int moe_down_knob() {
-  const char *v = getenv("MMV_MOE_DOWN");
-  if (!v || !*v) return 0;
-  static bool printed = false;
-  if (!printed) {
-    fprintf(stderr, "[moe_matvec] MMV_MOE_DOWN=%s\n", v);
-    printed = true;
-  }
-  return atoi(v);
-}
-
 MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
                   const int32_t *ids, const float *weights, const float *shared_w, float *Y,
                   int64_t ldy, uint8_t *ws, const mmv_moe_debug *dbg) {
@@ -1772,7 +1770,7 @@ MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
   a.P = B * L.top_k + (has_sh ? B : 0);
   a.routed_shared = has_sh ? 1 : 0;
   a.has_dbg = dbg != nullptr;
-  a.dbg = dbg ? *dbg : mmv_moe_debug{nullptr, nullptr, nullptr, nullptr, nullptr};
+  a.dbg = dbg ? *dbg : mmv_moe_debug{};
   a.logits = reinterpret_cast<float *>(ws + lay.logits);
   a.dpart = reinterpret_cast<float *>(ws + lay.dpart);
   a.nrows = B;
@@ -1806,8 +1804,10 @@ constexpr int kDownSplitMinB = 3;
 
 template <int B, int TI>
 void launch_down(const MoeArgs &a, hipStream_t s) {
-  const int knob = moe_down_knob();
-  if (knob == 2 || (knob != 1 && B >= kDownSplitMinB)) {
+  const int knob = path_switch(MMV_PATH_MOE_DOWN);
+  // the one-kernel path stages Q8_1(h) of all P pairs in LDS: only where it fits
+  const bool fits = (int64_t)a.P * a.L.inter <= kMaxDownStageElems;
+  if (!fits || knob == 2 || (knob != 1 && B >= kDownSplitMinB)) {
     const int slots = min(a.L.n_experts, B * a.L.top_k) + (a.L.sh_down_qs ? 1 : 0);
     const int ntile = (a.L.hidden + kDownPartRows - 1) / kDownPartRows;
     hipLaunchKernelGGL((k_moe_down_part<B, TI>), dim3(slots * ntile), dim3(256), 0, s, a);
@@ -1912,6 +1912,11 @@ hipError_t run_moe_experts(const mmv_moe_layer &L, const float *X, int64_t ldx, 
                            float *Y, int64_t ldy, uint8_t *ws, const mmv_moe_debug *dbg,
                            hipStream_t s) {
   const MoeArgs a = make_args(L, X, ldx, B, ids, weights, shared_w, Y, ldy, ws, dbg);
+  if (dbg && dbg->x_q8) {  // Q8_1(x) by the routine the gate/up workgroups stage x with
+    const hipError_t e = run_quantize_q8_1(X, L.hidden, ldx, B,
+                                           static_cast<uint8_t *>(dbg->x_q8), s);
+    if (e != hipSuccess) return e;
+  }
   if (B > MMV_MAX_BATCH) {
     launch_experts_rows(a, s);
     return hipGetLastError();
@@ -1970,7 +1975,7 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
     launch_experts_rows(a, s);
     return hipGetLastError();
   }
-  const int knob = moe_topk_knob();
+  const int knob = path_switch(MMV_PATH_MOE_TOPK);
   a.topk_in_k2 = knob > 0 ? 0 : (knob < 0 ? 1 : (B <= 2 ? 1 : 0));
   a.gather_ready = a.topk_in_k2 ? 0 : 1;
   switch (B) {

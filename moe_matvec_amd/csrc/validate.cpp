@@ -28,9 +28,6 @@ size_t span(int64_t rows, int64_t ld, int64_t cols, size_t elem) {
 }
 bool bad_batch(int32_t B) { return B < 1 || B > MMV_MAX_BATCH; }
 bool bad_moe_batch(int32_t B) { return B < 1 || B > MMV_MOE_MAX_BATCH; }
-int64_t moe_pairs(const mmv_moe_layer *L, int32_t B) {
-  return (int64_t)B * L->top_k + (L->sh_gate_qs ? B : 0);
-}
 
 template <int NO, int NI>
 bool any_overlap(const Range (&outs)[NO], const Range (&ins)[NI]) {
@@ -243,11 +240,9 @@ int check_mul_mat_id(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_
   if (bad_moe_batch(B)) return MMV_E_BATCH;
   const int32_t H = L->hidden, k = L->top_k;
   if (ldx < H || ldy < H || ldx > kMaxLd || ldy > kMaxLd) return MMV_E_SHAPE;
-  // x of at most 8 rows is staged per gate/up workgroup; only B <= 8 may
-  // stage Q8_1(h) of every pair in the down projection's LDS
+  // x of at most 8 rows is staged per gate/up workgroup (the down projection
+  // stages Q8_1(h) on chip only where it fits, else it runs by expert)
   if ((int64_t)std::min<int32_t>(B, MMV_MAX_BATCH) * H > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
-  if (B <= MMV_MAX_BATCH && moe_pairs(L, B) * (int64_t)L->inter > kMaxDownStageElems)
-    return MMV_E_SHAPE;
   if (!aligned(X, 16) || ldx % 4 != 0 || !aligned(ids, 4) || !aligned(weights, 4) ||
       !aligned(shared_w, 4) || !aligned(Y, 4))
     return MMV_E_ALIGN;
@@ -271,11 +266,9 @@ int check_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx, int3
   if (bad_moe_batch(B)) return MMV_E_BATCH;
   const int32_t H = L->hidden, k = L->top_k;
   if (ldx < H || ldy < H || ldx > kMaxLd || ldy > kMaxLd) return MMV_E_SHAPE;
-  // x of at most 8 rows is staged per gate/up workgroup; only B <= 8 may
-  // stage Q8_1(h) of every pair in the down projection's LDS
+  // x of at most 8 rows is staged per gate/up workgroup (the down projection
+  // stages Q8_1(h) on chip only where it fits, else it runs by expert)
   if ((int64_t)std::min<int32_t>(B, MMV_MAX_BATCH) * H > MMV_Q4_MAX_XK) return MMV_E_SHAPE;
-  if (B <= MMV_MAX_BATCH && moe_pairs(L, B) * (int64_t)L->inter > kMaxDownStageElems)
-    return MMV_E_SHAPE;
   if (!aligned(X, 16) || ldx % 4 != 0 || !aligned(ids, 4) || !aligned(weights, 4) ||
       !aligned(Y, 4))
     return MMV_E_ALIGN;

@@ -84,3 +84,99 @@ def check_route(orc, R, X, logits_gpu, ids_gpu, k, E):
             assert gap <= 2 * bound[b].max(), (b, j, gap)
         near += 1
     return near
+
+
+def check_ids_admissible(orc, R, X, ids_gpu, k):
+    """Every row's ids must be a top-k that fp32 rounding of the logits could
+    produce: distinct and in [0, E); each selected logit (float64) at least
+    every unselected one minus twice the forward-error bound; consecutive
+    slots in descending order up to the same margin.  Rows equal to the
+    float64 top-k pass trivially.  Returns (float64 logits, rows whose ids
+    differ from the float64 top-k)."""
+    ref = orc.router_logits(R, X)
+    bound = logit_bound(R, X)
+    E = R.shape[0]
+    ids_ref = orc.topk(ref.astype(np.float32), k)
+    differ = []
+    for b in range(X.shape[0]):
+        sel = ids_gpu[b].astype(np.int64)
+        assert ((sel >= 0) & (sel < E)).all(), (b, sel)
+        assert len(set(sel.tolist())) == k, (b, sel)
+        if np.array_equal(sel, ids_ref[b]):
+            continue
+        differ.append(b)
+        margin = 2 * bound[b].max()
+        lv = ref[b][sel]
+        rest = np.delete(ref[b], sel)
+        assert rest.size == 0 or lv.min() >= rest.max() - margin, (b, lv.min(), rest.max())
+        assert (np.diff(lv) <= margin).all(), (b, lv)
+    return ref, differ
+
+
+def moe_ref_with_ids(orc, ref, X, ids, logits64):
+    """The oracle's layer output for the given routing (ids taken as given):
+    weights from the float64 logits renormalised over those ids, gate/up,
+    Q8_1(h), down and the combine."""
+    w64 = orc.gate_weights(logits64, ids)
+    B = X.shape[0]
+    if ref.shared_gate_row is not None:
+        z = X.astype(np.float64) @ ref.shared_gate_row.astype(np.float64)
+        s64 = 1.0 / (1.0 + np.exp(-z))
+    else:
+        s64 = np.ones(B)
+    h = ref.gate_up(X, ids)
+    hq, hds = orc.quantize_q8_1(h)
+    return ref.down(hq, hds, ids, w64, s64)
+
+
+# ---------------------------------------------------------------------------
+# interchange blocks (array-of-structures) <-> the library's planar layout
+# ---------------------------------------------------------------------------
+
+def q8_1_to_blocks(codes: np.ndarray, ds: np.ndarray) -> np.ndarray:
+    """Planar Q8_1 (codes int8 [B, K], ds uint16 [B, K/32, 2]) -> 36-byte
+    blocks uint8 [B, K/32, 36]: d, s (fp16, little endian), 32 codes."""
+    B, K = codes.shape
+    nb = K // 32
+    out = np.empty((B, nb, 36), np.uint8)
+    out[:, :, :4] = np.ascontiguousarray(ds.reshape(B, nb, 2)).astype("<u2").view(np.uint8)
+    out[:, :, 4:] = np.ascontiguousarray(codes.reshape(B, nb, 32)).view(np.uint8)
+    return out
+
+
+def q8_1_from_blocks(blocks: np.ndarray):
+    """36-byte Q8_1 blocks uint8 [B, nb, 36] -> planar (codes int8 [B, 32 nb],
+    ds uint16 [B, nb, 2])."""
+    B, nb, _ = blocks.shape
+    ds = np.ascontiguousarray(blocks[:, :, :4]).view("<u2").reshape(B, nb, 2).astype(np.uint16)
+    codes = np.ascontiguousarray(blocks[:, :, 4:]).view(np.int8).reshape(B, nb * 32)
+    return codes, ds
+
+
+def q4_0_to_blocks(qs: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Planar Q4_0 (qs uint8 [N, K/32, 16], d uint16 [N, K/32]) -> 18-byte
+    blocks uint8 [N, K/32, 18]: d (fp16, little endian), 16 code bytes."""
+    N, nb, _ = qs.shape
+    out = np.empty((N, nb, 18), np.uint8)
+    out[:, :, :2] = np.ascontiguousarray(d).astype("<u2").view(np.uint8).reshape(N, nb, 2)
+    out[:, :, 2:] = qs
+    return out
+
+
+def q4_0_from_blocks(blocks: np.ndarray):
+    """18-byte Q4_0 blocks uint8 [N, nb, 18] -> planar (qs uint8 [N, nb, 16],
+    d uint16 [N, nb])."""
+    N, nb, _ = blocks.shape
+    d = np.ascontiguousarray(blocks[:, :, :2]).view("<u2").reshape(N, nb).astype(np.uint16)
+    return np.ascontiguousarray(blocks[:, :, 2:]), d
+
+
+def read_golden_blocks(path):
+    """{name: uint8 array} of the hex lines of a golden block file."""
+    out = {}
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            name, *hexes = line.split()
+            out[name] = np.array([int(h, 16) for h in hexes], np.uint8)
+    return out

@@ -37,3 +37,15 @@ def mm(dev):
     import moe_matvec_amd
     moe_matvec_amd.lib()  # raises if the library is not built: no fallback
     return moe_matvec_amd
+
+
+@pytest.fixture
+def path(mm):
+    """Force kernel variants (moe_matvec_testing.h) for one test:
+    path(NAME=value, ...); every switch returns to automatic afterwards."""
+    def setp(**kw):
+        for name, value in kw.items():
+            mm.set_path(name, value)
+    yield setp
+    for name in mm.PATH:
+        mm.set_path(name, 0)

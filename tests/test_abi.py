@@ -10,14 +10,15 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe_matvec.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if n.endswith(".h")]
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_BATCH, E_TOPK, E_WS, E_ALIAS, E_HIP, E_ARG = (
     0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("if", "defined")))
@@ -216,3 +217,33 @@ def test_argmax_validation(L):
     assert a(A, 5000, 5000, 2, A + 40, Cp, Dp, ws, None) == E_ALIAS            # ids inside Y
     assert a(A, 5000, 5000, 2, Bp, Bp + 4, Dp, ws, None) == E_ALIAS            # vals on ids
     assert a(A, 5000, 5000, 2, Bp, Cp, A + 1024, ws, None) == E_ALIAS          # ws inside Y
+
+
+def test_large_pair_count_times_inter_is_accepted(L):
+    # Q8_1(h) of P = B*k (+B) pairs times I no longer bounds the MoE calls: the
+    # down projection stages it on chip only where it fits and otherwise runs
+    # by expert.  Validation passes the shape checks and stops at the
+    # (deliberately short) workspace, so nothing is launched.
+    big = _layer(top_k=16, inter=1024)
+    for B in (1, 2, 3, 6, 8):
+        need = L.moe_workspace_bytes(C.byref(big), B)
+        assert need > 0
+        r = L.moe_mul_mat_id(C.byref(big), A, 2048, B, Bp, Bp + 0x1000, None, Cp, 2048, Dp,
+                             need - 1, None, None)
+        assert r == E_WS, B
+        r = L.moe_layer_decode(C.byref(big), A, 2048, B, Cp, 2048, None, None, Dp, need - 1,
+                               None)
+        assert r == E_WS, B
+
+
+def test_path_switches(L):
+    # the test-only variant switches: set returns the previous value, unknown
+    # switches are refused, and everything returns to automatic (0)
+    assert L.mmv_get_path(7) == 0
+    assert L.mmv_set_path(7, 1) == 0
+    assert L.mmv_get_path(7) == 1
+    assert L.mmv_set_path(7, 0) == 1
+    assert L.mmv_set_path(99, 1) == E_ARG and L.mmv_set_path(-1, 1) == E_ARG
+    assert L.mmv_get_path(99) == 0
+    for i in range(9):
+        assert L.mmv_get_path(i) == 0

@@ -78,7 +78,7 @@ def test_bf16_batch_invariance_and_determinism(mm, dev):
 
 
 @pytest.mark.parametrize("knob", ["1168216", "1328216", "1168316", "1088208", "1164216"])
-def test_bf16_lds_mfma_variants(mm, orc, dev, monkeypatch, knob):
+def test_bf16_lds_mfma_variants(mm, orc, dev, path, knob):
     # B >= 2, K % 512 == 0: the chunk loop instead of unrolled chunks, 32-row
     # workgroups, three chunks in flight and 8-row tiles give the default's
     # bits (a row's order depends on the waves per workgroup only); 4 waves
@@ -88,9 +88,9 @@ def test_bf16_lds_mfma_variants(mm, orc, dev, monkeypatch, knob):
         W = synth.bf16_weights(N, K, 0, "mlb", N, K, device=dev)
         X = synth.activations(B, K, 0, "mlb", N, K, device=dev)
         y0 = mm.gemv_bf16(W, X)
-        monkeypatch.setenv("MMV_BF16_ML", knob)
+        path(BF16_ML=int(knob))
         y = mm.gemv_bf16(W, X)
-        monkeypatch.delenv("MMV_BF16_ML")
+        path(BF16_ML=0)
         if knob == "1164216":
             assert rel_l2_rows(npc(y), npc(y0)) <= 1e-6
             assert rel_l2_rows(npc(y), orc.gemv_bf16(np16(W), npc(X))) <= BF16_TOL
@@ -98,11 +98,11 @@ def test_bf16_lds_mfma_variants(mm, orc, dev, monkeypatch, knob):
             assert torch.equal(y, y0)
 
 
-@pytest.mark.parametrize("knobs", [dict(MMV_BF16_XL="-1", MMV_BF16_R="1", MMV_BF16_WPB="1"),
-                                   dict(MMV_BF16_XL="-1", MMV_BF16_R="2", MMV_BF16_WPB="4"),
-                                   dict(MMV_BF16_XL="-1", MMV_BF16_R="4", MMV_BF16_WPB="1"),
-                                   dict(MMV_BF16_XL="2"), dict(MMV_BF16_XL="16")])
-def test_bf16_b1_variants_identical(mm, dev, monkeypatch, knobs):
+@pytest.mark.parametrize("knobs", [dict(BF16_XL=-1, BF16_ROWS=1, BF16_WAVES=1),
+                                   dict(BF16_XL=-1, BF16_ROWS=2, BF16_WAVES=4),
+                                   dict(BF16_XL=-1, BF16_ROWS=4, BF16_WAVES=1),
+                                   dict(BF16_XL=2), dict(BF16_XL=16)])
+def test_bf16_b1_variants_identical(mm, dev, path, knobs):
     # every B = 1 variant (x from L1/L2 or staged in LDS, rows per wave, waves
     # per workgroup) sums each row in the same order: all give the same bits
     for N, K in ((1000, 2560), (2560, 9728), (333, 1016), (300, 2048), (257, 4096),
@@ -110,23 +110,21 @@ def test_bf16_b1_variants_identical(mm, dev, monkeypatch, knobs):
         W = synth.bf16_weights(N, K, 0, "var", N, K, device=dev)
         x = synth.activations(1, K, 0, "var", N, K, device=dev)
         y0 = mm.gemv_bf16(W, x)
-        for k, v in knobs.items():
-            monkeypatch.setenv(k, v)
+        path(**knobs)
         y1 = mm.gemv_bf16(W, x)
-        for k in knobs:
-            monkeypatch.delenv(k)
+        path(**{k: 0 for k in knobs})
         assert torch.equal(y0, y1)
 
 
 @pytest.mark.parametrize("ks", ["4", "8", "16"])
-def test_bf16_mfma_split_variants(mm, orc, dev, monkeypatch, ks):
+def test_bf16_mfma_split_variants(mm, orc, dev, path, ks):
     # the B >= 2 path with 4, 8 or 16 waves per 16-row tile
     N, K, B = 100, 1016, 5
     W = synth.bf16_weights(N, K, 0, "mfma", device=dev)
     X = synth.activations(B, K, 0, "mfma", device=dev)
-    monkeypatch.setenv("MMV_BF16_WPB", ks)
+    path(BF16_WAVES=int(ks))
     y = mm.gemv_bf16(W, X)
-    monkeypatch.delenv("MMV_BF16_WPB")
+    path(BF16_WAVES=0)
     assert rel_l2_rows(npc(y), orc.gemv_bf16(np16(W), npc(X))) <= BF16_TOL
 
 
@@ -232,47 +230,6 @@ def test_q4_0_unit_scale_pin_bit_exact(mm, dev):
     assert np.array_equal(npc(y).astype(np.float64), want.numpy())
 
 
-@pytest.mark.parametrize("B", [8, 3])
-def test_q4_0_unit_scale_pin_matrix_cores(mm, dev, monkeypatch, B):
-    # the same exact case through a caller Q8_1 buffer on the int8 matrix
-    # cores (MMV_Q4_MF=1: exact int32 block dots, unit scales)
-    monkeypatch.setenv("MMV_Q4_MF", "1")
-    g = torch.Generator().manual_seed(4)
-    N, K = 333, 4096
-    codes = torch.randint(0, 16, (N, K // 32, 32), generator=g, dtype=torch.uint8)
-    qs = (codes[..., :16] | (codes[..., 16:] << 4)).contiguous()
-    d = torch.ones((N, K // 32), dtype=torch.float16)
-    x = torch.randint(-127, 128, (B, K), generator=g).float()
-    x.view(B, -1, 32)[:, :, 7] = -127.0
-    W = mm.Q4_0(qs.to(dev), d.to(dev))
-    xq = torch.empty(mm.q8_1_bytes(K, B), dtype=torch.uint8, device=dev)
-    y = mm.gemv_q4_0(W, x=x.to(dev), xq=xq)
-    want = x.double() @ (codes.reshape(N, K).double() - 8).T
-    assert np.array_equal(npc(y).astype(np.float64), want.numpy())
-
-
-@pytest.mark.parametrize("N,K,B", [(1000, 4096, 3), (17, 2048, 8), (4097, 4096, 2),
-                                   (33, 4096, 8), (2048, 2048, 5)])
-def test_q4_0_matrix_core_path(mm, orc, dev, monkeypatch, N, K, B):
-    monkeypatch.setenv("MMV_Q4_MF", "1")
-    W, qs, d = _q4(mm, N, K, dev, "mf")
-    X = synth.activations(B, K, 0, "q4mf", N, K, B, device=dev)
-    xq = mm.quantize_q8_1(X)
-    y = mm.gemv_q4_0(W, xq=xq, B=B)
-    torch.cuda.synchronize()
-    q_ref, ds_ref = orc.quantize_q8_1(npc(X))
-    assert rel_l2_rows(npc(y), orc.gemv_q4_0(qs, d, q_ref, ds_ref)) <= Q4_TOL
-    # every B >= 2 gives a row the same bits; the vector-ALU kernel (dot4)
-    # sums the same exact block products in another order
-    for b in range(B):
-        other = X[[b, (b + 1) % B]].contiguous()
-        y2 = mm.gemv_q4_0(W, xq=mm.quantize_q8_1(other), B=2)
-        assert torch.equal(y2[0], y[b])
-    monkeypatch.delenv("MMV_Q4_MF")
-    y_v = mm.gemv_q4_0(W, xq=xq, B=B)
-    assert rel_l2_rows(npc(y_v), npc(y)) <= 1e-6
-
-
 def test_q4_0_batch_invariance(mm, dev):
     N, K = 1500, 4096
     W, _, _ = _q4(mm, N, K, dev, "inv")
@@ -284,12 +241,12 @@ def test_q4_0_batch_invariance(mm, dev):
 
 
 @pytest.mark.parametrize("env", [
-    {"MMV_Q4_RP": "2"}, {"MMV_Q4_RP": "4"}, {"MMV_Q4_RP": "6"}, {"MMV_Q4_RP": "8"},
-    {"MMV_Q4_GENERIC": "1", "MMV_Q4_WG_PER_CU": "1"},
-    {"MMV_Q4_GENERIC": "1", "MMV_Q4_WG_PER_CU": "3"},
-    {"MMV_Q4_GENERIC": "1", "MMV_Q4_WG_PER_CU": "16"},
+    dict(Q4_RP=2), dict(Q4_RP=4), dict(Q4_RP=6), dict(Q4_RP=8),
+    dict(Q4_GENERIC=1, Q4_WG_PER_CU=1),
+    dict(Q4_GENERIC=1, Q4_WG_PER_CU=3),
+    dict(Q4_GENERIC=1, Q4_WG_PER_CU=16),
 ])
-def test_q4_0_grid_variants_identical(mm, dev, monkeypatch, env):
+def test_q4_0_grid_variants_identical(mm, dev, path, env):
     # rows per workgroup, the whole-row kernel versus the grid-stride one:
     # no row's sums change
     for N, K, B in ((4096, 4096, 1), (1100, 512, 8), (515, 2048, 3), (300, 8192, 2),
@@ -297,10 +254,8 @@ def test_q4_0_grid_variants_identical(mm, dev, monkeypatch, env):
         W, _, _ = _q4(mm, N, K, dev, "grid")
         X = synth.activations(B, K, 0, "q4grid", N, device=dev)
         y0 = mm.gemv_q4_0(W, x=X)
-        for k, v in env.items():
-            monkeypatch.setenv(k, v)
+        path(**env)
         y1 = mm.gemv_q4_0(W, x=X)
         y2 = mm.gemv_q4_0(W, xq=mm.quantize_q8_1(X), B=B)
-        for k in env:
-            monkeypatch.delenv(k)
+        path(**{k: 0 for k in env})
         assert torch.equal(y0, y1) and torch.equal(y0, y2)

@@ -5,7 +5,8 @@ import pytest
 import torch
 
 import synth
-from tests._util import build_moe, check_route, np16, npc, rel_l2_rows
+from tests._util import (build_moe, check_ids_admissible, check_route, moe_ref_with_ids, np16,
+                         npc, rel_l2_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +50,10 @@ def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
     ids, w, sw, _ = _route_and_check(mm, orc, layer, ref, X)
 
     P = layer.npairs(B)
-    dbg = dict(h=torch.full((P, I), np.nan, device=dev),
+    nan = lambda *shape: torch.full(shape, np.nan, device=dev)
+    dbg = dict(h=nan(P, I), gate_out=nan(P, I), up_out=nan(P, I), down_out=nan(P, H),
+               x_q8=torch.full((mm.q8_1_bytes(H, B),), 0xEE, dtype=torch.uint8, device=dev),
+               h_q8=torch.full((mm.q8_1_bytes(I, P),), 0xEE, dtype=torch.uint8, device=dev),
                unique=torch.full((B * k,), -1, dtype=torch.int32, device=dev),
                offsets=torch.full((B * k + 1,), -1, dtype=torch.int32, device=dev),
                pairs=torch.full((B * k,), -1, dtype=torch.int32, device=dev),
@@ -67,17 +71,48 @@ def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
     assert np.array_equal(npc(dbg["offsets"])[:U + 1], o_ref)
     assert np.array_equal(npc(dbg["pairs"]), p_ref)
 
-    # gate/up stage: h within tolerance of the oracle (float64 sums)
+    # Q8_1(x) as the gate/up workgroups stage it: bit-exact
+    xq_ref, xds_ref = orc.quantize_q8_1(npc(X))
+    xc, xds = mm.split_q8_1(dbg["x_q8"], B, H)
+    assert np.array_equal(npc(xc), xq_ref) and np.array_equal(np16(xds), xds_ref)
+
+    # gate and up of every pair, each against the oracle's W4A8 product on
+    # the same Q8_1(x): only the fp32 accumulation order differs
+    def mats(p):
+        if p < B * k:
+            e = int(ids_np.ravel()[p])
+            return p // k, (ref.gate_qs[e], ref.gate_d[e]), (ref.up_qs[e], ref.up_d[e]), \
+                (ref.down_qs[e], ref.down_d[e])
+        gq, gd, uq, ud, dq, dd = ref.shared
+        return p - B * k, (gq, gd), (uq, ud), (dq, dd)
+    g_gpu, u_gpu = npc(dbg["gate_out"]), npc(dbg["up_out"])
+    g_ref = np.empty((P, I))
+    u_ref = np.empty((P, I))
+    for p in range(P):
+        b, (gq, gd), (uq, ud), _ = mats(p)
+        g_ref[p] = orc.gemv_q4_0(gq, gd, xq_ref[b:b + 1], xds_ref[b:b + 1])[0]
+        u_ref[p] = orc.gemv_q4_0(uq, ud, xq_ref[b:b + 1], xds_ref[b:b + 1])[0]
+    assert rel_l2_rows(g_gpu, g_ref) <= 1e-5
+    assert rel_l2_rows(u_gpu, u_ref) <= 1e-5
+
+    # h = silu(gate) * up: within tolerance of the oracle (float64 sums)
     h_ref = ref.gate_up(npc(X), ids_np)
     h_gpu = npc(dbg["h"])
     assert rel_l2_rows(h_gpu, h_ref) <= MOE_TOL
-    # Q8_1 epilogue: bit-exact against the oracle quantizer on the GPU's h
+    # Q8_1 epilogue, read through the ABI: bit-exact against the oracle
+    # quantizer on the GPU's h
     hq_ref, hds_ref = orc.quantize_q8_1(h_gpu)
-    raw = npc(ws)
-    hq_gpu = raw[:P * I].view(np.int8).reshape(P, I)
-    hds_gpu = raw[P * I:P * I + 4 * P * (I // 32)].view(np.uint16).reshape(P, I // 32, 2)
+    hc, hds = mm.split_q8_1(dbg["h_q8"], P, I)
+    hq_gpu, hds_gpu = npc(hc), np16(hds)
     assert np.array_equal(hq_gpu, hq_ref)
     assert np.array_equal(hds_gpu, hds_ref)
+
+    # each pair's down product fed the GPU's own Q8_1(h)
+    d_gpu = npc(dbg["down_out"])
+    for p in range(P):
+        _, _, _, (dq, dd) = mats(p)
+        d_ref = orc.gemv_q4_0(dq, dd, hq_gpu[p:p + 1], hds_gpu[p:p + 1])[0]
+        assert rel_l2_rows(d_gpu[p][None], d_ref[None]) <= 1e-5, p
 
     # down stage fed the GPU's own Q8_1(h): only fp32 accumulation differs
     w64, s64 = npc(w).astype(np.float64), npc(sw).astype(np.float64)
@@ -94,9 +129,9 @@ def test_moe_staged_parity(mm, orc, dev, E, H, I, k, B, shared, sgate):
                                        (32, 512, 64, 4, 8), (20, 96, 64, 3, 2),
                                        (512, 2048, 512, 10, 8), (512, 2048, 512, 10, 16),
                                        (64, 512, 64, 6, 64), (96, 1024, 128, 6, 40)])
-def test_moe_layer_decode(mm, orc, dev, monkeypatch, topk_kernel, E, H, I, k, B):
+def test_moe_layer_decode(mm, orc, dev, path, topk_kernel, E, H, I, k, B):
     # "1": top-k and row lists in a kernel of their own; "0": in every gate/up workgroup
-    monkeypatch.setenv("MMV_MOE_TOPK_KERNEL", topk_kernel)
+    path(MOE_TOPK=1 if topk_kernel == "1" else -1)
     layer, ref = build_moe(mm, orc, E, H, I, k, 0, "dec", E, H, I, device=dev)
     X = synth.activations(B, H, 0, "dec", E, B, device=dev)
     ids = torch.empty((B, k), dtype=torch.int32, device=dev)
@@ -107,19 +142,24 @@ def test_moe_layer_decode(mm, orc, dev, monkeypatch, topk_kernel, E, H, I, k, B)
     y2 = mm.moe_layer_decode(layer, X, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
-    out = ref.layer(npc(X))
-    same = [b for b in range(B) if np.array_equal(npc(ids)[b], out["ids"][b])]
-    assert len(same) >= B - 1            # near ties in float64 logits are rare
-    assert rel_l2_rows(npc(y)[same], out["y"][same]) <= MOE_TOL
+    # every row: ids admissible under fp32 rounding of the logits (rows that
+    # differ from the float64 top-k only at near ties), and the output equal
+    # to the oracle's for the ids the GPU chose
+    ids_np = npc(ids)
+    lg64, differ = check_ids_admissible(orc, ref.router, npc(X), ids_np, k)
+    assert len(differ) <= max(1, B // 8), differ     # near ties are rare
+    y_ref = moe_ref_with_ids(orc, ref, npc(X), ids_np, lg64)
+    assert rel_l2_rows(npc(y), y_ref) <= MOE_TOL
+    np.testing.assert_allclose(npc(w), orc.gate_weights(lg64, ids_np), rtol=2e-5, atol=1e-6)
 
 
 @pytest.mark.parametrize("topk_kernel", ["0", "1"])
 @pytest.mark.parametrize("B", [1, 2, 5, 12])
-def test_moe_layer_decode_tied_router_rows(mm, orc, dev, monkeypatch, topk_kernel, B):
+def test_moe_layer_decode_tied_router_rows(mm, orc, dev, path, topk_kernel, B):
     # identical router rows give bit-identical logits: the selected experts and
     # their slot order must follow the lower index among equal logits, in the
     # per-workgroup rank selection (one row) as in the full top-k
-    monkeypatch.setenv("MMV_MOE_TOPK_KERNEL", topk_kernel)
+    path(MOE_TOPK=1 if topk_kernel == "1" else -1)
     E, H, I, k = 64, 512, 64, 8
     t = synth.moe_layer_tensors(E, H, I, 0, "ties", E, device=dev)
     X = synth.activations(B, H, 0, "ties", B, device=dev)
@@ -203,7 +243,7 @@ def test_moe_single_expert_and_no_shared(mm, orc, dev):
     (40, 256, 96, 5, False),      # I = 96: the runtime block loop, no shared expert
     (16, 224, 64, 3, True),       # H not a multiple of 64: a ragged last row tile
 ])
-def test_moe_down_paths_bit_identical(mm, orc, dev, monkeypatch, E, H, I, k, shared):
+def test_moe_down_paths_bit_identical(mm, orc, dev, path, E, H, I, k, shared):
     # the by-expert down projection (+ combine) and the one-kernel one form
     # each pair's product and each row's sum in the same order: same bits
     layer, ref = build_moe(mm, orc, E, H, I, k, 0, "dpath", E, H, I, shared=shared, device=dev)
@@ -212,8 +252,8 @@ def test_moe_down_paths_bit_identical(mm, orc, dev, monkeypatch, E, H, I, k, sha
         ids, w, sw, _ = mm.moe_route_topk(layer.router, X, k,
                                           shared_gate_row=layer.shared_gate_row)
         ys = []
-        for mode in ("1", "2"):
-            monkeypatch.setenv("MMV_MOE_DOWN", mode)
+        for mode in (1, 2):
+            path(MOE_DOWN=mode)
             ws = torch.full((mm.moe_workspace_bytes(layer, B),), 0x5A, dtype=torch.uint8,
                             device=dev)
             ys.append(mm.moe_mul_mat_id(layer, X, ids, w, sw if shared else None, workspace=ws))
@@ -304,3 +344,45 @@ def test_moe_ids_outside_range_add_nothing(mm, orc, dev, B):
     torch.cuda.synchronize()
     assert torch.isfinite(y_bad).all()
     assert torch.equal(y_bad, y_ref)
+
+
+def test_moe_exact_gate_up_and_silu(mm, orc, dev):
+    # unit fp16 scales and x = (127, 16, 1, 0, ...): Q8_1(x) has d = 1 and
+    # codes x, so every gate output is an exact integer g (chosen per row,
+    # from 0 through the bend of the curve to both tails) and every up
+    # output is exactly 1.  The staged gate/up outputs must be those integers
+    # bit for bit, and h = silu(g) within a few fp32 ulps of scipy's
+    # g * expit(g) (the kernel's exp and division round on their own).
+    from scipy.special import expit
+    from tests.test_oracle_moe import SILU_G
+    E, H, I, k = 3, 512, 512, 1
+    gate = np.full((E, I, H // 32, 32), 8, np.uint8)
+    up = np.full((E, I, H // 32, 32), 8, np.uint8)
+    tg = np.array([SILU_G[n % 32] * (1 if n < 256 else -1) for n in range(I)])
+    for n, g in enumerate(tg):
+        b = (int(g) + 8) // 16
+        gate[:, n, 0, 1], gate[:, n, 0, 2] = 8 + b, 8 + (int(g) - 16 * b)
+        up[:, n, 0, 2] = 9
+    pack = lambda c: torch.from_numpy((c[..., :16] | (c[..., 16:] << 4)).astype(np.uint8)).to(dev)
+    ones = lambda *sh: torch.ones(sh, dtype=torch.float16, device=dev)
+    down_qs = torch.full((E, H, I // 32, 16), 0x88, dtype=torch.uint8, device=dev)
+    router = torch.ones((E, H), device=dev)
+    layer = mm.MoeLayer(router, pack(gate), ones(E, I, H // 32), pack(up), ones(E, I, H // 32),
+                        down_qs, ones(E, H, I // 32), k)
+    X = torch.zeros((2, H), device=dev)
+    X[:, :3] = torch.tensor([127.0, 16.0, 1.0])
+    ids = torch.tensor([[1], [2]], dtype=torch.int32, device=dev)
+    w = torch.ones((2, 1), device=dev)
+    P = 2
+    dbg = dict(gate_out=torch.full((P, I), np.nan, device=dev),
+               up_out=torch.full((P, I), np.nan, device=dev),
+               h=torch.full((P, I), np.nan, device=dev))
+    y = mm.moe_mul_mat_id(layer, X, ids, w, debug=dbg)
+    torch.cuda.synchronize()
+    for p in range(P):
+        assert np.array_equal(npc(dbg["gate_out"])[p], tg.astype(np.float32))
+        assert (npc(dbg["up_out"])[p] == 1.0).all()
+        want = (tg * expit(tg)).astype(np.float32)
+        h = npc(dbg["h"])[p].astype(np.float64)
+        assert (np.abs(h - want) <= 4 * np.spacing(np.abs(want)) + 1e-30).all()
+    assert (npc(y) == 0.0).all()        # all-zero down weights (codes 8)

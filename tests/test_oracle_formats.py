@@ -1,5 +1,7 @@
 """Pins of the oracle's number-format conversions against independent
 implementations (numpy's float16 cast, torch's bfloat16 cast) and closed forms."""
+import os
+
 import numpy as np
 import torch
 
@@ -60,3 +62,47 @@ def test_bf16_against_torch(orc):
     h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     f = orc.bf16_to_f32(h)
     assert np.array_equal(f.view(np.uint32), h.astype(np.uint32) << 16)
+
+
+# ---------------------------------------------------------------------------
+# interchange blocks: the 36-byte Q8_1 and 18-byte Q4_0 blocks the pages name,
+# converted to and from the library's planar layout (test utilities)
+# ---------------------------------------------------------------------------
+
+def test_q8_1_interchange_block_golden(orc):
+    from tests._util import q8_1_from_blocks, q8_1_to_blocks, read_golden_blocks
+    from tests.test_oracle_q8_1 import _golden
+    g = read_golden_blocks(os.path.join(os.path.dirname(__file__), "golden",
+                                        "interchange_blocks.txt"))
+    blk = g["q8_1"].reshape(1, 1, 36)
+    x, q, d, s = _golden()
+    codes, ds = q8_1_from_blocks(blk)
+    assert np.array_equal(codes[0], q) and ds[0, 0, 0] == d and ds[0, 0, 1] == s
+    oq, ods = orc.quantize_q8_1(x[None])
+    assert np.array_equal(q8_1_to_blocks(oq, ods), blk)
+
+
+def test_q4_0_interchange_block_golden():
+    from tests._util import q4_0_from_blocks, q4_0_to_blocks, read_golden_blocks
+    from tests.test_oracle_gemv import _dense_q4
+    g = read_golden_blocks(os.path.join(os.path.dirname(__file__), "golden",
+                                        "interchange_blocks.txt"))
+    blk = g["q4_0"].reshape(1, 1, 18)
+    qs, d = q4_0_from_blocks(blk)
+    w = _dense_q4(qs, d)[0]
+    assert np.array_equal(w, np.array([(i % 16) - 8 for i in range(32)], np.float64))
+    assert np.array_equal(q4_0_to_blocks(qs, d), blk)
+
+
+def test_interchange_round_trips():
+    from tests._util import q4_0_from_blocks, q4_0_to_blocks, q8_1_from_blocks, q8_1_to_blocks
+    rng = np.random.default_rng(21)
+    codes = rng.integers(-127, 128, (3, 96)).astype(np.int8)
+    ds = rng.integers(0, 1 << 16, (3, 3, 2)).astype(np.uint16)
+    c2, d2 = q8_1_from_blocks(q8_1_to_blocks(codes, ds))
+    assert np.array_equal(c2, codes) and np.array_equal(d2, ds)
+    assert q8_1_to_blocks(codes, ds).nbytes == codes.nbytes + ds.nbytes   # same bytes
+    qs = rng.integers(0, 256, (5, 4, 16)).astype(np.uint8)
+    d = rng.integers(0, 1 << 16, (5, 4)).astype(np.uint16)
+    q2, e2 = q4_0_from_blocks(q4_0_to_blocks(qs, d))
+    assert np.array_equal(q2, qs) and np.array_equal(e2, d)

@@ -1,8 +1,10 @@
 """Pins of the oracle's router, top-k, gate weights, gather lists and whole MoE
 layer: numpy matmuls, a stable sort on (-value, index), Python's sorted(),
-closed forms, and a dense numpy restatement of the layer on small cases."""
+closed forms, scipy's logistic function for the SiLU between gate and up, and
+a dense numpy restatement of the layer on small cases."""
 import numpy as np
 import pytest
+from scipy.special import expit
 
 from tests.test_oracle_gemv import _dense_q4, _q8_dense
 
@@ -116,7 +118,7 @@ def _dense_layer(orc, L, X):
         s = np.ones(B)
     xq, xds = orc.quantize_q8_1(X)
     xhat = _q8_dense(xq, xds)
-    silu = lambda z: z / (1 + np.exp(-z))
+    silu = lambda z: z * expit(z)   # scipy's logistic function, not the oracle's formula
     Y = np.zeros((B, L.H))
     for b in range(B):
         experts = [(int(ids[b, j]), w[b, j], False) for j in range(L.k)]
@@ -195,3 +197,106 @@ def test_batched_rows_equal_single_rows(orc):
         one = L.layer(X[b:b + 1])
         assert np.array_equal(one["ids"][0], full["ids"][b])
         assert np.array_equal(one["y"][0], full["y"][b])
+
+
+# ---------------------------------------------------------------------------
+# SiLU between gate and up, reached through the layer's gate/up stage
+# ---------------------------------------------------------------------------
+
+# gate outputs g driven to exact integers (below): 0, the small values where
+# the curve bends, and the tails where silu(g) -> g (g -> +inf) and
+# silu(g) -> 0 from below (g -> -inf)
+SILU_G = [0, 1, -1, 2, -2, 3, -3, 5, -5, 8, -8, 10, -10, 17, -17, 20, -20, 30, -30,
+          40, -40, 60, -60, 88, -88, 100, -100, 119, -119, 50, -50, 7]
+
+
+def _silu_layer(orc, targets):
+    """One expert, H = I = 32, unit fp16 scales.  x = (127, 16, 1, 0, ...)
+    quantizes to exactly those codes with d = 1 (amax = 127).  Gate row n has
+    codes (8, 8 + b_n, 8 + c_n, 8, ...) with 16 b_n + c_n = target n, so
+    g_n = 16 b_n + c_n exactly; every up row has codes (8, 8, 9, 8, ...), so
+    u_n = 1.  Then h_n = silu(g_n) * 1."""
+    assert len(targets) == 32
+    E, H, I = 1, 32, 32
+    gate = np.full((E, I, 1, 32), 8, np.uint8)
+    up = np.full((E, I, 1, 32), 8, np.uint8)
+    for n, g in enumerate(targets):
+        b = (g + 8) // 16
+        c = g - 16 * b
+        assert -8 <= b <= 7 and -8 <= c <= 7, g
+        gate[0, n, 0, 1] = 8 + b
+        gate[0, n, 0, 2] = 8 + c
+        up[0, n, 0, 2] = 9
+    pack = lambda codes: (codes[..., :16] | (codes[..., 16:] << 4)).astype(np.uint8)
+    one = np.full((E, I, 1), 0x3C00, np.uint16)          # fp16 1.0
+    down_q = np.full((E, H, 1, 16), 0x88, np.uint8)
+    down_d = np.full((E, H, 1), 0x3C00, np.uint16)
+    router = np.ones((E, H), np.float32)
+    L = orc.MoE(router, pack(gate), one, pack(up), one.copy(), down_q, down_d, 1)
+    x = np.zeros((1, H), np.float32)
+    x[0, :3] = (127.0, 16.0, 1.0)
+    return L, x
+
+
+def test_silu_through_gate_up(orc):
+    L, x = _silu_layer(orc, SILU_G)
+    xq, xds = orc.quantize_q8_1(x)
+    assert xq[0, :3].tolist() == [127, 16, 1] and orc.f16_to_f32(xds[0, 0, :1])[0] == 1.0
+    h = L.gate_up(x, np.zeros((1, 1), np.int32))[0]
+    g = np.array(SILU_G, np.float64)
+    # the curve: h = g * sigma(g) with scipy's logistic function, to one fp32 ulp
+    want = (g * expit(g)).astype(np.float32)
+    assert (np.abs(h.astype(np.float64) - want) <= np.spacing(np.abs(want))).all()
+    # silu(0) = 0
+    assert h[SILU_G.index(0)] == 0.0
+    # large positive g: silu(g) = g (1 - e^-g) rounds to g itself in fp32
+    for gv in (20, 30, 40, 50, 60, 88, 100, 119):
+        assert h[SILU_G.index(gv)] == np.float32(gv)
+    # large negative g: silu(g) = g e^g / (1 + e^g), negative and vanishing
+    for gv, bound in ((-20, 1e-7), (-40, 1e-15), (-60, 1e-24), (-100, 1e-40)):
+        hv = float(h[SILU_G.index(gv)])
+        assert -bound < hv <= 0.0, (gv, hv)
+    assert float(h[SILU_G.index(-119)]) <= 0.0
+    # the sign of the curve: silu(g) > 0 for g > 0, silu(g) < 0 for g < 0 (finite tail)
+    for gv in (1, 2, 3, 5, 8, 10, 17):
+        assert h[SILU_G.index(gv)] > 0 and h[SILU_G.index(-gv)] < 0
+    # silu(g) - silu(-g) = g (sigma(g) + sigma(-g)) = g
+    for gv in (1, 2, 3, 5, 8, 10, 17, 20, 30):
+        d = float(h[SILU_G.index(gv)]) - float(h[SILU_G.index(-gv)])
+        assert abs(d - gv) <= 4 * np.spacing(np.float32(gv)), (gv, d)
+    # the minimum of silu lies near g = -1.28 at about -0.2785: the values at
+    # -1 and -2 sit above it and below zero
+    assert -0.2785 < h[SILU_G.index(-1)] < -0.26 and -0.2785 < h[SILU_G.index(-2)] < -0.23
+
+
+def test_admissibility_check_rejects_a_wrong_routing(orc):
+    # the rule the GPU decode tests apply to rows whose ids differ from the
+    # float64 top-k: the exact top-k passes, a swap of two near-equal logits
+    # passes, a swap that is not a near tie fails, and duplicates fail
+    from tests._util import check_ids_admissible
+    rng = np.random.default_rng(18)
+    E, H, k = 32, 256, 4
+    R = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    X = rng.standard_normal((2, H)).astype(np.float32)
+    lg = orc.router_logits(R, X)
+    ids = orc.topk(lg.astype(np.float32), k)
+    _, differ = check_ids_admissible(orc, R, X, ids, k)
+    assert differ == []
+    # plant a near tie: router row of the 5th-ranked expert := the 4th's
+    order = np.argsort(-lg[0], kind="stable")
+    R2 = R.copy()
+    R2[order[4]] = R2[order[3]]
+    lg2 = orc.router_logits(R2, X)
+    ids2 = orc.topk(lg2.astype(np.float32), k)
+    swapped = ids2.copy()
+    swapped[0, k - 1] = max(order[3], order[4])   # the higher index: lg2 equal
+    _, differ = check_ids_admissible(orc, R2, X, swapped, k)
+    assert differ == [0]
+    wrong = ids.copy()
+    wrong[0, k - 1] = order[E - 1]                 # the smallest logit of the row
+    with pytest.raises(AssertionError):
+        check_ids_admissible(orc, R, X, wrong, k)
+    dup = ids.copy()
+    dup[1, 1] = dup[1, 0]
+    with pytest.raises(AssertionError):
+        check_ids_admissible(orc, R, X, dup, k)
