@@ -45,7 +45,14 @@ __device__ __forceinline__ Q8Block q8_1_quantize8(f32x4 v) {
             ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
   r.qsum = group8_sum_i(q0 + q1 + q2 + q3);
   r.d16 = zero ? (uint16_t)0 : d16;
-  r.s16 = zero ? (uint16_t)0 : f32_to_f16_bits(__fmul_rn(d32, (float)r.qsum));
+  // s is the fp16 rounding of the fp32 product d32 * sum q: the product is
+  // pinned in a register first, since the compiler otherwise fuses the
+  // multiply and the conversion into one instruction that rounds once
+  // (v_fma_mixlo_f16), which differs where the fp32 product is an fp16
+  // halfway point
+  float ps = __fmul_rn(d32, (float)r.qsum);
+  asm volatile("" : "+v"(ps));
+  r.s16 = zero ? (uint16_t)0 : f32_to_f16_bits(ps);
   return r;
 }
 

@@ -180,3 +180,24 @@ def read_golden_blocks(path):
             name, *hexes = line.split()
             out[name] = np.array([int(h, 16) for h in hexes], np.uint8)
     return out
+
+
+def q8_1_halfway_blocks(orc, n, seed=0):
+    """n blocks of 32 fp32 values (rows of an array [n, 32]) whose Q8_1 block
+    sum is a rounding boundary: the fp32 product d32 * sum(q) lies exactly
+    halfway between two fp16 values while the exact product does not, so
+    rounding the fp32 product to fp16 (the definition) and rounding the exact
+    product once give different bits.  Found by a seeded search with the
+    oracle's codes."""
+    rng = np.random.default_rng(seed)
+    found = []
+    while len(found) < n:
+        x = rng.standard_normal((1 << 16, 32)).astype(np.float32)
+        q, _ = orc.quantize_q8_1(x.reshape(1, -1))
+        S = q.reshape(-1, 32).astype(np.int64).sum(1)
+        d32 = (np.abs(x).max(1) / np.float32(127.0)).astype(np.float32)
+        p32 = (d32 * S.astype(np.float32)).astype(np.float32)
+        exact = d32.astype(np.float64) * S
+        differ = p32.astype(np.float16).view(np.uint16) != exact.astype(np.float16).view(np.uint16)
+        found.extend(x[differ][: n - len(found)])
+    return np.stack(found[:n])

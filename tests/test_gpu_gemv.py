@@ -160,6 +160,21 @@ def test_quantize_q8_1_bit_exact(mm, orc, dev, B, K, scale):
     assert np.array_equal(np16(ds), ds_ref)
 
 
+def test_quantize_q8_1_halfway_block_sums(mm, orc, dev):
+    # blocks whose fp32 product d32 * sum q is an fp16 halfway point: s must be
+    # the rounding of the fp32 product (a fused multiply-convert rounds once
+    # and gives the other neighbour), in the standalone quantizer and in the
+    # MoE path's staged Q8_1(x), which use the same routine
+    from tests._util import q8_1_halfway_blocks
+    X = torch.from_numpy(q8_1_halfway_blocks(orc, 64).reshape(8, 256)).to(dev)
+    buf = mm.quantize_q8_1(X)
+    torch.cuda.synchronize()
+    q_ref, ds_ref = orc.quantize_q8_1(npc(X))
+    codes, ds = mm.split_q8_1(buf, 8, 256)
+    assert np.array_equal(npc(codes), q_ref)
+    assert np.array_equal(np16(ds), ds_ref)
+
+
 def test_quantize_q8_1_worked_example(mm, dev):
     from tests.test_oracle_q8_1 import _golden
     x, q, d, s = _golden()

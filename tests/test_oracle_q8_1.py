@@ -103,3 +103,19 @@ def test_row_stride_is_respected(orc):
     q1, d1 = orc.quantize_q8_1(x, K=64)
     q2, d2 = orc.quantize_q8_1(np.ascontiguousarray(x[:, :64]))
     assert np.array_equal(q1, q2) and np.array_equal(d1, d2)
+
+
+def test_block_sum_rounds_the_fp32_product(orc):
+    # s = fp16(d32 * sum q) with d32 * sum q an fp32 product: at blocks where
+    # that product is an fp16 halfway point, s follows round-to-nearest-even
+    # of the fp32 value, not the rounding of the exact product
+    from tests._util import q8_1_halfway_blocks
+    X = q8_1_halfway_blocks(orc, 8)
+    q, ds = orc.quantize_q8_1(X.reshape(1, -1))
+    S = q.reshape(8, 32).astype(np.int64).sum(1)
+    d32 = (np.abs(X).max(1) / np.float32(127.0)).astype(np.float32)
+    p32 = (d32 * S.astype(np.float32)).astype(np.float32)
+    assert np.array_equal(ds[0, :, 1], p32.astype(np.float16).view(np.uint16))
+    exact = d32.astype(np.float64) * S
+    assert not np.array_equal(ds[0, :, 1], exact.astype(np.float16).view(np.uint16))
+    assert np.array_equal(ds[0, :, 0], d32.astype(np.float16).view(np.uint16))
