@@ -307,6 +307,28 @@ int moe_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx,
                      void *workspace, size_t ws_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
+ * moe_layer_decode_noalloc -- moe_layer_decode without a caller workspace,
+ *   for callers that cannot allocate device memory: code under HIP graph
+ *   capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   The same kernels and results as moe_layer_decode (bit for bit); the
+ *   workspace is an array inside the library, MMV_NOALLOC_WS_BYTES bytes per
+ *   GPU, held from the module load until the process ends.  The call
+ *   allocates nothing.  A layer and B whose moe_workspace_bytes exceeds
+ *   MMV_NOALLOC_WS_BYTES is refused with MMV_E_WORKSPACE (512 experts,
+ *   H = 2048, I = 512, top-10 with a shared expert fit up to B = 64).
+ *   Every call on one GPU uses that GPU's one array, which keeps the last
+ *   call's contents (no call needs it cleared): calls that overlap in time
+ *   on one GPU (other streams, other threads) race and must not be issued;
+ *   calls ordered on one stream are fine.  The first call on each GPU looks
+ *   up the array's device address (a host-side runtime query).
+ * ------------------------------------------------------------------------ */
+#define MMV_NOALLOC_WS_BYTES ((size_t)8 << 20)
+size_t mmv_noalloc_ws_bytes(void);
+int moe_layer_decode_noalloc(const mmv_moe_layer *L, const float *X, int64_t ldx,
+                             int32_t B, float *Y, int64_t ldy,
+                             int32_t *ids, float *weights, void *stream);
+
+/* --------------------------------------------------------------------------
  * Measurement utility: device read-bandwidth probe.  ["hanzo-engine: A
  * Portable Single-Binary LLM Inference Engine", The Bandwidth Wall: decode
  * bandwidth is compared with a measured device roofline probe]

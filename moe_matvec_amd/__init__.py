@@ -20,7 +20,7 @@ __all__ = [
     "argmax_rows", "argmax_workspace_bytes", "Q4F32_MAX_XK",
     "moe_route_topk", "moe_mul_mat_id", "moe_layer_decode", "moe_workspace_bytes",
     "MAX_BATCH", "MOE_MAX_BATCH", "MAX_EXPERTS", "MAX_TOPK", "Q4_MAX_XK", "stream_read", "split_q8_1",
-    "PATH", "set_path", "get_path",
+    "PATH", "set_path", "get_path", "moe_layer_decode_noalloc", "NOALLOC_WS_BYTES",
 ]
 
 MAX_BATCH = 8
@@ -29,6 +29,7 @@ MAX_EXPERTS = 1024
 MAX_TOPK = 16
 Q4_MAX_XK = 49152
 Q4F32_MAX_XK = 16384
+NOALLOC_WS_BYTES = 8 << 20  # the library's own workspace of moe_layer_decode_noalloc
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmoe_matvec.so")
@@ -100,6 +101,9 @@ def lib():
                                          _i64, _P, C.c_size_t, C.POINTER(_Debug), _P]),
             "moe_layer_decode": (C.c_int, [C.POINTER(_Layer), _P, _i64, _i32, _P, _i64, _P,
                                            _P, _P, C.c_size_t, _P]),
+            "mmv_noalloc_ws_bytes": (C.c_size_t, []),
+            "moe_layer_decode_noalloc": (C.c_int, [C.POINTER(_Layer), _P, _i64, _i32, _P, _i64,
+                                                   _P, _P, _P]),
             "mmv_set_path": (C.c_int, [C.c_int, C.c_int]),
             "mmv_get_path": (C.c_int, [C.c_int]),
             "mmv_probe_slots": (C.c_int, []),
@@ -409,6 +413,21 @@ def moe_layer_decode(layer: MoeLayer, x: torch.Tensor, out=None, workspace=None,
     _check("moe_layer_decode", lib().moe_layer_decode(
         C.byref(layer._s), x2.data_ptr(), _ld(x2), B, y2.data_ptr(), _ld(y2), _ptr(ids),
         _ptr(weights), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+def moe_layer_decode_noalloc(layer: MoeLayer, x: torch.Tensor, out=None, ids=None, weights=None,
+                             stream=None):
+    """moe_layer_decode with the library's own workspace (allocates nothing
+    on the device when `out` is given; calls on one GPU must not overlap)."""
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    B = x2.shape[0]
+    if out is None:
+        out = torch.empty((B, layer.H), dtype=torch.float32, device=x.device)
+    y2 = out.unsqueeze(0) if out.dim() == 1 else out
+    _check("moe_layer_decode_noalloc", lib().moe_layer_decode_noalloc(
+        C.byref(layer._s), x2.data_ptr(), _ld(x2), B, y2.data_ptr(), _ld(y2), _ptr(ids),
+        _ptr(weights), _stream(stream)))
     return out
 
 

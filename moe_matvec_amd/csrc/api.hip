@@ -2,6 +2,7 @@
 // host (validate.cpp, no device access), then enqueue on the caller's
 // stream.  No allocation, no synchronization, no host reads of device data.
 #include <atomic>
+#include <mutex>
 
 #include "../../include/moe_matvec.h"
 #include "../../include/moe_matvec_testing.h"
@@ -23,6 +24,46 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 // kernel-variant switches (moe_matvec_testing.h): 0 = automatic
 std::atomic<int> g_path[MMV_PATH_COUNT];
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The library's own MoE workspace for moe_layer_decode_noalloc: one array per
+// GPU, held from the module load until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: the kernels get
+// the device address hipGetSymbolAddress returns, fetched once per device
+// with that device current, and only that address is used from then on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MMV_NOALLOC_WS_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// device address of this device's scratch array (looked up on first use)
+hipError_t scratch_on_current_device(uint8_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint8_t *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void *addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!addr) return hipErrorInvalidSymbol;
+      p = static_cast<uint8_t *>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -137,6 +178,33 @@ int moe_layer_decode(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_
       mmv::check_layer_decode(L, X, ldx, B, Y, ldy, ids, weights, workspace, ws_bytes);
   if (st != MMV_OK) return st;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const mmv::MoeWsLayout lay =
+      mmv::moe_ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, B,
+                         L->sh_gate_qs != nullptr);
+  int32_t *id = ids ? ids : reinterpret_cast<int32_t *>(ws + lay.ids);
+  float *w = weights ? weights : reinterpret_cast<float *>(ws + lay.weights);
+  return hip_status(mmv::run_moe_layer(*L, X, ldx, B, id, w, Y, ldy, ws, as_stream(stream)));
+}
+
+size_t mmv_noalloc_ws_bytes(void) { return MMV_NOALLOC_WS_BYTES; }
+
+int moe_layer_decode_noalloc(const mmv_moe_layer *L, const float *X, int64_t ldx, int32_t B,
+                             float *Y, int64_t ldy, int32_t *ids, float *weights,
+                             void *stream) {
+  // sizes first (no HIP call): a layer or batch whose workspace exceeds the
+  // library's array is refused before anything else
+  const size_t need = mmv::moe_ws_bytes(L, B);
+  if (need > MMV_NOALLOC_WS_BYTES) return MMV_E_WORKSPACE;
+  if (need == 0) {  // the layer or B is invalid: report why
+    const int st = mmv::check_layer_decode(L, X, ldx, B, Y, ldy, ids, weights, nullptr, 0);
+    return st != MMV_OK ? st : MMV_E_SHAPE;
+  }
+  uint8_t *ws = nullptr;
+  const hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  const int st = mmv::check_layer_decode(L, X, ldx, B, Y, ldy, ids, weights, ws,
+                                         MMV_NOALLOC_WS_BYTES);
+  if (st != MMV_OK) return st;
   const mmv::MoeWsLayout lay =
       mmv::moe_ws_layout(L->n_experts, L->hidden, L->inter, L->top_k, B,
                          L->sh_gate_qs != nullptr);

@@ -247,3 +247,18 @@ def test_path_switches(L):
     assert L.mmv_get_path(99) == 0
     for i in range(9):
         assert L.mmv_get_path(i) == 0
+
+
+def test_noalloc_refuses_oversized_layers(L):
+    # the library's own workspace: its size is exported, and a layer whose
+    # workspace exceeds it is refused before any device call
+    assert L.mmv_noalloc_ws_bytes() == 8 << 20
+    big = _layer(n_experts=1024, hidden=4096, inter=1024, top_k=16)
+    assert L.moe_workspace_bytes(C.byref(big), 64) > L.mmv_noalloc_ws_bytes()
+    assert L.moe_layer_decode_noalloc(C.byref(big), A, 4096, 64, Cp, 4096, None, None,
+                                      None) == E_WS
+    assert L.moe_layer_decode_noalloc(None, A, 2048, 1, Cp, 2048, None, None, None) == E_NULL
+    assert L.moe_layer_decode_noalloc(C.byref(_layer()), A, 2048, 0, Cp, 2048, None, None,
+                                      None) == E_BATCH
+    assert L.moe_layer_decode_noalloc(C.byref(_layer(top_k=17)), A, 2048, 1, Cp, 2048, None,
+                                      None, None) == E_TOPK
