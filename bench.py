@@ -457,7 +457,8 @@ def main():
         sections["q4_0"] = q
     if "w4a16" in only:
         q = {}
-        for copies, B in ((8 if args.quick else 32, 1), (8 if args.quick else 32, 4)):
+        for copies, B in ((8 if args.quick else 32, 1), (8 if args.quick else 32, 4),
+                          (8 if args.quick else 32, 8)):
             r = w4a16_section(mm, dev, copies, B, steps, warmup)
             q[f"copies{copies}_B{B}"] = r
             log(f"w4a16 copies={copies} B={B}: {r['GBps']:.0f} GB/s, {r['us_per_copy']:.2f} us/copy")

@@ -74,7 +74,7 @@ extern "C" {
 #define MMV_MAX_EXPERTS 1024  /* router rows E                              */
 #define MMV_MAX_TOPK    16    /* experts per row k                          */
 #define MMV_Q4_MAX_XK   49152 /* B*K limit of gemv_q4_0 (x staged in LDS)   */
-#define MMV_Q4F32_MAX_XK 16384 /* B*K limit of gemv_q4_0_f32 (fp32 x in LDS) */
+#define MMV_Q4F32_MAX_XK 36864 /* B*K limit of gemv_q4_0_f32 (fp32 x in LDS) */
 
 typedef enum {
   MMV_OK = 0,
@@ -157,8 +157,9 @@ int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,
  *    announces]
  *   Y[b*ldy + n] = sum_j d_w[n][j] * sum_i (code_i - 8) * X[b*ldx + 32j + i],
  *   fp32 arithmetic: per block s = sum_i code_i * x_i, then d_w * (s - 8 *
- *   sum_i x_i).  K / 32 in {16, 32, 64, 128, 256}; B * K <=
- *   MMV_Q4F32_MAX_XK (x of every row is staged in on-chip memory).
+ *   sum_i x_i).  Any K % 32 == 0 with B * K <= MMV_Q4F32_MAX_XK (x of
+ *   every row is staged in on-chip memory: B = 8 at K = 4096, B = 3 at
+ *   K = 11008, B = 1 up to K = 36864).
  *   X: B x K fp32, 16-byte aligned, ldx % 4 == 0.  Y: B x N fp32, ldy >= N.
  * ------------------------------------------------------------------------ */
 int gemv_q4_0_f32(const mmv_q4_0 *W, const float *X, int64_t ldx, int32_t B,

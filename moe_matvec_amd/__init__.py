@@ -28,7 +28,7 @@ MOE_MAX_BATCH = 64  # MoE calls: verify / prefill batches
 MAX_EXPERTS = 1024
 MAX_TOPK = 16
 Q4_MAX_XK = 49152
-Q4F32_MAX_XK = 16384
+Q4F32_MAX_XK = 36864
 NOALLOC_WS_BYTES = 8 << 20  # the library's own workspace of moe_layer_decode_noalloc
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

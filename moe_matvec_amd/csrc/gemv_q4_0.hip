@@ -254,16 +254,90 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
 // "Beating llama.cpp from Scratch on Consumer AMD" ("BF16 vs Quantization")
 // names W4A16 INT4 weights with on-the-fly dequantization as the variant
 // that trades integer unpacking for activation precision.  Same row layout
-// as k_gemv_q4_0_t (G lanes per row, RP rows per lane group, every weight
-// load issued after the first activation loads).  x is staged in LDS as
-// fp32 in a block-transposed layout ([b][q][j] float4, q = 0..7 within a
-// block, so lanes reading consecutive blocks read consecutive 16-byte
-// words), with each block's sum sx = sum_i x_i (fixed order).  Per block:
-// s1 = sum_i code_i * x_i (codes converted from bytes, k ascending through
-// the low then the high nibbles), value d_w * (s1 - 8 sx).  Every (row, b)
-// sum has one order for every B.
+// as k_gemv_q4_0_t (G lanes per row, RP rows per lane group, weight loads
+// issued after the first activation loads).  x is staged in LDS as fp32 in
+// a block-transposed layout ([b][q][j] float4, q = 0..7 within a block, so
+// lanes reading consecutive blocks read consecutive 16-byte words), with
+// each block's sum sx = sum_i x_i (fixed order).  Per block: s1 = sum_i
+// code_i * x_i (codes converted from bytes, k ascending through the low then
+// the high nibbles), value d_w * (s1 - 8 sx).  Every (row, b) sum runs over
+// the lane's blocks j = sub, sub + G, ... in ascending order, then the G-lane
+// sum: one order for every B and in both kernels below (same G), so rows
+// are bit-identical whatever the batch and the kernel.
 constexpr int kF32Pass = 8;  // float4 staging tasks per thread per pass
 
+// one float4 of x (task t of the [B][K/4] row-major x) to the staged layout;
+// the block's sum is formed by the 8 lanes holding it
+__device__ __forceinline__ void w4a16_stage4(f32x4 v, int t, int K, int nb, bool store,
+                                             f32x4 *xs, float *sx) {
+  asm volatile("" ::"v"(v));  // keep the load where it was issued
+  const float sum = group8_sum((v.x + v.y) + (v.z + v.w));
+  if (store) {  // uniform over each 8-lane group: the task count is a multiple of 8
+    const int b = t / (K / 4), r = t - b * (K / 4), j = r >> 3, q = r & 7;
+    xs[(b * 8 + q) * nb + j] = v;
+    if (q == 0) sx[b * nb + j] = sum;
+  }
+}
+
+// Block j (the lane's) for RP weight rows and the B x rows: each group of 4
+// code bytes is converted to fp32 once and used for every x row; x of all B
+// rows for those positions is read from LDS once and used for the RP rows.
+// For each (row, x row) the FMAs run low nibbles then high nibbles, bytes
+// ascending; then acc += d_w * (s1 - 8 sx).
+template <int B, int RP>
+__device__ __forceinline__ void w4a16_block(const u32x4 (&w)[RP], const float (&d)[RP],
+                                            const f32x4 *xs, const float *sx, int nb, int j,
+                                            float (&acc)[RP][B]) {
+  constexpr int DG = B > 4 ? 2 : 4;  // code dwords per step (registers: x of B rows)
+  float s1[RP][B];
+#pragma unroll
+  for (int p = 0; p < RP; ++p)
+#pragma unroll
+    for (int r = 0; r < B; ++r) s1[p][r] = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {        // low nibbles: codes 0..15; high: 16..31
+#pragma unroll
+    for (int d0 = 0; d0 < 4; d0 += DG) {
+      f32x4 xq[B][DG];
+#pragma unroll
+      for (int r = 0; r < B; ++r)
+#pragma unroll
+        for (int dd = 0; dd < DG; ++dd) xq[r][dd] = xs[(r * 8 + 4 * h + d0 + dd) * nb + j];
+#pragma unroll
+      for (int p = 0; p < RP; ++p) {
+        const uint32_t wd[4] = {w[p].x, w[p].y, w[p].z, w[p].w};
+        float cf[DG][4];
+#pragma unroll
+        for (int dd = 0; dd < DG; ++dd) {
+          const uint32_t c = (wd[d0 + dd] >> (4 * h)) & 0x0F0F0F0Fu;
+          cf[dd][0] = (float)(c & 0xFFu);
+          cf[dd][1] = (float)((c >> 8) & 0xFFu);
+          cf[dd][2] = (float)((c >> 16) & 0xFFu);
+          cf[dd][3] = (float)(c >> 24);
+        }
+#pragma unroll
+        for (int r = 0; r < B; ++r)
+#pragma unroll
+          for (int dd = 0; dd < DG; ++dd) {
+            s1[p][r] = fmaf(cf[dd][0], xq[r][dd].x, s1[p][r]);
+            s1[p][r] = fmaf(cf[dd][1], xq[r][dd].y, s1[p][r]);
+            s1[p][r] = fmaf(cf[dd][2], xq[r][dd].z, s1[p][r]);
+            s1[p][r] = fmaf(cf[dd][3], xq[r][dd].w, s1[p][r]);
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < B; ++r) {
+    const float sxr = sx[r * nb + j];
+#pragma unroll
+    for (int p = 0; p < RP; ++p) acc[p][r] = fmaf(d[p], fmaf(-8.0f, sxr, s1[p][r]), acc[p][r]);
+  }
+}
+
+// K = 32 * G * T exactly and B * K <= MMV_Q4F32_MAX_XK / 2 (x in at most
+// 66 KiB of LDS): a workgroup owns one row group, every weight load of it
+// issued up front.
 template <int B, int G, int RP, int T>
 __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int /*K*/,
@@ -290,14 +364,8 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
 #pragma unroll
     for (int m = 0; m < kF32Pass; ++m) {
       if (m >= np) break;
-      asm volatile("" ::"v"(v[m]));
       const int t = base + threadIdx.x + 256 * m;
-      const float s = group8_sum((v[m].x + v[m].y) + (v[m].z + v[m].w));
-      if (t < TOT) {  // uniform over each 8-lane group: TOT % 8 == 0
-        const int b = t / (K / 4), r = t - b * (K / 4), j = r >> 3, q = r & 7;
-        xs[(b * 8 + q) * nb + j] = v[m];
-        if (q == 0) sx[b * nb + j] = s;
-      }
+      w4a16_stage4(v[m], t, K, nb, t < TOT, xs, sx);
     }
   };
 
@@ -305,16 +373,16 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
   load_pass(0, xv);
   __builtin_amdgcn_sched_barrier(0);
   const int rbase = blockIdx.x * ROWS_WG + wv * ROWS_WAVE + grp;
-  u32x4 w[RP][T];
-  float d[RP][T];
+  u32x4 w[T][RP];
+  float d[T][RP];
 #pragma unroll
   for (int p = 0; p < RP; ++p) {
     const int64_t rowblk = (int64_t)min(rbase + p * RPP, N - 1) * nb;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int64_t blk = rowblk + sub + G * t;
-      w[p][t] = load_stream16(qs + blk * 16);
-      d[p][t] = f16_bits_to_f32(load_stream2(dw + blk));
+      w[t][p] = load_stream16(qs + blk * 16);
+      d[t][p] = f16_bits_to_f32(load_stream2(dw + blk));
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -331,60 +399,8 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
   for (int p = 0; p < RP; ++p)
 #pragma unroll
     for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
-  // Per block: the codes of a (row, group of 4 bytes) are converted to fp32
-  // once and used for every x row; x of all B rows for those positions is
-  // read from LDS once and used for the RP rows.  For each (row, x row) the
-  // FMAs run low nibbles then high nibbles, bytes ascending: one order for
-  // every B.
-  constexpr int DG = B > 4 ? 2 : 4;  // code dwords per step (registers: x of B rows)
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int j = sub + G * t;
-    float s1[RP][B];
-#pragma unroll
-    for (int p = 0; p < RP; ++p)
-#pragma unroll
-      for (int r = 0; r < B; ++r) s1[p][r] = 0.0f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {        // low nibbles: codes 0..15; high: 16..31
-#pragma unroll
-      for (int d0 = 0; d0 < 4; d0 += DG) {
-        f32x4 xq[B][DG];
-#pragma unroll
-        for (int r = 0; r < B; ++r)
-#pragma unroll
-          for (int dd = 0; dd < DG; ++dd) xq[r][dd] = xs[(r * 8 + 4 * h + d0 + dd) * nb + j];
-#pragma unroll
-        for (int p = 0; p < RP; ++p) {
-          const uint32_t wd[4] = {w[p][t].x, w[p][t].y, w[p][t].z, w[p][t].w};
-          float cf[DG][4];
-#pragma unroll
-          for (int dd = 0; dd < DG; ++dd) {
-            const uint32_t c = (wd[d0 + dd] >> (4 * h)) & 0x0F0F0F0Fu;
-            cf[dd][0] = (float)(c & 0xFFu);
-            cf[dd][1] = (float)((c >> 8) & 0xFFu);
-            cf[dd][2] = (float)((c >> 16) & 0xFFu);
-            cf[dd][3] = (float)(c >> 24);
-          }
-#pragma unroll
-          for (int r = 0; r < B; ++r)
-#pragma unroll
-            for (int dd = 0; dd < DG; ++dd) {
-              s1[p][r] = fmaf(cf[dd][0], xq[r][dd].x, s1[p][r]);
-              s1[p][r] = fmaf(cf[dd][1], xq[r][dd].y, s1[p][r]);
-              s1[p][r] = fmaf(cf[dd][2], xq[r][dd].z, s1[p][r]);
-              s1[p][r] = fmaf(cf[dd][3], xq[r][dd].w, s1[p][r]);
-            }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < B; ++r) {
-      const float sxr = sx[r * nb + j];
-#pragma unroll
-      for (int p = 0; p < RP; ++p) acc[p][r] = fmaf(d[p][t], fmaf(-8.0f, sxr, s1[p][r]), acc[p][r]);
-    }
-  }
+  for (int t = 0; t < T; ++t) w4a16_block<B, RP>(w[t], d[t], xs, sx, nb, sub + G * t, acc);
   float (&flat)[RP * B] = *reinterpret_cast<float(*)[RP * B]>(&acc[0][0]);
   gsum_last_n<G>(flat);
 #pragma unroll
@@ -393,6 +409,109 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
 #pragma unroll
     for (int r = 0; r < B; ++r)
       if (sub == G - 1 && row < N) Y[(int64_t)r * ldy + row] = acc[p][r];
+  }
+}
+
+// Any K % 32 == 0 with B * K <= MMV_Q4F32_MAX_XK: x of all B rows is staged
+// once per workgroup (up to ~150 KiB of LDS, one workgroup per compute
+// unit), and the workgroup walks row groups blockIdx.x, + gridDim.x, ...; a
+// lane's blocks of a row group go in chunks of TC, the next chunk (or the
+// next row group's first) in flight while the current one is multiplied.
+// Blocks past the row are clamped in bounds and skipped.
+template <int B, int G, int RP, int TC>
+__global__ __launch_bounds__(256) void k_gemv_q4_0_f32_g(
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
+    const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int RPP = 64 / G, ROWS_WAVE = RP * RPP, ROWS_WG = 4 * ROWS_WAVE;
+  const int nb = K >> 5, tot = B * (K >> 2);
+  const int nt = (nb + G - 1) / G;                          // blocks per lane and row
+  const int nch = (nt + TC - 1) / TC;                       // chunks per row group
+  const int ngroups = (N + ROWS_WG - 1) / ROWS_WG;
+  f32x4 *xs = reinterpret_cast<f32x4 *>(smem);              // [B][8][nb]
+  float *sx = reinterpret_cast<float *>(smem + (size_t)B * K * 4);  // [B][nb]
+  const int lane = threadIdx.x & 63, sub = lane % G, grp = lane / G, wv = threadIdx.x >> 6;
+
+  // the weights of chunk c of row group gi (blocks sub + G * (TC c + i))
+  auto load_chunk = [&](int gi, int c, u32x4 (&w)[TC][RP], float (&d)[TC][RP]) {
+    const int rbase = gi * ROWS_WG + wv * ROWS_WAVE + grp;
+#pragma unroll
+    for (int p = 0; p < RP; ++p) {
+      const int64_t rowblk = (int64_t)min(rbase + p * RPP, N - 1) * nb;
+#pragma unroll
+      for (int i = 0; i < TC; ++i) {
+        const int64_t blk = rowblk + min(sub + G * (TC * c + i), nb - 1);
+        w[i][p] = load_stream16(qs + blk * 16);
+        d[i][p] = f16_bits_to_f32(load_stream2(dw + blk));
+      }
+    }
+  };
+
+  // x: a first pass of loads, then the first chunk of weights, then staging
+  f32x4 xv[kF32Pass];
+  auto load_pass = [&](int base) {
+#pragma unroll
+    for (int m = 0; m < kF32Pass; ++m) {
+      const int t = min(base + (int)threadIdx.x + 256 * m, tot - 1);
+      const int b = t / (K / 4), r = t - b * (K / 4);
+      xv[m] = load_f4(X + (int64_t)b * ldx + 4 * r);
+    }
+  };
+  auto store_pass = [&](int base) {
+#pragma unroll
+    for (int m = 0; m < kF32Pass; ++m) {
+      const int t = base + threadIdx.x + 256 * m;
+      w4a16_stage4(xv[m], t, K, nb, t < tot, xs, sx);
+    }
+  };
+  load_pass(0);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 wa[TC][RP], wb[TC][RP];
+  float da[TC][RP], db[TC][RP];
+  int gi = blockIdx.x;
+  if (gi < ngroups) load_chunk(gi, 0, wa, da);  // uniform
+  __builtin_amdgcn_sched_barrier(0);
+  store_pass(0);
+  for (int base = 256 * kF32Pass; base < tot; base += 256 * kF32Pass) {
+    load_pass(base);
+    store_pass(base);
+  }
+  __syncthreads();
+
+  for (; gi < ngroups; gi += gridDim.x) {
+    const int rbase = gi * ROWS_WG + wv * ROWS_WAVE + grp;
+    float acc[RP][B];
+#pragma unroll
+    for (int p = 0; p < RP; ++p)
+#pragma unroll
+      for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+      // next: chunk c + 1 of this group, or chunk 0 of the next group
+      const bool last = c + 1 == nch;
+      const int gn = last ? gi + (int)gridDim.x : gi, cn = last ? 0 : c + 1;
+      if (gn < ngroups) load_chunk(gn, cn, wb, db);  // uniform
+#pragma unroll
+      for (int i = 0; i < TC; ++i) {
+        const int j = sub + G * (TC * c + i);
+        if (j < nb) w4a16_block<B, RP>(wa[i], da[i], xs, sx, nb, j, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < TC; ++i)
+#pragma unroll
+        for (int p = 0; p < RP; ++p) {
+          wa[i][p] = wb[i][p];
+          da[i][p] = db[i][p];
+        }
+    }
+    float (&flat)[RP * B] = *reinterpret_cast<float(*)[RP * B]>(&acc[0][0]);
+    gsum_last_n<G>(flat);
+#pragma unroll
+    for (int p = 0; p < RP; ++p) {
+      const int row = rbase + p * RPP;
+#pragma unroll
+      for (int r = 0; r < B; ++r)
+        if (sub == G - 1 && row < N) Y[(int64_t)r * ldy + row] = acc[p][r];
+    }
   }
 }
 
@@ -513,17 +632,51 @@ hipError_t launch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, con
   return hipGetLastError();
 }
 
+// the general kernel: x of all rows in LDS (up to the B * K limit), one
+// workgroup per compute unit when that takes more than 80 KiB
+template <int B, int G, int TC>
+hipError_t launch_q4_f32_g(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                           int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+  constexpr int RP = 2;
+  constexpr int rows_wg = 4 * RP * (64 / G);
+  constexpr size_t kMaxLds = (size_t)MMV_Q4F32_MAX_XK * 4 + (size_t)MMV_Q4F32_MAX_XK / 32 * 4;
+  const size_t lds = (size_t)B * K * 4 + (size_t)B * (K / 32) * 4;
+  if (lds > 65536) {  // above the default dynamic-LDS limit: raise it once per kernel
+    static const hipError_t raised = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_gemv_q4_0_f32_g<B, G, RP, TC>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (raised != hipSuccess) return raised;
+  }
+  const int ngroups = (N + rows_wg - 1) / rows_wg;
+  const int per_cu = lds > 81920 ? 1 : 2;
+  const int grid = min(ngroups, per_cu * cu_count());
+  hipLaunchKernelGGL((k_gemv_q4_0_f32_g<B, G, RP, TC>), dim3(grid), dim3(256), lds, s, qs, d, N,
+                     K, X, ldx, Y, ldy);
+  return hipGetLastError();
+}
+
 template <int B>
 hipError_t dispatch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                            int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
-  switch (K / 32) {
-    case 16: return launch_q4_f32<B, 16, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
-    case 32: return launch_q4_f32<B, 32, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
-    case 64: return launch_q4_f32<B, 64, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
-    case 128: return launch_q4_f32<B, 64, 2>(qs, d, N, K, X, ldx, Y, ldy, s);
-    case 256: return launch_q4_f32<B, 64, 4>(qs, d, N, K, X, ldx, Y, ldy, s);
+  const int nb = K / 32;
+  // whole rows per lane, one row group per workgroup: x of B rows in at
+  // most 66 KiB of LDS
+  if ((int64_t)B * K <= 16384) {
+    switch (nb) {
+      case 16: return launch_q4_f32<B, 16, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 32: return launch_q4_f32<B, 32, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 64: return launch_q4_f32<B, 64, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 128: return launch_q4_f32<B, 64, 2>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 256: return launch_q4_f32<B, 64, 4>(qs, d, N, K, X, ldx, Y, ldy, s);
+      default: break;
+    }
   }
-  return hipErrorInvalidValue;
+  // any other K, or more rows: the general kernel with the same lanes per
+  // row (hence the same per-row order and bits)
+  constexpr int TC = B > 4 ? 2 : 4;
+  if (nb <= 16) return launch_q4_f32_g<B, 16, TC>(qs, d, N, K, X, ldx, Y, ldy, s);
+  if (nb <= 32) return launch_q4_f32_g<B, 32, TC>(qs, d, N, K, X, ldx, Y, ldy, s);
+  return launch_q4_f32_g<B, 64, TC>(qs, d, N, K, X, ldx, Y, ldy, s);
 }
 
 }  // namespace

@@ -102,10 +102,8 @@ int check_gemv_q4_0_f32(const mmv_q4_0 *W, const float *X, int64_t ldx, int32_t 
   if (!W || !W->qs || !W->d || !X || !Y) return MMV_E_NULL;
   if (bad_batch(B)) return MMV_E_BATCH;
   const int32_t N = W->N, K = W->K;
-  if (N < 1 || K % 32 != 0 || ldx < K || ldy < N || ldx > kMaxLd || ldy > kMaxLd)
+  if (N < 1 || K < 32 || K % 32 != 0 || ldx < K || ldy < N || ldx > kMaxLd || ldy > kMaxLd)
     return MMV_E_SHAPE;
-  const int nb = K / 32;
-  if (nb != 16 && nb != 32 && nb != 64 && nb != 128 && nb != 256) return MMV_E_SHAPE;
   if ((int64_t)B * K > MMV_Q4F32_MAX_XK) return MMV_E_SHAPE;
   if (!aligned(W->qs, 16) || !aligned(W->d, 2) || !aligned(Y, 4)) return MMV_E_ALIGN;
   if (!aligned(X, 16) || ldx % 4 != 0) return MMV_E_ALIGN;

@@ -191,8 +191,9 @@ def test_gemv_q4_0_f32_validation(L):
     assert g(None, Cp, 512, 1, Dp, 64, None) == E_NULL
     assert g(C.byref(W), None, 512, 1, Dp, 64, None) == E_NULL
     assert g(C.byref(W), Cp, 512, 0, Dp, 64, None) == E_BATCH
-    assert g(C.byref(_q4(A, Bp, 64, 96)), Cp, 96, 1, Dp, 64, None) == E_SHAPE   # K/32 = 3
-    assert g(C.byref(_q4(A, Bp, 64, 4096)), Cp, 4096, 5, Dp, 64, None) == E_SHAPE  # B*K
+    assert g(C.byref(_q4(A, Bp, 64, 80)), Cp, 96, 1, Dp, 64, None) == E_SHAPE    # K % 32
+    assert g(C.byref(_q4(A, Bp, 64, 8192)), Cp, 8192, 5, Dp, 64, None) == E_SHAPE  # B*K
+    assert g(C.byref(_q4(A, Bp, 64, 36896)), Cp, 36896, 1, Dp, 64, None) == E_SHAPE
     assert g(C.byref(W), Cp, 500, 1, Dp, 64, None) == E_SHAPE                  # ldx < K
     assert g(C.byref(W), Cp + 4, 512, 1, Dp, 64, None) == E_ALIGN
     assert g(C.byref(W), Cp, 514, 2, Dp, 64, None) == E_ALIGN                  # ldx % 4

@@ -116,6 +116,9 @@ def _q4(mm, N, K, dev, *tags):
 @pytest.mark.parametrize("N,K,B", [
     (4096, 4096, 1), (11008, 4096, 1), (4096, 4096, 4), (1000, 512, 8), (515, 1024, 3),
     (4097, 2048, 8), (300, 8192, 2), (9, 4096, 4), (1, 512, 1), (2560, 8192, 1),
+    # the general kernel: more rows at K = 4096 (up to the 8 of a batch), any K % 32
+    (11008, 4096, 8), (4096, 4096, 5), (9728, 2560, 8), (2560, 2560, 1), (1000, 96, 3),
+    (333, 11008, 3), (700, 8192, 4), (65, 36864, 1), (2049, 32, 8), (17, 9728, 2),
 ])
 def test_w4a16_parity(mm, orc, dev, N, K, B):
     W, qs, d = _q4(mm, N, K, dev)
@@ -126,11 +129,13 @@ def test_w4a16_parity(mm, orc, dev, N, K, B):
     assert rel_l2_rows(npc(y), ref) <= Q4_TOL
 
 
-def test_w4a16_integer_pin_bit_exact(mm, orc, dev):
+@pytest.mark.parametrize("N,K,B", [(777, 2048, 8), (300, 2560, 8), (129, 4096, 8),
+                                   (65, 11008, 3)])
+def test_w4a16_integer_pin_bit_exact(mm, orc, dev, N, K, B):
     # power-of-two scales and integer activations: every partial sum is an
     # exact fp32 value, so the product must match the float64 oracle exactly
+    # (the whole-row kernel at 2048 x 8, the general one otherwise)
     g = torch.Generator().manual_seed(3)
-    N, K, B = 777, 2048, 8
     qs = torch.randint(0, 256, (N, K // 32, 16), generator=g, dtype=torch.uint8)
     scales = torch.tensor([1.0, 0.5, 2.0, 0.25], dtype=torch.float16)
     d = scales[torch.randint(0, 4, (N, K // 32), generator=g)]
@@ -142,10 +147,13 @@ def test_w4a16_integer_pin_bit_exact(mm, orc, dev):
 
 
 def test_w4a16_batch_invariance(mm, dev):
-    # every (row, b) sum is taken in one order for every B
-    for N, K in ((2000, 2048), (700, 8192)):
+    # every (row, b) sum is taken in one order for every B, in both kernels
+    # (whole rows per lane for B * K <= 16384 and K / 32 in {16, ..., 256},
+    # the general one otherwise: the same lanes per row)
+    for N, K in ((2000, 2048), (700, 8192), (1300, 4096), (129, 2560), (65, 96),
+                 (40, 11008)):
         W, _, _ = _q4(mm, N, K, dev, "inv")
-        Bmax = min(8, 16384 // K)
+        Bmax = min(8, mm.Q4F32_MAX_XK // K)
         X = synth.activations(Bmax, K, 0, "w4a16inv", K, device=dev)
         yB = mm.gemv_q4_0_f32(W, X)
         assert torch.equal(yB, mm.gemv_q4_0_f32(W, X))
