@@ -2,26 +2,37 @@
 """Benchmark of the decode matrix-vector path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
-                    [--only dense,q4,w4a16,lmhead,moe256,moe512,moe512v] [--profile-kernel]
+                    [--only dense,q4,w4a16,lmhead,moe256,moe512,moe512v]
+                    [--profile WORKLOAD]  (one workload's graph, for rocprofv3 counter runs)
+                    [--summarize-counters FETCH_DIR WRITE_DIR]  (counter CSVs -> markdown)
 
 The headline step is one pass over the dense BF16 decode matvec set: 36 layer
 copies (5.85 GB, far past the 256 MB Infinity Cache) of attn-out 2560x2560,
 fused gate+up 2 x 9728x2560 and down 2560x9728, batch 1, each matrix with
 its own synthetic N(0,1) activation row, captured in one HIP graph and
-replayed K times.  `value` is algorithmic bytes / time in GB/s.  The same
-JSON line carries the other workloads (B = 8 dense, Q4_0 x Q8_1 GEMV, the
-W4A16 Q4_0 GEMV, the 248320 x 2560 LM head with its on-device argmax, the
-256- and 512-expert MoE layers) under "sections", the roofline of the
-dominant kernel and the CPU oracle's throughput on a bounded sample.
+replayed K times.  `value` is algorithmic bytes / time in GB/s over exactly
+K replays.  Every timed quantity is also sampled 7 times (K replays each):
+mean, Student-t 95% interval and coefficient of variation (flagged above
+5%).  The same JSON line carries the other workloads (B = 8 dense, Q4_0 x
+Q8_1, W4A16, the 248320 x 2560 LM head with its argmax, the 256- and
+512-expert MoE layers), tokens/s equivalents, the dependent-launch floor,
+the roofline of the dominant kernel, the read probe, a manifest, a GPU
+contention check and the CPU oracle's throughput on bounded samples of the
+five workloads (single-threaded and on every core of the host's share).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
+import math
 import os
+import platform
 import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +41,8 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = ("achieved HBM GB/s (% of MI355X peak) for batch-1 GEMV; MoE layer µs/token")
+REPS = 7               # samples per timed quantity
+CV_FLAG = 0.05         # coefficient of variation above which a sample set is flagged
 
 
 def log(msg):
@@ -56,21 +69,44 @@ def capture(fn):
     return g
 
 
-def time_graph(g, steps, warmup):
-    """Seconds per replay over `steps` replays, bracketed by synchronize and
-    events on the replaying stream."""
+def time_replays(run, steps):
+    """Seconds per call of run() over `steps` calls, bracketed by
+    synchronize and events on the current stream (the graphs replay on it)."""
     import torch
-    for _ in range(warmup):
-        g.replay()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
     for _ in range(steps):
-        g.replay()
+        run()
     e1.record(st)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3 / steps
+
+
+def sample(run, steps, warmup, reps=REPS):
+    """reps samples of seconds per call, each over `steps` calls."""
+    for _ in range(warmup):
+        run()
+    return [time_replays(run, steps) for _ in range(reps)]
+
+
+def stats(samples, scale=1.0):
+    """mean, Student-t 95% half-width, coefficient of variation of samples*scale."""
+    from scipy import stats as st
+    x = [s * scale for s in samples]
+    n = len(x)
+    m = sum(x) / n
+    sd = math.sqrt(sum((v - m) ** 2 for v in x) / (n - 1)) if n > 1 else 0.0
+    half = st.t.ppf(0.975, n - 1) * sd / math.sqrt(n) if n > 1 else float("nan")
+    cv = sd / m if m else float("nan")
+    return dict(mean=m, ci95=half, cv=cv, cv_flag=bool(cv > CV_FLAG), n=n)
+
+
+def timed_graph(g, steps, warmup):
+    """(samples, stats) for replays of graph g."""
+    s = sample(g.replay, steps, warmup)
+    return s, stats(s)
 
 
 # ---------------------------------------------------------------------------
@@ -96,7 +132,9 @@ def build_dense(dev, layers):
     return W
 
 
-def dense_section(mm, dev, W, layers, B, steps, warmup):
+def dense_section(mm, dev, W, layers, B, steps, warmup, eager=False):
+    """One graph over every layer copy; `head` also times exactly `steps`
+    replays on their own (the headline measurement)."""
     import torch
     import synth
     X = {n: synth.activations(layers * B, K, 0, "dense-x", n, B, device=dev).view(layers, B, K)
@@ -108,11 +146,22 @@ def dense_section(mm, dev, W, layers, B, steps, warmup):
             for n in DENSE_SHAPES:
                 mm.gemv_bf16(W[n][l], X[n][l], out=Y[n][l])
     g = capture(step)
-    t = time_graph(g, steps, warmup)
+    for _ in range(warmup):
+        g.replay()
+    t_head = time_replays(g.replay, steps)          # exactly `steps` replays
+    samples = [t_head] + [time_replays(g.replay, steps) for _ in range(REPS - 1)]
+    st = stats(samples, 1e6 / layers)
+    t = t_head
     nbytes = layers * dense_bytes(B)
-    return dict(B=B, layers=layers, launches_per_layer=3, s_per_step=t,
-                us_per_layer=t / layers * 1e6, GBps=nbytes / t / 1e9,
-                frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS, bytes_per_step=nbytes)
+    res = dict(B=B, layers=layers, launches_per_layer=3, s_per_step=t,
+               us_per_layer=t / layers * 1e6, us_per_layer_stats=st,
+               GBps=nbytes / t / 1e9, GBps_mean=nbytes / (st["mean"] * layers / 1e6) / 1e9,
+               frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS, bytes_per_step=nbytes,
+               tokens_per_s_equiv=B / t)
+    if eager:  # the same pass launched from the host one call at a time, no graph
+        te = sample(step, 3, 1, reps=3)
+        res["eager_us_per_layer"] = stats(te, 1e6 / layers)
+    return res
 
 
 def dominant_kernel(mm, dev, W, layers, steps, warmup):
@@ -128,10 +177,29 @@ def dominant_kernel(mm, dev, W, layers, steps, warmup):
         for l in range(layers):
             mm.gemv_bf16(W["gate_up"][l], X[l], out=Y[l])
     g = capture(step)
-    t = time_graph(g, steps, warmup) / layers
+    s, st = timed_graph(g, steps, warmup)
+    t = st["mean"] / layers
     per_launch = 2 * N * K + 4 * K + 4 * N
     return dict(kernel="k_gemv_bf16_xl<1, 5, 8, 1, 5> (gate+up 19456x2560, B=1)", s_per_launch=t,
+                us_per_launch_stats=stats(s, 1e6 / layers),
                 bytes_per_launch=per_launch, GBps=per_launch / t / 1e9)
+
+
+def launch_floor(mm, dev, steps, warmup, n=200):
+    """Time per dependent launch of a one-workgroup kernel (quantize_q8_1 of
+    32 values) in a graph of n of them: the fixed cost each launch of a
+    decode pass pays before its own work."""
+    import torch
+    x = torch.ones((1, 32), device=dev)
+    q = torch.empty(mm.q8_1_bytes(32, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        for _ in range(n):
+            mm.quantize_q8_1(x, out=q)
+    g = capture(step)
+    s, st = timed_graph(g, max(2, steps // 4), warmup)
+    return dict(kernel="k_quantize_q8_1, 1 workgroup", launches_per_graph=n,
+                us_per_launch=stats(s, 1e6 / n))
 
 
 # ---------------------------------------------------------------------------
@@ -145,7 +213,7 @@ def q4_bytes(B):
     return sum(N * K // 32 * 18 + 4 * B * K + 4 * B * N for N, K in Q4_SHAPES)
 
 
-def q4_section(mm, dev, copies, B, steps, warmup):
+def q4_mats(mm, dev, copies):
     import torch
     import synth
     mats = []
@@ -157,6 +225,13 @@ def q4_section(mm, dev, copies, B, steps, warmup):
         d[:] = d1
         mats.append((qs, d))
     Ws = [[mm.Q4_0(qs[c], d[c]) for (qs, d) in mats] for c in range(copies)]
+    return mats, Ws
+
+
+def q4_section(mm, dev, copies, B, steps, warmup, graph_only=False):
+    import torch
+    import synth
+    mats, Ws = q4_mats(mm, dev, copies)
     K = Q4_SHAPES[0][1]
     X = synth.activations(copies * B, K, 0, "q4bench-x", B, device=dev).view(copies, B, K)
     Ys = [[torch.empty((B, N), device=dev) for N, _ in Q4_SHAPES] for _ in range(copies)]
@@ -171,30 +246,27 @@ def q4_section(mm, dev, copies, B, steps, warmup):
             for i, W in enumerate(Ws[c]):
                 mm.gemv_q4_0(W, x=X[c], xq=xq, out=Ys[c][i])
     g = capture(step)
-    t = time_graph(g, steps, warmup)
+    if graph_only:
+        return g, (mats, Ws, X, Ys, xq)
+    s, st = timed_graph(g, steps, warmup)
+    t = st["mean"]
     nbytes = copies * q4_bytes(B)
     del mats, Ws
     return dict(B=B, copies=copies, act_quant="in-kernel" if B == 1 else "separate pass",
                 launches_per_copy=len(Q4_SHAPES) * (1 if B == 1 else 2),
                 stored_GB=copies * sum(N * K // 32 * 18 for N, K in Q4_SHAPES) / 1e9,
-                s_per_step=t, us_per_copy=t / copies * 1e6, GBps=nbytes / t / 1e9,
-                frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS)
+                s_per_step=t, us_per_copy=t / copies * 1e6,
+                us_per_copy_stats=stats(s, 1e6 / copies), GBps=nbytes / t / 1e9,
+                frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS,
+                tokens_per_s_equiv=B / (t / copies * 32))
 
 
-def w4a16_section(mm, dev, copies, B, steps, warmup):
+def w4a16_section(mm, dev, copies, B, steps, warmup, graph_only=False):
     """The Q4_0 shapes with fp32 activations (no Q8_1 step): one launch per
     product at every B."""
     import torch
     import synth
-    mats = []
-    for N, K in Q4_SHAPES:
-        qs1, d1 = synth.q4_0_weights(N, K, 0, "q4bench", N, device=dev)
-        qs = torch.empty((copies,) + tuple(qs1.shape), dtype=torch.uint8, device=dev)
-        d = torch.empty((copies,) + tuple(d1.shape), dtype=torch.float16, device=dev)
-        qs[:] = qs1
-        d[:] = d1
-        mats.append((qs, d))
-    Ws = [[mm.Q4_0(qs[c], d[c]) for (qs, d) in mats] for c in range(copies)]
+    mats, Ws = q4_mats(mm, dev, copies)
     K = Q4_SHAPES[0][1]
     X = synth.activations(copies * B, K, 0, "w4a16bench-x", B, device=dev).view(copies, B, K)
     Ys = [[torch.empty((B, N), device=dev) for N, _ in Q4_SHAPES] for _ in range(copies)]
@@ -204,12 +276,15 @@ def w4a16_section(mm, dev, copies, B, steps, warmup):
             for i, W in enumerate(Ws[c]):
                 mm.gemv_q4_0_f32(W, X[c], out=Ys[c][i])
     g = capture(step)
-    t = time_graph(g, steps, warmup)
+    if graph_only:
+        return g, (mats, Ws, X, Ys)
+    s, st = timed_graph(g, steps, warmup)
+    t = st["mean"]
     nbytes = copies * q4_bytes(B)
     del mats, Ws
     return dict(B=B, copies=copies, launches_per_copy=len(Q4_SHAPES), s_per_step=t,
-                us_per_copy=t / copies * 1e6, GBps=nbytes / t / 1e9,
-                frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS)
+                us_per_copy=t / copies * 1e6, us_per_copy_stats=stats(s, 1e6 / copies),
+                GBps=nbytes / t / 1e9, frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS)
 
 
 # ---------------------------------------------------------------------------
@@ -241,11 +316,14 @@ def lm_head_section(mm, dev, Bs, steps, warmup):
         def both():
             gemv()
             mm.argmax_rows(Y, ids=ids, vals=vals, workspace=ws)
-        t_g = time_graph(capture(gemv), steps, warmup)
-        t_a = time_graph(capture(amax), steps, warmup) / reps
-        t_b = time_graph(capture(both), steps, warmup)
+        sg, stg = timed_graph(capture(gemv), steps, warmup)
+        sa, sta = timed_graph(capture(amax), steps, warmup)
+        sb, stb = timed_graph(capture(both), steps, warmup)
+        t_g, t_a, t_b = stg["mean"], sta["mean"] / reps, stb["mean"]
         gbytes = 2 * LM_VOCAB * LM_HID + 4 * B * LM_HID + 4 * B * LM_VOCAB
-        res[f"B{B}"] = dict(us_gemv=t_g * 1e6, us_argmax=t_a * 1e6, us_gemv_argmax=t_b * 1e6,
+        res[f"B{B}"] = dict(us_gemv=t_g * 1e6, us_gemv_stats=stats(sg, 1e6),
+                            us_argmax=t_a * 1e6, us_gemv_argmax=t_b * 1e6,
+                            us_gemv_argmax_stats=stats(sb, 1e6),
                             gemv_GBps=gbytes / t_g / 1e9,
                             gemv_frac_of_peak=gbytes / t_g / 1e9 / PEAK_HBM_GBPS,
                             argmax_GBps=4 * B * LM_VOCAB / t_a / 1e9,
@@ -260,7 +338,18 @@ def lm_head_section(mm, dev, Bs, steps, warmup):
 # MoE layers
 # ---------------------------------------------------------------------------
 
-def moe_section(mm, dev, E, k, layers, Bs, steps, warmup, H=2048, I=512):
+MOE_LAYERS = {256: 40, 512: 48}   # layer copies of the two MoE configurations
+
+
+def moe_launches(B, H):
+    if B <= 2:
+        return 3
+    if B <= 8:
+        return 5
+    return 6 if H in (1024, 2048) else 5 + (B + 7) // 8
+
+
+def moe_build(mm, dev, E, k, layers, H=2048, I=512):
     import torch
     import synth
     t1 = synth.moe_layer_tensors(E, H, I, 0, "moebench", E, device=dev)
@@ -276,62 +365,111 @@ def moe_section(mm, dev, E, k, layers, Bs, steps, warmup, H=2048, I=512):
     lay = [mm.MoeLayer(big["router"][l], big["gate_qs"][l], big["gate_d"][l], big["up_qs"][l],
                        big["up_d"][l], big["down_qs"][l], big["down_d"][l], k,
                        shared={n: v[l] for n, v in sh.items()}) for l in range(layers)]
+    return lay, (big, sh)
+
+
+def moe_graph(mm, dev, lay, E, k, B, H=2048):
+    import torch
+    import synth
+    layers = len(lay)
+    X = synth.activations(layers * B, H, 0, "moebench-x", E, B, device=dev).view(layers, B, H)
+    Y = torch.empty((layers, B, H), device=dev)
+    ids = torch.empty((layers, B, k), dtype=torch.int32, device=dev)
+    ws = torch.empty((layers, mm.moe_workspace_bytes(lay[0], B)), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        for l in range(layers):
+            mm.moe_layer_decode(lay[l], X[l], out=Y[l], workspace=ws[l], ids=ids[l])
+    return capture(step), (X, Y, ids, ws)
+
+
+def moe_section(mm, dev, E, k, layers, Bs, steps, warmup, H=2048, I=512):
+    import torch
+    lay, keep = moe_build(mm, dev, E, k, layers, H, I)
     expert_bytes = lay[0].expert_bytes()
     stored = layers * (E * H * 4 + (E + 1) * expert_bytes)
     res = dict(E=E, k=k, shared=1, H=H, I=I, layers=layers, stored_GB=stored / 1e9)
     for B in Bs:
-        X = synth.activations(layers * B, H, 0, "moebench-x", E, B, device=dev).view(layers, B, H)
-        Y = torch.empty((layers, B, H), device=dev)
-        ids = torch.empty((layers, B, k), dtype=torch.int32, device=dev)
-        ws = torch.empty((layers, mm.moe_workspace_bytes(lay[0], B)), dtype=torch.uint8,
-                         device=dev)
-
-        def step():
-            for l in range(layers):
-                mm.moe_layer_decode(lay[l], X[l], out=Y[l], workspace=ws[l], ids=ids[l])
-        g = capture(step)
-        t = time_graph(g, steps, warmup)
-        idn = ids.cpu().numpy()
+        g, bufs = moe_graph(mm, dev, lay, E, k, B, H)
+        s, st = timed_graph(g, steps, warmup)
+        t = st["mean"]
+        idn = bufs[2].cpu().numpy()
         uniq = [len(set(idn[l].ravel().tolist())) for l in range(layers)]
         nbytes = sum(E * H * 4 + 4 * B * H * 2 + (u + 1) * expert_bytes for u in uniq)
+        n_cfg = MOE_LAYERS.get(E, layers)
         res[f"B{B}"] = dict(us_per_layer=t / layers * 1e6,
+                            us_per_layer_stats=stats(s, 1e6 / layers),
                             us_per_layer_per_token=t / layers / B * 1e6,
                             mean_unique_experts=sum(uniq) / layers,
                             MB_per_layer=nbytes / layers / 1e6, GBps=nbytes / t / 1e9,
                             frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS,
-                            launches_per_layer=(3 if B <= 2 else 5) if B <= 8
-                            else (6 if H in (1024, 2048) else 5 + (B + 7) // 8))
-        del X, Y, ids, ws, g
+                            launches_per_layer=moe_launches(B, H),
+                            launches_per_token=moe_launches(B, H) * n_cfg / B,
+                            tokens_per_s_equiv=B / (t / layers * n_cfg))
+        del g, bufs
     if len(Bs) > 1 and 1 in Bs:
         res["ratio_Bmax_B1_time"] = res[f"B{max(Bs)}"]["us_per_layer"] / res["B1"]["us_per_layer"]
-    del lay, big, sh
+    del lay, keep
     torch.cuda.empty_cache()
     return res
 
 
-def bw_probe(mm, dev, gb=8.0):
+# ---------------------------------------------------------------------------
+# read probe
+# ---------------------------------------------------------------------------
+
+def bw_probe(mm, dev, steps, warmup, gb=8.0):
     """Achievable streaming-read bandwidth: the library's read probe over a
-    large buffer (128-bit non-temporal loads, grid-stride)."""
+    large buffer (one-shot workgroups, 128-bit non-temporal loads)."""
     import torch
     n = int(gb * 1e9) // 16 * 4
     a = torch.ones(n, dtype=torch.int32, device=dev)
     out = torch.empty(mm.lib().mmv_probe_slots(), dtype=torch.int32, device=dev)
     g = capture(lambda: mm.stream_read(a, out=out))
-    t = time_graph(g, 5, 2)
+    s, st = timed_graph(g, max(2, steps // 4), warmup)
     del a, g
     torch.cuda.empty_cache()
-    return dict(kind="mmv_stream_read over one buffer", GB=n * 4 / 1e9, GBps=n * 4 / t / 1e9)
+    return dict(kind="mmv_stream_read over one buffer (32 KiB per workgroup)", GB=n * 4 / 1e9,
+                GBps=n * 4 / st["mean"] / 1e9, s_stats=st)
 
+
+# ---------------------------------------------------------------------------
+# counter runs (rocprofv3 --pmc): one workload's graph plus calibration kernels
+# ---------------------------------------------------------------------------
 
 CAL_BYTES = 1 << 30
+PROFILE_WORKLOADS = ("dense_gate_up", "q4_b1", "q4_b8", "w4a16_b1", "w4a16_b8", "moe256_b1",
+                     "moe512_b8")
 
 
-def profile_kernel(mm, dev, W, layers):
-    """For rocprofv3 counter runs: the dominant kernel's launches, then two
-    calibration kernels of known traffic: the read probe over 1 GiB (reads
-    only) and an int16 fill of 1 GiB (writes only)."""
+def profile_workload(mm, dev, name):
+    """Replays one workload's graph 3 times, then the two calibration kernels
+    of known traffic: the read probe over exactly 1 GiB (reads only) and an
+    int16 fill of exactly 1 GiB (torch, writes only)."""
     import torch
-    dom = dominant_kernel(mm, dev, W, layers, 3, 1)
+    keep = None
+    if name == "dense_gate_up":
+        W = build_dense(dev, 36)
+        dominant_kernel(mm, dev, W, 36, 3, 1)
+    elif name in ("q4_b1", "q4_b8"):
+        g, keep = q4_section(mm, dev, 32, 1 if name == "q4_b1" else 8, 0, 0, graph_only=True)
+        for _ in range(3):
+            g.replay()
+    elif name in ("w4a16_b1", "w4a16_b8"):
+        g, keep = w4a16_section(mm, dev, 32, 1 if name == "w4a16_b1" else 8, 0, 0,
+                                graph_only=True)
+        for _ in range(3):
+            g.replay()
+    elif name in ("moe256_b1", "moe512_b8"):
+        E, k, B = (256, 8, 1) if name == "moe256_b1" else (512, 10, 8)
+        lay, keep = moe_build(mm, dev, E, k, MOE_LAYERS[E])
+        g, bufs = moe_graph(mm, dev, lay, E, k, B)
+        for _ in range(3):
+            g.replay()
+    else:
+        raise SystemExit(f"unknown workload {name}; one of {PROFILE_WORKLOADS}")
+    torch.cuda.synchronize()
     buf = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
     out = torch.empty(mm.lib().mmv_probe_slots(), dtype=torch.int32, device=dev)
     for _ in range(3):
@@ -341,38 +479,186 @@ def profile_kernel(mm, dev, W, layers):
     for _ in range(3):
         fillbuf.fill_(7)
     torch.cuda.synchronize()
-    log(f"profile run: dominant {dom['s_per_launch'] * 1e6:.2f} us/launch; "
-        f"calibration read and fill of {CAL_BYTES} bytes")
-    return dom
+    log(f"profile run {name} done; calibration read and fill of {CAL_BYTES} bytes")
+
+
+def _counter_rows(d, counter):
+    """{kernel name: [per-dispatch counter values]} from a rocprofv3 --pmc csv."""
+    paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = {}
+    for p in paths:
+        for r in csv.DictReader(open(p)):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", "")
+            out.setdefault(name, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir, title):
+    """Markdown: calibrated HBM bytes per dispatch of every library kernel in
+    the two counter runs.  FETCH_SIZE and WRITE_SIZE are in KiB; the factor
+    per counter comes from the calibration kernel of the same run (1 GiB read
+    by the probe; 1 GiB written by a fill)."""
+    fe, wr = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    probe = [k for k in fe if "k_stream_read" in k]
+    fill = [k for k in wr if "FillFunctor" in k or "fill" in k.lower()]
+    f_cal = (CAL_BYTES / (sum(fe[probe[0]]) / len(fe[probe[0]]) * 1024)) if probe else None
+    w_cal = (CAL_BYTES / (max(wr[fill[0]]) * 1024)) if fill else None
+    lines = [f"# {title}", "",
+             "| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
+             "calibrated MB read | calibrated MB written |", "|---|---|---|---|---|---|"]
+    for k in sorted(set(fe) | set(wr)):
+        if "mmv::" not in k:
+            continue
+        f = sum(fe.get(k, [0])) / max(1, len(fe.get(k, [])))
+        w = sum(wr.get(k, [0])) / max(1, len(wr.get(k, [])))
+        fr = f * 1024 * f_cal / 1e6 if f_cal else float("nan")
+        wb = w * 1024 * w_cal / 1e6 if w_cal else float("nan")
+        lines.append(f"| `{k}` | {len(fe.get(k, []))} | {f:.1f} | {w:.1f} | {fr:.3f} | {wb:.3f} |")
+    lines += ["", f"read calibration factor: {f_cal}", f"write calibration factor: {w_cal}"]
+    return "\n".join(lines)
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle on a bounded sample of the headline workload
+# CPU baseline: the oracle on bounded samples of the five workloads
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(budget_s=12.0):
+def cpu_info():
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(avail, share) if share > 0 else avail
+    return dict(model=model, nproc=os.cpu_count(), affinity=avail, threads=max(1, threads))
+
+
+def _cpu_workloads():
+    """(name, unit bytes, description, make(seed) -> callable) per workload;
+    each callable runs one unit of the workload through the oracle."""
     import numpy as np
     import torch
 
     import oracle
     import synth
-    W = {n: synth.bf16_weights(N, K, 0, "dense", n).view(torch.int16).numpy().view(np.uint16)
-         for n, (N, K) in DENSE_SHAPES.items()}
-    X = {n: synth.activations(1, K, 0, "cpu-x", n).numpy() for n, (N, K) in DENSE_SHAPES.items()}
-    oracle.lib()
-    nbytes, t0, passes = 0, time.perf_counter(), 0
-    while True:
-        for n in DENSE_SHAPES:
-            oracle.gemv_bf16(W[n], X[n])
-        passes += 1
-        nbytes += dense_bytes(1)
+
+    def bf16(N, K, *tags):
+        return synth.bf16_weights(N, K, 0, *tags).view(torch.int16).numpy().view(np.uint16)
+
+    def c1(seed):
+        W = bf16(1024, 1024, "c1")
+        x = synth.activations(1, 1024, seed, "cpu-c1").numpy()
+        return lambda: oracle.gemv_bf16(W, x)
+
+    dense_W = {}
+
+    def c2(seed):
+        if not dense_W:
+            dense_W.update({n: bf16(N, K, "dense", n) for n, (N, K) in DENSE_SHAPES.items()})
+        X = {n: synth.activations(1, K, seed, "cpu-x", n).numpy()
+             for n, (N, K) in DENSE_SHAPES.items()}
+        return lambda: [oracle.gemv_bf16(dense_W[n], X[n]) for n in DENSE_SHAPES]
+
+    q4 = []
+
+    def c3(seed):
+        if not q4:
+            q4.extend((synth.q4_0_weights(N, K, 0, "q4bench", N)) for N, K in Q4_SHAPES)
+        x = synth.activations(1, 4096, seed, "cpu-c3").numpy()
+
+        def run():
+            xq, xds = oracle.quantize_q8_1(x)
+            for qs, d in q4:
+                oracle.gemv_q4_0(qs.numpy(), d.view(torch.int16).numpy().view(np.uint16), xq, xds)
+        return run
+
+    moe = {}
+
+    def moe_cfg(E, k, B):
+        # the oracle's time does not depend on the weight values: uniform
+        # random codes and scales of the right magnitude (numpy, fast)
+        def make(seed):
+            if E not in moe:
+                rng = np.random.default_rng(E)
+                H, I = 2048, 512
+                q = lambda *sh: rng.integers(0, 256, sh + (16,), dtype=np.uint8)
+                d = lambda *sh: (rng.random(sh, dtype=np.float32) * 0.005 + 0.001).astype(
+                    np.float16).view(np.uint16)
+                router = (rng.standard_normal((E, H), dtype=np.float32) * 0.02)
+                moe[E] = oracle.MoE(router, q(E, I, H // 32), d(E, I, H // 32),
+                                    q(E, I, H // 32), d(E, I, H // 32), q(E, H, I // 32),
+                                    d(E, H, I // 32), k,
+                                    shared=(q(I, H // 32), d(I, H // 32), q(I, H // 32),
+                                            d(I, H // 32), q(H, I // 32), d(H, I // 32)))
+            X = synth.activations(B, 2048, seed, "cpu-moe", E, B).numpy()
+            return lambda: moe[E].layer(X)
+        return make
+
+    exp_bytes = 3 * (512 * 2048 // 32) * 18
+    return [
+        ("C1 BF16 1024x1024, B=1", 2 * 1024 * 1024 + 8 * 1024, "GEMV", c1),
+        ("C2 dense BF16 layer (attn-out, gate+up, down), B=1", dense_bytes(1), "layer", c2),
+        ("C3 Q4_0 4096^2 + 11008x4096, B=1", q4_bytes(1), "pair", c3),
+        ("C4 MoE E=256 top-8 + shared, B=1", 256 * 2048 * 4 + 9 * exp_bytes, "layer",
+         moe_cfg(256, 8, 1)),
+        ("C5 MoE E=512 top-10 + shared, B=1", 512 * 2048 * 4 + 11 * exp_bytes, "layer",
+         moe_cfg(512, 10, 1)),
+    ]
+
+
+def cpu_baseline(budget_s=2.5):
+    """Each workload through the oracle: single-threaded for about budget_s,
+    then on every core of the host's share (one independent unit per thread,
+    the oracle's C code running in parallel: ctypes releases the GIL)."""
+    info = cpu_info()
+    res = dict(cpu=info, configs={})
+    T = info["threads"]
+    for name, nbytes, unit, make in _cpu_workloads():
+        run = make(0)
+        run()  # first call: builds and loads the oracle, touches the data
+        n, t0 = 0, time.perf_counter()
+        while True:
+            run()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+        single = dict(units=n, seconds=el, us_per_unit=el / n * 1e6, GBps=n * nbytes / el / 1e9)
+        runs = [make(1 + i) for i in range(T)]
+        counts = [0] * T
+        stop = [False]
+
+        def worker(i):
+            while not stop[0]:
+                runs[i]()
+                counts[i] += 1
+        th = [threading.Thread(target=worker, args=(i,)) for i in range(T)]
+        t0 = time.perf_counter()
+        for t in th:
+            t.start()
+        time.sleep(budget_s)
+        stop[0] = True
+        for t in th:
+            t.join()
         el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return dict(value=nbytes / el / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"{passes} pass(es) of one dense BF16 layer copy (attn-out, gate+up, "
-                       f"down; 162.5 MB of weights), batch 1, single-threaded C oracle, "
-                       f"{el:.1f} s")
+        allc = dict(threads=T, units=sum(counts), seconds=el,
+                    units_per_s=sum(counts) / el, GBps=sum(counts) * nbytes / el / 1e9)
+        res["configs"][name] = dict(unit=unit, algorithmic_bytes_per_unit=nbytes,
+                                    single_thread=single, all_cores=allc)
+        log(f"cpu oracle {name}: {single['GBps']:.2f} GB/s single, "
+            f"{allc['GBps']:.2f} GB/s on {T} threads")
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -399,6 +685,46 @@ def traffic_from_profiles():
 
 
 # ---------------------------------------------------------------------------
+# manifest and contention gate
+# ---------------------------------------------------------------------------
+
+def manifest(torch, dev):
+    h = hashlib.sha256()
+    for sub in ("include", os.path.join("moe_matvec_amd", "csrc")):
+        for p in sorted(glob.glob(os.path.join(ROOT, sub, "*"))):
+            h.update(open(p, "rb").read())
+    lib = os.path.join(ROOT, "moe_matvec_amd", "libmoe_matvec.so")
+    return dict(source_sha256=h.hexdigest()[:16],
+                library_sha256=hashlib.sha256(open(lib, "rb").read()).hexdigest()[:16],
+                torch=torch.__version__, hip=getattr(torch.version, "hip", None),
+                device=torch.cuda.get_device_name(dev), host=platform.node(),
+                utc=time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()), argv=sys.argv[1:])
+
+
+def contention():
+    """Other processes holding the GPU driver open, and the GPU busy percentage,
+    sampled before the timed work (a busy GPU makes every number suspect)."""
+    me = os.getpid()
+    others = []
+    for d in glob.glob("/sys/class/kfd/kfd/proc/*"):
+        pid = os.path.basename(d)
+        if pid.isdigit() and int(pid) != me:
+            others.append(int(pid))
+    busy = []
+    for p in glob.glob("/sys/class/drm/card*/device/gpu_busy_percent"):
+        try:
+            vals = []
+            for _ in range(5):
+                vals.append(int(open(p).read().strip()))
+                time.sleep(0.01)
+            busy.append(max(vals))
+        except (OSError, ValueError):
+            pass
+    flag = bool(others) or any(b > 15 for b in busy)
+    return dict(other_kfd_processes=others, gpu_busy_percent_max=busy, contended=flag)
+
+
+# ---------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -408,9 +734,16 @@ def main():
     ap.add_argument("--only", default="dense,q4,w4a16,lmhead,moe256,moe512,moe512v")
     ap.add_argument("--quick", action="store_true", help="fewer layer copies (smoke timing)")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--profile-kernel", action="store_true",
-                    help="run only the dominant kernel's graph (for rocprofv3 counters)")
+    ap.add_argument("--profile", choices=PROFILE_WORKLOADS,
+                    help="run only this workload's graph and the calibration kernels "
+                         "(for rocprofv3 counter runs)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print a markdown summary of two rocprofv3 counter runs")
+    ap.add_argument("--title", default="HBM traffic per dispatch")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.title))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(the matvec would shard by output rows or by experts, with no exchange "
@@ -422,19 +755,24 @@ def main():
     import moe_matvec_amd as mm
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.profile:
+        profile_workload(mm, dev, args.profile)
+        return
     only = set(args.only.split(","))
     steps, warmup = args.steps, args.warmup
     dense_layers = 4 if args.quick else 36
+    gate = contention()
+    if gate["contended"]:
+        log(f"WARNING: GPU contended before timing: {gate}")
 
     log(f"device {torch.cuda.get_device_name(dev)}; building dense BF16 workload "
         f"({dense_layers} layer copies)")
     W = build_dense(dev, dense_layers)
-    if args.profile_kernel:
-        profile_kernel(mm, dev, W, dense_layers)
-        return
     sections = {}
-    head = dense_section(mm, dev, W, dense_layers, 1, steps, warmup)
-    log(f"dense B=1: {head['GBps']:.0f} GB/s, {head['us_per_layer']:.2f} us/layer")
+    head = dense_section(mm, dev, W, dense_layers, 1, steps, warmup, eager=True)
+    log(f"dense B=1: {head['GBps']:.0f} GB/s, {head['us_per_layer']:.2f} us/layer "
+        f"(mean of {REPS}: {head['us_per_layer_stats']['mean']:.2f} +- "
+        f"{head['us_per_layer_stats']['ci95']:.2f})")
     dom = dominant_kernel(mm, dev, W, dense_layers, steps, warmup)
     log(f"dominant kernel: {dom['GBps']:.0f} GB/s, {dom['s_per_launch']*1e6:.2f} us/launch")
     sections["dense_bf16"] = {"B1": head}
@@ -445,6 +783,11 @@ def main():
         log(f"dense B=8: {b8['GBps']:.0f} GB/s, ratio {sections['dense_bf16']['ratio_B8_B1_time']:.2f}")
     del W
     torch.cuda.empty_cache()
+    sections["launch_floor"] = launch_floor(mm, dev, steps, warmup)
+    fl = sections["launch_floor"]["us_per_launch"]["mean"]
+    sections["dense_bf16"]["B1"]["launches_per_token"] = 3 * dense_layers
+    sections["dense_bf16"]["B1"]["launch_floor_us_per_token"] = 3 * dense_layers * fl
+    log(f"dependent launch floor: {fl:.2f} us per launch")
 
     if "q4" in only:
         q = {}
@@ -475,25 +818,40 @@ def main():
         sections["moe_e256_top8"] = r
         log(f"moe E=256: {r['B1']['us_per_layer']:.2f} us/layer, {r['B1']['GBps']:.0f} GB/s")
     if "moe512" in only:
-        r = moe_section(mm, dev, 512, 10, 4 if args.quick else 48, [1, 4, 8], steps, warmup)
+        r = moe_section(mm, dev, 512, 10, 4 if args.quick else 48, [1, 2, 4, 8], steps, warmup)
         sections["moe_e512_top10"] = r
         log("moe E=512: " + ", ".join(f"B{b} {r[f'B{b}']['us_per_layer']:.2f} us"
-                                      for b in (1, 4, 8)))
+                                      for b in (1, 2, 4, 8)))
     if "moe512v" in only:  # verify / prefill batches: the row-list path (B > 8)
         r = moe_section(mm, dev, 512, 10, 4 if args.quick else 48, [16, 32, 64], steps, warmup)
         sections["moe_e512_top10_verify"] = r
         log("moe E=512 verify: " + ", ".join(
             f"B{b} {r[f'B{b}']['us_per_layer']:.1f} us ({r[f'B{b}']['us_per_layer_per_token']:.2f}"
             f" us/token, {r[f'B{b}']['GBps']:.0f} GB/s)" for b in (16, 32, 64)))
-    sections["bw_probe"] = bw_probe(mm, dev)
+    sections["bw_probe"] = bw_probe(mm, dev, steps, warmup)
+    log(f"read probe: {sections['bw_probe']['GBps']:.0f} GB/s")
 
-    cpu = None if args.no_cpu else cpu_baseline()
+    cpu = None
+    if not args.no_cpu:
+        cb = cpu_baseline()
+        sections["cpu_oracle"] = cb
+        c2 = cb["configs"]["C2 dense BF16 layer (attn-out, gate+up, down), B=1"]
+        cpu = dict(value=c2["all_cores"]["GBps"], unit="GB/s",
+                   cores=c2["all_cores"]["threads"], kind="oracle",
+                   sample=(f"{c2['all_cores']['units']} dense BF16 layer passes (attn-out, "
+                           f"gate+up, down; 162.5 MB of weights, batch 1) by the C oracle on "
+                           f"{c2['all_cores']['threads']} threads in "
+                           f"{c2['all_cores']['seconds']:.1f} s (one independent pass per "
+                           f"thread); single-threaded "
+                           f"{c2['single_thread']['GBps']:.3f} GB/s; CPU "
+                           f"{cb['cpu']['model']}, nproc {cb['cpu']['nproc']}"))
     traffic = traffic_from_profiles()
     roof = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": dom["GBps"] / PEAK_HBM_GBPS, "traffic": traffic,
             "frac_of_probe": dom["GBps"] / sections["bw_probe"]["GBps"],
             "kernel": dom["kernel"], "bytes_per_launch": dom["bytes_per_launch"],
-            "us_per_launch": dom["s_per_launch"] * 1e6}
+            "us_per_launch": dom["s_per_launch"] * 1e6,
+            "us_per_launch_stats": dom["us_per_launch_stats"]}
     line = {
         "metric": METRIC,
         "value": head["GBps"],
@@ -512,9 +870,13 @@ def main():
                                 "launch), down 2560x9728; weights N(0,0.02) bf16, x N(0,1) "
                                 "fp32, fp32 accumulate; one HIP graph per pass"),
                    "weights": "bf16", "batch": 1, "layers": dense_layers,
-                   "frac_of_peak": head["frac_of_peak"]},
+                   "frac_of_peak": head["frac_of_peak"],
+                   "tokens_per_s_equiv": head["tokens_per_s_equiv"]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "stats": head["us_per_layer_stats"],
+        "manifest": manifest(torch, dev),
+        "contention": gate,
         "sections": sections,
     }
     print(json.dumps(line), flush=True)

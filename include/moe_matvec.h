@@ -333,9 +333,11 @@ int moe_layer_decode_noalloc(const mmv_moe_layer *L, const float *X, int64_t ldx
  * Measurement utility: device read-bandwidth probe.  ["hanzo-engine: A
  * Portable Single-Binary LLM Inference Engine", The Bandwidth Wall: decode
  * bandwidth is compared with a measured device roofline probe]
- *   Streams `bytes` (multiple of 16, buf 16-byte aligned) with 128-bit
- *   non-temporal loads from a fixed grid and writes one xor-fold word per
- *   wave to out[0 .. mmv_probe_slots()).  Timing is the caller's.
+ *   Streams `bytes` (multiple of 16, at most 2^38; buf 16-byte aligned) with
+ *   128-bit non-temporal loads, 32 KiB per one-shot workgroup, and writes
+ *   one xor-fold word per wave to out[(wave index) % mmv_probe_slots()]
+ *   (waves sharing a slot overwrite it: the words only keep the loads).
+ *   Timing is the caller's.
  * ------------------------------------------------------------------------ */
 int mmv_probe_slots(void);
 int mmv_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream);

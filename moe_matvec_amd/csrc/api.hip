@@ -217,7 +217,8 @@ int mmv_probe_slots(void) { return mmv::probe_slots(); }
 
 int mmv_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream) {
   if (!buf || !out) return MMV_E_NULL;
-  if (bytes < 16 || bytes % 16 != 0) return MMV_E_SHAPE;
+  // a dispatch counts its work-items in 32 bits: at most 2^24 workgroups of 32 KiB
+  if (bytes < 16 || bytes % 16 != 0 || bytes > ((size_t)1 << 38)) return MMV_E_SHAPE;
   if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0)
     return MMV_E_ALIGN;
   const uintptr_t o = reinterpret_cast<uintptr_t>(out), b = reinterpret_cast<uintptr_t>(buf);

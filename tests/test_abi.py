@@ -263,3 +263,17 @@ def test_noalloc_refuses_oversized_layers(L):
                                       None) == E_BATCH
     assert L.moe_layer_decode_noalloc(C.byref(_layer(top_k=17)), A, 2048, 1, Cp, 2048, None,
                                       None, None) == E_TOPK
+
+
+def test_stream_read_validation(L):
+    s = L.mmv_stream_read
+    n = L.mmv_probe_slots()
+    assert n > 0
+    assert s(None, 1 << 20, Bp, None) == E_NULL
+    assert s(A, 1 << 20, None, None) == E_NULL
+    assert s(A, 8, Bp, None) == E_SHAPE
+    assert s(A, (1 << 20) + 8, Bp, None) == E_SHAPE
+    assert s(A, (1 << 38) + 16, Bp, None) == E_SHAPE        # one dispatch's work-item count
+    assert s(A + 8, 1 << 20, Bp, None) == E_ALIGN
+    assert s(A, 1 << 20, Bp + 2, None) == E_ALIGN
+    assert s(A, 1 << 20, A + 64, None) == E_ALIAS
