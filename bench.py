@@ -5,6 +5,7 @@
                     [--only dense,q4,w4a16,lmhead,moe256,moe512,moe512v]
                     [--profile WORKLOAD]  (one workload's graph, for rocprofv3 counter runs)
                     [--summarize-counters FETCH_DIR WRITE_DIR]  (counter CSVs -> markdown)
+                    [--summarize-trace TRACE_DIR]  (kernel-trace CSV -> markdown)
 
 The headline step is one pass over the dense BF16 decode matvec set: 36 layer
 copies (5.85 GB, far past the 256 MB Infinity Cache) of attn-out 2560x2560,
@@ -483,30 +484,34 @@ def profile_workload(mm, dev, name):
 
 
 def _counter_rows(d, counter):
-    """{kernel name: [per-dispatch counter values]} from a rocprofv3 --pmc csv."""
+    """{full kernel name: [per-dispatch counter values]} from rocprofv3 --pmc csv files."""
     paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no counter_collection.csv under {d}")
     out = {}
     for p in paths:
         for r in csv.DictReader(open(p)):
-            if r.get("Counter_Name") != counter:
-                continue
-            name = re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", "")
-            out.setdefault(name, []).append(float(r["Counter_Value"]))
+            if r.get("Counter_Name") == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
     return out
+
+
+def _short(name):
+    """mmv::k_name<template args> from a full kernel name."""
+    name = name.replace("void ", "")
+    return re.sub(r"\(.*", "", name) if name.startswith("mmv::") else name[:60]
 
 
 def summarize_counters(fetch_dir, write_dir, title):
     """Markdown: calibrated HBM bytes per dispatch of every library kernel in
     the two counter runs.  FETCH_SIZE and WRITE_SIZE are in KiB; the factor
     per counter comes from the calibration kernel of the same run (1 GiB read
-    by the probe; 1 GiB written by a fill)."""
+    by the probe; 1 GiB written by an int16 fill, the largest fill dispatch)."""
     fe, wr = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
-    probe = [k for k in fe if "k_stream_read" in k]
-    fill = [k for k in wr if "FillFunctor" in k or "fill" in k.lower()]
-    f_cal = (CAL_BYTES / (sum(fe[probe[0]]) / len(fe[probe[0]]) * 1024)) if probe else None
-    w_cal = (CAL_BYTES / (max(wr[fill[0]]) * 1024)) if fill else None
+    probe = [v for k, vs in fe.items() if "k_stream_read" in k for v in vs]
+    fills = [v for k, vs in wr.items() if "FillFunctor" in k for v in vs]
+    f_cal = CAL_BYTES / (sum(probe) / len(probe) * 1024) if probe else None
+    w_cal = CAL_BYTES / (max(fills) * 1024) if fills else None
     lines = [f"# {title}", "",
              "| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
              "calibrated MB read | calibrated MB written |", "|---|---|---|---|---|---|"]
@@ -517,8 +522,39 @@ def summarize_counters(fetch_dir, write_dir, title):
         w = sum(wr.get(k, [0])) / max(1, len(wr.get(k, [])))
         fr = f * 1024 * f_cal / 1e6 if f_cal else float("nan")
         wb = w * 1024 * w_cal / 1e6 if w_cal else float("nan")
-        lines.append(f"| `{k}` | {len(fe.get(k, []))} | {f:.1f} | {w:.1f} | {fr:.3f} | {wb:.3f} |")
+        lines.append(f"| `{_short(k)}` | {len(fe.get(k, []))} | {f:.1f} | {w:.1f} | {fr:.3f} | "
+                     f"{wb:.3f} |")
     lines += ["", f"read calibration factor: {f_cal}", f"write calibration factor: {w_cal}"]
+    return "\n".join(lines)
+
+
+def summarize_trace(trace_dir, title):
+    """Markdown: every library kernel's calls and durations from a rocprofv3
+    --kernel-trace run, sorted by total time, and the dominant kernel's
+    dispatches split by grid size."""
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    per, grid = {}, {}
+    for p in paths:
+        for r in csv.DictReader(open(p)):
+            if "mmv::" not in r["Kernel_Name"]:
+                continue
+            k = _short(r["Kernel_Name"])
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per.setdefault(k, []).append(us)
+            if k.startswith("mmv::k_gemv_bf16_xl<1, 5, 8, 1, 5>"):
+                grid.setdefault(int(r["Grid_Size_X"]), []).append(us)
+    lines = [f"# {title}", "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    if grid:
+        lines += ["", "`k_gemv_bf16_xl<1, 5, 8, 1, 5>` dispatches by grid (threads; 512-thread "
+                  "workgroups of 8 rows):", "", "| grid threads | rows (N) | dispatches | avg us | "
+                  "min us |", "|---|---|---|---|---|"]
+        for gsz, v in sorted(grid.items()):
+            lines.append(f"| {gsz} | {gsz // 512 * 8} | {len(v)} | {sum(v) / len(v):.2f} | "
+                         f"{min(v):.2f} |")
     return "\n".join(lines)
 
 
@@ -739,10 +775,15 @@ def main():
                          "(for rocprofv3 counter runs)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print a markdown summary of two rocprofv3 counter runs")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print a markdown summary of a rocprofv3 --kernel-trace run")
     ap.add_argument("--title", default="HBM traffic per dispatch")
     args = ap.parse_args()
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.title))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.title))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
