@@ -559,6 +559,78 @@ def summarize_trace(trace_dir, title):
 
 
 # ---------------------------------------------------------------------------
+# MoE kernel timeline (the timeline build of the library)
+# ---------------------------------------------------------------------------
+
+TL_KINDS = [("router", ["start", "end"]),
+            ("router (x in LDS)", ["start", "x staged"]),
+            ("top-k + row lists", ["start", "top-k done", "lists published"]),
+            ("gate/up", ["start", "routing known", "weights issued", "products done",
+                         "Q8_1(h) stored"]),
+            ("down (one kernel)", ["start", "row lists in LDS", "weights issued",
+                                   "Q8_1(h) staged", "stored"]),
+            ("down by expert", ["start", "weights issued", "stored"]),
+            ("combine", ["start", "stored"])]
+
+
+def moe_timeline(mm, dev, warmup):
+    """Markdown: per kernel of one MoE layer (the last of a graph replay over
+    every layer copy), the workgroups' times at each noted point relative to
+    the first router workgroup's start (min / median / max, us), and the gaps
+    between kernels; also the layer time of this build next to it."""
+    import numpy as np
+    import torch
+    tl_bytes = mm.lib().mmv_timeline(None, 1, None)
+    if tl_bytes == 0:
+        raise SystemExit("this library notes no timeline: build it with "
+                         "`python -m moe_matvec_amd.build --timeline`")
+    n_kinds, slots, points = len(TL_KINDS), 4096, 8
+    buf = torch.zeros(tl_bytes // 8, dtype=torch.int64, device=dev)
+    lines = ["| workload | kernel | workgroups | point | min | median | max |",
+             "|---|---|---|---|---|---|---|"]
+    gaps = []
+    for E, k, Bs in ((256, 8, [1]), (512, 10, [1, 8])):
+        layers = MOE_LAYERS[E]
+        lay, keep = moe_build(mm, dev, E, k, layers)
+        for B in Bs:
+            g, bufs = moe_graph(mm, dev, lay, E, k, B)
+            s, st = timed_graph(g, 5, warmup)
+            torch.cuda.synchronize()
+            mm.lib().mmv_timeline(None, 1, torch.cuda.current_stream().cuda_stream)
+            g.replay()
+            mm.lib().mmv_timeline(buf.data_ptr(), 0, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            a = buf.cpu().numpy().reshape(n_kinds, slots, points).astype(np.float64) / 100.0
+            # every router workgroup runs in every layer: their stamps are the last
+            # layer's; a workgroup of another kernel that exited early (an
+            # unused expert slot) may hold an earlier layer's stamps: dropped
+            t0 = min(a[i][a[i][:, 0] > 0, 0].min() for i in (0, 1) if (a[i][:, 0] > 0).any())
+            wl = f"E={E} k={k} B={B} ({st['mean'] / layers * 1e6:.2f} us/layer in this build)"
+            order = []
+            for i, (kname, pnames) in enumerate(TL_KINDS):
+                rows = a[i][a[i][:, 0] >= t0]
+                if len(rows) == 0:
+                    continue
+                last = len(pnames) - 1
+                rows = rows[rows[:, last] > 0]
+                order.append((rows[:, 0].min() - t0, rows[:, last].max() - t0, kname))
+                for j, pn in enumerate(pnames):
+                    v = rows[:, j] - t0
+                    lines.append(f"| {wl} | {kname} | {len(rows)} | {pn} | {v.min():.2f} | "
+                                 f"{np.median(v):.2f} | {v.max():.2f} |")
+                wl = ""
+            order.sort()
+            for (s0, e0, n0), (s1, e1, n1) in zip(order, order[1:]):
+                gaps.append(f"| E={E} B={B} | {n0} -> {n1} | {s1 - e0:.2f} |")
+            del g, bufs
+        del lay, keep
+        torch.cuda.empty_cache()
+    return "\n".join(lines + ["", "Gap from the last workgroup of a kernel to the first of the "
+                               "next (us):", "", "| workload | kernels | gap |", "|---|---|---|"]
+                      + gaps)
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on bounded samples of the five workloads
 # ---------------------------------------------------------------------------
 
@@ -777,6 +849,9 @@ def main():
                     help="print a markdown summary of two rocprofv3 counter runs")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print a markdown summary of a rocprofv3 --kernel-trace run")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-phase timeline of the MoE kernels (needs the timeline build, "
+                         "libmoe_matvec_timeline.so)")
     ap.add_argument("--title", default="HBM traffic per dispatch")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -794,8 +869,17 @@ def main():
 
     import torch
     import moe_matvec_amd as mm
+    if args.timeline:
+        from moe_matvec_amd import build as mmbuild
+        if not os.path.exists(mmbuild.SO_TIMELINE):
+            raise SystemExit("build the timeline library first: "
+                             "python -m moe_matvec_amd.build --timeline")
+        mm.library_path = mmbuild.SO_TIMELINE
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.timeline:
+        print(moe_timeline(mm, dev, args.warmup))
+        return
     if args.profile:
         profile_workload(mm, dev, args.profile)
         return

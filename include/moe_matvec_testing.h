@@ -17,6 +17,8 @@
 #ifndef MOE_MATVEC_TESTING_H
 #define MOE_MATVEC_TESTING_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -56,6 +58,18 @@ enum mmv_path_switch {
 int mmv_set_path(int which, int value);
 /* Current value of switch `which` (0 for an unknown switch). */
 int mmv_get_path(int which);
+
+/* Timeline of the MoE kernels, for measurement.  Only a library built with
+ * the timeline option (python -m moe_matvec_amd.build --timeline ->
+ * libmoe_matvec_timeline.so) notes, per workgroup of the MoE kernels, the
+ * chip's 100 MHz constant clock at fixed points of its work; the normal
+ * library does nothing here and returns 0.  Copies the array of the last
+ * launches ([7 kernel kinds: router, LDS router, top-k + row lists, gate/up,
+ * down, down by expert, combine][4096 workgroups][8 points] uint64, 0 where
+ * nothing was noted) to the device buffer dst when dst is not NULL, then
+ * zeroes it when `clear` is nonzero; both ordered on `stream`.  Returns the
+ * array's size in bytes. */
+size_t mmv_timeline(void *dst, int clear, void *stream);
 
 #ifdef __cplusplus
 }

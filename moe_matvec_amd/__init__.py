@@ -104,6 +104,7 @@ def lib():
             "mmv_noalloc_ws_bytes": (C.c_size_t, []),
             "moe_layer_decode_noalloc": (C.c_int, [C.POINTER(_Layer), _P, _i64, _i32, _P, _i64,
                                                    _P, _P, _P]),
+            "mmv_timeline": (C.c_size_t, [_P, C.c_int, _P]),
             "mmv_set_path": (C.c_int, [C.c_int, C.c_int]),
             "mmv_get_path": (C.c_int, [C.c_int]),
             "mmv_probe_slots": (C.c_int, []),

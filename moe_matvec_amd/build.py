@@ -1,6 +1,8 @@
 """Build libmoe_matvec.so in-tree with hipcc for gfx950.
 
-    python -m moe_matvec_amd.build          # compile (always recompiles)
+    python -m moe_matvec_amd.build             # compile (always recompiles)
+    python -m moe_matvec_amd.build --timeline  # the measurement build with MoE kernel
+                                               # timestamps: libmoe_matvec_timeline.so
 
 The library is one shared object: the HIP kernels, the host launchers and the
 extern "C" ABI of include/moe_matvec.h.  Each source is compiled to an object
@@ -19,6 +21,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libmoe_matvec.so")
+SO_TIMELINE = os.path.join(HERE, "libmoe_matvec_timeline.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "validate.cpp", "gemv_bf16.hip", "gemv_q4_0.hip", "moe.hip", "probe.hip",
@@ -44,7 +47,12 @@ def _noise_free(text: str) -> str:
     return "\n".join(keep)
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
+def build(verbose: bool = False, extra_flags=None, timeline: bool = False) -> str:
+    """Compile every source and link the library (the timeline build adds
+    -DMMV_TIMELINE and writes libmoe_matvec_timeline.so instead)."""
+    out = SO_TIMELINE if timeline else SO
+    if timeline:
+        extra_flags = list(extra_flags or []) + ["-DMMV_TIMELINE=1"]
     jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with tempfile.TemporaryDirectory(prefix="mmv_build_") as tmpdir:
         objs, running, failed = [], [], []
@@ -79,7 +87,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
                 sys.stderr.write(f"--- {src}\n{msg}\n")
             raise RuntimeError("hipcc failed building libmoe_matvec.so: "
                                + ", ".join(s for s, _ in failed))
-        tmp = SO + ".tmp"
+        tmp = out + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -87,9 +95,9 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         if res.returncode != 0:
             sys.stderr.write(res.stdout + res.stderr)
             raise RuntimeError("hipcc failed linking libmoe_matvec.so")
-        os.replace(tmp, SO)
-    return SO
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))

@@ -52,6 +52,40 @@ namespace mmv {
 constexpr int kMaxPairs = MMV_MAX_BATCH * MMV_MAX_TOPK;  // 128
 
 // ---------------------------------------------------------------------------
+// Timeline build (-DMMV_TIMELINE, a separate library for measurement): thread
+// 0 of every workgroup of the MoE kernels notes the chip's constant 100 MHz
+// clock (s_memrealtime) at fixed points into LDS, and at its end writes them
+// to a device array: [kernel kind][workgroup][point].  In the normal build
+// the macros are empty.
+// ---------------------------------------------------------------------------
+enum TlKind { kTlRouter, kTlRouterLds, kTlTopkGather, kTlGateUp, kTlDown, kTlDownPart,
+              kTlCombine, kTlKinds };
+constexpr int kTlSlots = 4096, kTlPoints = 8;
+#ifdef MMV_TIMELINE
+__device__ uint64_t g_timeline[kTlKinds][kTlSlots][kTlPoints];
+__shared__ uint64_t s_timeline[kTlPoints];
+#define MMV_TL(i)                                                                        \
+  do {                                                                                   \
+    if (threadIdx.x == 0) s_timeline[i] = __builtin_amdgcn_s_memrealtime();             \
+  } while (0)
+#define MMV_TL_END(kind, i)                                                              \
+  do {                                                                                   \
+    if (threadIdx.x == 0) {                                                              \
+      s_timeline[i] = __builtin_amdgcn_s_memrealtime();                                  \
+      if (blockIdx.x < (unsigned)kTlSlots)                                               \
+        for (int q_ = 0; q_ <= (i); ++q_) g_timeline[kind][blockIdx.x][q_] = s_timeline[q_]; \
+    }                                                                                    \
+  } while (0)
+#else
+#define MMV_TL(i) \
+  do {            \
+  } while (0)
+#define MMV_TL_END(kind, i) \
+  do {                      \
+  } while (0)
+#endif
+
+// ---------------------------------------------------------------------------
 // router rows: logits[b * ldl + e] = R[e] . x_b (row E = shared gate row)
 // ---------------------------------------------------------------------------
 // HC = H / 256 float4 chunks per lane (compile time: every load issued up
@@ -300,6 +334,7 @@ __global__ __launch_bounds__(256) void k_router_lds(const float *__restrict__ R,
   const int e0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RW;
   const int rows = E + (shg ? 1 : 0);
   const int b0 = blockIdx.y * 8, nb = min(8, B - b0);
+  MMV_TL(0);
   f32x4 r[RW][HC];
 #pragma unroll
   for (int j = 0; j < RW; ++j) {
@@ -318,6 +353,7 @@ __global__ __launch_bounds__(256) void k_router_lds(const float *__restrict__ R,
 #pragma unroll
   for (int m = 0; m < PER; ++m) xs4[threadIdx.x + 256 * m] = xv[m];
   __syncthreads();
+  MMV_TL_END(kTlRouterLds, 1);  // x staged: the products follow (thread 0's wave)
   if (e0 >= rows) return;  // uniform over the wave; no barrier follows
   auto chain = [&](float &acc, const f32x4 &w, const f32x4 &x) {
     acc = fmaf(w.x, x.x, acc);
@@ -708,6 +744,7 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // every weight load issued before any wait
+  MMV_TL(2);
   mid();
   const XStage st = xstage_at(smem, B, H);
   if constexpr (PRE > 0) {
@@ -816,6 +853,7 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
     }
   }
   __syncthreads();
+  MMV_TL(3);
 
   // Q8_1 epilogue: the 32 h values of (row r, tile) are one block
   if (threadIdx.x < (unsigned)(8 * nr)) {
@@ -842,6 +880,7 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
       }
     }
   }
+  MMV_TL_END(kTlGateUp, 4);
 }
 
 // both scale planes 16-byte aligned (the chunked scale loads)
@@ -873,6 +912,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
   const int slot0 = blockIdx.x / ntiles, tile = blockIdx.x - slot0 * ntiles;
   const bool shared_slot = a.routed_shared && slot0 == 0;
   const int slot = slot0 - a.routed_shared;
+  MMV_TL(0);
 
   // B <= 2: the activations of every row are loaded before routing (they do
   // not depend on it) and stay in registers until the weights are in flight
@@ -896,6 +936,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     }
     ids = s_ids;
   }
+  MMV_TL(1);  // routing known (top-k inside, or the row lists next)
   // row lists for the down kernel (and the debug copies), from block 0
   auto publish_gather = [&]() {
     const int t = threadIdx.x;
@@ -1000,10 +1041,12 @@ __global__ __launch_bounds__(256) void k_moe_router(MoeArgs a) {
   const mmv_moe_layer &L = a.L;
   const int E = L.n_experts, H = L.hidden;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  MMV_TL(0);
   if (e < E + (L.shared_gate_row ? 1 : 0)) {
     const float *row = e < E ? L.router + (int64_t)e * H : L.shared_gate_row;
     router_row<B, HC>(row, H, a.X, a.ldx, a.logits + e, E + 1);
   }
+  MMV_TL_END(kTlRouter, 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1019,8 +1062,10 @@ __global__ __launch_bounds__(512) void k_moe_topk_gather(MoeArgs a) {
   __shared__ float s_sw[MMV_MAX_BATCH];
   const mmv_moe_layer &L = a.L;
   const int E = L.n_experts, k = L.top_k, Bk = B * k, t = threadIdx.x;
+  MMV_TL(0);
   topk_any(a.logits, E + 1, E, B, k, L.shared_gate_row ? 1 : 0, s_ids, s_w, s_sw);
   __syncthreads();
+  MMV_TL(1);
   if (t < Bk) { a.ids_out[t] = s_ids[t]; a.weights_out[t] = s_w[t]; }
   if (t < B) a.shared_w_out[t] = s_sw[t];
   build_gather<cmin(B * MMV_MAX_TOPK, kMaxPairs), 64 * B>(s_ids, Bk, E, g);
@@ -1029,6 +1074,7 @@ __global__ __launch_bounds__(512) void k_moe_topk_gather(MoeArgs a) {
   if (t < g.U) gl[1 + t] = g.unique[t];
   if (t <= g.U) gl[1 + Bk + t] = g.offsets[t];
   if (t < g.offsets[g.U]) gl[2 + 2 * Bk + t] = g.pairs[t];
+  MMV_TL_END(kTlTopkGather, 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -1106,6 +1152,7 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
   const bool has_sh = L.sh_down_qs != nullptr;
   const int t = threadIdx.x;
 
+  MMV_TL(0);
   // ---- prologue loads: row lists and pair weights
   const int gl_n = 3 * Bk + 2;
   const int g0 = a.gather[min(t, gl_n - 1)];
@@ -1132,6 +1179,7 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
   // pairs that no expert list holds (ids outside [0, E)) add zero
   for (int i = t; i < 4 * (kMaxPairs + MMV_MAX_BATCH); i += 64 * NWV) (&s_dot[0][0])[i] = 0.0f;
   __syncthreads();
+  MMV_TL(1);  // row lists in LDS
   const int U = s_U;
   // per-wave expert lists: class = id % NWV, ascending; shared expert (index
   // U) appended to wave 0
@@ -1202,6 +1250,7 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
     if (n > NF) load_chunk(NF, cha);  // uniform over the wave
   }
   __builtin_amdgcn_sched_barrier(0);
+  MMV_TL(2);
 
   // ---- Q8_1(h) from global memory straight into LDS (global_load_lds: a
   // wave instruction fills 64 consecutive 16- or 4-byte LDS slots, lane l
@@ -1237,6 +1286,7 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS writes done; the barrier publishes them
   __syncthreads();
+  MMV_TL(3);  // Q8_1(h) staged
 
   // Each pair's product with its expert is formed whole, in one order for
   // every B and whichever wave holds the expert: per lane the blocks it owns
@@ -1377,6 +1427,7 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
     const int r = blockIdx.x * 4 + q;
     if (sub == 0 && r < H) a.Y[(int64_t)b * a.ldy + r] = v;
   }
+  MMV_TL_END(kTlDown, 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -1413,6 +1464,7 @@ __global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
   const bool shared_slot = has_sh && slot0 == 0;
   const int u = slot0 - has_sh;  // < Bk: every list entry read below is in bounds
   const int32_t *gl = a.gather;
+  MMV_TL(0);
   const uint8_t *dq;
   const uint16_t *dd;
   int np, pbase;
@@ -1449,6 +1501,7 @@ __global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  MMV_TL(1);
   const HqView hv = hq_view(a.hq, a.P, I);
   auto store_dots = [&](int p, float (&v)[RP]) {
     gsum_last_n<16, RP>(v);  // the same sums as row16_sum, interleaved
@@ -1530,6 +1583,7 @@ __global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
   };
   pair_group(0);
   for (int r0 = NP; r0 < np; r0 += NP) pair_group(r0);  // uniform
+  MMV_TL_END(kTlDownPart, 2);
 }
 
 // Y[b][n] = tree_j (w[b k + j] dot_{b k + j}[n]) + s_b dot_{Bk + b}[n] with
@@ -1541,6 +1595,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
   const int H = L.hidden, k = L.top_k, E = L.n_experts, Bk = (B > 0 ? B : a.nrows) * k;
   const int b = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
   const int nc = min(n, H - 1);
+  MMV_TL(0);
   const bool has_sh = L.sh_down_qs != nullptr;
   static_assert(MMV_MAX_TOPK <= 16, "slots per row");
   float d[16], pr[16];
@@ -1561,6 +1616,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs a) {
   float v = down_combine_tree(pr);
   if (has_sh) v = fmaf(a.shared_w ? a.shared_w[b] : 1.0f, dsh, v);
   if (n < H) a.Y[(int64_t)b * a.ldy + n] = v;
+  if (b == 0) MMV_TL_END(kTlCombine, 1);
   if (a.has_dbg && a.dbg.down_out && n < H) {  // each pair's product, unweighted
     for (int j = 0; j < k; ++j) {
       const int e = a.ids[b * k + j];
@@ -1996,3 +2052,25 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
 }
 
 }  // namespace mmv
+
+// Timeline of the last MoE launches (timeline builds only): copies the stamp
+// array ([7 kinds][4096 workgroups][8 points] uint64 of the 100 MHz clock,
+// 0 where nothing was noted) to dst if dst is given, then clears it if
+// `clear`.  Returns the array's size in bytes, or 0 in the normal build.
+extern "C" size_t mmv_timeline(void *dst, int clear, void *stream) {
+#ifdef MMV_TIMELINE
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void *addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(mmv::g_timeline)) != hipSuccess) return 0;
+  if (dst && hipMemcpyAsync(dst, addr, sizeof(mmv::g_timeline), hipMemcpyDeviceToDevice, s) !=
+                 hipSuccess)
+    return 0;
+  if (clear && hipMemsetAsync(addr, 0, sizeof(mmv::g_timeline), s) != hipSuccess) return 0;
+  return sizeof(mmv::g_timeline);
+#else
+  (void)dst;
+  (void)clear;
+  (void)stream;
+  return 0;
+#endif
+}
