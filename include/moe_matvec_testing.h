@@ -31,7 +31,7 @@ enum mmv_path_switch {
    * k-steps are grouped differently, so rows agree within rounding) */
   MMV_PATH_BF16_WAVES = 1,
   /* gemv_bf16, B = 1, K % 512 == 0: waves per workgroup of the kernel that
-   * stages x on chip (2, 4, 8 or 16); -1 = the per-wave kernel */
+   * stages x on chip (2, 4, 5, 8, 10 or 16); -1 = the per-wave kernel */
   MMV_PATH_BF16_XL = 2,
   /* gemv_bf16, B >= 2, K % 512 == 0: matrix-core shape
    * 10000 * rows + 1000 * waves + 100 * chunks in flight + tile rows,

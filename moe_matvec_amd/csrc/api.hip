@@ -72,6 +72,22 @@ int path_switch(int which) {
   if (which < 0 || which >= MMV_PATH_COUNT) return 0;
   return g_path[which].load(std::memory_order_relaxed);
 }
+
+// a data race between first calls on a device only stores the same value
+// twice; a device the query fails on counts as 256 CUs
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 }  // namespace mmv
 
 extern "C" {

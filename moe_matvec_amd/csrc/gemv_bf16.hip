@@ -581,10 +581,27 @@ hipError_t launch_xl(const Bf16Args &a) {
 
 template <int NI>
 hipError_t dispatch_xl(const Bf16Args &a, int WPB) {
+  if (WPB == 10) return launch_xl<1, NI, 10, 1>(a);
+  if (WPB == 5) return launch_xl<1, NI, 5, 1>(a);
   if (WPB >= 16) return launch_xl<1, NI, 16, 1>(a);
   if (WPB >= 8) return launch_xl<1, NI, 8, 1>(a);
   if (WPB >= 4) return launch_xl<1, NI, 4, 1>(a);
   return launch_xl<1, NI, 2, 1>(a);
+}
+
+// waves per workgroup (one row each) for N rows at B = 1 when rows are few:
+// of 10, 8, 5 and 4, the one whose rounds of one workgroup per CU
+// leave the fewest wave slots empty; ties go to the larger workgroup
+inline int xl_waves(int N) {
+  const int64_t cus = cu_count();
+  int best = 10;
+  int64_t best_idle = -1;
+  for (int w : {10, 8, 5, 4}) {
+    const int64_t wgs = (N + w - 1) / w, rounds = (wgs + cus - 1) / cus;
+    const int64_t idle = rounds * cus * w - N;
+    if (best_idle < 0 || idle < best_idle) best = w, best_idle = idle;
+  }
+  return best;
 }
 
 template <int B>
@@ -601,11 +618,13 @@ hipError_t dispatch_b(const Bf16Args &a) {
     const int kr = path_switch(MMV_PATH_BF16_ROWS), kw = path_switch(MMV_PATH_BF16_WAVES);
     const int kx = path_switch(MMV_PATH_BF16_XL);
     if (a.K % 512 == 0) {
-      // x staged once per workgroup in LDS: measured faster for long rows
-      // (2560 x 9728: 4 waves per workgroup) and for many rows (19456 x 2560:
-      // 8); for 2560 x 2560 the per-wave kernel is as fast
+      // x staged once per workgroup in LDS.  Many rows (19456 x 2560): 8
+      // waves per workgroup.  Fewer rows: a workgroup size that spreads the
+      // rows evenly over the CUs (2560 x 9728: 256 workgroups of 10 waves,
+      // 9.9 us, against 10.9 us for 640 of 4, whose last round leaves CUs
+      // idle; 2560 x 2560: 4.25 against 4.31 us for the per-wave kernel)
       const int NI = a.K / 512;
-      const int xl = kx != 0 ? kx : (NI >= 8 ? 4 : (NI >= 4 && a.N >= 8192 ? 8 : -1));
+      const int xl = kx != 0 ? kx : (NI >= 4 && a.N >= 8192 ? 8 : (NI >= 4 ? xl_waves(a.N) : -1));
       if (xl > 0) {
         switch (NI) {
           case 4: return dispatch_xl<4>(a, xl);

@@ -515,26 +515,6 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32_g(
   }
 }
 
-namespace {
-
-// compute units of the current device, queried once per device (a data
-// race between first calls only writes the same value twice)
-int cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
-}  // namespace
-
 template <int B, int G, int RP>
 static hipError_t launch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
                             const float *X, int64_t ldx, const uint8_t *Xq, float *Y,

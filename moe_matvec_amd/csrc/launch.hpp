@@ -14,6 +14,9 @@ namespace mmv {
 // value of a kernel-variant switch (moe_matvec_testing.h); 0 = automatic
 int path_switch(int which);
 
+// compute units of the current device (queried once per device)
+int cu_count();
+
 hipError_t run_gemv_bf16(const uint16_t *W, int N, int K, int64_t ldw,
                          const float *X, int64_t ldx, int B, float *Y, int64_t ldy,
                          hipStream_t s);

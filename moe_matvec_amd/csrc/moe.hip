@@ -60,8 +60,8 @@ constexpr int kMaxPairs = MMV_MAX_BATCH * MMV_MAX_TOPK;  // 128
 // ---------------------------------------------------------------------------
 enum TlKind { kTlRouter, kTlRouterLds, kTlTopkGather, kTlGateUp, kTlDown, kTlDownPart,
               kTlCombine, kTlKinds };
-constexpr int kTlSlots = 4096, kTlPoints = 8;
 #ifdef MMV_TIMELINE
+constexpr int kTlSlots = 4096, kTlPoints = 8;
 __device__ uint64_t g_timeline[kTlKinds][kTlSlots][kTlPoints];
 __shared__ uint64_t s_timeline[kTlPoints];
 #define MMV_TL(i)                                                                        \
@@ -1040,7 +1040,7 @@ template <int B, int HC>
 __global__ __launch_bounds__(256) void k_moe_router(MoeArgs a) {
   const mmv_moe_layer &L = a.L;
   const int E = L.n_experts, H = L.hidden;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int e = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   MMV_TL(0);
   if (e < E + (L.shared_gate_row ? 1 : 0)) {
     const float *row = e < E ? L.router + (int64_t)e * H : L.shared_gate_row;
@@ -1876,9 +1876,12 @@ void launch_down(const MoeArgs &a, hipStream_t s) {
                      a);
 }
 
+// one router row (one wave) per workgroup: the E + 1 rows spread over every
+// CU (E = 256, B = 1: the gate/up kernel starts 0.4 us earlier than with
+// four rows per workgroup; at E = 512 the rows outnumber the CUs anyway)
 template <int B, int HC>
 void launch_router_k1(const MoeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((k_moe_router<B, HC>), dim3(a.router_wgs), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_moe_router<B, HC>), dim3(a.router_wgs), dim3(64), 0, s, a);
 }
 
 template <int B>
@@ -2001,7 +2004,7 @@ hipError_t run_moe_layer(const mmv_moe_layer &L, const float *X, int64_t ldx, in
   a.ids_out = ids;
   a.weights_out = weights;
   a.shared_w_out = sw;
-  a.router_wgs = (L.n_experts + (L.shared_gate_row ? 1 : 0) + 3) / 4;
+  a.router_wgs = L.n_experts + (L.shared_gate_row ? 1 : 0);
   // Top-k in every gate/up workgroup costs no launch and is cheapest for
   // one or two rows; for more rows it grows with B in every workgroup, and
   // one workgroup of its own (plus a launch) costs less.  A grid-wide

@@ -101,12 +101,13 @@ def test_bf16_lds_mfma_variants(mm, orc, dev, path, knob):
 @pytest.mark.parametrize("knobs", [dict(BF16_XL=-1, BF16_ROWS=1, BF16_WAVES=1),
                                    dict(BF16_XL=-1, BF16_ROWS=2, BF16_WAVES=4),
                                    dict(BF16_XL=-1, BF16_ROWS=4, BF16_WAVES=1),
-                                   dict(BF16_XL=2), dict(BF16_XL=16)])
+                                   dict(BF16_XL=2), dict(BF16_XL=4), dict(BF16_XL=5),
+                                   dict(BF16_XL=8), dict(BF16_XL=10), dict(BF16_XL=16)])
 def test_bf16_b1_variants_identical(mm, dev, path, knobs):
     # every B = 1 variant (x from L1/L2 or staged in LDS, rows per wave, waves
     # per workgroup) sums each row in the same order: all give the same bits
     for N, K in ((1000, 2560), (2560, 9728), (333, 1016), (300, 2048), (257, 4096),
-                 (100, 8192), (9000, 2560)):
+                 (100, 8192), (9000, 2560), (2561, 9728), (2555, 2560), (4097, 4096)):
         W = synth.bf16_weights(N, K, 0, "var", N, K, device=dev)
         x = synth.activations(1, K, 0, "var", N, K, device=dev)
         y0 = mm.gemv_bf16(W, x)
