@@ -204,12 +204,17 @@ int moe_route_topk(const float *router, int32_t E, int32_t H,
                    int32_t *ids, float *weights, float *shared_w,
                    void *stream);
 
-/* One MoE layer's weights.  Routed experts are stacked expert-major and
- * contiguous: expert e's gate block (i, j) is at
- * gate_qs + ((e*I + i)*(H/32) + j)*16 and gate_d[(e*I + i)*(H/32) + j];
- * up likewise; down is H x I per expert.  The shared expert has one
- * matrix of each (sh_*_qs == NULL: no shared expert).  H % 32 == 0,
- * I % 32 == 0. */
+/* One MoE layer's weights.  Routed experts are stacked expert-major, as in
+ * a stacked expert tensor of the model file [FOURTEEN: "The router with 257
+ * rows": the experts of a layer as one stacked tensor, the shared expert
+ * beside it]: expert e's gate block (i, j) is at
+ * gate_qs + e*gate_qs_stride + (i*(H/32) + j)*16 and
+ * gate_d[e*gate_d_stride + i*(H/32) + j]; up likewise; down is H x I per
+ * expert.  A zero stride means contiguous experts (qs: I*H/2 bytes, d:
+ * I*H/32 elements, for all three matrices).  A nonzero qs stride is a
+ * multiple of 16 bytes and at least I*H/2; a nonzero d stride is at least
+ * I*H/32 (else MMV_E_SHAPE).  The shared expert has one matrix of each
+ * (sh_*_qs == NULL: no shared expert).  H % 32 == 0, I % 32 == 0. */
 typedef struct {
   int32_t n_experts;              /* E */
   int32_t hidden;                 /* H */
@@ -221,6 +226,8 @@ typedef struct {
   const uint16_t *gate_d, *up_d, *down_d;
   const uint8_t *sh_gate_qs, *sh_up_qs, *sh_down_qs;
   const uint16_t *sh_gate_d, *sh_up_d, *sh_down_d;
+  int64_t gate_qs_stride, up_qs_stride, down_qs_stride;  /* bytes, 0: contiguous  */
+  int64_t gate_d_stride, up_d_stride, down_d_stride;     /* elements, 0: contiguous */
 } mmv_moe_layer;
 
 /* Optional staged outputs of moe_mul_mat_id, for tests: device buffers the

@@ -59,7 +59,10 @@ class _Layer(C.Structure):
                 ("gate_qs", _P), ("up_qs", _P), ("down_qs", _P),
                 ("gate_d", _P), ("up_d", _P), ("down_d", _P),
                 ("sh_gate_qs", _P), ("sh_up_qs", _P), ("sh_down_qs", _P),
-                ("sh_gate_d", _P), ("sh_up_d", _P), ("sh_down_d", _P)]
+                ("sh_gate_d", _P), ("sh_up_d", _P), ("sh_down_d", _P),
+                ("gate_qs_stride", C.c_int64), ("up_qs_stride", C.c_int64),
+                ("down_qs_stride", C.c_int64), ("gate_d_stride", C.c_int64),
+                ("up_d_stride", C.c_int64), ("down_d_stride", C.c_int64)]
 
 
 class _Debug(C.Structure):
@@ -328,6 +331,9 @@ class MoeLayer:
     gate/up: qs uint8 [E, I, H/32, 16], d float16 [E, I, H/32]
     down:    qs uint8 [E, H, I/32, 16], d float16 [E, H, I/32]
     shared:  dict with the same keys without the E dimension, or None.
+    A routed tensor may step between experts by more than one expert's size
+    (a view such as big[:, :I] of a padded stack): each expert must be
+    contiguous; the expert stride goes to the library.
     """
 
     def __init__(self, router, gate_qs, gate_d, up_qs, up_d, down_qs, down_d, top_k,
@@ -340,15 +346,16 @@ class MoeLayer:
                       down_qs=down_qs, down_d=down_d)
         self.shared = shared
         self.shared_gate_row = shared_gate_row
-        for name, t in self.t.items():
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
         s = _Layer()
         s.n_experts, s.hidden, s.inter, s.top_k = self.E, self.H, self.I, top_k
         s.router = router.data_ptr()
         s.shared_gate_row = _ptr(shared_gate_row)
         for name, t in self.t.items():
+            if not t[0].is_contiguous():
+                raise ValueError(f"{name}: each expert must be contiguous")
             setattr(s, name, t.data_ptr())
+            # bytes (qs, uint8) or elements (d, fp16) from one expert to the next
+            setattr(s, name + "_stride", t.stride(0) if self.E > 1 else 0)
         if shared is not None:
             for name in ("gate_qs", "gate_d", "up_qs", "up_d", "down_qs", "down_d"):
                 setattr(s, "sh_" + name, shared[name].data_ptr())

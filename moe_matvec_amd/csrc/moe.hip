@@ -658,6 +658,16 @@ struct MoeArgs {
   int32_t *work;     // B > 8: [0] count, then (slot << 4 | row group) gate/up items
 };
 
+// expert e's gate and up planes (strides resolved on the host)
+__device__ __forceinline__ void expert_gate_up(const mmv_moe_layer &L, int e, const uint8_t *&gq,
+                                               const uint16_t *&gd, const uint8_t *&uq,
+                                               const uint16_t *&ud) {
+  gq = L.gate_qs + e * L.gate_qs_stride;
+  gd = L.gate_d + e * L.gate_d_stride;
+  uq = L.up_qs + e * L.up_qs_stride;
+  ud = L.up_d + e * L.up_d_stride;
+}
+
 // Published row lists (workspace): [0] U, [1, 1+Bk) unique experts,
 // [1+Bk, 2+2Bk) offsets, [2+2Bk, 2+3Bk) pairs.  Thread t of a 256-thread
 // workgroup holds entries t and t + 256 (gl_n = 3 Bk + 2 <= 386).
@@ -952,7 +962,6 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
       if (a.dbg.n_unique && t == 0) a.dbg.n_unique[0] = g.U;
     }
   };
-  const int nbh = H >> 5;
 
   if constexpr (B == 1) {
     if (a.topk_in_k2) {
@@ -966,9 +975,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
       if (shared_slot) {
         gq = L.sh_gate_qs; gd = L.sh_gate_d; uq = L.sh_up_qs; ud = L.sh_up_d;
       } else {
-        const int64_t eo = (int64_t)s_ids[slot] * I * nbh;
-        gq = L.gate_qs + eo * 16; gd = L.gate_d + eo;
-        uq = L.up_qs + eo * 16; ud = L.up_d + eo;
+        expert_gate_up(L, s_ids[slot], gq, gd, uq, ud);
       }
       if (threadIdx.x == 0) {
         rowmap[0] = 0;
@@ -1009,9 +1016,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
     gq = L.sh_gate_qs; gd = L.sh_gate_d; uq = L.sh_up_qs; ud = L.sh_up_d;
     nr = B;
   } else {
-    const int64_t eo = (int64_t)g.unique[slot] * I * nbh;
-    gq = L.gate_qs + eo * 16; gd = L.gate_d + eo;
-    uq = L.up_qs + eo * 16; ud = L.up_d + eo;
+    expert_gate_up(L, g.unique[slot], gq, gd, uq, ud);
     // an expert appears at most once per row when ids are valid (distinct
     // within a row); the clamp keeps duplicated ids memory-safe
     nr = min(g.offsets[slot + 1] - g.offsets[slot], B);
@@ -1218,8 +1223,8 @@ __global__ __launch_bounds__(64 * NWV) void k_moe_down(MoeArgs a) {
   auto expert_ptr = [&](int c, const uint8_t *&dq, const uint16_t *&dd) {
     const int u = n > 0 ? wl[min(c, n - 1)] : -1;
     if (u >= 0 && u < U) {
-      const int64_t eo = (int64_t)s_unique[u] * H * nbi;
-      dq = L.down_qs + eo * 16; dd = L.down_d + eo;
+      dq = L.down_qs + s_unique[u] * L.down_qs_stride;
+      dd = L.down_d + s_unique[u] * L.down_d_stride;
     } else if (u == U) {
       dq = L.sh_down_qs; dd = L.sh_down_d;
     } else {
@@ -1474,8 +1479,8 @@ __global__ __launch_bounds__(256) void k_moe_down_part(MoeArgs a) {
   } else {
     const int U = gl[0], e = gl[1 + u], o0 = gl[1 + Bk + u], o1 = gl[2 + Bk + u];
     if (u >= U) return;  // uniform over the workgroup
-    const int64_t eo = (int64_t)e * H * nbi;
-    dq = L.down_qs + eo * 16; dd = L.down_d + eo;
+    dq = L.down_qs + e * L.down_qs_stride;
+    dd = L.down_d + e * L.down_d_stride;
     np = min(o1 - o0, Bv);  // a row meets an expert once: at most one pair per row
     pbase = o0;
   }
@@ -1767,8 +1772,8 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_rows(MoeArgs a) {
   __shared__ float hbuf[MMV_MAX_BATCH][32];
   extern __shared__ __align__(16) uint8_t smem[];
   const mmv_moe_layer &L = a.L;
-  const int k = L.top_k, H = L.hidden, I = L.inter, B = a.nrows, Bk = B * k;
-  const int ntiles = I >> 5, nbh = H >> 5;
+  const int k = L.top_k, I = L.inter, B = a.nrows, Bk = B * k;
+  const int ntiles = I >> 5;
   const int wi = blockIdx.x / ntiles, tile = blockIdx.x - wi * ntiles;
   // the count and this item's record in one round trip (wi is below the
   // record capacity, so the record is in bounds even past the count)
@@ -1785,9 +1790,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_rows(MoeArgs a) {
   if (shared_slot) {
     gq = L.sh_gate_qs; gd = L.sh_gate_d; uq = L.sh_up_qs; ud = L.sh_up_d;
   } else {
-    const int64_t eo = (int64_t)e * I * nbh;
-    gq = L.gate_qs + eo * 16; gd = L.gate_d + eo;
-    uq = L.up_qs + eo * 16; ud = L.up_d + eo;
+    expert_gate_up(L, e, gq, gd, uq, ud);
   }
   int ncv = nc;  // opaque: with its range known the compiler unrolls per row count
   asm volatile("" : "+s"(ncv));
@@ -1812,6 +1815,15 @@ MoeArgs make_args(const mmv_moe_layer &L, const float *X, int64_t ldx, int B,
                   int64_t ldy, uint8_t *ws, const mmv_moe_debug *dbg) {
   MoeArgs a;
   a.L = L;
+  // expert strides resolved here: the kernels always step by them
+  const int64_t nb = (int64_t)L.inter * (L.hidden / 32);
+  auto fix = [](int64_t &st, int64_t dflt) { if (st == 0) st = dflt; };
+  fix(a.L.gate_qs_stride, 16 * nb);
+  fix(a.L.up_qs_stride, 16 * nb);
+  fix(a.L.down_qs_stride, 16 * nb);
+  fix(a.L.gate_d_stride, nb);
+  fix(a.L.up_d_stride, nb);
+  fix(a.L.down_d_stride, nb);
   a.X = X;
   a.ldx = ldx;
   a.ids = ids;
@@ -1910,12 +1922,13 @@ int rows_work_max(const MoeArgs &a) {
 }
 
 // every gate / up scale plane 16-byte aligned: the experts' planes start
-// at multiples of I * H / 32 * 2 bytes from the layer's
+// at multiples of their d stride (2 bytes per element) from the layer's
 bool rows_scales16(const MoeArgs &a) {
   const mmv_moe_layer &L = a.L;
   auto al = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool sh = !a.routed_shared || (al(L.sh_gate_d) && al(L.sh_up_d));
-  return al(L.gate_d) && al(L.up_d) && sh && ((int64_t)L.inter * (L.hidden / 32) * 2) % 16 == 0;
+  return al(L.gate_d) && al(L.up_d) && sh && (L.gate_d_stride * 2) % 16 == 0 &&
+         (L.up_d_stride * 2) % 16 == 0;
 }
 
 template <int T>

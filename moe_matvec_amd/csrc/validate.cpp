@@ -8,6 +8,7 @@ namespace mmv {
 namespace {
 
 constexpr int64_t kMaxLd = int64_t(1) << 40;
+constexpr int64_t kMaxStride = int64_t(1) << 40;  // expert strides (bytes or elements)
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -186,6 +187,15 @@ int check_moe_layer(const mmv_moe_layer *L) {
               !aligned(L->sh_up_d, 2) || !aligned(L->sh_down_d, 2)))
     return MMV_E_ALIGN;
   if (L->shared_gate_row && !aligned(L->shared_gate_row, 16)) return MMV_E_ALIGN;
+  // expert strides: 0 (contiguous) or at least one expert's plane
+  const int64_t nb = (int64_t)I * (H / 32);
+  const int64_t qs_st[3] = {L->gate_qs_stride, L->up_qs_stride, L->down_qs_stride};
+  const int64_t d_st[3] = {L->gate_d_stride, L->up_d_stride, L->down_d_stride};
+  for (int m = 0; m < 3; ++m) {
+    if (qs_st[m] != 0 && (qs_st[m] < 16 * nb || qs_st[m] % 16 != 0 || qs_st[m] > kMaxStride))
+      return MMV_E_SHAPE;
+    if (d_st[m] != 0 && (d_st[m] < nb || d_st[m] > kMaxStride)) return MMV_E_SHAPE;
+  }
   return MMV_OK;
 }
 
@@ -200,17 +210,22 @@ namespace {
 struct LayerRanges {
   Range r[13];
 };
+// bytes from the first expert's plane to the end of the last one's
+size_t stack_bytes(int64_t E, int64_t stride, int64_t one) {
+  return (size_t)((stride ? stride : one) * (E - 1) + one);
+}
 LayerRanges layer_ranges(const mmv_moe_layer *L) {
   const int64_t E = L->n_experts, H = L->hidden, I = L->inter;
+  const int64_t nb = I * H / 32;  // blocks of one expert's matrix
   LayerRanges lr;
   lr.r[0] = rng(L->router, (size_t)(4 * E * H));
   lr.r[1] = L->shared_gate_row ? rng(L->shared_gate_row, (size_t)(4 * H)) : none();
-  lr.r[2] = q4_qs(L->gate_qs, E * I, H);
-  lr.r[3] = q4_qs(L->up_qs, E * I, H);
-  lr.r[4] = q4_qs(L->down_qs, E * H, I);
-  lr.r[5] = q4_d(L->gate_d, E * I, H);
-  lr.r[6] = q4_d(L->up_d, E * I, H);
-  lr.r[7] = q4_d(L->down_d, E * H, I);
+  lr.r[2] = rng(L->gate_qs, stack_bytes(E, L->gate_qs_stride, 16 * nb));
+  lr.r[3] = rng(L->up_qs, stack_bytes(E, L->up_qs_stride, 16 * nb));
+  lr.r[4] = rng(L->down_qs, stack_bytes(E, L->down_qs_stride, 16 * nb));
+  lr.r[5] = rng(L->gate_d, 2 * stack_bytes(E, L->gate_d_stride, nb));
+  lr.r[6] = rng(L->up_d, 2 * stack_bytes(E, L->up_d_stride, nb));
+  lr.r[7] = rng(L->down_d, 2 * stack_bytes(E, L->down_d_stride, nb));
   const bool sh = L->sh_gate_qs != nullptr;
   lr.r[8] = sh ? q4_qs(L->sh_gate_qs, I, H) : none();
   lr.r[9] = sh ? q4_qs(L->sh_up_qs, I, H) : none();

@@ -175,6 +175,34 @@ def test_mul_mat_id_validation(L):
     assert call(ws=X) == E_ALIAS
 
 
+def test_layer_expert_strides(L):
+    # strides between routed experts: 0 = contiguous, else at least one
+    # expert's plane (qs: a multiple of 16 bytes); the alias check covers
+    # the strided extent
+    f = L.moe_mul_mat_id
+    one_qs, one_d = 512 * 2048 // 2, 512 * 2048 // 32   # one expert's planes (I = 512, H = 2048)
+
+    def call(layer, Y=Cp):
+        need = L.moe_workspace_bytes(C.byref(layer), 1)
+        return f(C.byref(layer), A, 2048, 1, Bp, Bp + 0x1000, None, Y, 2048, Dp,
+                 max(need, 1 << 20), None, None)
+    for name, bad in (("gate_qs_stride", one_qs - 16), ("up_qs_stride", one_qs + 8),
+                      ("down_qs_stride", -16), ("gate_d_stride", one_d - 1),
+                      ("down_d_stride", -1), ("up_d_stride", 1 << 41)):
+        lay = _layer(**{name: bad})
+        assert L.moe_workspace_bytes(C.byref(lay), 1) == 0, name
+        assert call(lay) == E_SHAPE, name
+    for name, good in (("gate_qs_stride", one_qs + 16), ("down_qs_stride", 1 << 20),
+                       ("up_d_stride", one_d + 1), ("down_d_stride", 2 * one_d)):
+        assert L.moe_workspace_bytes(C.byref(_layer(**{name: good})), 1) > 0, name
+    # an output 160 MB into gate_qs: past 256 contiguous experts (128 MB),
+    # inside them at a 1 MB stride (every call here must fail validation, so
+    # the contiguous case, which would pass it, is not called)
+    Y = 0x1100000000 + 0xA000000
+    assert call(_layer(gate_qs_stride=1 << 20), Y=Y) == E_ALIAS
+    assert call(_layer(down_d_stride=1 << 24), Y=0x1600000000 + (1 << 32)) == E_ALIAS
+
+
 def test_layer_decode_validation(L):
     f = L.moe_layer_decode
     lay = _layer()

@@ -386,3 +386,38 @@ def test_moe_exact_gate_up_and_silu(mm, orc, dev):
         h = npc(dbg["h"])[p].astype(np.float64)
         assert (np.abs(h - want) <= 4 * np.spacing(np.abs(want)) + 1e-30).all()
     assert (npc(y) == 0.0).all()        # all-zero down weights (codes 8)
+
+
+def _strided(t, extra, fill):
+    """t [E, ...] as a view into a padded stack: each expert's bytes followed
+    by `extra` elements of `fill` (never read when the strides are right)."""
+    E, n = t.shape[0], t[0].numel()
+    big = torch.empty((E, n + extra), dtype=t.dtype, device=t.device)
+    big.view(torch.uint8).fill_(fill)
+    big[:, :n] = t.reshape(E, n)
+    v = big[:, :n].view(t.shape)
+    assert v.stride(0) == n + extra and v[0].is_contiguous()
+    return v
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d_extra", [3, 8])      # 8: scale planes stay 16-byte aligned
+@pytest.mark.parametrize("B", [1, 2, 5, 16])
+def test_moe_expert_strides(mm, orc, dev, d_extra, B):
+    # experts with padding between them (layer-level expert strides) give the
+    # bits of the contiguous stack on every launch path
+    E, H, I, k = 64, 1024, 512, 6
+    t = synth.moe_layer_tensors(E, H, I, 0, "strides", shared=True, device=dev)
+    base = mm.MoeLayer(t["router"], t["gate_qs"], t["gate_d"], t["up_qs"], t["up_d"],
+                       t["down_qs"], t["down_d"], k, shared=t["shared"])
+    v = {name: _strided(t[name], 48 if name.endswith("qs") else d_extra, 0xFF)
+         for name in ("gate_qs", "gate_d", "up_qs", "up_d", "down_qs", "down_d")}
+    lay = mm.MoeLayer(t["router"], v["gate_qs"], v["gate_d"], v["up_qs"], v["up_d"],
+                      v["down_qs"], v["down_d"], k, shared=t["shared"])
+    assert lay._s.gate_qs_stride == I * H // 2 + 48 and lay._s.down_d_stride == H * I // 32 + d_extra
+    X = synth.activations(B, H, 0, "strides", B, device=dev)
+    y0 = mm.moe_layer_decode(base, X)
+    y1 = mm.moe_layer_decode(lay, X)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1).all()
+    assert torch.equal(y0, y1)
