@@ -135,17 +135,22 @@ def build_dense(dev, layers):
 
 def dense_section(mm, dev, W, layers, B, steps, warmup, eager=False):
     """One graph over every layer copy; `head` also times exactly `steps`
-    replays on their own (the headline measurement)."""
+    replays on their own (the headline measurement).  The pass is one
+    dependency chain: attn-out reads the previous layer's down output, gate+up
+    reads attn-out's output, down reads the gate half of gate+up's output
+    (the elementwise SiLU(gate) * up between them is not part of this set)."""
     import torch
     import synth
-    X = {n: synth.activations(layers * B, K, 0, "dense-x", n, B, device=dev).view(layers, B, K)
-         for n, (N, K) in DENSE_SHAPES.items()}
+    x0 = synth.activations(B, DENSE_SHAPES["attn_out"][1], 0, "dense-x", B, device=dev)
     Y = {n: torch.empty((layers, B, N), device=dev) for n, (N, K) in DENSE_SHAPES.items()}
+    n_gate = DENSE_SHAPES["down"][1]
 
     def step():
         for l in range(layers):
-            for n in DENSE_SHAPES:
-                mm.gemv_bf16(W[n][l], X[n][l], out=Y[n][l])
+            x = x0 if l == 0 else Y["down"][l - 1]
+            mm.gemv_bf16(W["attn_out"][l], x, out=Y["attn_out"][l])
+            mm.gemv_bf16(W["gate_up"][l], Y["attn_out"][l], out=Y["gate_up"][l])
+            mm.gemv_bf16(W["down"][l], Y["gate_up"][l][:, :n_gate], out=Y["down"][l])
     g = capture(step)
     for _ in range(warmup):
         g.replay()
