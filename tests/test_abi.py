@@ -274,7 +274,11 @@ def test_path_switches(L):
     assert L.mmv_set_path(7, 0) == 1
     assert L.mmv_set_path(99, 1) == E_ARG and L.mmv_set_path(-1, 1) == E_ARG
     assert L.mmv_get_path(99) == 0
-    for i in range(9):
+    import moe_matvec_amd as m
+    n = len(m.PATH)
+    assert sorted(m.PATH.values()) == list(range(n))
+    assert L.mmv_set_path(n, 1) == E_ARG                   # one past the last switch
+    for i in range(n):
         assert L.mmv_get_path(i) == 0
 
 
