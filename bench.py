@@ -191,6 +191,67 @@ def dominant_kernel(mm, dev, W, layers, steps, warmup):
                 bytes_per_launch=per_launch, GBps=per_launch / t / 1e9)
 
 
+def dense_per_matrix(mm, dev, W, layers, B, steps, warmup):
+    """Each dense shape alone: its `layers` launches (one per layer copy,
+    independent inputs) back to back in one graph; us and GB/s per launch."""
+    import torch
+    import synth
+    out = {}
+    for name, (N, K) in DENSE_SHAPES.items():
+        X = synth.activations(layers * B, K, 0, "mat-x", name, B, device=dev).view(layers, B, K)
+        Y = torch.empty((layers, B, N), device=dev)
+
+        def step():
+            for l in range(layers):
+                mm.gemv_bf16(W[name][l], X[l], out=Y[l])
+        g = capture(step)
+        s, st = timed_graph(g, steps, warmup)
+        t = st["mean"] / layers
+        nbytes = 2 * N * K + 4 * B * K + 4 * B * N
+        out[name] = dict(N=N, K=K, us_per_launch_stats=stats(s, 1e6 / layers),
+                         GBps=nbytes / t / 1e9, frac_of_peak=nbytes / t / 1e9 / PEAK_HBM_GBPS)
+        del g
+    return out
+
+
+def cache_resident(mm, dev, W, reps, steps, warmup):
+    """Copy scaling: one layer copy of the dense set (162 MB, within the 256 MB
+    Infinity Cache) run `reps` times per graph, against the 36-copy pass; and
+    the 1024 x 1024 correctness shape (2 MiB, in L2).  Both are flagged
+    cache-resident: they show what the copies defeat, not HBM speed."""
+    import torch
+    import synth
+    x0 = synth.activations(1, DENSE_SHAPES["attn_out"][1], 0, "cache-x", device=dev)
+    Y = {n: torch.empty((1, N), device=dev) for n, (N, K) in DENSE_SHAPES.items()}
+    n_gate = DENSE_SHAPES["down"][1]
+
+    def step():
+        for r in range(reps):
+            mm.gemv_bf16(W["attn_out"][0], x0 if r == 0 else Y["down"], out=Y["attn_out"])
+            mm.gemv_bf16(W["gate_up"][0], Y["attn_out"], out=Y["gate_up"])
+            mm.gemv_bf16(W["down"][0], Y["gate_up"][:, :n_gate], out=Y["down"])
+    g = capture(step)
+    s, st = timed_graph(g, steps, warmup)
+    t = st["mean"] / reps
+    one = dict(reps=reps, us_per_layer_stats=stats(s, 1e6 / reps), GBps=dense_bytes(1) / t / 1e9,
+               cache_resident=True)
+    del g
+    W1 = synth.bf16_weights(1024, 1024, 0, "c1", device=dev)
+    x1 = synth.activations(1, 1024, 0, "c1", device=dev)
+    y1 = torch.empty((1, 1024), device=dev)
+
+    def step1():
+        for _ in range(reps):
+            mm.gemv_bf16(W1, x1, out=y1)
+    g = capture(step1)
+    s, st = timed_graph(g, steps, warmup)
+    t = st["mean"] / reps
+    nb = 2 * 1024 * 1024 + 4 * 1024 + 4 * 1024
+    c1 = dict(shape="1024x1024, B=1", us_per_launch_stats=stats(s, 1e6 / reps),
+              GBps=nb / t / 1e9, cache_resident=True)
+    return one, c1
+
+
 def launch_floor(mm, dev, steps, warmup, n=200):
     """Time per dependent launch of a one-workgroup kernel (quantize_q8_1 of
     32 values) in a graph of n of them: the fixed cost each launch of a
@@ -911,6 +972,17 @@ def main():
         sections["dense_bf16"]["B8"] = b8
         sections["dense_bf16"]["ratio_B8_B1_time"] = b8["s_per_step"] / head["s_per_step"]
         log(f"dense B=8: {b8['GBps']:.0f} GB/s, ratio {sections['dense_bf16']['ratio_B8_B1_time']:.2f}")
+        sections["dense_bf16"]["per_matrix"] = {
+            f"B{B}": dense_per_matrix(mm, dev, W, dense_layers, B, steps, warmup) for B in (1, 8)}
+        for B in (1, 8):
+            pm = sections["dense_bf16"]["per_matrix"][f"B{B}"]
+            log(f"dense per matrix B={B}: " + ", ".join(
+                f"{n} {v['us_per_launch_stats']['mean']:.2f} us" for n, v in pm.items()))
+        one, c1 = cache_resident(mm, dev, W, dense_layers, steps, warmup)
+        sections["dense_bf16"]["one_copy_cache_resident"] = one
+        sections["c1_cache_resident"] = c1
+        log(f"one dense copy repeated (cache-resident): {one['GBps']:.0f} GB/s; "
+            f"C1 1024x1024: {c1['GBps']:.0f} GB/s")
     del W
     torch.cuda.empty_cache()
     sections["launch_floor"] = launch_floor(mm, dev, steps, warmup)
