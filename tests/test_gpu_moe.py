@@ -153,6 +153,31 @@ def test_moe_layer_decode(mm, orc, dev, path, topk_kernel, E, H, I, k, B):
     np.testing.assert_allclose(npc(w), orc.gate_weights(lg64, ids_np), rtol=2e-5, atol=1e-6)
 
 
+@pytest.mark.parametrize("E,H,I,k,B,shared", [
+    (1, 32, 32, 1, 1, True),       # one expert, the smallest H and I
+    (1, 32, 32, 1, 8, False),
+    (4, 64, 32, 4, 3, True),       # k = E: every expert selected
+    (16, 256, 64, 16, 8, True),    # k = E = the largest top-k
+    (16, 32, 32, 16, 64, True),    # ... at the largest batch
+    (8, 32, 64, 1, 64, False),     # k = 1 at the largest batch
+])
+def test_moe_layer_decode_degenerate(mm, orc, dev, E, H, I, k, B, shared):
+    layer, ref = build_moe(mm, orc, E, H, I, k, 0, "degen", E, H, I, shared=shared, device=dev)
+    X = synth.activations(B, H, 0, "degen", E, B, device=dev)
+    ids = torch.empty((B, k), dtype=torch.int32, device=dev)
+    w = torch.empty((B, k), dtype=torch.float32, device=dev)
+    y = mm.moe_layer_decode(layer, X, ids=ids, weights=w)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    ids_np = npc(ids)
+    lg64, differ = check_ids_admissible(orc, ref.router, npc(X), ids_np, k)
+    y_ref = moe_ref_with_ids(orc, ref, npc(X), ids_np, lg64)
+    assert rel_l2_rows(npc(y), y_ref) <= MOE_TOL
+    np.testing.assert_allclose(npc(w), orc.gate_weights(lg64, ids_np), rtol=2e-5, atol=1e-6)
+    if k == E:   # every row selects every expert: weights are the full softmax
+        assert np.allclose(npc(w).sum(axis=1), 1.0, atol=1e-5)
+
+
 @pytest.mark.parametrize("topk_kernel", ["0", "1"])
 @pytest.mark.parametrize("B", [1, 2, 5, 12])
 def test_moe_layer_decode_tied_router_rows(mm, orc, dev, path, topk_kernel, B):
