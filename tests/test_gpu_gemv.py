@@ -25,6 +25,8 @@ Q4_TOL = 2e-3     # rel-L2 per output row for Q4_0 x Q8_1 GEMV (vs the W4A8 resu
     (2560, 9728, 1),
     (513, 8, 5),
     (9, 4096, 8),
+    (1, 512, 1),          # a single output row
+    (1, 8, 8),            # a single row of the smallest K
 ])
 def test_bf16_parity(mm, orc, dev, N, K, B):
     W = synth.bf16_weights(N, K, 0, "bf16", N, K, device=dev)
@@ -197,6 +199,7 @@ def _q4(mm, N, K, dev, *tags):
 @pytest.mark.parametrize("N,K,B", [
     (4096, 4096, 1), (1100, 4096, 8), (2048, 512, 1), (515, 512, 8),
     (333, 2048, 3), (77, 96, 2), (64, 32, 1), (130, 1024, 6), (700, 8192, 2),
+    (1, 32, 1), (1, 4096, 8),
 ])
 def test_q4_0_parity(mm, orc, dev, N, K, B):
     W, qs, d = _q4(mm, N, K, dev)
