@@ -593,6 +593,213 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
   return launch_q4<B, 64, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
 }
 
+// ---- W4A16 on the matrix cores ------------------------------------------
+// With B rows of x the fp32 kernels spend 32 FMAs per block, weight row and
+// x row; v_mfma_f32_16x16x32_bf16 takes one Q4_0 block of 16 weight rows:
+//  - A (16 rows x 32 k): lane l serves row l % 16 from the 4 code bytes
+//    4 (l / 16) .. + 3 of the block, i.e. k = 4 (l / 16) + {0..3} (low
+//    nibbles) and 16 + 4 (l / 16) + {0..3} (high nibbles), each code as the
+//    bf16 value 128 + c (exact), one byte permute per two codes (0x43 is
+//    the high byte of 128.0);
+//  - B (32 k x 16 columns): x of the B rows as bf16 hi (columns 0..7) and
+//    bf16 lo = bf16(x - hi) (columns 8..15; x - hi is exact in fp32),
+//    stored in the same k order as A, so each lane reads its 8 values at
+//    once; columns past B repeat row 0 and are never read back;
+//  - per block and column: S = sum (128 + c) x_part, and the block's term
+//    d_w (S - 136 sum x_part) = d_w sum (c - 8) x_part; the block sums of
+//    x_part come from the same instruction with A = 1;
+//  - y = the hi column plus the lo column, over the blocks.
+// Rows agree with the fp32 kernels within rounding and bit for bit across
+// every B this kernel takes (column b depends only on x row b).
+// A workgroup of 8 waves stages x once, each wave keeps the x columns and
+// block sums of its eighth of the blocks (at most 16: K <= 4096) in
+// registers, and the workgroup walks 16-row tiles (persistent grid). A
+// wave's 16 rows x 16 blocks of codes arrive by row-contiguous 16-byte
+// loads (16 lanes per row), three tiles ahead, and pass through the wave's
+// own LDS tile into the A layout.
+constexpr int kMfCB = 16;                 // blocks per wave and tile, at most
+constexpr int kMfMaxXK = 32768;           // B * K: x planes in LDS
+constexpr int kMfTileBytes = 16 * 272;    // per wave: [block][row] 16 bytes, +16 per block
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// one tile of a wave: load i of lane l holds row 4 i + l / 16, block l % 16
+// of the wave's blocks; the scales of row l % 16 at blocks 4 (l / 16) + {0..3}
+struct MfChunk {
+  u32x4 w[4];
+  uint16_t d[4];
+};
+
+__device__ __forceinline__ void mf_load(MfChunk &c, const uint8_t *__restrict__ qs,
+                                        const uint16_t *__restrict__ dw, int N, int nb,
+                                        int row0, int jb, int lane) {
+  const int64_t jw = min(jb + (lane & 15), nb - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = min(row0 + 4 * i + (lane >> 4), N - 1);
+    c.w[i] = load_stream16(qs + (row * nb + jw) * 16);
+  }
+  const int64_t rowd = min(row0 + (lane & 15), N - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c.d[i] = dw[rowd * nb + min(jb + 4 * (lane >> 4) + i, nb - 1)];
+}
+
+template <int B>
+__global__ __launch_bounds__(512) void k_gemv_q4_0_f32_mf(
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
+    const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy) {
+  extern __shared__ __align__(16) uint8_t smem[];    // x planes, then the waves' code tiles
+  __shared__ __align__(16) float s_d[8][kMfCB][16];  // [wave][block][row] scales
+  __shared__ float s_part[2][8][16][9];              // [parity][wave][row][b] tile sums
+  const int nb = K >> 5, KP = K + 8;
+  uint16_t *xpl = reinterpret_cast<uint16_t *>(smem);  // [2B][KP] bf16
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int ntiles = (N + 15) >> 4;
+  const int nbw = (nb + 7) >> 3;  // blocks per wave and tile (<= 16)
+  const int jw0 = min(nb, wv * nbw), jw1 = min(nb, jw0 + nbw);
+  int t = blockIdx.x;
+  const int G = gridDim.x;
+
+  // x (at most two float4 per row and thread: K <= 4096), then the first
+  // tile's codes, in this order so that staging x waits for x only; x ->
+  // hi / lo planes in the k order of the A operand
+  const int k4 = K >> 2;
+  f32x4 v[2][B];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kk = min(512 * h + tid, k4 - 1);
+#pragma unroll
+    for (int b = 0; b < B; ++b) v[h][b] = load_f4(X + (int64_t)b * ldx + 4 * kk);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  u32x4 xreg[kMfCB];
+  float creg[kMfCB];
+  MfChunk cur;
+  mf_load(cur, qs, dw, N, nb, 16 * t, jw0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // (no test: past K / 4 a thread repeats the last float4, same value to
+    // the same place, so that no load moves into a branch)
+    const int kk = min(512 * h + tid, k4 - 1);
+    {
+      const int k = 4 * kk, q = k & 31;
+      const int pos = (k - q) + 2 * (q & 12) + ((q >> 2) & 4);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const f32x4 x4 = v[h][b];
+        const uint32_t h0 =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x4.x, x4.y}, bf16x2));
+        const uint32_t h1 =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x4.z, x4.w}, bf16x2));
+        const uint32_t l0 = __builtin_bit_cast(
+            uint32_t,
+            __builtin_convertvector(f32x2{x4.x - bf16_lo(h0), x4.y - bf16_hi(h0)}, bf16x2));
+        const uint32_t l1 = __builtin_bit_cast(
+            uint32_t,
+            __builtin_convertvector(f32x2{x4.z - bf16_lo(h1), x4.w - bf16_hi(h1)}, bf16x2));
+        *reinterpret_cast<u32x2 *>(xpl + (size_t)b * KP + pos) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2 *>(xpl + (size_t)(B + b) * KP + pos) = u32x2{l0, l1};
+      }
+    }
+  }
+  __syncthreads();
+
+  // this lane's B column (plane row (col / 8) B + col % 8, row 0 past B)
+  // at the wave's blocks, and 136 * its block sums (A = 1)
+  {
+    const int bc = (col & 7) < B ? (col & 7) : 0;
+    const uint16_t *xrow = xpl + (size_t)((col >> 3) * B + bc) * KP + 8 * kg;
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+    for (int u = 0; u < kMfCB; ++u) {
+      xreg[u] = *reinterpret_cast<const u32x4 *>(xrow + 32 * min(jw0 + u, nb - 1));
+      const f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8v, ones), __builtin_bit_cast(bf16x8v, xreg[u]), zero, 0, 0,
+          0);
+      creg[u] = 136.0f * s.x;
+    }
+  }
+  __syncthreads();  // the x planes are dead: the code tiles take their place
+
+  uint8_t *wt = smem + wv * kMfTileBytes;
+  float *sdw = &s_d[wv][0][0];
+  int par = 0;
+  // one tile: codes to the A layout ([block][row] 16 bytes), scales as fp32
+  // [block][row] (blocks past the wave's share weigh 0), the 16 blocks, then
+  // the lo column onto the hi column (lanes col + 8 -> col) and the 8 waves'
+  // shares; the next tile writes the other parity of s_part, the one after
+  // that comes after the next barrier, when these reads are done
+  auto tile = [&](const MfChunk &c, int tt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4 *>(wt + col * 272 + (4 * i + kg) * 16) = c.w[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sdw[(4 * kg + i) * 16 + col] = jw0 + 4 * kg + i < jw1 ? f16_bits_to_f32(c.d[i]) : 0.0f;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile stores
+    __builtin_amdgcn_wave_barrier();
+    f32x4 acc = zero;
+#pragma unroll
+    for (int u = 0; u < kMfCB; ++u) {
+      const uint32_t w = *reinterpret_cast<const uint32_t *>(wt + u * 272 + col * 16 + 4 * kg);
+      const uint32_t mlo = w & 0x0F0F0F0Fu, mhi = (w >> 4) & 0x0F0F0F0Fu;
+      u32x4 av;
+      av.x = __builtin_amdgcn_perm(0x43434343u, mlo, 0x04010400u);
+      av.y = __builtin_amdgcn_perm(0x43434343u, mlo, 0x04030402u);
+      av.z = __builtin_amdgcn_perm(0x43434343u, mhi, 0x04010400u);
+      av.w = __builtin_amdgcn_perm(0x43434343u, mhi, 0x04030402u);
+      const f32x4 s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8v, av), __builtin_bit_cast(bf16x8v, xreg[u]), zero, 0, 0, 0);
+      // scales of rows 4 kg .. 4 kg + 3 at this block
+      const f32x4 sd = *reinterpret_cast<const f32x4 *>(sdw + u * 16 + 4 * kg);
+      const float cr = creg[u];
+      acc.x = fmaf(sd.x, s4.x - cr, acc.x);
+      acc.y = fmaf(sd.y, s4.y - cr, acc.y);
+      acc.z = fmaf(sd.z, s4.z - cr, acc.z);
+      acc.w = fmaf(sd.w, s4.w - cr, acc.w);
+    }
+    __builtin_amdgcn_wave_barrier();  // the tile and s_d are rewritten next time
+    acc.x += dpp_f32<0x128>(acc.x);   // row_ror:8
+    acc.y += dpp_f32<0x128>(acc.y);
+    acc.z += dpp_f32<0x128>(acc.z);
+    acc.w += dpp_f32<0x128>(acc.w);
+    if (col < B) {
+      s_part[par][wv][4 * kg + 0][col] = acc.x;
+      s_part[par][wv][4 * kg + 1][col] = acc.y;
+      s_part[par][wv][4 * kg + 2][col] = acc.z;
+      s_part[par][wv][4 * kg + 3][col] = acc.w;
+    }
+    __syncthreads();
+    if (tid < 16 * B) {
+      const int b = tid >> 4, row = tid & 15;
+      float v = 0.0f;
+#pragma unroll
+      for (int w8 = 0; w8 < 8; ++w8) v += s_part[par][w8][row][b];
+      const int n = 16 * tt + row;
+      if (n < N) Y[(int64_t)b * ldy + n] = v;
+    }
+    par ^= 1;
+  };
+  // every tile but the last with the next one's loads in flight (issued
+  // before the compute, unconditionally, so that only this tile's loads
+  // have to land); the last one without
+  while (true) {
+    const int t2 = t + G;
+    if (t2 >= ntiles) break;  // uniform over the workgroup
+    MfChunk nxt;
+    mf_load(nxt, qs, dw, N, nb, 16 * t2, jw0, lane);
+    tile(cur, t);
+    t = t2;
+    cur = nxt;
+  }
+  tile(cur, t);
+}
+
 namespace {
 
 template <int B, int G, int T>
@@ -609,6 +816,26 @@ hipError_t launch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, con
   }
   hipLaunchKernelGGL((k_gemv_q4_0_f32<B, G, RP, T>), dim3((N + rows_wg - 1) / rows_wg),
                      dim3(256), lds, s, qs, d, N, K, X, ldx, Y, ldy);
+  return hipGetLastError();
+}
+
+// W4A16 on the matrix cores: a persistent grid, one 8-wave workgroup per CU
+// (over 128 VGPRs per lane)
+template <int B>
+hipError_t launch_q4_f32_mf(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                            int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+  constexpr size_t kMaxLds = (size_t)4 * kMfMaxXK + (size_t)4 * B * 8;
+  const size_t xb = (size_t)4 * B * (K + 8), tiles = (size_t)8 * kMfTileBytes;
+  const size_t lds = xb > tiles ? xb : tiles;
+  if (lds > 65536) {  // above the default dynamic-LDS limit: raise it once per kernel
+    static const hipError_t raised = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_gemv_q4_0_f32_mf<B>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (raised != hipSuccess) return raised;
+  }
+  const int grid = min((N + 15) / 16, cu_count());
+  hipLaunchKernelGGL((k_gemv_q4_0_f32_mf<B>), dim3(grid), dim3(512), lds, s, qs, d, N, K, X,
+                     ldx, Y, ldy);
   return hipGetLastError();
 }
 
@@ -639,6 +866,12 @@ template <int B>
 hipError_t dispatch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                            int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
   const int nb = K / 32;
+  // three or more rows and K <= 4096: the matrix cores
+  {
+    const int sw = path_switch(MMV_PATH_Q4F32_MF);
+    if (sw >= 0 && B >= (sw > 0 ? sw : 3) && nb <= 8 * kMfCB && (int64_t)B * K <= kMfMaxXK)
+      return launch_q4_f32_mf<B>(qs, d, N, K, X, ldx, Y, ldy, s);
+  }
   // whole rows per lane, one row group per workgroup: x of B rows in at
   // most 66 KiB of LDS
   if ((int64_t)B * K <= 16384) {

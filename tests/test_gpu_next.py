@@ -12,6 +12,7 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 1e-3   # rel-L2 per output row, BF16 GEMV
 Q4_TOL = 2e-3     # rel-L2 per output row, Q4_0 weight products
+W4A16_ARITH_TOL = 1e-4  # rel-L2 per row, W4A16 against float64: what its arithmetic keeps
 
 VOCAB, HID = 248320, 2560   # LM head of the 2560-wide model
 
@@ -147,9 +148,11 @@ def test_w4a16_integer_pin_bit_exact(mm, orc, dev, N, K, B):
 
 
 def test_w4a16_batch_invariance(mm, dev):
-    # every (row, b) sum is taken in one order for every B, in both kernels
-    # (whole rows per lane for B * K <= 16384 and K / 32 in {16, ..., 256},
-    # the general one otherwise: the same lanes per row)
+    # each row of a B-row call against the same row in other calls: bit for
+    # bit within one kernel family (the fp32 kernels: every B for K > 4096 and
+    # B <= 2 otherwise, each (row, b) sum in one order; the matrix-core
+    # kernel: B >= 3 at K <= 4096, column b depending on x row b only), within
+    # rounding across the two
     for N, K in ((2000, 2048), (700, 8192), (1300, 4096), (129, 2560), (65, 96),
                  (40, 11008)):
         W, _, _ = _q4(mm, N, K, dev, "inv")
@@ -157,8 +160,36 @@ def test_w4a16_batch_invariance(mm, dev):
         X = synth.activations(Bmax, K, 0, "w4a16inv", K, device=dev)
         yB = mm.gemv_q4_0_f32(W, X)
         assert torch.equal(yB, mm.gemv_q4_0_f32(W, X))
+        mf = K <= 4096 and Bmax >= 3
         for b in range(Bmax):
-            assert torch.equal(yB[b], mm.gemv_q4_0_f32(W, X[b].clone()))
+            y1 = mm.gemv_q4_0_f32(W, X[b].clone())
+            if not mf:
+                assert torch.equal(yB[b], y1)
+                continue
+            y3 = mm.gemv_q4_0_f32(W, X[[b, (b + 1) % Bmax, (b + 2) % Bmax]].clone())
+            assert torch.equal(yB[b], y3[0])
+            assert torch.equal(y1, mm.gemv_q4_0_f32(W, X[[b, b]].clone())[1])
+            assert rel_l2_rows(npc(yB[b]), npc(y1).astype(np.float64)) <= 2e-5
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (20000, 4096), (1000, 96), (777, 2560),
+                                 (33, 32)])
+def test_w4a16_both_kernels_every_b(mm, orc, dev, path, N, K):
+    # the matrix-core kernel forced from B = 1 and the fp32 kernels forced at
+    # every B, both against the oracle (20000 rows: several tiles per
+    # workgroup on any GPU of up to 1250 compute units)
+    W, qs, d = _q4(mm, N, K, dev, "both")
+    for B in range(1, 9):
+        X = synth.activations(B, K, 0, "w4a16both", N, K, B, device=dev)
+        ref = orc.gemv_q4_0_f32(qs, d, npc(X))
+        for sw in (1, -1):
+            path(Q4F32_MF=sw)
+            y = mm.gemv_q4_0_f32(W, X)
+            torch.cuda.synchronize()
+            # and the bound of the arithmetic: x kept to 2^-17 (bf16 hi + lo) or
+            # exact (fp32), fp32 sums (rel-L2 ~5e-6 measured); a lost lo plane
+            # alone would give ~2^-9
+            assert rel_l2_rows(npc(y), ref) <= W4A16_ARITH_TOL, (B, sw)
 
 
 def test_w4a16_strided_x_and_y(mm, orc, dev):
