@@ -135,7 +135,11 @@ int quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B,
  *   [FOURTEEN: "Dense matvecs (warp_coop Q4_0)"; four rows per wave for
  *    K <= 512 in "Eight levers that worked"]
  *   Y[b*ldy + n] = sum_j d_w[n][j] * d_x[b][j] * I[b][n][j],
- *   I[b][n][j] = sum_i (code_i - 8) * q_x[b][32j + i]  (exact int32).
+ *   I[b][n][j] = sum_i (code_i - 8) * q_x[b][32j + i]  (exact int32), then
+ *   fp32 scaling and sums.  K <= 4096 with B >= 3 (fp32 x) or B >= 7 (a
+ *   Q8_1 buffer) runs on the int8 matrix cores, the rest on dot4 kernels;
+ *   the two sum the blocks in different orders, so rows agree within
+ *   rounding (rel-L2 ~1e-7) across them and bit for bit within each.
  *   Activations, one of three ways (the codes are bit-identical in all):
  *     X only:  fp32 B x K, quantized to Q8_1 inside every workgroup (one
  *              launch; the better choice at B = 1);
@@ -145,6 +149,8 @@ int quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B,
  *              Q8_1(X)), then the product reads Xq (two launches; the
  *              better choice at B >= 2, where repeating the quantization
  *              in every workgroup costs more than the extra launch).
+ *   X only and Xq give bit-identical rows where they take the same kernel
+ *   (B <= 2, B >= 7 or K > 4096).
  *   B*K <= MMV_Q4_MAX_XK.  Y: B x N fp32, ldy >= N.
  * ------------------------------------------------------------------------ */
 int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,

@@ -53,7 +53,11 @@ enum mmv_path_switch {
   /* gemv_q4_0_f32 on the matrix cores: 0 = from B = 3, n > 0 = from B = n,
    * -1 = never (the fp32 kernels; rows agree within rounding) */
   MMV_PATH_Q4F32_MF = 9,
-  MMV_PATH_COUNT = 10
+  /* gemv_q4_0 on the matrix cores (K <= 4096): 0 = from B = 3 for fp32 x,
+   * from B = 7 for a Q8_1 buffer; n > 0 = from B = n; -1 = never (the dot4
+   * kernels; rows agree within rounding) */
+  MMV_PATH_Q4_MF = 10,
+  MMV_PATH_COUNT = 11
 };
 
 /* Sets switch `which` to `value` (0 = automatic); returns the previous value,

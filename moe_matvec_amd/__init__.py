@@ -74,7 +74,7 @@ _DEBUG_FIELDS = [f for f, _ in _Debug._fields_]
 
 # kernel-variant switches of include/moe_matvec_testing.h (tests and measurements only)
 PATH = dict(BF16_ROWS=0, BF16_WAVES=1, BF16_XL=2, BF16_ML=3, Q4_RP=4, Q4_GENERIC=5,
-            Q4_WG_PER_CU=6, MOE_TOPK=7, MOE_DOWN=8, Q4F32_MF=9)
+            Q4_WG_PER_CU=6, MOE_TOPK=7, MOE_DOWN=8, Q4F32_MF=9, Q4_MF=10)
 
 
 _lib = None

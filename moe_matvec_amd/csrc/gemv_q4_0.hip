@@ -575,11 +575,24 @@ static hipError_t launch_q4_rp(const uint8_t *qs, const uint16_t *d, int N, int 
 }
 
 template <int B>
+hipError_t launch_q4_mf(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                        int64_t ldx, const uint8_t *Xq, float *Y, int64_t ldy, hipStream_t s);
+
+template <int B>
 static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
                               const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                               int64_t ldy, hipStream_t s) {
   const int nb = K / 32;
   constexpr int RP = B <= 2 ? 2 : 4;
+  // K <= 4096: the matrix cores from B = 3 for fp32 x (quantized in every
+  // workgroup: the dot4 kernels' repeated quantization is the bound there),
+  // from B = 7 for a Q8_1 buffer (4096^2 + 11008 x 4096 per pair, dot4 /
+  // matrix cores: B = 6 19.5 / 20.2 us, B = 7 21.2 / 20.5, B = 8 22.9 / 21.0)
+  {
+    const int sw = path_switch(MMV_PATH_Q4_MF);
+    if (sw >= 0 && B >= (sw > 0 ? sw : (X ? 3 : 7)) && nb <= 128)
+      return launch_q4_mf<B>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  }
   // whole blocks per lane: every load of a row group in flight together
   if (path_switch(MMV_PATH_Q4_GENERIC) <= 0) {
     if (nb == 16) return launch_q4_rp<B, 16, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
@@ -798,6 +811,198 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_f32_mf(
     cur = nxt;
   }
   tile(cur, t);
+}
+
+// ---- Q4_0 x Q8_1 on the matrix cores -------------------------------------
+// The same tiling as W4A16 on the matrix cores, with v_mfma_i32_16x16x32_i8:
+//  - A: lane l's 4 code bytes of the block, masked into 4 low-nibble and 4
+//    high-nibble codes (unsigned int8 0..15, k as above);
+//  - B: the Q8_1 codes of x row l % 16 (l % 16 < B) in the same k order;
+//  - per block and x row: S = sum code * q (exact int32), I = S - 8 sum q
+//    (sum q from the same instruction with A = 1), then y += (d_w d_x) I in
+//    fp32 -- I is the block's exact integer dot of the W4A8 product.
+// x comes as fp32 (quantized to Q8_1 in every workgroup by the one device
+// routine, so the codes equal the standalone quantizer's) or as a Q8_1
+// buffer. Rows are bit-identical across every B this kernel takes.
+template <int B, bool FROM_X>
+__global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
+    const float *__restrict__ X, int64_t ldx, const uint8_t *__restrict__ Xq,
+    float *__restrict__ Y, int64_t ldy) {
+  // x codes and scales, then the code tiles (typed views of one dynamic
+  // LDS block, indexed in 32 bits)
+  extern __shared__ __align__(16) uint8_t smem[];
+  extern __shared__ __align__(16) uint32_t smem_u[];
+  extern __shared__ __align__(16) float smem_f[];
+  __shared__ __align__(16) float s_d[8][kMfCB][16];  // [wave][block][row] weight scales
+  __shared__ float s_part[2][8][16][9];              // [parity][wave][row][b] tile sums
+  const int nb = K >> 5, KP = K + 16;
+  // [B][KP] int8 codes at smem (bytes K .. K + 15 of a row unused), then
+  // [B][nb] fp32 x scales and one spare word, from word dx0
+  const unsigned dx0 = B * KP / 4;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int ntiles = (N + 15) >> 4;
+  const int nbw = (nb + 7) >> 3;  // blocks per wave and tile (<= 16)
+  const int jw0 = min(nb, wv * nbw), jw1 = min(nb, jw0 + nbw);
+  int t = blockIdx.x;
+  const int G = gridDim.x;
+
+  // x (at most two groups of 4 values per row and thread: K <= 4096), then
+  // the first tile's codes, in this order so that staging x waits for x
+  // only; the x codes go to LDS in the k order of the A operand
+  const int k4 = K >> 2;
+  f32x4 v[FROM_X ? 2 : 1][FROM_X ? B : 1];
+  uint32_t c[FROM_X ? 1 : 2][FROM_X ? 1 : B];
+  uint16_t dq[FROM_X ? 1 : 2];  // x scales of a Q8_1 buffer: B * nb <= 1024
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kk = min(512 * h + tid, k4 - 1);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if constexpr (FROM_X)
+        v[h][b] = load_f4(X + (int64_t)b * ldx + 4 * kk);
+      else
+        c[h][b] = *reinterpret_cast<const uint32_t *>(Xq + (size_t)b * K + 4 * kk);
+    }
+    if constexpr (!FROM_X)
+      dq[h] = reinterpret_cast<const uint16_t *>(Xq + (size_t)B * K)[2 * min(512 * h + tid, B * nb - 1)];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  MfChunk cur;
+  mf_load(cur, qs, dw, N, nb, 16 * t, jw0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // past K / 4 a thread works on the last group of 4 values and stores
+    // into unused words (no branch, so that no load moves into one); Q8_1
+    // takes whole 8-lane groups (32 values), which K % 32 == 0 keeps either
+    // wholly inside or wholly past the row
+    // (row offsets as running sums: a multiply-add here becomes a 64-bit
+    // one whose unused half reads a register with a load in flight)
+    const int kr = 512 * h + tid, kk = min(kr, k4 - 1);
+    const bool in = kr < k4, lead = in && (kk & 7) == 0;
+    const unsigned k = 4 * kk, q = k & 31;
+    unsigned cw = (in ? (k - q) + 2 * (q & 12) + ((q >> 2) & 4) : (unsigned)K) >> 2;
+    unsigned di = dx0 + (kk >> 3);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      uint32_t codes;
+      if constexpr (FROM_X) {
+        const Q8Block qb = q8_1_quantize8(v[h][b]);
+        codes = qb.codes;
+        smem_f[lead ? di : dx0 + B * nb] = f16_bits_to_f32(qb.d16);
+      } else {
+        codes = c[h][b];
+      }
+      smem_u[cw] = codes;
+      cw += KP >> 2;
+      di += nb;
+    }
+    if constexpr (!FROM_X) {
+      const int i = 512 * h + tid;
+      smem_f[i < B * nb ? dx0 + i : dx0 + B * nb] = f16_bits_to_f32(dq[h]);
+    }
+  }
+  __syncthreads();
+
+  // this lane's B column (x row col, row 0 past B) at the wave's blocks, its
+  // scale and 8 * its code sum (A = 1)
+  typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+  const i32x4v izero = {0, 0, 0, 0};
+  int64_t xq[kMfCB];
+  float dx[kMfCB];
+  int q8[kMfCB];
+  {
+    const int bc = col < B ? col : 0;
+    const int xrow = (bc * KP + 8 * kg) >> 2;
+#pragma unroll
+    for (int u = 0; u < kMfCB; ++u) {
+      const int j = min(jw0 + u, nb - 1);
+      xq[u] = (int64_t)smem_u[xrow + 8 * j] | ((int64_t)smem_u[xrow + 8 * j + 1] << 32);
+      dx[u] = smem_f[dx0 + bc * nb + j];
+      const i32x4v s = __builtin_amdgcn_mfma_i32_16x16x32_i8(0x0101010101010101ll, xq[u],
+                                                             izero, 0, 0, 0);
+      q8[u] = 8 * s.x;
+    }
+  }
+  __syncthreads();  // x is in registers: the code tiles take its place
+
+  const int wt = wv * kMfTileBytes / 4;  // this wave's code tile, in words
+  float *sdw = &s_d[wv][0][0];
+  int par = 0;
+  // one tile, as in the W4A16 kernel (s_part parities alternate)
+  auto tile = [&](const MfChunk &ch, int tt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4 *>(&smem_u[wt + col * 68 + (4 * i + kg) * 4]) = ch.w[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sdw[(4 * kg + i) * 16 + col] = jw0 + 4 * kg + i < jw1 ? f16_bits_to_f32(ch.d[i]) : 0.0f;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile stores
+    __builtin_amdgcn_wave_barrier();
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < kMfCB; ++u) {
+      const uint32_t w = smem_u[wt + u * 68 + col * 4 + kg];
+      const uint64_t a = (uint64_t)(w & 0x0F0F0F0Fu) | ((uint64_t)((w >> 4) & 0x0F0F0F0Fu) << 32);
+      const i32x4v s4 =
+          __builtin_amdgcn_mfma_i32_16x16x32_i8((int64_t)a, xq[u], izero, 0, 0, 0);
+      const f32x4 sd = *reinterpret_cast<const f32x4 *>(sdw + u * 16 + 4 * kg);
+      const float d = dx[u];
+      const int c8 = q8[u];
+      acc.x = fmaf(sd.x * d, (float)(s4.x - c8), acc.x);
+      acc.y = fmaf(sd.y * d, (float)(s4.y - c8), acc.y);
+      acc.z = fmaf(sd.z * d, (float)(s4.z - c8), acc.z);
+      acc.w = fmaf(sd.w * d, (float)(s4.w - c8), acc.w);
+    }
+    __builtin_amdgcn_wave_barrier();  // the tile and s_d are rewritten next time
+    if (col < B) {
+      s_part[par][wv][4 * kg + 0][col] = acc.x;
+      s_part[par][wv][4 * kg + 1][col] = acc.y;
+      s_part[par][wv][4 * kg + 2][col] = acc.z;
+      s_part[par][wv][4 * kg + 3][col] = acc.w;
+    }
+    __syncthreads();
+    if (tid < 16 * B) {
+      const int b = tid >> 4, row = tid & 15;
+      float v8 = 0.0f;
+#pragma unroll
+      for (int w8 = 0; w8 < 8; ++w8) v8 += s_part[par][w8][row][b];
+      const int n = 16 * tt + row;
+      if (n < N) Y[(int64_t)b * ldy + n] = v8;
+    }
+    par ^= 1;
+  };
+  // every tile but the last with the next one's loads in flight (issued
+  // before the compute, unconditionally); the last one without
+  while (true) {
+    const int t2 = t + G;
+    if (t2 >= ntiles) break;  // uniform over the workgroup
+    MfChunk nxt;
+    mf_load(nxt, qs, dw, N, nb, 16 * t2, jw0, lane);
+    tile(cur, t);
+    t = t2;
+    cur = nxt;
+  }
+  tile(cur, t);
+}
+
+// a persistent grid, one 8-wave workgroup per CU (over 128 VGPRs per lane)
+template <int B>
+hipError_t launch_q4_mf(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                        int64_t ldx, const uint8_t *Xq, float *Y, int64_t ldy, hipStream_t s) {
+  const size_t xb = (size_t)B * (K + 16) + (size_t)4 * B * (K / 32) + 4;
+  const size_t tiles = (size_t)8 * kMfTileBytes;
+  const size_t lds = xb > tiles ? xb : tiles;  // at most 41 KiB (B = 8, K = 4096)
+  const int grid = min((N + 15) / 16, cu_count());
+  if (X)
+    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, true>), dim3(grid), dim3(512), lds, s, qs, d, N, K, X,
+                       ldx, Xq, Y, ldy);
+  else
+    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, false>), dim3(grid), dim3(512), lds, s, qs, d, N, K,
+                       X, ldx, Xq, Y, ldy);
+  return hipGetLastError();
 }
 
 namespace {
