@@ -34,11 +34,15 @@
  *    caller's next synchronization.
  *  - Results are deterministic: no floating-point atomics; repeated calls
  *    on the same inputs give bit-identical outputs.  Each row of a B-row
- *    call equals the 1-row call on that row, bit for bit, for every entry
- *    point except gemv_bf16: there rows are bit-identical across every
- *    B >= 2, and the B = 1 result (fp32 fused multiply-adds) agrees with the
- *    B >= 2 result (matrix cores on x split into bf16 high + low parts)
- *    within rounding, not bit for bit.
+ *    call equals the 1-row call on that row, bit for bit, for
+ *    quantize_q8_1, argmax_rows and the MoE calls.  The GEMVs switch to the
+ *    matrix cores at some B, and each kernel sums in its own order: rows
+ *    are bit-identical across the B one kernel serves and agree within
+ *    rounding across kernels.  gemv_bf16: B = 1 (fp32 fused multiply-adds)
+ *    against B >= 2 (x split into bf16 high + low parts).  gemv_q4_0 at
+ *    K <= 4096: B <= 2 against B >= 3 for fp32 x, B <= 6 against B >= 7
+ *    for a Q8_1 buffer (the exact block integers are the same).
+ *    gemv_q4_0_f32 at K <= 4096: B <= 2 against B >= 3.
  *  - Outputs must not overlap inputs (MMV_E_ALIAS).
  *
  * Data formats
