@@ -42,7 +42,7 @@
  *    against B >= 2 (x split into bf16 high + low parts).  gemv_q4_0 at
  *    K <= 4096: B <= 2 against B >= 3 for fp32 x, B <= 6 against B >= 7
  *    for a Q8_1 buffer (the exact block integers are the same).
- *    gemv_q4_0_f32 at K <= 4096: B <= 2 against B >= 3.
+ *    gemv_q4_0_f32 at K <= 4096: B = 1 against B >= 2.
  *  - Outputs must not overlap inputs (MMV_E_ALIAS).
  *
  * Data formats
@@ -166,8 +166,8 @@ int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,
  *    dequantization) and the dequant-gemv kernels its closing paragraph
  *    announces]
  *   Y[b*ldy + n] = sum_j d_w[n][j] * sum_i (code_i - 8) * X[b*ldx + 32j + i],
- *   fp32 sums.  B <= 2 or K > 4096: fp32 arithmetic, per block s =
- *   sum_i code_i * x_i, then d_w * (s - 8 * sum_i x_i).  B >= 3 with
+ *   fp32 sums.  B = 1 or K > 4096: fp32 arithmetic, per block s =
+ *   sum_i code_i * x_i, then d_w * (s - 8 * sum_i x_i).  B >= 2 with
  *   K <= 4096: the matrix cores, x split into bf16 hi + lo (x kept to
  *   2^-17 relative), per block d_w * (sum_i (128 + code_i) x_part - 136 *
  *   sum_i x_part); the two agree within rounding (rel-L2 ~1e-5), and each

@@ -50,7 +50,7 @@ enum mmv_path_switch {
   /* moe_mul_mat_id / moe_layer_decode, B <= 8: 1 = the one-kernel down
    * projection; 2 = the down projection by expert plus a combine kernel */
   MMV_PATH_MOE_DOWN = 8,
-  /* gemv_q4_0_f32 on the matrix cores: 0 = from B = 3, n > 0 = from B = n,
+  /* gemv_q4_0_f32 on the matrix cores: 0 = from B = 2, n > 0 = from B = n,
    * -1 = never (the fp32 kernels; rows agree within rounding) */
   MMV_PATH_Q4F32_MF = 9,
   /* gemv_q4_0 on the matrix cores (K <= 4096): 0 = from B = 3 for fp32 x,

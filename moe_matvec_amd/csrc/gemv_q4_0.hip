@@ -574,6 +574,15 @@ static hipError_t launch_q4_rp(const uint8_t *qs, const uint16_t *d, int N, int 
   return launch_q4_t<B, G, 2, T>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
 }
 
+// shape of the matrix-core kernels (below)
+constexpr int kMfW = 16;                  // waves per workgroup, each 1/16 of K
+constexpr int kMfT = 64 * kMfW;           // threads per workgroup
+constexpr int kMfCB = 8;                  // blocks per wave and tile, at most (K <= 4096)
+constexpr int kMfLD = kMfCB / 4;          // 16-byte code loads and scales per lane and tile
+constexpr int kMfXH = 1024 / kMfT;        // staging steps per thread (K / 4 <= 1024)
+constexpr int kMfMaxXK = 32768;           // B * K: x planes in LDS
+constexpr int kMfTileBytes = kMfCB * 272; // per wave: [block][row] 16 bytes, +16 per block
+
 template <int B>
 hipError_t launch_q4_mf(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                         int64_t ldx, const uint8_t *Xq, float *Y, int64_t ldy, hipStream_t s);
@@ -590,7 +599,7 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
   // matrix cores: B = 6 19.5 / 20.2 us, B = 7 21.2 / 20.5, B = 8 22.9 / 21.0)
   {
     const int sw = path_switch(MMV_PATH_Q4_MF);
-    if (sw >= 0 && B >= (sw > 0 ? sw : (X ? 3 : 7)) && nb <= 128)
+    if (sw >= 0 && B >= (sw > 0 ? sw : (X ? 3 : 7)) && nb <= kMfW * kMfCB)
       return launch_q4_mf<B>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   }
   // whole blocks per lane: every load of a row group in flight together
@@ -624,54 +633,55 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
 //  - y = the hi column plus the lo column, over the blocks.
 // Rows agree with the fp32 kernels within rounding and bit for bit across
 // every B this kernel takes (column b depends only on x row b).
-// A workgroup of 8 waves stages x once, each wave keeps the x columns and
-// block sums of its eighth of the blocks (at most 16: K <= 4096) in
-// registers, and the workgroup walks 16-row tiles (persistent grid). A
-// wave's 16 rows x 16 blocks of codes arrive by row-contiguous 16-byte
-// loads (16 lanes per row), three tiles ahead, and pass through the wave's
-// own LDS tile into the A layout.
-constexpr int kMfCB = 16;                 // blocks per wave and tile, at most
-constexpr int kMfMaxXK = 32768;           // B * K: x planes in LDS
-constexpr int kMfTileBytes = 16 * 272;    // per wave: [block][row] 16 bytes, +16 per block
+// A workgroup of 16 waves stages x once, each wave keeps the x columns and
+// block sums of its 1/16 of the blocks (at most 8: K <= 4096) in registers,
+// and the workgroup walks 16-row tiles (persistent grid, one workgroup per
+// CU: 4 waves per SIMD at <= 128 VGPRs). A wave's 16 rows x 8 blocks of
+// codes arrive by row-contiguous 16-byte loads (8 lanes per row, 128 bytes)
+// one tile ahead, and pass through the wave's own LDS tile into the A
+// layout. (8 waves of 16 blocks measured the same for W4A16 and 10% slower
+// for Q4_0 x Q8_1 from fp32 x, whose quantization then has half the threads.)
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// one tile of a wave: load i of lane l holds row 4 i + l / 16, block l % 16
-// of the wave's blocks; the scales of row l % 16 at blocks 4 (l / 16) + {0..3}
+// one tile of a wave: load i of lane l holds row (64 / kMfCB) i + l / kMfCB,
+// block l % kMfCB of the wave's blocks (kMfCB lanes read a row's codes, one
+// contiguous run); the scales of row l % 16 at blocks kMfLD (l / 16) + i
 struct MfChunk {
-  u32x4 w[4];
-  uint16_t d[4];
+  u32x4 w[kMfLD];
+  uint16_t d[kMfLD];
 };
 
 __device__ __forceinline__ void mf_load(MfChunk &c, const uint8_t *__restrict__ qs,
                                         const uint16_t *__restrict__ dw, int N, int nb,
                                         int row0, int jb, int lane) {
-  const int64_t jw = min(jb + (lane & 15), nb - 1);
+  const int64_t jw = min(jb + lane % kMfCB, nb - 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = min(row0 + 4 * i + (lane >> 4), N - 1);
+  for (int i = 0; i < kMfLD; ++i) {
+    const int64_t row = min(row0 + (64 / kMfCB) * i + lane / kMfCB, N - 1);
     c.w[i] = load_stream16(qs + (row * nb + jw) * 16);
   }
   const int64_t rowd = min(row0 + (lane & 15), N - 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c.d[i] = dw[rowd * nb + min(jb + 4 * (lane >> 4) + i, nb - 1)];
+  for (int i = 0; i < kMfLD; ++i)
+    c.d[i] = dw[rowd * nb + min(jb + kMfLD * (lane >> 4) + i, nb - 1)];
 }
 
 template <int B>
-__global__ __launch_bounds__(512) void k_gemv_q4_0_f32_mf(
+__global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
     const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy) {
   extern __shared__ __align__(16) uint8_t smem[];    // x planes, then the waves' code tiles
-  __shared__ __align__(16) float s_d[8][kMfCB][16];  // [wave][block][row] scales
-  __shared__ float s_part[2][8][16][9];              // [parity][wave][row][b] tile sums
+  __shared__ __align__(16) float s_d[kMfW][kMfCB][16];  // [wave][block][row] scales
+  __shared__ float s_part[2][kMfW][16][9];              // [parity][wave][row][b] tile sums
   const int nb = K >> 5, KP = K + 8;
   uint16_t *xpl = reinterpret_cast<uint16_t *>(smem);  // [2B][KP] bf16
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int ntiles = (N + 15) >> 4;
-  const int nbw = (nb + 7) >> 3;  // blocks per wave and tile (<= 16)
+  const int nbw = (nb + kMfW - 1) / kMfW;  // blocks per wave and tile (<= kMfCB)
   const int jw0 = min(nb, wv * nbw), jw1 = min(nb, jw0 + nbw);
   int t = blockIdx.x;
   const int G = gridDim.x;
@@ -680,10 +690,10 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_f32_mf(
   // tile's codes, in this order so that staging x waits for x only; x ->
   // hi / lo planes in the k order of the A operand
   const int k4 = K >> 2;
-  f32x4 v[2][B];
+  f32x4 v[kMfXH][B];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int kk = min(512 * h + tid, k4 - 1);
+  for (int h = 0; h < kMfXH; ++h) {
+    const int kk = min(kMfT * h + tid, k4 - 1);
 #pragma unroll
     for (int b = 0; b < B; ++b) v[h][b] = load_f4(X + (int64_t)b * ldx + 4 * kk);
   }
@@ -695,10 +705,10 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_f32_mf(
   mf_load(cur, qs, dw, N, nb, 16 * t, jw0, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kMfXH; ++h) {
     // (no test: past K / 4 a thread repeats the last float4, same value to
     // the same place, so that no load moves into a branch)
-    const int kk = min(512 * h + tid, k4 - 1);
+    const int kk = min(kMfT * h + tid, k4 - 1);
     {
       const int k = 4 * kk, q = k & 31;
       const int pos = (k - q) + 2 * (q & 12) + ((q >> 2) & 4);
@@ -749,11 +759,13 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_f32_mf(
   // that comes after the next barrier, when these reads are done
   auto tile = [&](const MfChunk &c, int tt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4 *>(wt + col * 272 + (4 * i + kg) * 16) = c.w[i];
+    for (int i = 0; i < kMfLD; ++i)
+      *reinterpret_cast<u32x4 *>(wt + (lane % kMfCB) * 272 +
+                                 ((64 / kMfCB) * i + lane / kMfCB) * 16) = c.w[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sdw[(4 * kg + i) * 16 + col] = jw0 + 4 * kg + i < jw1 ? f16_bits_to_f32(c.d[i]) : 0.0f;
+    for (int i = 0; i < kMfLD; ++i)
+      sdw[(kMfLD * kg + i) * 16 + col] =
+          jw0 + kMfLD * kg + i < jw1 ? f16_bits_to_f32(c.d[i]) : 0.0f;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile stores
     __builtin_amdgcn_wave_barrier();
     f32x4 acc = zero;
@@ -792,7 +804,7 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_f32_mf(
       const int b = tid >> 4, row = tid & 15;
       float v = 0.0f;
 #pragma unroll
-      for (int w8 = 0; w8 < 8; ++w8) v += s_part[par][w8][row][b];
+      for (int w8 = 0; w8 < kMfW; ++w8) v += s_part[par][w8][row][b];
       const int n = 16 * tt + row;
       if (n < N) Y[(int64_t)b * ldy + n] = v;
     }
@@ -825,7 +837,7 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_f32_mf(
 // routine, so the codes equal the standalone quantizer's) or as a Q8_1
 // buffer. Rows are bit-identical across every B this kernel takes.
 template <int B, bool FROM_X>
-__global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
+__global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
     const float *__restrict__ X, int64_t ldx, const uint8_t *__restrict__ Xq,
     float *__restrict__ Y, int64_t ldy) {
@@ -834,8 +846,8 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
   extern __shared__ __align__(16) uint8_t smem[];
   extern __shared__ __align__(16) uint32_t smem_u[];
   extern __shared__ __align__(16) float smem_f[];
-  __shared__ __align__(16) float s_d[8][kMfCB][16];  // [wave][block][row] weight scales
-  __shared__ float s_part[2][8][16][9];              // [parity][wave][row][b] tile sums
+  __shared__ __align__(16) float s_d[kMfW][kMfCB][16];  // [wave][block][row] weight scales
+  __shared__ float s_part[2][kMfW][16][9];              // [parity][wave][row][b] tile sums
   const int nb = K >> 5, KP = K + 16;
   // [B][KP] int8 codes at smem (bytes K .. K + 15 of a row unused), then
   // [B][nb] fp32 x scales and one spare word, from word dx0
@@ -843,7 +855,7 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int ntiles = (N + 15) >> 4;
-  const int nbw = (nb + 7) >> 3;  // blocks per wave and tile (<= 16)
+  const int nbw = (nb + kMfW - 1) / kMfW;  // blocks per wave and tile (<= kMfCB)
   const int jw0 = min(nb, wv * nbw), jw1 = min(nb, jw0 + nbw);
   int t = blockIdx.x;
   const int G = gridDim.x;
@@ -852,12 +864,12 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
   // the first tile's codes, in this order so that staging x waits for x
   // only; the x codes go to LDS in the k order of the A operand
   const int k4 = K >> 2;
-  f32x4 v[FROM_X ? 2 : 1][FROM_X ? B : 1];
-  uint32_t c[FROM_X ? 1 : 2][FROM_X ? 1 : B];
-  uint16_t dq[FROM_X ? 1 : 2];  // x scales of a Q8_1 buffer: B * nb <= 1024
+  f32x4 v[FROM_X ? kMfXH : 1][FROM_X ? B : 1];
+  uint32_t c[FROM_X ? 1 : kMfXH][FROM_X ? 1 : B];
+  uint16_t dq[FROM_X ? 1 : kMfXH];  // x scales of a Q8_1 buffer: B * nb <= 1024
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int kk = min(512 * h + tid, k4 - 1);
+  for (int h = 0; h < kMfXH; ++h) {
+    const int kk = min(kMfT * h + tid, k4 - 1);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       if constexpr (FROM_X)
@@ -866,21 +878,21 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
         c[h][b] = *reinterpret_cast<const uint32_t *>(Xq + (size_t)b * K + 4 * kk);
     }
     if constexpr (!FROM_X)
-      dq[h] = reinterpret_cast<const uint16_t *>(Xq + (size_t)B * K)[2 * min(512 * h + tid, B * nb - 1)];
+      dq[h] = reinterpret_cast<const uint16_t *>(Xq + (size_t)B * K)[2 * min(kMfT * h + tid, B * nb - 1)];
   }
   __builtin_amdgcn_sched_barrier(0);
   MfChunk cur;
   mf_load(cur, qs, dw, N, nb, 16 * t, jw0, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kMfXH; ++h) {
     // past K / 4 a thread works on the last group of 4 values and stores
     // into unused words (no branch, so that no load moves into one); Q8_1
     // takes whole 8-lane groups (32 values), which K % 32 == 0 keeps either
     // wholly inside or wholly past the row
     // (row offsets as running sums: a multiply-add here becomes a 64-bit
     // one whose unused half reads a register with a load in flight)
-    const int kr = 512 * h + tid, kk = min(kr, k4 - 1);
+    const int kr = kMfT * h + tid, kk = min(kr, k4 - 1);
     const bool in = kr < k4, lead = in && (kk & 7) == 0;
     const unsigned k = 4 * kk, q = k & 31;
     unsigned cw = (in ? (k - q) + 2 * (q & 12) + ((q >> 2) & 4) : (unsigned)K) >> 2;
@@ -900,7 +912,7 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
       di += nb;
     }
     if constexpr (!FROM_X) {
-      const int i = 512 * h + tid;
+      const int i = kMfT * h + tid;
       smem_f[i < B * nb ? dx0 + i : dx0 + B * nb] = f16_bits_to_f32(dq[h]);
     }
   }
@@ -934,11 +946,13 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
   // one tile, as in the W4A16 kernel (s_part parities alternate)
   auto tile = [&](const MfChunk &ch, int tt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4 *>(&smem_u[wt + col * 68 + (4 * i + kg) * 4]) = ch.w[i];
+    for (int i = 0; i < kMfLD; ++i)
+      *reinterpret_cast<u32x4 *>(
+          &smem_u[wt + (lane % kMfCB) * 68 + ((64 / kMfCB) * i + lane / kMfCB) * 4]) = ch.w[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sdw[(4 * kg + i) * 16 + col] = jw0 + 4 * kg + i < jw1 ? f16_bits_to_f32(ch.d[i]) : 0.0f;
+    for (int i = 0; i < kMfLD; ++i)
+      sdw[(kMfLD * kg + i) * 16 + col] =
+          jw0 + kMfLD * kg + i < jw1 ? f16_bits_to_f32(ch.d[i]) : 0.0f;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile stores
     __builtin_amdgcn_wave_barrier();
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -968,7 +982,7 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
       const int b = tid >> 4, row = tid & 15;
       float v8 = 0.0f;
 #pragma unroll
-      for (int w8 = 0; w8 < 8; ++w8) v8 += s_part[par][w8][row][b];
+      for (int w8 = 0; w8 < kMfW; ++w8) v8 += s_part[par][w8][row][b];
       const int n = 16 * tt + row;
       if (n < N) Y[(int64_t)b * ldy + n] = v8;
     }
@@ -988,19 +1002,19 @@ __global__ __launch_bounds__(512) void k_gemv_q4_0_mf(
   tile(cur, t);
 }
 
-// a persistent grid, one 8-wave workgroup per CU (over 128 VGPRs per lane)
+// a persistent grid, one 16-wave workgroup per CU
 template <int B>
 hipError_t launch_q4_mf(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                         int64_t ldx, const uint8_t *Xq, float *Y, int64_t ldy, hipStream_t s) {
   const size_t xb = (size_t)B * (K + 16) + (size_t)4 * B * (K / 32) + 4;
-  const size_t tiles = (size_t)8 * kMfTileBytes;
+  const size_t tiles = (size_t)kMfW * kMfTileBytes;
   const size_t lds = xb > tiles ? xb : tiles;  // at most 41 KiB (B = 8, K = 4096)
   const int grid = min((N + 15) / 16, cu_count());
   if (X)
-    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, true>), dim3(grid), dim3(512), lds, s, qs, d, N, K, X,
+    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, true>), dim3(grid), dim3(kMfT), lds, s, qs, d, N, K, X,
                        ldx, Xq, Y, ldy);
   else
-    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, false>), dim3(grid), dim3(512), lds, s, qs, d, N, K,
+    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, false>), dim3(grid), dim3(kMfT), lds, s, qs, d, N, K,
                        X, ldx, Xq, Y, ldy);
   return hipGetLastError();
 }
@@ -1024,13 +1038,12 @@ hipError_t launch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, con
   return hipGetLastError();
 }
 
-// W4A16 on the matrix cores: a persistent grid, one 8-wave workgroup per CU
-// (over 128 VGPRs per lane)
+// W4A16 on the matrix cores: a persistent grid, one 16-wave workgroup per CU
 template <int B>
 hipError_t launch_q4_f32_mf(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                             int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
   constexpr size_t kMaxLds = (size_t)4 * kMfMaxXK + (size_t)4 * B * 8;
-  const size_t xb = (size_t)4 * B * (K + 8), tiles = (size_t)8 * kMfTileBytes;
+  const size_t xb = (size_t)4 * B * (K + 8), tiles = (size_t)kMfW * kMfTileBytes;
   const size_t lds = xb > tiles ? xb : tiles;
   if (lds > 65536) {  // above the default dynamic-LDS limit: raise it once per kernel
     static const hipError_t raised = hipFuncSetAttribute(
@@ -1039,7 +1052,7 @@ hipError_t launch_q4_f32_mf(const uint8_t *qs, const uint16_t *d, int N, int K, 
     if (raised != hipSuccess) return raised;
   }
   const int grid = min((N + 15) / 16, cu_count());
-  hipLaunchKernelGGL((k_gemv_q4_0_f32_mf<B>), dim3(grid), dim3(512), lds, s, qs, d, N, K, X,
+  hipLaunchKernelGGL((k_gemv_q4_0_f32_mf<B>), dim3(grid), dim3(kMfT), lds, s, qs, d, N, K, X,
                      ldx, Y, ldy);
   return hipGetLastError();
 }
@@ -1071,10 +1084,10 @@ template <int B>
 hipError_t dispatch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                            int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
   const int nb = K / 32;
-  // three or more rows and K <= 4096: the matrix cores
+  // two or more rows and K <= 4096: the matrix cores
   {
     const int sw = path_switch(MMV_PATH_Q4F32_MF);
-    if (sw >= 0 && B >= (sw > 0 ? sw : 3) && nb <= 8 * kMfCB && (int64_t)B * K <= kMfMaxXK)
+    if (sw >= 0 && B >= (sw > 0 ? sw : 2) && nb <= kMfW * kMfCB && (int64_t)B * K <= kMfMaxXK)
       return launch_q4_f32_mf<B>(qs, d, N, K, X, ldx, Y, ldy, s);
   }
   // whole rows per lane, one row group per workgroup: x of B rows in at

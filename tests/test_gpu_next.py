@@ -150,8 +150,8 @@ def test_w4a16_integer_pin_bit_exact(mm, orc, dev, N, K, B):
 def test_w4a16_batch_invariance(mm, dev):
     # each row of a B-row call against the same row in other calls: bit for
     # bit within one kernel family (the fp32 kernels: every B for K > 4096 and
-    # B <= 2 otherwise, each (row, b) sum in one order; the matrix-core
-    # kernel: B >= 3 at K <= 4096, column b depending on x row b only), within
+    # B = 1 otherwise, each (row, b) sum in one order; the matrix-core kernel:
+    # B >= 2 at K <= 4096, column b depending on x row b only), within
     # rounding across the two
     for N, K in ((2000, 2048), (700, 8192), (1300, 4096), (129, 2560), (65, 96),
                  (40, 11008)):
@@ -160,15 +160,14 @@ def test_w4a16_batch_invariance(mm, dev):
         X = synth.activations(Bmax, K, 0, "w4a16inv", K, device=dev)
         yB = mm.gemv_q4_0_f32(W, X)
         assert torch.equal(yB, mm.gemv_q4_0_f32(W, X))
-        mf = K <= 4096 and Bmax >= 3
+        mf = K <= 4096 and Bmax >= 2
         for b in range(Bmax):
             y1 = mm.gemv_q4_0_f32(W, X[b].clone())
             if not mf:
                 assert torch.equal(yB[b], y1)
                 continue
-            y3 = mm.gemv_q4_0_f32(W, X[[b, (b + 1) % Bmax, (b + 2) % Bmax]].clone())
-            assert torch.equal(yB[b], y3[0])
-            assert torch.equal(y1, mm.gemv_q4_0_f32(W, X[[b, b]].clone())[1])
+            y2 = mm.gemv_q4_0_f32(W, X[[b, (b + 1) % Bmax]].clone())
+            assert torch.equal(yB[b], y2[0])
             assert rel_l2_rows(npc(yB[b]), npc(y1).astype(np.float64)) <= 2e-5
 
 
