@@ -595,11 +595,11 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
   constexpr int RP = B <= 2 ? 2 : 4;
   // K <= 4096: the matrix cores from B = 3 for fp32 x (quantized in every
   // workgroup: the dot4 kernels' repeated quantization is the bound there),
-  // from B = 7 for a Q8_1 buffer (4096^2 + 11008 x 4096 per pair, dot4 /
-  // matrix cores: B = 6 19.5 / 20.2 us, B = 7 21.2 / 20.5, B = 8 22.9 / 21.0)
+  // from B = 6 for a Q8_1 buffer (4096^2 + 11008 x 4096 per pair, dot4 /
+  // matrix cores: B = 5 17.9 / 18.1 us, B = 6 19.3 / 18.3, B = 8 22.5 / 19.0)
   {
     const int sw = path_switch(MMV_PATH_Q4_MF);
-    if (sw >= 0 && B >= (sw > 0 ? sw : (X ? 3 : 7)) && nb <= kMfW * kMfCB)
+    if (sw >= 0 && B >= (sw > 0 ? sw : (X ? 3 : 6)) && nb <= kMfW * kMfCB)
       return launch_q4_mf<B>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   }
   // whole blocks per lane: every load of a row group in flight together
@@ -700,7 +700,7 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
   __builtin_amdgcn_sched_barrier(0);
   const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
   u32x4 xreg[kMfCB];
-  float creg[kMfCB];
+  f32x4 creg[kMfCB];  // -136 sum x_part in all four entries: the accumulator S starts from
   MfChunk cur;
   mf_load(cur, qs, dw, N, nb, 16 * t, jw0, lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -744,7 +744,8 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
       const f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           __builtin_bit_cast(bf16x8v, ones), __builtin_bit_cast(bf16x8v, xreg[u]), zero, 0, 0,
           0);
-      creg[u] = 136.0f * s.x;
+      const float c = -136.0f * s.x;
+      creg[u] = f32x4{c, c, c, c};
     }
   }
   __syncthreads();  // the x planes are dead: the code tiles take their place
@@ -778,15 +779,16 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
       av.y = __builtin_amdgcn_perm(0x43434343u, mlo, 0x04030402u);
       av.z = __builtin_amdgcn_perm(0x43434343u, mhi, 0x04010400u);
       av.w = __builtin_amdgcn_perm(0x43434343u, mhi, 0x04030402u);
+      // S - 136 sum x_part (the accumulator starts from the correction)
       const f32x4 s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8v, av), __builtin_bit_cast(bf16x8v, xreg[u]), zero, 0, 0, 0);
+          __builtin_bit_cast(bf16x8v, av), __builtin_bit_cast(bf16x8v, xreg[u]), creg[u], 0, 0,
+          0);
       // scales of rows 4 kg .. 4 kg + 3 at this block
       const f32x4 sd = *reinterpret_cast<const f32x4 *>(sdw + u * 16 + 4 * kg);
-      const float cr = creg[u];
-      acc.x = fmaf(sd.x, s4.x - cr, acc.x);
-      acc.y = fmaf(sd.y, s4.y - cr, acc.y);
-      acc.z = fmaf(sd.z, s4.z - cr, acc.z);
-      acc.w = fmaf(sd.w, s4.w - cr, acc.w);
+      acc.x = fmaf(sd.x, s4.x, acc.x);
+      acc.y = fmaf(sd.y, s4.y, acc.y);
+      acc.z = fmaf(sd.z, s4.z, acc.z);
+      acc.w = fmaf(sd.w, s4.w, acc.w);
     }
     __builtin_amdgcn_wave_barrier();  // the tile and s_d are rewritten next time
     acc.x += dpp_f32<0x128>(acc.x);   // row_ror:8
@@ -826,13 +828,20 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
 }
 
 // ---- Q4_0 x Q8_1 on the matrix cores -------------------------------------
-// The same tiling as W4A16 on the matrix cores, with v_mfma_i32_16x16x32_i8:
-//  - A: lane l's 4 code bytes of the block, masked into 4 low-nibble and 4
-//    high-nibble codes (unsigned int8 0..15, k as above);
-//  - B: the Q8_1 codes of x row l % 16 (l % 16 < B) in the same k order;
+// The same tiling as W4A16 on the matrix cores, with v_mfma_i32_16x16x64_i8
+// on two blocks at once (int8 needs no hi / lo columns, so the 16 columns
+// hold 8 x rows twice: block j in columns 0..7, block j + 1 in 8..15):
+//  - A (16 rows x 64 k): lanes 0..31 serve block j, 32..63 block j + 1;
+//    lane l takes the 8 code bytes 8 ((l / 16) % 2) .. + 7 of its block,
+//    masked into 8 low-nibble and 8 high-nibble codes (unsigned int8 0..15);
+//  - B (64 k x 16 columns): column c < 8 holds the Q8_1 codes of x row c at
+//    block j in lanes 0..31 and zeros in 32..63, column c + 8 the same row
+//    at block j + 1 in lanes 32..63 and zeros in 0..31; the x codes sit in
+//    LDS in the k order of A, so a lane reads its 16 at once;
 //  - per block and x row: S = sum code * q (exact int32), I = S - 8 sum q
 //    (sum q from the same instruction with A = 1), then y += (d_w d_x) I in
-//    fp32 -- I is the block's exact integer dot of the W4A8 product.
+//    fp32 -- I is the block's exact integer dot of the W4A8 product; column
+//    c + 8 folds onto column c at the end.
 // x comes as fp32 (quantized to Q8_1 in every workgroup by the one device
 // routine, so the codes equal the standalone quantizer's) or as a Q8_1
 // buffer. Rows are bit-identical across every B this kernel takes.
@@ -895,7 +904,7 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
     const int kr = kMfT * h + tid, kk = min(kr, k4 - 1);
     const bool in = kr < k4, lead = in && (kk & 7) == 0;
     const unsigned k = 4 * kk, q = k & 31;
-    unsigned cw = (in ? (k - q) + 2 * (q & 12) + ((q >> 2) & 4) : (unsigned)K) >> 2;
+    unsigned cw = (in ? (k - q) + 16 * ((q >> 3) & 1) + (q & 7) + 8 * (q >> 4) : (unsigned)K) >> 2;
     unsigned di = dx0 + (kk >> 3);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -918,24 +927,29 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
   }
   __syncthreads();
 
-  // this lane's B column (x row col, row 0 past B) at the wave's blocks, its
-  // scale and 8 * its code sum (A = 1)
+  // this lane's B operand per block pair (x row col % 8, row 0 past B; its
+  // 16 codes, or zeros where its column takes the other block of the pair),
+  // and its column's scale and 8 * code sum (A = 1)
   typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
   const i32x4v izero = {0, 0, 0, 0};
-  int64_t xq[kMfCB];
-  float dx[kMfCB];
-  int q8[kMfCB];
+  constexpr int NP = kMfCB / 2;  // block pairs per wave and tile
+  i32x4v xq[NP];
+  float dx[NP];
+  i32x4v nq8[NP];  // -8 sum q in all four entries: the accumulator the block dot starts from
   {
-    const int bc = col < B ? col : 0;
-    const int xrow = (bc * KP + 8 * kg) >> 2;
+    const int bc = (col & 7) < B ? (col & 7) : 0;
+    const bool mine = (col >= 8) == (kg >= 2);
+    const int xrow = (bc * KP + 16 * (kg & 1)) >> 2;
+    const i32x4v ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
-    for (int u = 0; u < kMfCB; ++u) {
-      const int j = min(jw0 + u, nb - 1);
-      xq[u] = (int64_t)smem_u[xrow + 8 * j] | ((int64_t)smem_u[xrow + 8 * j + 1] << 32);
-      dx[u] = smem_f[dx0 + bc * nb + j];
-      const i32x4v s = __builtin_amdgcn_mfma_i32_16x16x32_i8(0x0101010101010101ll, xq[u],
-                                                             izero, 0, 0, 0);
-      q8[u] = 8 * s.x;
+    for (int p = 0; p < NP; ++p) {
+      const int jb = min(jw0 + 2 * p + (kg >> 1), nb - 1);   // this lane's B rows
+      const int jc = min(jw0 + 2 * p + (col >> 3), nb - 1);  // this lane's column
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(&smem_u[xrow + 8 * jb]);
+      xq[p] = mine ? __builtin_bit_cast(i32x4v, v) : izero;
+      dx[p] = smem_f[dx0 + bc * nb + jc];
+      const i32x4v s = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, xq[p], izero, 0, 0, 0);
+      nq8[p] = i32x4v{-8 * s.x, -8 * s.x, -8 * s.x, -8 * s.x};
     }
   }
   __syncthreads();  // x is in registers: the code tiles take its place
@@ -957,20 +971,30 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
     __builtin_amdgcn_wave_barrier();
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < kMfCB; ++u) {
-      const uint32_t w = smem_u[wt + u * 68 + col * 4 + kg];
-      const uint64_t a = (uint64_t)(w & 0x0F0F0F0Fu) | ((uint64_t)((w >> 4) & 0x0F0F0F0Fu) << 32);
-      const i32x4v s4 =
-          __builtin_amdgcn_mfma_i32_16x16x32_i8((int64_t)a, xq[u], izero, 0, 0, 0);
-      const f32x4 sd = *reinterpret_cast<const f32x4 *>(sdw + u * 16 + 4 * kg);
-      const float d = dx[u];
-      const int c8 = q8[u];
-      acc.x = fmaf(sd.x * d, (float)(s4.x - c8), acc.x);
-      acc.y = fmaf(sd.y * d, (float)(s4.y - c8), acc.y);
-      acc.z = fmaf(sd.z * d, (float)(s4.z - c8), acc.z);
-      acc.w = fmaf(sd.w * d, (float)(s4.w - c8), acc.w);
+    for (int p = 0; p < NP; ++p) {
+      // A: row col, block 2p + kg / 2, code bytes 8 (kg % 2) .. + 7
+      const u32x2 w = *reinterpret_cast<const u32x2 *>(
+          &smem_u[wt + (2 * p + (kg >> 1)) * 68 + col * 4 + 2 * (kg & 1)]);
+      i32x4v a;
+      a.x = (int)(w.x & 0x0F0F0F0Fu);
+      a.y = (int)(w.y & 0x0F0F0F0Fu);
+      a.z = (int)((w.x >> 4) & 0x0F0F0F0Fu);
+      a.w = (int)((w.y >> 4) & 0x0F0F0F0Fu);
+      // I = sum code * q - 8 sum q, exact
+      const i32x4v i4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xq[p], nq8[p], 0, 0, 0);
+      // this lane's outputs: rows 4 kg .. + 3 of column col, block 2p + col / 8
+      const f32x4 sd = *reinterpret_cast<const f32x4 *>(sdw + (2 * p + (col >> 3)) * 16 + 4 * kg);
+      const float d = dx[p];
+      acc.x = fmaf(sd.x * d, (float)i4.x, acc.x);
+      acc.y = fmaf(sd.y * d, (float)i4.y, acc.y);
+      acc.z = fmaf(sd.z * d, (float)i4.z, acc.z);
+      acc.w = fmaf(sd.w * d, (float)i4.w, acc.w);
     }
     __builtin_amdgcn_wave_barrier();  // the tile and s_d are rewritten next time
+    acc.x += dpp_f32<0x128>(acc.x);   // row_ror:8: the odd blocks (columns 8..15) onto
+    acc.y += dpp_f32<0x128>(acc.y);   // the even ones (columns 0..7)
+    acc.z += dpp_f32<0x128>(acc.z);
+    acc.w += dpp_f32<0x128>(acc.w);
     if (col < B) {
       s_part[par][wv][4 * kg + 0][col] = acc.x;
       s_part[par][wv][4 * kg + 1][col] = acc.y;
