@@ -627,9 +627,10 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
 //    bf16 lo = bf16(x - hi) (columns 8..15; x - hi is exact in fp32),
 //    stored in the same k order as A, so each lane reads its 8 values at
 //    once; columns past B repeat row 0 and are never read back;
-//  - per block and column: S = sum (128 + c) x_part, and the block's term
-//    d_w (S - 136 sum x_part) = d_w sum (c - 8) x_part; the block sums of
-//    x_part come from the same instruction with A = 1;
+//  - per block and column: S = sum (128 + c) x_part - 136 sum x_part =
+//    sum (c - 8) x_part (the accumulator starts at -136 sum x_part, the
+//    block sums of x_part coming from the same instruction with A = 1),
+//    then d_w S;
 //  - y = the hi column plus the lo column, over the blocks.
 // Rows agree with the fp32 kernels within rounding and bit for bit across
 // every B this kernel takes (column b depends only on x row b).
@@ -686,9 +687,9 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
   int t = blockIdx.x;
   const int G = gridDim.x;
 
-  // x (at most two float4 per row and thread: K <= 4096), then the first
-  // tile's codes, in this order so that staging x waits for x only; x ->
-  // hi / lo planes in the k order of the A operand
+  // x (kMfXH float4 per row and thread: K <= 4096), then the first tile's
+  // codes, in this order so that staging x waits for x only; x -> hi / lo
+  // planes in the k order of the A operand
   const int k4 = K >> 2;
   f32x4 v[kMfXH][B];
 #pragma unroll
@@ -869,7 +870,7 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
   int t = blockIdx.x;
   const int G = gridDim.x;
 
-  // x (at most two groups of 4 values per row and thread: K <= 4096), then
+  // x (kMfXH groups of 4 values per row and thread: K <= 4096), then
   // the first tile's codes, in this order so that staging x waits for x
   // only; the x codes go to LDS in the k order of the A operand
   const int k4 = K >> 2;

@@ -279,7 +279,7 @@ def test_q4_0_batch_invariance(mm, dev):
 
 
 @pytest.mark.parametrize("N,K", [(4096, 4096), (20000, 4096), (1000, 96), (777, 2560),
-                                 (33, 3840)])
+                                 (33, 3840), (16, 512), (1, 128), (17, 32)])
 def test_q4_0_both_kernels_every_b(mm, orc, dev, path, N, K):
     # the matrix-core kernel forced from B = 1 and the dot4 kernels forced at
     # every B, from fp32 x and from a Q8_1 buffer (the same rows bit for bit),

@@ -172,7 +172,7 @@ def test_w4a16_batch_invariance(mm, dev):
 
 
 @pytest.mark.parametrize("N,K", [(4096, 4096), (20000, 4096), (1000, 96), (777, 2560),
-                                 (33, 32)])
+                                 (33, 32), (16, 512), (1, 128), (17, 32)])
 def test_w4a16_both_kernels_every_b(mm, orc, dev, path, N, K):
     # the matrix-core kernel forced from B = 1 and the fp32 kernels forced at
     # every B, both against the oracle (20000 rows: several tiles per
