@@ -299,6 +299,29 @@ def test_q4_0_both_kernels_every_b(mm, orc, dev, path, N, K):
             assert rel_l2_rows(npc(y), ref) <= Q4_ARITH_TOL, (B, sw)
 
 
+@pytest.mark.parametrize("B", [2, 3, 5, 7])
+def test_q4_0_strided_x_and_y(mm, orc, dev, B):
+    # x rows with ldx > K at an offset, y rows with ldy > N (the padding must
+    # stay untouched), from fp32 x and from a Q8_1 buffer: the dot4 kernels
+    # (B = 2; B = 3, 5 from the buffer) and the matrix cores (B = 3, 5, 7
+    # from x; B = 7 from the buffer)
+    N, K = 1200, 1024
+    W, qs, d = _q4(mm, N, K, dev, "stride")
+    Xb = synth.activations(B, K + 64, 0, "q4s", B, device=dev)
+    X = Xb[:, 32:32 + K]
+    q_ref, ds_ref = orc.quantize_q8_1(npc(X))
+    ref = orc.gemv_q4_0(qs, d, q_ref, ds_ref)
+    for use_xq in (False, True):
+        Yb = torch.full((B, N + 7), 123.0, device=dev)
+        if use_xq:
+            mm.gemv_q4_0(W, xq=mm.quantize_q8_1(X), B=B, out=Yb[:, :N])
+        else:
+            mm.gemv_q4_0(W, x=X, out=Yb[:, :N])
+        torch.cuda.synchronize()
+        assert rel_l2_rows(npc(Yb[:, :N]), ref) <= Q4_ARITH_TOL
+        assert torch.all(Yb[:, N:] == 123.0)
+
+
 @pytest.mark.parametrize("env", [
     dict(Q4_RP=2), dict(Q4_RP=4), dict(Q4_RP=6), dict(Q4_RP=8),
     dict(Q4_GENERIC=1, Q4_WG_PER_CU=1),
