@@ -166,14 +166,15 @@ int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,
  *    dequantization) and the dequant-gemv kernels its closing paragraph
  *    announces]
  *   Y[b*ldy + n] = sum_j d_w[n][j] * sum_i (code_i - 8) * X[b*ldx + 32j + i],
- *   fp32 sums.  B = 1 or K > 4096: fp32 arithmetic, per block s =
- *   sum_i code_i * x_i, then d_w * (s - 8 * sum_i x_i).  B >= 2 with
- *   K <= 4096: the matrix cores, x split into bf16 hi + lo (x kept to
- *   2^-17 relative), per block d_w * (sum_i (128 + code_i) x_part - 136 *
- *   sum_i x_part); the two agree within rounding (rel-L2 ~1e-5), and each
- *   is bit-identical across the B it serves.  Any K % 32 == 0 with
- *   B * K <= MMV_Q4F32_MAX_XK (x of every row is staged in on-chip memory:
- *   B = 8 at K = 4096, B = 3 at K = 11008, B = 1 up to K = 36864).
+ *   fp32 sums.  x is split into bf16 hi + lo (x kept to 2^-17 relative) and
+ *   each code enters as bf16 128 + code, so every product is exact; per
+ *   block d_w * (sum_i (128 + code_i) (hi_i + lo_i) - 136 * sum_i (hi_i +
+ *   lo_i)).  B = 1 or K > 4096: two codes per v_dot2 (fp32 accumulation);
+ *   B >= 2 with K <= 4096: the matrix cores.  The two agree within rounding
+ *   (rel-L2 ~1e-5), and each is bit-identical across the B it serves.
+ *   Any K % 32 == 0 with B * K <= MMV_Q4F32_MAX_XK (x of every row is
+ *   staged in on-chip memory: B = 8 at K = 4096, B = 3 at K = 11008,
+ *   B = 1 up to K = 36864).
  *   X: B x K fp32, 16-byte aligned, ldx % 4 == 0.  Y: B x N fp32, ldy >= N.
  * ------------------------------------------------------------------------ */
 int gemv_q4_0_f32(const mmv_q4_0 *W, const float *X, int64_t ldx, int32_t B,

@@ -161,24 +161,27 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(
   }
 }
 
-// Whole-row variant: K = 32 * G * T exactly, so each lane owns T blocks of
-// each of its RP rows, and a workgroup owns one group of 4 * RP * (64 / G)
-// consecutive rows.  The activation loads are issued first, then all RP * T
-// weight loads of the group; the activation is quantized into LDS while the
-// weights are in flight (loads complete in issue order).  Per-row arithmetic
-// order is the same as in k_gemv_q4_0: block j's integer sum scaled by
-// d_w * d_x and accumulated over j = sub, sub + G, ..., then a G-lane sum.
-template <int B, int G, int RP, int T, bool FROM_X>
+// Whole-row variant: K = 32 * G * T, or with RAG any K <= 32 * G * T, so
+// each lane owns at most T blocks of each of its RP rows (blocks sub + G t;
+// past a ragged row's last block the load repeats that block, in bounds,
+// and the step is skipped), and a workgroup
+// owns one group of 4 * RP * (64 / G) consecutive rows.  The activation
+// loads are issued first, then all RP * T weight loads of the group; the
+// activation is quantized into LDS while the weights are in flight (loads
+// complete in issue order).  Per-row arithmetic order is the same as in
+// k_gemv_q4_0: block j's integer sum scaled by d_w * d_x and accumulated
+// over j = sub, sub + G, ..., then a G-lane sum.
+template <int B, int G, int RP, int T, bool FROM_X, bool RAG>
 __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
-    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int /*K*/,
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int Kr,
     const float *__restrict__ X, int64_t ldx, const uint8_t *__restrict__ Xq,
     float *__restrict__ Y, int64_t ldy) {
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int K = 32 * G * T;  // the launcher checks K against this
   constexpr int RPP = 64 / G;
   constexpr int ROWS_WAVE = RP * RPP;
   constexpr int ROWS_WG = 4 * ROWS_WAVE;
-  constexpr int nb = G * T;
+  // RAG: K <= 32 G T at run time (the launcher checks it); else exactly 32 G T
+  const int K = RAG ? Kr : 32 * G * T, nb = K >> 5;
   const int lane = threadIdx.x & 63;
   const int sub = lane % G, grp = lane / G;
   const int wv = threadIdx.x >> 6;
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
     const int64_t rowblk = (int64_t)min(rbase + p * RPP, N - 1) * nb;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const int64_t blk = rowblk + sub + G * t;
+      const int64_t blk = rowblk + min(sub + G * t, nb - 1);
       w[p][t] = load_stream16(qs + blk * 16);
       d[p][t] = f16_bits_to_f32(load_stream2(dw + blk));
     }
@@ -226,16 +229,18 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int j = sub + G * t;
+    if (j < nb) {  // false only in the last step of a ragged row
 #pragma unroll
-    for (int r = 0; r < B; ++r) {
-      const i32x4 xa = xstage_lo(st, r, K, j);
-      const i32x4 xb = xstage_hi(st, r, K, j);
-      const int xs = st.qsum[r * nb + j];
-      const float dx = st.d[r * nb + j];
+      for (int r = 0; r < B; ++r) {
+        const i32x4 xa = xstage_lo(st, r, K, j);
+        const i32x4 xb = xstage_hi(st, r, K, j);
+        const int xs = st.qsum[r * nb + j];
+        const float dx = st.d[r * nb + j];
 #pragma unroll
-      for (int p = 0; p < RP; ++p) {
-        const int I = q4_block_isum(w[p][t], xa, xb, xs);
-        acc[p][r] = fmaf(d[p][t] * dx, (float)I, acc[p][r]);
+        for (int p = 0; p < RP; ++p) {
+          const int I = q4_block_isum(w[p][t], xa, xb, xs);
+          acc[p][r] = fmaf(d[p][t] * dx, (float)I, acc[p][r]);
+        }
       }
     }
   }
@@ -255,35 +260,70 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
 // names W4A16 INT4 weights with on-the-fly dequantization as the variant
 // that trades integer unpacking for activation precision.  Same row layout
 // as k_gemv_q4_0_t (G lanes per row, RP rows per lane group, weight loads
-// issued after the first activation loads).  x is staged in LDS as fp32 in
-// a block-transposed layout ([b][q][j] float4, q = 0..7 within a block, so
-// lanes reading consecutive blocks read consecutive 16-byte words), with
-// each block's sum sx = sum_i x_i (fixed order).  Per block: s1 = sum_i
-// code_i * x_i (codes converted from bytes, k ascending through the low then
-// the high nibbles), value d_w * (s1 - 8 sx).  Every (row, b) sum runs over
-// the lane's blocks j = sub, sub + G, ... in ascending order, then the G-lane
-// sum: one order for every B and in both kernels below (same G), so rows
-// are bit-identical whatever the batch and the kernel.
+// issued after the first activation loads).  x is split into bf16 high and
+// low parts (x - hi is exact in fp32; lo keeps the next 8 bits, so hi + lo
+// is x to 2^-17 relative) and staged in LDS block-transposed: 16 bytes per
+// (b, q, j), q = 0..7 within a block, holding hi(x0 x1), hi(x2 x3),
+// lo(x0 x1), lo(x2 x3) of positions 4q..4q+3, so lanes reading consecutive
+// blocks read consecutive 16-byte words.  Each block's -136 sum_i (hi + lo)
+// is staged beside it.  A code becomes bf16 128 + c by one v_perm per two
+// codes (exponent byte 0x43 above the code byte), and v_dot2c_f32_bf16 takes
+// two codes times two x parts per instruction (products exact in fp32).  Per
+// block: S = -136 sum (hi + lo), then S += (128 + c) . hi and (128 + c) . lo
+// (k ascending through the low then the high nibbles), value d_w * S =
+// d_w sum (c - 8)(hi + lo).  Every (row, b) sum runs over the lane's blocks
+// j = sub, sub + G, ... in ascending order, then the G-lane sum: one order
+// for every B and in both kernels below (same G), so rows are bit-identical
+// whatever the batch and the kernel.
 constexpr int kF32Pass = 8;  // float4 staging tasks per thread per pass
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {  // round to nearest even
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// row of task t (0 <= t < B * per_row) of a row-major [B][per_row] array:
+// no division for one or two rows
+template <int B>
+__device__ __forceinline__ int task_row(int t, int per_row) {
+  if constexpr (B == 1) return 0;
+  else if constexpr (B == 2) return t >= per_row ? 1 : 0;
+  else return t / per_row;
+}
 
 // one float4 of x (task t of the [B][K/4] row-major x) to the staged layout;
 // the block's sum is formed by the 8 lanes holding it
+template <int B>
 __device__ __forceinline__ void w4a16_stage4(f32x4 v, int t, int K, int nb, bool store,
                                              f32x4 *xs, float *sx) {
   asm volatile("" ::"v"(v));  // keep the load where it was issued
-  const float sum = group8_sum((v.x + v.y) + (v.z + v.w));
+  const uint32_t h0 = bf16_pair(v.x, v.y), h1 = bf16_pair(v.z, v.w);
+  const uint32_t l0 = bf16_pair(v.x - bf16_lo(h0), v.y - bf16_hi(h0));
+  const uint32_t l1 = bf16_pair(v.z - bf16_lo(h1), v.w - bf16_hi(h1));
+  // the sum of the values the products see (hi + lo), by dot products with 1
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  float s4 = __builtin_amdgcn_fdot2_f32_bf16(one, __builtin_bit_cast(bf16x2, h0), 0.0f, false);
+  s4 = __builtin_amdgcn_fdot2_f32_bf16(one, __builtin_bit_cast(bf16x2, h1), s4, false);
+  s4 = __builtin_amdgcn_fdot2_f32_bf16(one, __builtin_bit_cast(bf16x2, l0), s4, false);
+  s4 = __builtin_amdgcn_fdot2_f32_bf16(one, __builtin_bit_cast(bf16x2, l1), s4, false);
+  const float sum = group8_sum(s4);
   if (store) {  // uniform over each 8-lane group: the task count is a multiple of 8
-    const int b = t / (K / 4), r = t - b * (K / 4), j = r >> 3, q = r & 7;
-    xs[(b * 8 + q) * nb + j] = v;
-    if (q == 0) sx[b * nb + j] = sum;
+    const int b = task_row<B>(t, K / 4), r = t - b * (K / 4), j = r >> 3, q = r & 7;
+    xs[(b * 8 + q) * nb + j] = __builtin_bit_cast(f32x4, u32x4{h0, h1, l0, l1});
+    if (q == 0) sx[b * nb + j] = -136.0f * sum;
   }
 }
 
-// Block j (the lane's) for RP weight rows and the B x rows: each group of 4
-// code bytes is converted to fp32 once and used for every x row; x of all B
-// rows for those positions is read from LDS once and used for the RP rows.
-// For each (row, x row) the FMAs run low nibbles then high nibbles, bytes
-// ascending; then acc += d_w * (s1 - 8 sx).
+// Block j (the lane's) for RP weight rows and the B x rows: each code dword
+// becomes two bf16 pairs once and serves every x row; x of all B rows for
+// those positions is read from LDS once and serves the RP rows.  For each
+// (row, x row) the sum starts at the staged -136 sum x and runs low nibbles
+// then high nibbles, bytes ascending, hi before lo per byte pair; then
+// acc += d_w * S.  (The x words are copied out of the vector before the
+// bit cast: clang's __builtin_bit_cast of a vector element lvalue such as
+// v.y reads element 0.)
 template <int B, int RP>
 __device__ __forceinline__ void w4a16_block(const u32x4 (&w)[RP], const float (&d)[RP],
                                             const f32x4 *xs, const float *sx, int nb, int j,
@@ -291,63 +331,69 @@ __device__ __forceinline__ void w4a16_block(const u32x4 (&w)[RP], const float (&
   constexpr int DG = B > 4 ? 2 : 4;  // code dwords per step (registers: x of B rows)
   float s1[RP][B];
 #pragma unroll
-  for (int p = 0; p < RP; ++p)
+  for (int r = 0; r < B; ++r) {
+    const float c = sx[r * nb + j];
 #pragma unroll
-    for (int r = 0; r < B; ++r) s1[p][r] = 0.0f;
+    for (int p = 0; p < RP; ++p) s1[p][r] = c;
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {        // low nibbles: codes 0..15; high: 16..31
 #pragma unroll
     for (int d0 = 0; d0 < 4; d0 += DG) {
-      f32x4 xq[B][DG];
+      bf16x2 xq[B][DG][4];  // hi(x0 x1), hi(x2 x3), lo(x0 x1), lo(x2 x3)
 #pragma unroll
       for (int r = 0; r < B; ++r)
 #pragma unroll
-        for (int dd = 0; dd < DG; ++dd) xq[r][dd] = xs[(r * 8 + 4 * h + d0 + dd) * nb + j];
+        for (int dd = 0; dd < DG; ++dd) {
+          const u32x4 v = __builtin_bit_cast(u32x4, xs[(r * 8 + 4 * h + d0 + dd) * nb + j]);
+          const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xq[r][dd][i] = __builtin_bit_cast(bf16x2, e[i]);
+        }
 #pragma unroll
       for (int p = 0; p < RP; ++p) {
         const uint32_t wd[4] = {w[p].x, w[p].y, w[p].z, w[p].w};
-        float cf[DG][4];
+        bf16x2 a01[DG], a23[DG];
 #pragma unroll
         for (int dd = 0; dd < DG; ++dd) {
           const uint32_t c = (wd[d0 + dd] >> (4 * h)) & 0x0F0F0F0Fu;
-          cf[dd][0] = (float)(c & 0xFFu);
-          cf[dd][1] = (float)((c >> 8) & 0xFFu);
-          cf[dd][2] = (float)((c >> 16) & 0xFFu);
-          cf[dd][3] = (float)(c >> 24);
+          // bytes {c0, 0x43, c1, 0x43}: bf16 128 + c0 and 128 + c1 (c < 128)
+          a01[dd] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(0x43434343u, c, 0x04010400u));
+          a23[dd] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(0x43434343u, c, 0x04030402u));
         }
 #pragma unroll
         for (int r = 0; r < B; ++r)
 #pragma unroll
           for (int dd = 0; dd < DG; ++dd) {
-            s1[p][r] = fmaf(cf[dd][0], xq[r][dd].x, s1[p][r]);
-            s1[p][r] = fmaf(cf[dd][1], xq[r][dd].y, s1[p][r]);
-            s1[p][r] = fmaf(cf[dd][2], xq[r][dd].z, s1[p][r]);
-            s1[p][r] = fmaf(cf[dd][3], xq[r][dd].w, s1[p][r]);
+            float s = s1[p][r];
+            s = __builtin_amdgcn_fdot2_f32_bf16(a01[dd], xq[r][dd][0], s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(a23[dd], xq[r][dd][1], s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(a01[dd], xq[r][dd][2], s, false);
+            s = __builtin_amdgcn_fdot2_f32_bf16(a23[dd], xq[r][dd][3], s, false);
+            s1[p][r] = s;
           }
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < B; ++r) {
-    const float sxr = sx[r * nb + j];
+  for (int r = 0; r < B; ++r)
 #pragma unroll
-    for (int p = 0; p < RP; ++p) acc[p][r] = fmaf(d[p], fmaf(-8.0f, sxr, s1[p][r]), acc[p][r]);
-  }
+    for (int p = 0; p < RP; ++p) acc[p][r] = fmaf(d[p], s1[p][r], acc[p][r]);
 }
 
-// K = 32 * G * T exactly and B * K <= MMV_Q4F32_MAX_XK / 2 (x in at most
-// 66 KiB of LDS): a workgroup owns one row group, every weight load of it
-// issued up front.
-template <int B, int G, int RP, int T>
+// K = 32 * G * T, or with RAG any K <= 32 * G * T (as in k_gemv_q4_0_t, a
+// ragged row's last step loads its last block again and skips it), and
+// B * K <= 16384 (x in at most 66 KiB of LDS): a workgroup owns one row
+// group, every weight load of it issued up front.
+template <int B, int G, int RP, int T, bool RAG>
 __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
-    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int /*K*/,
+    const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int Kr,
     const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy) {
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int K = 32 * G * T, nb = G * T;
+  const int K = RAG ? Kr : 32 * G * T, nb = K >> 5;  // RAG: the launcher checks K
   constexpr int RPP = 64 / G, ROWS_WAVE = RP * RPP, ROWS_WG = 4 * ROWS_WAVE;
-  constexpr int TOT = B * K / 4;                          // float4 staging tasks
-  constexpr int NPASS = (TOT + 256 * kF32Pass - 1) / (256 * kF32Pass);
-  constexpr int P0 = cmin(kF32Pass, (TOT + 255) / 256);   // first pass per thread
+  const int TOT = B * K / 4;                              // float4 staging tasks
+  const int P0 = min(kF32Pass, (TOT + 255) / 256);        // first pass per thread
   f32x4 *xs = reinterpret_cast<f32x4 *>(smem);            // [B][8][nb]
   float *sx = reinterpret_cast<float *>(smem + (size_t)B * K * 4);  // [B][nb]
   const int lane = threadIdx.x & 63, sub = lane % G, grp = lane / G, wv = threadIdx.x >> 6;
@@ -356,7 +402,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
 #pragma unroll
     for (int m = 0; m < kF32Pass; ++m) {
       const int t = min(base + (int)threadIdx.x + 256 * m, TOT - 1);
-      const int b = t / (K / 4), r = t - b * (K / 4);
+      const int b = task_row<B>(t, K / 4), r = t - b * (K / 4);
       v[m] = load_f4(X + (int64_t)b * ldx + 4 * r);
     }
   };
@@ -365,7 +411,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
     for (int m = 0; m < kF32Pass; ++m) {
       if (m >= np) break;
       const int t = base + threadIdx.x + 256 * m;
-      w4a16_stage4(v[m], t, K, nb, t < TOT, xs, sx);
+      w4a16_stage4<B>(v[m], t, K, nb, t < TOT, xs, sx);
     }
   };
 
@@ -380,17 +426,16 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
     const int64_t rowblk = (int64_t)min(rbase + p * RPP, N - 1) * nb;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const int64_t blk = rowblk + sub + G * t;
+      const int64_t blk = rowblk + min(sub + G * t, nb - 1);
       w[t][p] = load_stream16(qs + blk * 16);
       d[t][p] = f16_bits_to_f32(load_stream2(dw + blk));
     }
   }
   __builtin_amdgcn_sched_barrier(0);
   store_pass(0, xv, P0);
-#pragma unroll
-  for (int ps = 1; ps < NPASS; ++ps) {
-    load_pass(256 * kF32Pass * ps, xv);
-    store_pass(256 * kF32Pass * ps, xv, kF32Pass);
+  for (int base = 256 * kF32Pass; base < TOT; base += 256 * kF32Pass) {
+    load_pass(base, xv);
+    store_pass(base, xv, kF32Pass);
   }
   __syncthreads();
 
@@ -400,7 +445,8 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
 #pragma unroll
     for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
 #pragma unroll
-  for (int t = 0; t < T; ++t) w4a16_block<B, RP>(w[t], d[t], xs, sx, nb, sub + G * t, acc);
+  for (int t = 0; t < T; ++t)  // the test is false only in the last step of a ragged row
+    if (sub + G * t < nb) w4a16_block<B, RP>(w[t], d[t], xs, sx, nb, sub + G * t, acc);
   float (&flat)[RP * B] = *reinterpret_cast<float(*)[RP * B]>(&acc[0][0]);
   gsum_last_n<G>(flat);
 #pragma unroll
@@ -453,7 +499,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32_g(
 #pragma unroll
     for (int m = 0; m < kF32Pass; ++m) {
       const int t = min(base + (int)threadIdx.x + 256 * m, tot - 1);
-      const int b = t / (K / 4), r = t - b * (K / 4);
+      const int b = task_row<B>(t, K / 4), r = t - b * (K / 4);
       xv[m] = load_f4(X + (int64_t)b * ldx + 4 * r);
     }
   };
@@ -461,7 +507,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32_g(
 #pragma unroll
     for (int m = 0; m < kF32Pass; ++m) {
       const int t = base + threadIdx.x + 256 * m;
-      w4a16_stage4(xv[m], t, K, nb, t < tot, xs, sx);
+      w4a16_stage4<B>(xv[m], t, K, nb, t < tot, xs, sx);
     }
   };
   load_pass(0);
@@ -531,7 +577,7 @@ static hipError_t launch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
   return hipGetLastError();
 }
 
-template <int B, int G, int RP, int T>
+template <int B, int G, int RP, int T, bool RAG = false>
 static hipError_t launch_q4_t(const uint8_t *qs, const uint16_t *d, int N, int K,
                               const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                               int64_t ldy, hipStream_t s) {
@@ -539,12 +585,37 @@ static hipError_t launch_q4_t(const uint8_t *qs, const uint16_t *d, int N, int K
   const int ngroups = (N + rows_wg - 1) / rows_wg;
   const size_t lds = xstage_bytes(B, K);
   if (X)
-    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, true>), dim3(ngroups), dim3(256), lds, s, qs,
-                       d, N, K, X, ldx, Xq, Y, ldy);
+    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, true, RAG>), dim3(ngroups), dim3(256), lds,
+                       s, qs, d, N, K, X, ldx, Xq, Y, ldy);
   else
-    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, false>), dim3(ngroups), dim3(256), lds, s,
-                       qs, d, N, K, X, ldx, Xq, Y, ldy);
+    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, false, RAG>), dim3(ngroups), dim3(256), lds,
+                       s, qs, d, N, K, X, ldx, Xq, Y, ldy);
   return hipGetLastError();
+}
+
+// B <= 2, a row of 64 < nb <= 512 blocks that is not a whole number of
+// 64-block steps: the whole-row kernel with T = ceil(nb / 64) steps, the last
+// one ragged, 4 rows per lane group (up to 32 weight blocks in flight per
+// lane, 244 VGPRs at most, no spills).  Measured at 4096 x 11008 and
+// 4096 x 14336, B = 1 / 2, against 2 rows per lane group (twice the
+// workgroups, each quantizing x): 10.1 / 14.5 and 11.4 / 17.2 us against
+// 10.9 / 16.4 and 12.8 / 20.1 us; the grid-stride kernel took 13.7 / 20.2 and
+// 15.8 / 24.7 us (one block per lane in flight)
+template <int B>
+static hipError_t launch_q4_rag(const uint8_t *qs, const uint16_t *d, int N, int K,
+                                const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
+                                int64_t ldy, hipStream_t s) {
+  static_assert(B <= 2, "ragged whole-row launches are built for one or two rows");
+  switch (((K >> 5) + 63) / 64) {
+    case 2: return launch_q4_t<B, 64, 4, 2, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 3: return launch_q4_t<B, 64, 4, 3, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 4: return launch_q4_t<B, 64, 4, 4, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 5: return launch_q4_t<B, 64, 4, 5, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 6: return launch_q4_t<B, 64, 4, 6, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 7: return launch_q4_t<B, 64, 4, 7, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    case 8: return launch_q4_t<B, 64, 4, 8, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Rows per lane group (2, 4, 6 or 8; the MMV_PATH_Q4_RP switch overrides):
@@ -609,6 +680,9 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
     if (nb == 64) return launch_q4_rp<B, 64, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 128) return launch_q4_rp<B, 64, 2>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 256) return launch_q4_rp<B, 64, 4>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    if constexpr (B <= 2)
+      if (nb > 64 && nb <= 512)
+        return launch_q4_rag<B>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   }
   if (nb <= 16) return launch_q4<B, 16, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   if (nb <= 32) return launch_q4<B, 32, RP>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
@@ -644,8 +718,6 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
 // for Q4_0 x Q8_1 from fp32 x, whose quantization then has half the threads.)
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // one tile of a wave: load i of lane l holds row (64 / kMfCB) i + l / kMfCB,
 // block l % kMfCB of the wave's blocks (kMfCB lanes read a row's codes, one
@@ -1046,21 +1118,46 @@ hipError_t launch_q4_mf(const uint8_t *qs, const uint16_t *d, int N, int K, cons
 
 namespace {
 
-template <int B, int G, int T>
+template <int B, int G, int T, bool RAG = false>
 hipError_t launch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                          int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
-  constexpr int RP = T >= 4 ? 2 : 4;
+  // rows per lane group: 2 for the 8192-long rows, 4 otherwise (ragged rows:
+  // 4096 x 11008 at B = 1 11.0 against 11.6 us with 2)
+  constexpr int RP = (T >= 4 && !RAG) ? 2 : 4;
   constexpr int rows_wg = 4 * RP * (64 / G);
   const size_t lds = (size_t)B * K * 4 + (size_t)B * (K / 32) * 4;
   if (lds > 65536) {  // above the default dynamic-LDS limit: raise it once per kernel
     static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_gemv_q4_0_f32<B, G, RP, T>),
+        reinterpret_cast<const void *>(&k_gemv_q4_0_f32<B, G, RP, T, RAG>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 32 * G * T * B * 4 + G * T * B * 4);
     if (raised != hipSuccess) return raised;
   }
-  hipLaunchKernelGGL((k_gemv_q4_0_f32<B, G, RP, T>), dim3((N + rows_wg - 1) / rows_wg),
+  hipLaunchKernelGGL((k_gemv_q4_0_f32<B, G, RP, T, RAG>), dim3((N + rows_wg - 1) / rows_wg),
                      dim3(256), lds, s, qs, d, N, K, X, ldx, Y, ldy);
   return hipGetLastError();
+}
+
+// B <= 2 and 64 < nb <= 512 blocks, not a whole number of 64-block steps:
+// the whole-row kernel with T = ceil(nb / 64) steps, the last one ragged
+// (B * K <= 16384: T <= 8 for one row, T <= 4 for two)
+template <int B>
+hipError_t launch_q4_f32_rag(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                             int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+  static_assert(B <= 2, "ragged whole-row launches are built for one or two rows");
+  switch (((K >> 5) + 63) / 64) {
+    case 2: return launch_q4_f32<B, 64, 2, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 3: return launch_q4_f32<B, 64, 3, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 4: return launch_q4_f32<B, 64, 4, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+  }
+  if constexpr (B == 1) {
+    switch (((K >> 5) + 63) / 64) {
+      case 5: return launch_q4_f32<B, 64, 5, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 6: return launch_q4_f32<B, 64, 6, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 7: return launch_q4_f32<B, 64, 7, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 8: return launch_q4_f32<B, 64, 8, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 // W4A16 on the matrix cores: a persistent grid, one 16-wave workgroup per CU
@@ -1126,6 +1223,9 @@ hipError_t dispatch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, c
       case 256: return launch_q4_f32<B, 64, 4>(qs, d, N, K, X, ldx, Y, ldy, s);
       default: break;
     }
+    if constexpr (B <= 2)
+      if (nb > 64 && nb <= 512)
+        return launch_q4_f32_rag<B>(qs, d, N, K, X, ldx, Y, ldy, s);
   }
   // any other K, or more rows: the general kernel with the same lanes per
   // row (hence the same per-row order and bits)

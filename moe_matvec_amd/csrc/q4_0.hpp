@@ -50,9 +50,15 @@ __device__ __forceinline__ i32x4 xstage_lo(XStage st, int r, int K, int j) {
 __device__ __forceinline__ i32x4 xstage_hi(XStage st, int r, int K, int j) {
   return *reinterpret_cast<const i32x4 *>(st.codes + (size_t)r * K + (K >> 1) + 16 * j);
 }
-// LDS offset of 16-byte chunk c of a row-major [rows][K] code buffer
-__device__ __forceinline__ size_t xstage_chunk_off(int c, int K) {
-  const int nb = K >> 5, r = c / (2 * nb), rem = c - r * 2 * nb;
+// row of task t (0 <= t < nrows * per_row) of a row-major [nrows][per_row]
+// task array: no division for one or two rows (nrows is a constant where the
+// GEMV kernels inline this)
+__device__ __forceinline__ int stage_row(int t, int per_row, int nrows) {
+  return nrows == 1 ? 0 : nrows == 2 ? (t >= per_row ? 1 : 0) : t / per_row;
+}
+// LDS offset of 16-byte chunk c of a row-major [nrows][K] code buffer
+__device__ __forceinline__ size_t xstage_chunk_off(int c, int K, int nrows) {
+  const int nb = K >> 5, r = stage_row(c, 2 * nb, nrows), rem = c - r * 2 * nb;
   return (size_t)r * K + (size_t)(rem & 1) * (K >> 1) + 16 * (rem >> 1);
 }
 __host__ __device__ inline size_t xstage_bytes(int nrows, int K) {
@@ -88,7 +94,7 @@ __device__ __forceinline__ void xpre_load(const float *__restrict__ X, int64_t l
 #pragma unroll
   for (int i = 0; i < MAXT; ++i) {
     const int t = min(base + (int)threadIdx.x + i * nth, total - 1);
-    const int r = t / (nb * 8);
+    const int r = stage_row(t, nb * 8, nrows);
     const int rem = t - r * nb * 8;
     const int row = rowmap ? rowmap[r] : r;
     p.v[i] = load_f4(X + (int64_t)row * ldx + 4 * rem);
@@ -109,7 +115,7 @@ __device__ __forceinline__ void xpre_quantize(const XPre<MAXT> &p, int nrows, in
     const int t = base + (int)threadIdx.x + i * nth;
     if (t < total) {  // uniform over each 8-lane group: total % 8 == 0
       const Q8Block q = q8_1_quantize8(p.v[i]);
-      const int r = t / (nb * 8);
+      const int r = stage_row(t, nb * 8, nrows);
       const int rem = t - r * nb * 8;
       const int j = rem >> 3, s = rem & 7;
       *reinterpret_cast<uint32_t *>(st.codes + xstage_code_off(r, K, j, 4 * s)) = q.codes;
@@ -177,7 +183,7 @@ __device__ __forceinline__ void xq_pre_store(const XqPre<MAXC> &p, int nrows, in
     uint32_t dsv = p.ds[i];
     asm volatile("" : "+v"(dsv));
     if (t < total) {  // uniform over each lane pair: total is even
-      *reinterpret_cast<i32x4 *>(st.codes + xstage_chunk_off(t, K)) = p.c[i];
+      *reinterpret_cast<i32x4 *>(st.codes + xstage_chunk_off(t, K, nrows)) = p.c[i];
       if ((t & 1) == 0) {
         st.d[t >> 1] = f16_bits_to_f32((uint16_t)(dsv & 0xFFFFu));
         st.qsum[t >> 1] = sum;

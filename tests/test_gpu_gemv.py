@@ -299,6 +299,29 @@ def test_q4_0_both_kernels_every_b(mm, orc, dev, path, N, K):
             assert rel_l2_rows(npc(y), ref) <= Q4_ARITH_TOL, (B, sw)
 
 
+@pytest.mark.parametrize("N,K", [(1000, 11008), (257, 9728), (300, 14336), (33, 16352),
+                                 (129, 2560), (65, 3840), (70, 6144)])
+@pytest.mark.parametrize("B", [1, 2])
+def test_q4_0_ragged_rows_equal_grid_stride(mm, orc, dev, path, N, K, B):
+    # rows of 64 < K/32 <= 512 blocks that are not whole 64-block steps (the
+    # down projections of the 7B-9B models among them) take the whole-row
+    # kernel with a ragged last step at B <= 2: the same rows, bit for bit, as
+    # the grid-stride kernel, from fp32 x and from a Q8_1 buffer, and the
+    # oracle's on the same codes; the rows of 16352 end one block short of
+    # eight 64-block steps
+    W, qs, d = _q4(mm, N, K, dev, "ragged")
+    X = synth.activations(B, K, 0, "q4ragged", N, K, device=dev)
+    xq = mm.quantize_q8_1(X)
+    y = mm.gemv_q4_0(W, x=X)
+    y_q = mm.gemv_q4_0(W, xq=xq, B=B)
+    path(Q4_GENERIC=1)
+    y_g = mm.gemv_q4_0(W, x=X)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_q) and torch.equal(y, y_g)
+    q_ref, ds_ref = orc.quantize_q8_1(npc(X))
+    assert rel_l2_rows(npc(y), orc.gemv_q4_0(qs, d, q_ref, ds_ref)) <= Q4_ARITH_TOL
+
+
 @pytest.mark.parametrize("B", [2, 3, 5, 7])
 def test_q4_0_strided_x_and_y(mm, orc, dev, B):
     # x rows with ldx > K at an offset, y rows with ldy > N (the padding must

@@ -191,6 +191,26 @@ def test_w4a16_both_kernels_every_b(mm, orc, dev, path, N, K):
             assert rel_l2_rows(npc(y), ref) <= W4A16_ARITH_TOL, (B, sw)
 
 
+@pytest.mark.parametrize("N,K,B", [(1000, 11008, 1), (257, 9728, 1), (300, 14336, 1),
+                                   (33, 16352, 1), (70, 6144, 2), (129, 2560, 1),
+                                   (65, 3840, 1)])
+def test_w4a16_ragged_rows(mm, orc, dev, N, K, B):
+    # B * K <= 16384 and 64 < K/32 <= 512 blocks, not whole 64-block steps:
+    # the whole-row kernel with a ragged last step, against the oracle, and
+    # above K = 4096 against the rows of a call with enough x rows for the
+    # grid-stride kernel (same lanes per row, so the same bits)
+    W, qs, d = _q4(mm, N, K, dev, "ragged")
+    Bg = 16384 // K + 1                      # rows that no longer fit the whole-row kernel
+    X = synth.activations(max(B, Bg), K, 0, "w4a16ragged", N, K, device=dev)
+    y = mm.gemv_q4_0_f32(W, X[:B].clone())
+    torch.cuda.synchronize()
+    assert rel_l2_rows(npc(y), orc.gemv_q4_0_f32(qs, d, npc(X[:B]))) <= W4A16_ARITH_TOL
+    if K > 4096 and Bg * K <= mm.Q4F32_MAX_XK:
+        yg = mm.gemv_q4_0_f32(W, X[:Bg].clone())
+        torch.cuda.synchronize()
+        assert torch.equal(y, yg[:B])
+
+
 def test_w4a16_strided_x_and_y(mm, orc, dev):
     N, K, B = 1200, 1024, 5
     W, qs, d = _q4(mm, N, K, dev, "stride")
