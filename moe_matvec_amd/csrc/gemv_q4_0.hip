@@ -320,8 +320,8 @@ __device__ __forceinline__ void w4a16_stage4(f32x4 v, int t, int K, int nb, bool
 // becomes two bf16 pairs once and serves every x row; x of all B rows for
 // those positions is read from LDS once and serves the RP rows.  For each
 // (row, x row) the sum starts at the staged -136 sum x and runs low nibbles
-// then high nibbles, bytes ascending, hi before lo per byte pair; then
-// acc += d_w * S.  (The x words are copied out of the vector before the
+// then high nibbles, dwords ascending, per dword the hi parts of its four
+// codes and then the lo parts; then acc += d_w * S.  (The x words are copied out of the vector before the
 // bit cast: clang's __builtin_bit_cast of a vector element lvalue such as
 // v.y reads element 0.)
 template <int B, int RP>

@@ -185,9 +185,9 @@ def test_w4a16_both_kernels_every_b(mm, orc, dev, path, N, K):
             path(Q4F32_MF=sw)
             y = mm.gemv_q4_0_f32(W, X)
             torch.cuda.synchronize()
-            # and the bound of the arithmetic: x kept to 2^-17 (bf16 hi + lo) or
-            # exact (fp32), fp32 sums (rel-L2 ~5e-6 measured); a lost lo plane
-            # alone would give ~2^-9
+            # and the bound of the arithmetic: x kept to 2^-17 (bf16 hi + lo) in
+            # both kernels, exact products, fp32 sums (rel-L2 ~5e-6 measured); a
+            # lost lo part alone would give ~2^-9
             assert rel_l2_rows(npc(y), ref) <= W4A16_ARITH_TOL, (B, sw)
 
 
