@@ -593,27 +593,33 @@ static hipError_t launch_q4_t(const uint8_t *qs, const uint16_t *d, int N, int K
   return hipGetLastError();
 }
 
-// B <= 2, a row of 64 < nb <= 512 blocks that is not a whole number of
+// B <= 4, a row of 64 < nb <= 512 blocks that is not a whole number of
 // 64-block steps: the whole-row kernel with T = ceil(nb / 64) steps, the last
 // one ragged, 4 rows per lane group (up to 32 weight blocks in flight per
-// lane, 244 VGPRs at most, no spills).  Measured at 4096 x 11008 and
-// 4096 x 14336, B = 1 / 2, against 2 rows per lane group (twice the
-// workgroups, each quantizing x): 10.1 / 14.5 and 11.4 / 17.2 us against
-// 10.9 / 16.4 and 12.8 / 20.1 us; the grid-stride kernel took 13.7 / 20.2 and
-// 15.8 / 24.7 us (one block per lane in flight)
+// lane, 244 VGPRs at most, no spills; B * K <= MMV_Q4_MAX_XK keeps the staged
+// x under 64 KiB).  Measured at 4096 x 11008 and 4096 x 14336, B = 1 / 2,
+// against 2 rows per lane group (twice the workgroups, each quantizing x):
+// 10.1 / 14.5 and 11.4 / 17.2 us against 10.9 / 16.4 and 12.8 / 20.1 us; the
+// grid-stride kernel took 13.7 / 20.2 and 15.8 / 24.7 us (one block per lane
+// in flight).  At B = 3 / 4 from a Q8_1 buffer, 4096 x 11008: 12.7 / 13.8
+// against 19.2 / 20.8 us (from fp32 x: 20.7 / 24.9 against 28.7 / 33.8)
 template <int B>
 static hipError_t launch_q4_rag(const uint8_t *qs, const uint16_t *d, int N, int K,
                                 const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                                 int64_t ldy, hipStream_t s) {
-  static_assert(B <= 2, "ragged whole-row launches are built for one or two rows");
+  static_assert(B <= 4, "ragged whole-row launches are built for up to four rows");
   switch (((K >> 5) + 63) / 64) {
     case 2: return launch_q4_t<B, 64, 4, 2, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     case 3: return launch_q4_t<B, 64, 4, 3, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     case 4: return launch_q4_t<B, 64, 4, 4, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     case 5: return launch_q4_t<B, 64, 4, 5, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     case 6: return launch_q4_t<B, 64, 4, 6, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    case 7: return launch_q4_t<B, 64, 4, 7, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    case 8: return launch_q4_t<B, 64, 4, 8, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+  }
+  if constexpr (B <= 3) {  // B * K <= MMV_Q4_MAX_XK
+    switch (((K >> 5) + 63) / 64) {
+      case 7: return launch_q4_t<B, 64, 4, 7, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 8: return launch_q4_t<B, 64, 4, 8, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    }
   }
   return hipErrorInvalidValue;
 }
@@ -680,7 +686,7 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
     if (nb == 64) return launch_q4_rp<B, 64, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 128) return launch_q4_rp<B, 64, 2>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 256) return launch_q4_rp<B, 64, 4>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    if constexpr (B <= 2)
+    if constexpr (B <= 4)
       if (nb > 64 && nb <= 512)
         return launch_q4_rag<B>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   }
@@ -1137,22 +1143,23 @@ hipError_t launch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, con
   return hipGetLastError();
 }
 
-// B <= 2 and 64 < nb <= 512 blocks, not a whole number of 64-block steps:
-// the whole-row kernel with T = ceil(nb / 64) steps, the last one ragged
-// (B * K <= 16384: T <= 8 for one row, T <= 4 for two)
+// B <= 3 and 64 < nb <= 512 blocks: the whole-row kernel with T =
+// ceil(nb / 64) steps, the last one ragged where nb is not a multiple of 64
+// (B * K <= MMV_Q4F32_MAX_XK: T <= 8 for one or two rows, T <= 6 for three;
+// above 64 KiB of staged x the launcher raises the workgroup's LDS limit)
 template <int B>
 hipError_t launch_q4_f32_rag(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                              int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
-  static_assert(B <= 2, "ragged whole-row launches are built for one or two rows");
+  static_assert(B <= 3, "ragged whole-row launches are built for up to three rows");
   switch (((K >> 5) + 63) / 64) {
     case 2: return launch_q4_f32<B, 64, 2, true>(qs, d, N, K, X, ldx, Y, ldy, s);
     case 3: return launch_q4_f32<B, 64, 3, true>(qs, d, N, K, X, ldx, Y, ldy, s);
     case 4: return launch_q4_f32<B, 64, 4, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 5: return launch_q4_f32<B, 64, 5, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+    case 6: return launch_q4_f32<B, 64, 6, true>(qs, d, N, K, X, ldx, Y, ldy, s);
   }
-  if constexpr (B == 1) {
+  if constexpr (B <= 2) {  // B * K <= MMV_Q4F32_MAX_XK
     switch (((K >> 5) + 63) / 64) {
-      case 5: return launch_q4_f32<B, 64, 5, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-      case 6: return launch_q4_f32<B, 64, 6, true>(qs, d, N, K, X, ldx, Y, ldy, s);
       case 7: return launch_q4_f32<B, 64, 7, true>(qs, d, N, K, X, ldx, Y, ldy, s);
       case 8: return launch_q4_f32<B, 64, 8, true>(qs, d, N, K, X, ldx, Y, ldy, s);
     }
@@ -1223,10 +1230,20 @@ hipError_t dispatch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, c
       case 256: return launch_q4_f32<B, 64, 4>(qs, d, N, K, X, ldx, Y, ldy, s);
       default: break;
     }
-    if constexpr (B <= 2)
-      if (nb > 64 && nb <= 512)
-        return launch_q4_f32_rag<B>(qs, d, N, K, X, ldx, Y, ldy, s);
   }
+  // ragged rows (and whole ones past 16384 = B * K): the whole-row kernel
+  // with a ragged last step, above B * K = 16384 only when its workgroups of
+  // 16 rows fit the CUs in one round (x of all B rows, up to 152 KiB, is
+  // staged by every workgroup; at 11008 x 8192 and 14336 x 6144, B = 3, two
+  // or more rounds took 39.1 and 33.2 us against 31.2 and 25.5 us on the
+  // general kernel, which stages x once per CU)
+  if constexpr (B <= 3)
+    if (nb > 64 && nb <= 512 && (int64_t)B * K <= MMV_Q4F32_MAX_XK) {
+      const int64_t lds = (int64_t)B * K * 4 + (int64_t)B * nb * 4;
+      const int per_cu = (int)(163840 / lds);
+      if ((int64_t)B * K <= 16384 || (N + 15) / 16 <= per_cu * cu_count())
+        return launch_q4_f32_rag<B>(qs, d, N, K, X, ldx, Y, ldy, s);
+    }
   // any other K, or more rows: the general kernel with the same lanes per
   // row (hence the same per-row order and bits)
   constexpr int TC = B > 4 ? 2 : 4;

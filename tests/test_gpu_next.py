@@ -193,19 +193,27 @@ def test_w4a16_both_kernels_every_b(mm, orc, dev, path, N, K):
 
 @pytest.mark.parametrize("N,K,B", [(1000, 11008, 1), (257, 9728, 1), (300, 14336, 1),
                                    (33, 16352, 1), (70, 6144, 2), (129, 2560, 1),
-                                   (65, 3840, 1)])
+                                   (65, 3840, 1), (1000, 11008, 2), (129, 9728, 3),
+                                   (300, 11008, 3), (70, 14336, 2), (300, 8192, 3),
+                                   (4500, 8192, 3)])
 def test_w4a16_ragged_rows(mm, orc, dev, N, K, B):
-    # B * K <= 16384 and 64 < K/32 <= 512 blocks, not whole 64-block steps:
-    # the whole-row kernel with a ragged last step, against the oracle, and
-    # above K = 4096 against the rows of a call with enough x rows for the
-    # grid-stride kernel (same lanes per row, so the same bits)
+    # 64 < K/32 <= 512 blocks: the whole-row kernel with a ragged last step
+    # (B <= 3; past B * K = 16384 only while its workgroups fit the CUs in one
+    # round, so 4500 rows at B = 3 take the general kernel on a GPU of up to
+    # 281 CUs), against the oracle; every row equals the 1-row call on it
+    # (same lanes per row, so the same bits in both kernels), and at B = 1
+    # above K = 4096 the row of a call with enough x rows for the general
+    # kernel
     W, qs, d = _q4(mm, N, K, dev, "ragged")
-    Bg = 16384 // K + 1                      # rows that no longer fit the whole-row kernel
+    Bg = 16384 // K + 1                      # rows that no longer fit the whole-row kernel at B = 1
     X = synth.activations(max(B, Bg), K, 0, "w4a16ragged", N, K, device=dev)
     y = mm.gemv_q4_0_f32(W, X[:B].clone())
     torch.cuda.synchronize()
     assert rel_l2_rows(npc(y), orc.gemv_q4_0_f32(qs, d, npc(X[:B]))) <= W4A16_ARITH_TOL
-    if K > 4096 and Bg * K <= mm.Q4F32_MAX_XK:
+    if B > 1 and K > 4096:
+        for b in range(B):
+            assert torch.equal(y[b], mm.gemv_q4_0_f32(W, X[b].clone())), b
+    if B == 1 and K > 4096 and Bg * K <= mm.Q4F32_MAX_XK:
         yg = mm.gemv_q4_0_f32(W, X[:Bg].clone())
         torch.cuda.synchronize()
         assert torch.equal(y, yg[:B])
