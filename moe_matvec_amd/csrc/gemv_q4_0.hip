@@ -188,7 +188,11 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
 
   // first pass of the activation loads, ahead of the weights: B * G * T / 32
   // float4 tasks (or B * G * T / 128 16-byte code tasks) per thread in all
-  constexpr int MAXT = cmin(kStageMaxT, cmax(1, B * G * T / 32));
+  // (one row of a ragged long row: all of x in the first pass, 2T tasks,
+  // where the registers allow it, so that no L2 round trip of x follows the
+  // weight loads)
+  constexpr int MAXT = (RAG && B == 1 && T <= 7) ? 2 * T
+                                                 : cmin(kStageMaxT, cmax(1, B * G * T / 32));
   constexpr int MAXC = cmin(kStageMaxC, cmax(1, B * G * T / 128));
   XPre<FROM_X ? MAXT : 1> xp;
   XqPre<FROM_X ? 1 : MAXC> qp;
@@ -393,29 +397,33 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
   const int K = RAG ? Kr : 32 * G * T, nb = K >> 5;  // RAG: the launcher checks K
   constexpr int RPP = 64 / G, ROWS_WAVE = RP * RPP, ROWS_WG = 4 * ROWS_WAVE;
   const int TOT = B * K / 4;                              // float4 staging tasks
-  const int P0 = min(kF32Pass, (TOT + 255) / 256);        // first pass per thread
   f32x4 *xs = reinterpret_cast<f32x4 *>(smem);            // [B][8][nb]
   float *sx = reinterpret_cast<float *>(smem + (size_t)B * K * 4);  // [B][nb]
   const int lane = threadIdx.x & 63, sub = lane % G, grp = lane / G, wv = threadIdx.x >> 6;
 
-  auto load_pass = [&](int base, f32x4 (&v)[kF32Pass]) {
+  auto load_pass = [&](int base, auto &v) {
+    constexpr int NP = sizeof(v) / sizeof(v[0]);
 #pragma unroll
-    for (int m = 0; m < kF32Pass; ++m) {
+    for (int m = 0; m < NP; ++m) {
       const int t = min(base + (int)threadIdx.x + 256 * m, TOT - 1);
       const int b = task_row<B>(t, K / 4), r = t - b * (K / 4);
       v[m] = load_f4(X + (int64_t)b * ldx + 4 * r);
     }
   };
-  auto store_pass = [&](int base, const f32x4 (&v)[kF32Pass], int np) {
+  auto store_pass = [&](int base, const auto &v, int np) {
+    constexpr int NP = sizeof(v) / sizeof(v[0]);
 #pragma unroll
-    for (int m = 0; m < kF32Pass; ++m) {
-      if (m >= np) break;
+    for (int m = 0; m < NP; ++m) {
       const int t = base + threadIdx.x + 256 * m;
-      w4a16_stage4<B>(v[m], t, K, nb, t < TOT, xs, sx);
+      if (m < np) w4a16_stage4<B>(v[m], t, K, nb, t < TOT, xs, sx);
     }
   };
 
-  f32x4 xv[kF32Pass];
+  // the first pass: kF32Pass tasks per thread, or for one ragged long row
+  // all of x (2T tasks) where the registers allow it
+  constexpr int NP0 = (RAG && B == 1 && T <= 7 && 2 * T > kF32Pass) ? 2 * T : kF32Pass;
+  const int P0 = min(NP0, (TOT + 255) / 256);  // first-pass tasks per thread
+  f32x4 xv[NP0];
   load_pass(0, xv);
   __builtin_amdgcn_sched_barrier(0);
   const int rbase = blockIdx.x * ROWS_WG + wv * ROWS_WAVE + grp;
@@ -433,9 +441,10 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
   }
   __builtin_amdgcn_sched_barrier(0);
   store_pass(0, xv, P0);
-  for (int base = 256 * kF32Pass; base < TOT; base += 256 * kF32Pass) {
-    load_pass(base, xv);
-    store_pass(base, xv, kF32Pass);
+  for (int base = 256 * NP0; base < TOT; base += 256 * kF32Pass) {
+    f32x4 xr[kF32Pass];
+    load_pass(base, xr);
+    store_pass(base, xr, kF32Pass);
   }
   __syncthreads();
 
