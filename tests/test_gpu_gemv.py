@@ -300,7 +300,7 @@ def test_q4_0_both_kernels_every_b(mm, orc, dev, path, N, K):
 
 
 @pytest.mark.parametrize("N,K", [(1000, 11008), (257, 9728), (300, 14336), (33, 16352),
-                                 (129, 2560), (65, 3840), (70, 6144)])
+                                 (129, 2560), (65, 3840), (70, 6144), (200, 2080)])
 @pytest.mark.parametrize("B", [1, 2, 3, 4])
 def test_q4_0_ragged_rows_equal_grid_stride(mm, orc, dev, path, N, K, B):
     # rows of 64 < K/32 <= 512 blocks that are not whole 64-block steps (the
@@ -308,7 +308,8 @@ def test_q4_0_ragged_rows_equal_grid_stride(mm, orc, dev, path, N, K, B):
     # kernel with a ragged last step at B <= 4: the same rows, bit for bit, as
     # the grid-stride kernel, from fp32 x and from a Q8_1 buffer, and the
     # oracle's on the same codes; the rows of 16352 end one block short of
-    # eight 64-block steps (the int8 matrix cores, which take K <= 4096 from
+    # eight 64-block steps, those of 2080 one block into the second (the int8
+    # matrix cores, which take K <= 4096 from
     # B = 3, are held off: their sums run in another order)
     if B * K > mm.Q4_MAX_XK:
         pytest.skip("B * K above the staging limit")

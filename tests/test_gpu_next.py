@@ -195,7 +195,7 @@ def test_w4a16_both_kernels_every_b(mm, orc, dev, path, N, K):
                                    (33, 16352, 1), (70, 6144, 2), (129, 2560, 1),
                                    (65, 3840, 1), (1000, 11008, 2), (129, 9728, 3),
                                    (300, 11008, 3), (70, 14336, 2), (300, 8192, 3),
-                                   (4500, 8192, 3)])
+                                   (4500, 8192, 3), (200, 2080, 1)])
 def test_w4a16_ragged_rows(mm, orc, dev, N, K, B):
     # 64 < K/32 <= 512 blocks: the whole-row kernel with a ragged last step
     # (B <= 3; past B * K = 16384 only while its workgroups fit the CUs in one
