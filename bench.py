@@ -507,7 +507,31 @@ def bw_probe(mm, dev, steps, warmup, gb=8.0):
 
 CAL_BYTES = 1 << 30
 PROFILE_WORKLOADS = ("dense_gate_up", "q4_b1", "q4_b8", "w4a16_b1", "w4a16_b8", "moe256_b1",
-                     "moe512_b8")
+                     "moe512_b8", "q4_ragged_b1")
+
+
+def q4_ragged_graph(mm, dev, copies):
+    """4096 x 11008 Q4_0 at B = 1 (rows of 344 blocks: the whole-row kernels'
+    ragged last step), the W4A8 product from fp32 x and the W4A16 product of
+    each copy, in one graph."""
+    import torch
+    import synth
+    N, K = 4096, 11008
+    qs1, d1 = synth.q4_0_weights(N, K, 0, "q4ragged", N, device=dev)
+    qs = torch.empty((copies,) + tuple(qs1.shape), dtype=torch.uint8, device=dev)
+    d = torch.empty((copies,) + tuple(d1.shape), dtype=torch.float16, device=dev)
+    qs[:] = qs1
+    d[:] = d1
+    Ws = [mm.Q4_0(qs[c], d[c]) for c in range(copies)]
+    X = synth.activations(copies, K, 0, "q4ragged-x", device=dev).view(copies, 1, K)
+    Y8 = [torch.empty((1, N), device=dev) for _ in range(copies)]
+    Y16 = [torch.empty((1, N), device=dev) for _ in range(copies)]
+
+    def step():
+        for c in range(copies):
+            mm.gemv_q4_0(Ws[c], x=X[c], out=Y8[c])
+            mm.gemv_q4_0_f32(Ws[c], X[c], out=Y16[c])
+    return capture(step), (qs, d, Ws, X, Y8, Y16)
 
 
 def profile_workload(mm, dev, name):
@@ -526,6 +550,10 @@ def profile_workload(mm, dev, name):
     elif name in ("w4a16_b1", "w4a16_b8"):
         g, keep = w4a16_section(mm, dev, 32, 1 if name == "w4a16_b1" else 8, 0, 0,
                                 graph_only=True)
+        for _ in range(3):
+            g.replay()
+    elif name == "q4_ragged_b1":
+        g, keep = q4_ragged_graph(mm, dev, 32)
         for _ in range(3):
             g.replay()
     elif name in ("moe256_b1", "moe512_b8"):
