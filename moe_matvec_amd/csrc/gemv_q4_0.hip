@@ -164,22 +164,23 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0(
 // Whole-row variant: K = 32 * G * T, or with RAG any K <= 32 * G * T, so
 // each lane owns at most T blocks of each of its RP rows (blocks sub + G t;
 // past a ragged row's last block the load repeats that block, in bounds,
-// and the step is skipped), and a workgroup
-// owns one group of 4 * RP * (64 / G) consecutive rows.  The activation
+// and the step is skipped), and a workgroup of NW waves owns one group of
+// NW * RP * (64 / G) consecutive rows.  The activation
 // loads are issued first, then all RP * T weight loads of the group; the
 // activation is quantized into LDS while the weights are in flight (loads
 // complete in issue order).  Per-row arithmetic order is the same as in
 // k_gemv_q4_0: block j's integer sum scaled by d_w * d_x and accumulated
 // over j = sub, sub + G, ..., then a G-lane sum.
-template <int B, int G, int RP, int T, bool FROM_X, bool RAG>
-__global__ __launch_bounds__(256) void k_gemv_q4_0_t(
+template <int B, int G, int RP, int T, bool FROM_X, bool RAG, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_t(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int Kr,
     const float *__restrict__ X, int64_t ldx, const uint8_t *__restrict__ Xq,
     float *__restrict__ Y, int64_t ldy) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int RPP = 64 / G;
   constexpr int ROWS_WAVE = RP * RPP;
-  constexpr int ROWS_WG = 4 * ROWS_WAVE;
+  constexpr int NT = 64 * NW;  // threads per workgroup
+  constexpr int ROWS_WG = NW * ROWS_WAVE;
   // RAG: K <= 32 G T at run time (the launcher checks it); else exactly 32 G T
   const int K = RAG ? Kr : 32 * G * T, nb = K >> 5;
   const int lane = threadIdx.x & 63;
@@ -191,13 +192,13 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
   // (one row of a ragged long row: all of x in the first pass, 2T tasks,
   // where the registers allow it, so that no L2 round trip of x follows the
   // weight loads)
-  constexpr int MAXT = (RAG && B == 1 && T <= 7) ? 2 * T
+  constexpr int MAXT = (RAG && B == 1 && T <= 7) ? cmax(1, 8 * G * T / NT)
                                                  : cmin(kStageMaxT, cmax(1, B * G * T / 32));
   constexpr int MAXC = cmin(kStageMaxC, cmax(1, B * G * T / 128));
   XPre<FROM_X ? MAXT : 1> xp;
   XqPre<FROM_X ? 1 : MAXC> qp;
-  if constexpr (FROM_X) xpre_load(X, ldx, nullptr, B, K, xp, 0, 256);
-  else xq_pre_load(Xq, B, B, K, qp, 0, 256);
+  if constexpr (FROM_X) xpre_load(X, ldx, nullptr, B, K, xp, 0, NT);
+  else xq_pre_load(Xq, B, B, K, qp, 0, NT);
   __builtin_amdgcn_sched_barrier(0);  // keep the weight loads behind these
 
   const int rbase = blockIdx.x * ROWS_WG + wv * ROWS_WAVE + grp;
@@ -217,11 +218,11 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_t(
 
   const XStage st = xstage_at(smem, B, K);
   if constexpr (FROM_X) {
-    xpre_quantize(xp, B, K, st, 0, 256);
-    stage_quantize(X, ldx, nullptr, B, K, st, MAXT * 256, 256);
+    xpre_quantize(xp, B, K, st, 0, NT);
+    stage_quantize(X, ldx, nullptr, B, K, st, MAXT * NT, NT);
   } else {
-    xq_pre_store(qp, B, K, st, 0, 256);
-    stage_copy_q8(Xq, B, B, K, st, MAXC * 256, 256);
+    xq_pre_store(qp, B, K, st, 0, NT);
+    stage_copy_q8(Xq, B, B, K, st, MAXC * NT, NT);
   }
   __syncthreads();
 
@@ -389,13 +390,14 @@ __device__ __forceinline__ void w4a16_block(const u32x4 (&w)[RP], const float (&
 // ragged row's last step loads its last block again and skips it), and
 // B * K <= 16384 (x in at most 66 KiB of LDS): a workgroup owns one row
 // group, every weight load of it issued up front.
-template <int B, int G, int RP, int T, bool RAG>
-__global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
+template <int B, int G, int RP, int T, bool RAG, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_f32(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int Kr,
     const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = RAG ? Kr : 32 * G * T, nb = K >> 5;  // RAG: the launcher checks K
-  constexpr int RPP = 64 / G, ROWS_WAVE = RP * RPP, ROWS_WG = 4 * ROWS_WAVE;
+  constexpr int NT = 64 * NW;  // threads per workgroup
+  constexpr int RPP = 64 / G, ROWS_WAVE = RP * RPP, ROWS_WG = NW * ROWS_WAVE;
   const int TOT = B * K / 4;                              // float4 staging tasks
   f32x4 *xs = reinterpret_cast<f32x4 *>(smem);            // [B][8][nb]
   float *sx = reinterpret_cast<float *>(smem + (size_t)B * K * 4);  // [B][nb]
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
     constexpr int NP = sizeof(v) / sizeof(v[0]);
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-      const int t = min(base + (int)threadIdx.x + 256 * m, TOT - 1);
+      const int t = min(base + (int)threadIdx.x + NT * m, TOT - 1);
       const int b = task_row<B>(t, K / 4), r = t - b * (K / 4);
       v[m] = load_f4(X + (int64_t)b * ldx + 4 * r);
     }
@@ -414,15 +416,16 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
     constexpr int NP = sizeof(v) / sizeof(v[0]);
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-      const int t = base + threadIdx.x + 256 * m;
+      const int t = base + threadIdx.x + NT * m;
       if (m < np) w4a16_stage4<B>(v[m], t, K, nb, t < TOT, xs, sx);
     }
   };
 
   // the first pass: kF32Pass tasks per thread, or for one ragged long row
-  // all of x (2T tasks) where the registers allow it
-  constexpr int NP0 = (RAG && B == 1 && T <= 7 && 2 * T > kF32Pass) ? 2 * T : kF32Pass;
-  const int P0 = min(NP0, (TOT + 255) / 256);  // first-pass tasks per thread
+  // all of x (8 G T / NT tasks) where the registers allow it
+  constexpr int NALL = 8 * G * T / NT;
+  constexpr int NP0 = (RAG && B == 1 && T <= 7 && NALL > kF32Pass) ? NALL : kF32Pass;
+  const int P0 = min(NP0, (TOT + NT - 1) / NT);  // first-pass tasks per thread
   f32x4 xv[NP0];
   load_pass(0, xv);
   __builtin_amdgcn_sched_barrier(0);
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32(
   }
   __builtin_amdgcn_sched_barrier(0);
   store_pass(0, xv, P0);
-  for (int base = 256 * NP0; base < TOT; base += 256 * kF32Pass) {
+  for (int base = NT * NP0; base < TOT; base += NT * kF32Pass) {
     f32x4 xr[kF32Pass];
     load_pass(base, xr);
     store_pass(base, xr, kF32Pass);
@@ -586,19 +589,19 @@ static hipError_t launch_q4(const uint8_t *qs, const uint16_t *d, int N, int K,
   return hipGetLastError();
 }
 
-template <int B, int G, int RP, int T, bool RAG = false>
+template <int B, int G, int RP, int T, bool RAG = false, int NW = 4>
 static hipError_t launch_q4_t(const uint8_t *qs, const uint16_t *d, int N, int K,
                               const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                               int64_t ldy, hipStream_t s) {
-  constexpr int rows_wg = 4 * RP * (64 / G);
+  constexpr int rows_wg = NW * RP * (64 / G);
   const int ngroups = (N + rows_wg - 1) / rows_wg;
   const size_t lds = xstage_bytes(B, K);
   if (X)
-    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, true, RAG>), dim3(ngroups), dim3(256), lds,
-                       s, qs, d, N, K, X, ldx, Xq, Y, ldy);
+    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, true, RAG, NW>), dim3(ngroups),
+                       dim3(64 * NW), lds, s, qs, d, N, K, X, ldx, Xq, Y, ldy);
   else
-    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, false, RAG>), dim3(ngroups), dim3(256), lds,
-                       s, qs, d, N, K, X, ldx, Xq, Y, ldy);
+    hipLaunchKernelGGL((k_gemv_q4_0_t<B, G, RP, T, false, RAG, NW>), dim3(ngroups),
+                       dim3(64 * NW), lds, s, qs, d, N, K, X, ldx, Xq, Y, ldy);
   return hipGetLastError();
 }
 
@@ -617,17 +620,33 @@ static hipError_t launch_q4_rag(const uint8_t *qs, const uint16_t *d, int N, int
                                 const float *X, int64_t ldx, const uint8_t *Xq, float *Y,
                                 int64_t ldy, hipStream_t s) {
   static_assert(B <= 4, "ragged whole-row launches are built for up to four rows");
-  switch (((K >> 5) + 63) / 64) {
-    case 2: return launch_q4_t<B, 64, 4, 2, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    case 3: return launch_q4_t<B, 64, 4, 3, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    case 4: return launch_q4_t<B, 64, 4, 4, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    case 5: return launch_q4_t<B, 64, 4, 5, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    case 6: return launch_q4_t<B, 64, 4, 6, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-  }
-  if constexpr (B <= 3) {  // B * K <= MMV_Q4_MAX_XK
+  if constexpr (B == 1) {
+    // one row: workgroups of 8 waves with 2 rows per lane group (the same 16
+    // rows and grid), so each wave quantizes half as much of x and a SIMD
+    // holds two waves: 4096 x 11008 9.8 -> 8.3 us, 4096 x 14336
+    // 11.2 -> 9.5 us, 2560 x 9728 7.7 -> 6.6 us
     switch (((K >> 5) + 63) / 64) {
-      case 7: return launch_q4_t<B, 64, 4, 7, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-      case 8: return launch_q4_t<B, 64, 4, 8, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 2: return launch_q4_t<B, 64, 2, 2, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 3: return launch_q4_t<B, 64, 2, 3, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 4: return launch_q4_t<B, 64, 2, 4, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 5: return launch_q4_t<B, 64, 2, 5, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 6: return launch_q4_t<B, 64, 2, 6, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 7: return launch_q4_t<B, 64, 2, 7, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 8: return launch_q4_t<B, 64, 2, 8, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    }
+  } else {
+    switch (((K >> 5) + 63) / 64) {
+      case 2: return launch_q4_t<B, 64, 4, 2, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 3: return launch_q4_t<B, 64, 4, 3, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 4: return launch_q4_t<B, 64, 4, 4, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 5: return launch_q4_t<B, 64, 4, 5, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 6: return launch_q4_t<B, 64, 4, 6, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    }
+    if constexpr (B <= 3) {  // B * K <= MMV_Q4_MAX_XK
+      switch (((K >> 5) + 63) / 64) {
+        case 7: return launch_q4_t<B, 64, 4, 7, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+        case 8: return launch_q4_t<B, 64, 4, 8, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      }
     }
   }
   return hipErrorInvalidValue;
@@ -692,6 +711,15 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
   if (path_switch(MMV_PATH_Q4_GENERIC) <= 0) {
     if (nb == 16) return launch_q4_rp<B, 16, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 32) return launch_q4_rp<B, 32, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+    // one row, two or four 64-block steps: workgroups of 8 waves, 2 rows per
+    // lane group (the same 16 rows per workgroup; half the quantization of x
+    // per wave, two waves per SIMD), unless the rows-per-lane-group switch
+    // asks for a 4-wave variant
+    if constexpr (B == 1)
+      if (path_switch(MMV_PATH_Q4_RP) == 0) {
+        if (nb == 128) return launch_q4_t<B, 64, 2, 2, false, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+        if (nb == 256) return launch_q4_t<B, 64, 2, 4, false, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      }
     if (nb == 64) return launch_q4_rp<B, 64, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 128) return launch_q4_rp<B, 64, 2>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 256) return launch_q4_rp<B, 64, 4>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
@@ -1133,22 +1161,23 @@ hipError_t launch_q4_mf(const uint8_t *qs, const uint16_t *d, int N, int K, cons
 
 namespace {
 
-template <int B, int G, int T, bool RAG = false>
+template <int B, int G, int T, bool RAG = false, int NW = 4>
 hipError_t launch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                          int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
   // rows per lane group: 2 for the 8192-long rows, 4 otherwise (ragged rows:
-  // 4096 x 11008 at B = 1 11.0 against 11.6 us with 2)
-  constexpr int RP = (T >= 4 && !RAG) ? 2 : 4;
-  constexpr int rows_wg = 4 * RP * (64 / G);
+  // 4096 x 11008 at B = 1 11.0 against 11.6 us with 2); 8-wave workgroups
+  // keep the workgroup's rows with half as many per lane group
+  constexpr int RP = ((T >= 4 && !RAG) ? 2 : 4) * 4 / NW;
+  constexpr int rows_wg = NW * RP * (64 / G);
   const size_t lds = (size_t)B * K * 4 + (size_t)B * (K / 32) * 4;
   if (lds > 65536) {  // above the default dynamic-LDS limit: raise it once per kernel
     static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_gemv_q4_0_f32<B, G, RP, T, RAG>),
+        reinterpret_cast<const void *>(&k_gemv_q4_0_f32<B, G, RP, T, RAG, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 32 * G * T * B * 4 + G * T * B * 4);
     if (raised != hipSuccess) return raised;
   }
-  hipLaunchKernelGGL((k_gemv_q4_0_f32<B, G, RP, T, RAG>), dim3((N + rows_wg - 1) / rows_wg),
-                     dim3(256), lds, s, qs, d, N, K, X, ldx, Y, ldy);
+  hipLaunchKernelGGL((k_gemv_q4_0_f32<B, G, RP, T, RAG, NW>), dim3((N + rows_wg - 1) / rows_wg),
+                     dim3(64 * NW), lds, s, qs, d, N, K, X, ldx, Y, ldy);
   return hipGetLastError();
 }
 
@@ -1160,17 +1189,32 @@ template <int B>
 hipError_t launch_q4_f32_rag(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
                              int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
   static_assert(B <= 3, "ragged whole-row launches are built for up to three rows");
-  switch (((K >> 5) + 63) / 64) {
-    case 2: return launch_q4_f32<B, 64, 2, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-    case 3: return launch_q4_f32<B, 64, 3, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-    case 4: return launch_q4_f32<B, 64, 4, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-    case 5: return launch_q4_f32<B, 64, 5, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-    case 6: return launch_q4_f32<B, 64, 6, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-  }
-  if constexpr (B <= 2) {  // B * K <= MMV_Q4F32_MAX_XK
+  if constexpr (B == 1) {
+    // one row of three or more steps: 8-wave workgroups with 2 rows per lane
+    // group (4096 x 11008 10.95 -> 10.35 us, 4096 x 14336 12.4 -> 11.8 us;
+    // two steps measured slower: 9728 x 2560 7.3 -> 7.7 us)
     switch (((K >> 5) + 63) / 64) {
-      case 7: return launch_q4_f32<B, 64, 7, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-      case 8: return launch_q4_f32<B, 64, 8, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 2: return launch_q4_f32<B, 64, 2, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 3: return launch_q4_f32<B, 64, 3, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 4: return launch_q4_f32<B, 64, 4, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 5: return launch_q4_f32<B, 64, 5, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 6: return launch_q4_f32<B, 64, 6, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 7: return launch_q4_f32<B, 64, 7, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 8: return launch_q4_f32<B, 64, 8, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+    }
+  } else {
+    switch (((K >> 5) + 63) / 64) {
+      case 2: return launch_q4_f32<B, 64, 2, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 3: return launch_q4_f32<B, 64, 3, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 4: return launch_q4_f32<B, 64, 4, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 5: return launch_q4_f32<B, 64, 5, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 6: return launch_q4_f32<B, 64, 6, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+    }
+    if constexpr (B == 2) {  // B * K <= MMV_Q4F32_MAX_XK
+      switch (((K >> 5) + 63) / 64) {
+        case 7: return launch_q4_f32<B, 64, 7, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+        case 8: return launch_q4_f32<B, 64, 8, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      }
     }
   }
   return hipErrorInvalidValue;
@@ -1235,7 +1279,8 @@ hipError_t dispatch_q4_f32(const uint8_t *qs, const uint16_t *d, int N, int K, c
       case 16: return launch_q4_f32<B, 16, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
       case 32: return launch_q4_f32<B, 32, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
       case 64: return launch_q4_f32<B, 64, 1>(qs, d, N, K, X, ldx, Y, ldy, s);
-      case 128: return launch_q4_f32<B, 64, 2>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 128:  // one row: 8-wave workgroups, as for the W4A8 kernel
+        return launch_q4_f32<B, 64, 2, false, B == 1 ? 8 : 4>(qs, d, N, K, X, ldx, Y, ldy, s);
       case 256: return launch_q4_f32<B, 64, 4>(qs, d, N, K, X, ldx, Y, ldy, s);
       default: break;
     }
