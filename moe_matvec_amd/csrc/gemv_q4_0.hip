@@ -634,18 +634,20 @@ static hipError_t launch_q4_rag(const uint8_t *qs, const uint16_t *d, int N, int
       case 7: return launch_q4_t<B, 64, 2, 7, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
       case 8: return launch_q4_t<B, 64, 2, 8, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     }
-  } else {
+  } else {  // also 8 waves of 2 rows per lane group (4096 x 11008, B = 2 / 3 / 4: from fp32 x
+            // 14.5 / 20.7 / 24.9 -> 12.1 / 16.9 / 19.7 us, from a Q8_1 buffer 10.4 / 12.7 /
+            // 13.7 -> 10.0 / 11.4 / 12.4 us)
     switch (((K >> 5) + 63) / 64) {
-      case 2: return launch_q4_t<B, 64, 4, 2, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-      case 3: return launch_q4_t<B, 64, 4, 3, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-      case 4: return launch_q4_t<B, 64, 4, 4, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-      case 5: return launch_q4_t<B, 64, 4, 5, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-      case 6: return launch_q4_t<B, 64, 4, 6, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 2: return launch_q4_t<B, 64, 2, 2, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 3: return launch_q4_t<B, 64, 2, 3, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 4: return launch_q4_t<B, 64, 2, 4, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 5: return launch_q4_t<B, 64, 2, 5, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+      case 6: return launch_q4_t<B, 64, 2, 6, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     }
     if constexpr (B <= 3) {  // B * K <= MMV_Q4_MAX_XK
       switch (((K >> 5) + 63) / 64) {
-        case 7: return launch_q4_t<B, 64, 4, 7, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-        case 8: return launch_q4_t<B, 64, 4, 8, true>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+        case 7: return launch_q4_t<B, 64, 2, 7, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
+        case 8: return launch_q4_t<B, 64, 2, 8, true, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
       }
     }
   }
@@ -711,12 +713,14 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
   if (path_switch(MMV_PATH_Q4_GENERIC) <= 0) {
     if (nb == 16) return launch_q4_rp<B, 16, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
     if (nb == 32) return launch_q4_rp<B, 32, 1>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
-    // one row, two or four 64-block steps: workgroups of 8 waves, 2 rows per
-    // lane group (the same 16 rows per workgroup; half the quantization of x
-    // per wave, two waves per SIMD), unless the rows-per-lane-group switch
-    // asks for a 4-wave variant
-    if constexpr (B == 1)
-      if (path_switch(MMV_PATH_Q4_RP) == 0) {
+    // two or four 64-block steps: workgroups of 8 waves, 2 rows per lane
+    // group (the same 16 rows per workgroup; half of x's quantization or copy
+    // per wave, two waves per SIMD) for one or two rows, and up to four rows
+    // when the workgroup quantizes x itself, unless the rows-per-lane-group
+    // switch asks for a 4-wave variant.  From a Q8_1 buffer at B = 3 / 4,
+    // 4096 x 8192 measured 8.0 / 8.7 us with 4 waves against 8.4 / 9.1 with 8
+    if constexpr (B <= 4)
+      if ((B <= 2 || X) && path_switch(MMV_PATH_Q4_RP) == 0) {
         if (nb == 128) return launch_q4_t<B, 64, 2, 2, false, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
         if (nb == 256) return launch_q4_t<B, 64, 2, 4, false, 8>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
       }
