@@ -1206,18 +1206,20 @@ hipError_t launch_q4_f32_rag(const uint8_t *qs, const uint16_t *d, int N, int K,
       case 7: return launch_q4_f32<B, 64, 7, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
       case 8: return launch_q4_f32<B, 64, 8, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
     }
-  } else {
+  } else {  // two or three rows: 8-wave workgroups at every step count (4096 x 11008
+            // B = 2 / 3 14.9 / 21.1 -> 14.2 / 19.5 us, 2560 x 9728 B = 3 16.9 -> 14.9 us,
+            // 4096 x 6144 B = 2 8.95 -> 7.94 us)
     switch (((K >> 5) + 63) / 64) {
-      case 2: return launch_q4_f32<B, 64, 2, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-      case 3: return launch_q4_f32<B, 64, 3, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-      case 4: return launch_q4_f32<B, 64, 4, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-      case 5: return launch_q4_f32<B, 64, 5, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-      case 6: return launch_q4_f32<B, 64, 6, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 2: return launch_q4_f32<B, 64, 2, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 3: return launch_q4_f32<B, 64, 3, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 4: return launch_q4_f32<B, 64, 4, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 5: return launch_q4_f32<B, 64, 5, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+      case 6: return launch_q4_f32<B, 64, 6, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
     }
     if constexpr (B == 2) {  // B * K <= MMV_Q4F32_MAX_XK
       switch (((K >> 5) + 63) / 64) {
-        case 7: return launch_q4_f32<B, 64, 7, true>(qs, d, N, K, X, ldx, Y, ldy, s);
-        case 8: return launch_q4_f32<B, 64, 8, true>(qs, d, N, K, X, ldx, Y, ldy, s);
+        case 7: return launch_q4_f32<B, 64, 7, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+        case 8: return launch_q4_f32<B, 64, 8, true, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
       }
     }
   }
