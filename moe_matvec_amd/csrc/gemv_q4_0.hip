@@ -476,12 +476,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_f32(
 // lane's blocks of a row group go in chunks of TC, the next chunk (or the
 // next row group's first) in flight while the current one is multiplied.
 // Blocks past the row are clamped in bounds and skipped.
-template <int B, int G, int RP, int TC>
-__global__ __launch_bounds__(256) void k_gemv_q4_0_f32_g(
+template <int B, int G, int RP, int TC, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_f32_g(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
     const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy) {
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int RPP = 64 / G, ROWS_WAVE = RP * RPP, ROWS_WG = 4 * ROWS_WAVE;
+  constexpr int NT = 64 * NW;  // threads per workgroup
+  constexpr int RPP = 64 / G, ROWS_WAVE = RP * RPP, ROWS_WG = NW * ROWS_WAVE;
   const int nb = K >> 5, tot = B * (K >> 2);
   const int nt = (nb + G - 1) / G;                          // blocks per lane and row
   const int nch = (nt + TC - 1) / TC;                       // chunks per row group
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32_g(
   auto load_pass = [&](int base) {
 #pragma unroll
     for (int m = 0; m < kF32Pass; ++m) {
-      const int t = min(base + (int)threadIdx.x + 256 * m, tot - 1);
+      const int t = min(base + (int)threadIdx.x + NT * m, tot - 1);
       const int b = task_row<B>(t, K / 4), r = t - b * (K / 4);
       xv[m] = load_f4(X + (int64_t)b * ldx + 4 * r);
     }
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32_g(
   auto store_pass = [&](int base) {
 #pragma unroll
     for (int m = 0; m < kF32Pass; ++m) {
-      const int t = base + threadIdx.x + 256 * m;
+      const int t = base + threadIdx.x + NT * m;
       w4a16_stage4<B>(xv[m], t, K, nb, t < tot, xs, sx);
     }
   };
@@ -530,7 +531,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_0_f32_g(
   if (gi < ngroups) load_chunk(gi, 0, wa, da);  // uniform
   __builtin_amdgcn_sched_barrier(0);
   store_pass(0);
-  for (int base = 256 * kF32Pass; base < tot; base += 256 * kF32Pass) {
+  for (int base = NT * kF32Pass; base < tot; base += NT * kF32Pass) {
     load_pass(base);
     store_pass(base);
   }
@@ -1245,27 +1246,42 @@ hipError_t launch_q4_f32_mf(const uint8_t *qs, const uint16_t *d, int N, int K, 
   return hipGetLastError();
 }
 
-// the general kernel: x of all rows in LDS (up to the B * K limit), one
-// workgroup per compute unit when that takes more than 80 KiB
-template <int B, int G, int TC>
-hipError_t launch_q4_f32_g(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
-                           int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+// the general kernel with NW waves per workgroup
+template <int B, int G, int TC, int NW>
+hipError_t launch_q4_f32_gw(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                            int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
   constexpr int RP = 2;
-  constexpr int rows_wg = 4 * RP * (64 / G);
+  constexpr int rows_wg = NW * RP * (64 / G);
   constexpr size_t kMaxLds = (size_t)MMV_Q4F32_MAX_XK * 4 + (size_t)MMV_Q4F32_MAX_XK / 32 * 4;
   const size_t lds = (size_t)B * K * 4 + (size_t)B * (K / 32) * 4;
   if (lds > 65536) {  // above the default dynamic-LDS limit: raise it once per kernel
     static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_gemv_q4_0_f32_g<B, G, RP, TC>),
+        reinterpret_cast<const void *>(&k_gemv_q4_0_f32_g<B, G, RP, TC, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
     if (raised != hipSuccess) return raised;
   }
   const int ngroups = (N + rows_wg - 1) / rows_wg;
   const int per_cu = lds > 81920 ? 1 : 2;
   const int grid = min(ngroups, per_cu * cu_count());
-  hipLaunchKernelGGL((k_gemv_q4_0_f32_g<B, G, RP, TC>), dim3(grid), dim3(256), lds, s, qs, d, N,
-                     K, X, ldx, Y, ldy);
+  hipLaunchKernelGGL((k_gemv_q4_0_f32_g<B, G, RP, TC, NW>), dim3(grid), dim3(64 * NW), lds, s,
+                     qs, d, N, K, X, ldx, Y, ldy);
   return hipGetLastError();
+}
+
+// the general kernel: x of all rows in LDS (up to the B * K limit), one
+// workgroup per compute unit when that takes more than 80 KiB, and then 8
+// waves of 2 rows per lane group (16-row groups): 8192 x 28672 at B = 1
+// 41.1 -> 33.7 us, 4096 x 18432 at B = 2 24.2 -> 20.4 us, 11008 x 8192 at
+// B = 3 31.4 -> 25.6 us.  With two workgroups per CU the 16-row groups split
+// unevenly (14336 x 6144, B = 3: 25.9 -> 31.4 us), so 4 waves stay there, and
+// from B = 4 the 8-wave instances spill registers.
+template <int B, int G, int TC>
+hipError_t launch_q4_f32_g(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                           int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+  const size_t lds = (size_t)B * K * 4 + (size_t)B * (K / 32) * 4;
+  if constexpr (G == 64 && B <= 3)
+    if (lds > 81920) return launch_q4_f32_gw<B, G, TC, 8>(qs, d, N, K, X, ldx, Y, ldy, s);
+  return launch_q4_f32_gw<B, G, TC, 4>(qs, d, N, K, X, ldx, Y, ldy, s);
 }
 
 template <int B>

@@ -195,12 +195,14 @@ def test_w4a16_both_kernels_every_b(mm, orc, dev, path, N, K):
                                    (33, 16352, 1), (70, 6144, 2), (129, 2560, 1),
                                    (65, 3840, 1), (1000, 11008, 2), (129, 9728, 3),
                                    (300, 11008, 3), (70, 14336, 2), (300, 8192, 3),
-                                   (4500, 8192, 3), (200, 2080, 1)])
+                                   (4500, 8192, 3), (200, 2080, 1), (300, 18432, 2)])
 def test_w4a16_ragged_rows(mm, orc, dev, N, K, B):
     # 64 < K/32 <= 512 blocks: the whole-row kernel with a ragged last step
     # (B <= 3; past B * K = 16384 only while its workgroups fit the CUs in one
     # round, so 4500 rows at B = 3 take the general kernel on a GPU of up to
-    # 281 CUs), against the oracle; every row equals the 1-row call on it
+    # 281 CUs; rows of 576 blocks always do, as 8-wave workgroups at B = 2
+    # and 4-wave ones at B = 1), against the oracle; every row equals the
+    # 1-row call on it
     # (same lanes per row, so the same bits in both kernels), and at B = 1
     # above K = 4096 the row of a call with enough x rows for the general
     # kernel
