@@ -1,5 +1,6 @@
-// gemv_q4_0.hip -- Q4_0 weights x Q8_1 activations, and the standalone
-// activation quantizer.
+// gemv_q4_0.hip -- Q4_0 weights x Q8_1 activations (v_dot4 and int8
+// matrix-core kernels), Q4_0 weights x fp32 activations (W4A16: v_dot2 and
+// bf16 matrix-core kernels), and the standalone activation quantizer.
 //
 // "Fourteen hours to 100 tokens per second" (The trace that changed
 // everything) lists the dense Q4_0 matvecs and quantize_q8_1 as separate
@@ -16,8 +17,10 @@
 //    sum, then one fp32 scale and fma per activation row;
 //  - each x block read from LDS is reused for the RP rows a lane owns;
 //  - group partials are combined by a fixed xor butterfly; the per-row
-//    arithmetic is the same for every B, so rows of a batched call match
-//    single-row calls bit for bit.
+//    arithmetic of the v_dot4 kernels is the same for every B and every
+//    workgroup shape (4 or 8 waves, any rows per lane group), so their rows
+//    of a batched call match single-row calls bit for bit; the matrix-core
+//    kernels below sum in their own orders.
 #include <atomic>
 
 #include "common.hpp"
@@ -655,8 +658,10 @@ static hipError_t launch_q4_rag(const uint8_t *qs, const uint16_t *d, int N, int
   return hipErrorInvalidValue;
 }
 
-// Rows per lane group (2, 4, 6 or 8; the MMV_PATH_Q4_RP switch overrides):
-// 4 by default.
+// Rows per lane group of the 4-wave workgroups (2, 4, 6 or 8; the
+// MMV_PATH_Q4_RP switch overrides): 4 by default.  (At B <= 4 the dispatch
+// below prefers 8 waves of 2 rows per lane group where that measured
+// faster.)
 // Measured on the 4096 x 4096 and 11008 x 4096 shapes at B = 1, four rows
 // per lane group (16 per workgroup) beat both two (twice the workgroups,
 // each repeating the activation staging) and six or eight (fewer waves to
