@@ -696,7 +696,7 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 // rowmap[0..nr) are loaded here, into stage rows 0..nr-1.
 // mid() runs once the weight loads are in flight, before the activations
 // are staged (uniform control flow; it may contain barriers).
-template <int B, int T, int PRE, bool SC, typename Mid>
+template <int B, int T, int PRE, bool SC, int NW, typename Mid>
 __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq,
                                              const uint16_t *gd, const uint8_t *uq,
                                              const uint16_t *ud, int tile, int nr,
@@ -706,17 +706,21 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
   const int H = a.L.hidden, I = a.L.inter, nbh = H >> 5, ntiles = I >> 5;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int sub = lane & 15, q = lane >> 4;
-  int64_t rowoff[4];
+  // NW waves share the tile's 32 rows: RPW rows of each matrix per wave, in
+  // NG groups of 4 (one row per 16-lane group); p < NG gate, p >= NG up
+  constexpr int NT = 64 * NW, RPW = 32 / NW, NG = RPW / 4, NP = 2 * NG;
+  static_assert(NW == 4 || (NW == 8 && PRE == 0 && !SC), "8 waves: no preloaded x, no chunked scales");
+  int64_t rowoff[NP];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) rowoff[p] = (int64_t)(tile * 32 + 8 * wv + 4 * (p & 1) + q) * nbh;
+  for (int p = 0; p < NP; ++p) rowoff[p] = (int64_t)(tile * 32 + RPW * wv + 4 * (p % NG) + q) * nbh;
 
   constexpr int TT = T > 0 ? T : 1;
   // activations first (loads complete in issue order), then the weights
-  // tasks of 4 values: nr * H / 4 <= B * 128 * T over 256 threads
-  constexpr int MAXT = (T > 0 && PRE == 0) ? cmax(1, cmin(B, 2) * T / 2) : 1;  // <= 2 rows
+  // tasks of 4 values: nr * H / 4 <= B * 128 * T over NT threads
+  constexpr int MAXT = (T > 0 && PRE == 0) ? cmax(1, cmin(B, 2) * T * 128 / NT) : 1;  // <= 2 rows
   XPre<MAXT> xp;
   __syncthreads();  // rowmap / pairmap visible
-  if constexpr (T > 0 && PRE == 0) xpre_load(a.X, a.ldx, rowmap, nr, H, xp, 0, 256);
+  if constexpr (T > 0 && PRE == 0) xpre_load(a.X, a.ldx, rowmap, nr, H, xp, 0, NT);
   // SC (T > 0, 16-byte aligned scale planes): a wave's 8 gate rows and 8 up
   // rows hold 2 x 8 x 32T bytes of fp16 scales, fetched as 16-byte chunks
   // (2T per row) by SCL loads per lane instead of one 2-byte load per (row,
@@ -738,16 +742,16 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
       scv[i] = load_stream16((m ? ud : gd) + (int64_t)(tile * 32 + 8 * wv + rl) * nbh + 8 * part);
     }
   }
-  u32x4 w[4][TT];
-  float dw[4][TT];
+  u32x4 w[NP][TT];
+  float dw[NP][TT];
   if constexpr (T > 0) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int j = sub + 16 * t;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint8_t *wq = p < 2 ? gq : uq;
-        const uint16_t *wd = p < 2 ? gd : ud;
+      for (int p = 0; p < NP; ++p) {
+        const uint8_t *wq = p < NG ? gq : uq;
+        const uint16_t *wd = p < NG ? gd : ud;
         w[p][t] = load_stream16(wq + (rowoff[p] + j) * 16);
         if constexpr (!SC) dw[p][t] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
       }
@@ -760,10 +764,10 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
   if constexpr (PRE > 0) {
     xpre_quantize(xall, B, H, st, 0, 256);
   } else if constexpr (T > 0) {
-    xpre_quantize(xp, nr, H, st, 0, 256);
+    xpre_quantize(xp, nr, H, st, 0, NT);
     // rows past the preloaded ones (B > 2), in passes of MAXT tasks: the
     // weights are in flight meanwhile, so registers are short here
-    stage_quantize<MAXT>(a.X, a.ldx, rowmap, nr, H, st, MAXT * 256, 256);
+    stage_quantize<MAXT>(a.X, a.ldx, rowmap, nr, H, st, MAXT * NT, NT);
   } else {
     stage_quantize(a.X, a.ldx, rowmap, nr, H, st);
   }
@@ -780,13 +784,13 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
   }
   __syncthreads();
   // gate row n and up row n of one activation row -> h (lanes sub == 0)
-  auto put_h = [&](int r, const float (&a4)[4]) {
+  auto put_h = [&](int r, const float (&a4)[NP]) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < NG; ++hh) {
       const float gv = row16_sum(a4[hh]);
-      const float uv = row16_sum(a4[2 + hh]);
+      const float uv = row16_sum(a4[NG + hh]);
       const float h = silu_f(gv) * uv;
-      const int nl = 8 * wv + 4 * hh + q;
+      const int nl = RPW * wv + 4 * hh + q;
       if (sub == 0) {
         hbuf[r][nl] = h;
         if (a.has_dbg) {
@@ -803,12 +807,12 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
 #pragma unroll
     for (int r = 0; r < B; ++r) srow[r] = PRE > 0 ? rowmap[min(r, nr - 1)] : r;
 
-    float acc[4][B];
+    float acc[NP][B];
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int r = 0; r < B; ++r) acc[p][r] = 0.0f;
-    auto block = [&](const u32x4 (&wb)[4], const float (&db)[4], int j) {
+    auto block = [&](const u32x4 (&wb)[NP], const float (&db)[NP], int j) {
 #pragma unroll
       for (int r = 0; r < B; ++r) {
         if (r < nr) {
@@ -818,7 +822,7 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
           const int xs = st.qsum[sr * nbh + j];
           const float dx = st.d[sr * nbh + j];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
+          for (int p = 0; p < NP; ++p) {
             const int Iv = q4_block_isum(wb[p], xa, xb, xs);
             acc[p][r] = fmaf(db[p] * dx, (float)Iv, acc[p][r]);
           }
@@ -828,10 +832,10 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
     if constexpr (T > 0) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        u32x4 wb[4];
-        float db[4];
+        u32x4 wb[NP];
+        float db[NP];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int p = 0; p < NP; ++p) {
           wb[p] = w[p][t];
           if constexpr (SC)
             db[p] = f16_bits_to_f32(s_sc[wv][p >> 1][4 * (p & 1) + q][sub + 16 * t]);
@@ -842,12 +846,12 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
       }
     } else {
       for (int j = sub; j < nbh; j += 16) {
-        u32x4 wb[4];
-        float db[4];
+        u32x4 wb[NP];
+        float db[NP];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint8_t *wq = p < 2 ? gq : uq;
-          const uint16_t *wd = p < 2 ? gd : ud;
+        for (int p = 0; p < NP; ++p) {
+          const uint8_t *wq = p < NG ? gq : uq;
+          const uint16_t *wd = p < NG ? gd : ud;
           wb[p] = load_stream16(wq + (rowoff[p] + j) * 16);
           db[p] = f16_bits_to_f32(load_stream2(wd + rowoff[p] + j));
         }
@@ -857,7 +861,9 @@ __device__ __forceinline__ void gate_up_tile(const MoeArgs &a, const uint8_t *gq
 #pragma unroll
     for (int r = 0; r < B; ++r) {
       if (r < nr) {
-        const float a4[4] = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+        float a4[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) a4[p] = acc[p][r];
         put_h(r, a4);
       }
     }
@@ -901,8 +907,8 @@ __device__ __forceinline__ bool scales16(const uint16_t *gd, const uint16_t *ud)
 // ---------------------------------------------------------------------------
 // K2: routed gate/up.  grid = (B*k [+1 shared]) slots x (I/32) tiles.
 // ---------------------------------------------------------------------------
-template <int B, int T>
-__global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
+template <int B, int T, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_moe_gate_up(MoeArgs a) {
   __shared__ GatherLds g;
   __shared__ int rowmap[MMV_MAX_BATCH];
   __shared__ int pairmap[MMV_MAX_BATCH];
@@ -988,10 +994,10 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
         }
       };
       if (T > 0 && scales16(gd, ud))  // uniform
-        gate_up_tile<B, T, PRE, (T > 0 && B <= 2)>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem,
+        gate_up_tile<B, T, PRE, (T > 0 && B <= 2), 4>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem,
                                          hbuf, xall, mid);
       else
-        gate_up_tile<B, T, PRE, false>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem, hbuf,
+        gate_up_tile<B, T, PRE, false, 4>(a, gq, gd, uq, ud, tile, 1, rowmap, pairmap, smem, hbuf,
                                        xall, mid);
       return;
     }
@@ -1031,10 +1037,10 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
   // time counts); more rows keep more workgroups per CU, and there the
   // extra registers cost more than the issue time saved (B = 8: +0.3 us)
   if (T > 0 && B <= 2 && scales16(gd, ud))  // uniform
-    gate_up_tile<B, T, PRE, (T > 0 && B <= 2)>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf,
+    gate_up_tile<B, T, PRE, (T > 0 && B <= 2), NW>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf,
                                      xall, []() {});
   else
-    gate_up_tile<B, T, PRE, false>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf,
+    gate_up_tile<B, T, PRE, false, NW>(a, gq, gd, uq, ud, tile, nr, rowmap, pairmap, smem, hbuf,
                                    xall, []() {});
 }
 
@@ -1804,7 +1810,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_rows(MoeArgs a) {
     rowmap[tr] = shared_slot ? p - Bk : p / k;
   }
   const XPre<1> none{};
-  gate_up_tile<MMV_MAX_BATCH, T, 0, SC>(a, gq, gd, uq, ud, tile, ncv, rowmap, pairmap, smem,
+  gate_up_tile<MMV_MAX_BATCH, T, 0, SC, 4>(a, gq, gd, uq, ud, tile, ncv, rowmap, pairmap, smem,
                                         hbuf, none, []() {});
 }
 
@@ -1857,7 +1863,12 @@ void launch_gate_up(const MoeArgs &a, hipStream_t s) {
   const int slots = B * a.L.top_k + (a.routed_shared ? 1 : 0);
   const int ntiles = a.L.inter / 32;
   const size_t lds = xstage_bytes(B, a.L.hidden);
-  hipLaunchKernelGGL((k_moe_gate_up<B, T>), dim3(slots * ntiles), dim3(256), lds, s, a);
+  // 8 waves of 4 rows per matrix for 3..6 rows: half the weight registers
+  // (93 VGPRs against 129-149), five waves per SIMD instead of three; E = 512
+  // us per layer, B = 3 / 4 / 5 / 6: 32.2 / 36.7 / 40.7 / 43.8 ->
+  // 31.0 / 35.2 / 40.5 / 42.7; level at B = 7 and 8
+  constexpr int NW = (B >= 3 && B <= 6 && T > 0) ? 8 : 4;
+  hipLaunchKernelGGL((k_moe_gate_up<B, T, NW>), dim3(slots * ntiles), dim3(64 * NW), lds, s, a);
 }
 
 // waves per workgroup: the 4 output rows' experts are split over them by id;
