@@ -327,6 +327,23 @@ def test_q4_0_ragged_rows_equal_grid_stride(mm, orc, dev, path, N, K, B):
     assert rel_l2_rows(npc(y), orc.gemv_q4_0(qs, d, q_ref, ds_ref)) <= Q4_ARITH_TOL
 
 
+@pytest.mark.parametrize("N,K,B", [(1, 4096, 1), (17, 8192, 1), (33, 4096, 2), (5, 11008, 1),
+                                   (3, 8192, 4)])
+def test_q4_0_fewer_rows_than_a_workgroup(mm, orc, dev, N, K, B):
+    # 8-wave workgroups own 16 rows: with fewer, the missing rows repeat the
+    # last one in bounds and store nothing; x and a Q8_1 buffer agree
+    W, qs, d = _q4(mm, N, K, dev, "few")
+    X = synth.activations(B, K, 0, "q4few", N, K, B, device=dev)
+    y = mm.gemv_q4_0(W, x=X)
+    y_q = mm.gemv_q4_0(W, xq=mm.quantize_q8_1(X), B=B)
+    torch.cuda.synchronize()
+    q_ref, ds_ref = orc.quantize_q8_1(npc(X))
+    ref = orc.gemv_q4_0(qs, d, q_ref, ds_ref)
+    assert y.shape == (B, N)
+    assert rel_l2_rows(npc(y), ref) <= Q4_ARITH_TOL
+    assert rel_l2_rows(npc(y_q), ref) <= Q4_ARITH_TOL
+
+
 @pytest.mark.parametrize("B", [2, 3, 5, 7])
 def test_q4_0_strided_x_and_y(mm, orc, dev, B):
     # x rows with ldx > K at an offset, y rows with ldy > N (the padding must

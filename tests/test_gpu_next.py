@@ -221,6 +221,18 @@ def test_w4a16_ragged_rows(mm, orc, dev, N, K, B):
         assert torch.equal(y, yg[:B])
 
 
+@pytest.mark.parametrize("N,K,B", [(1, 4096, 1), (17, 11008, 1), (5, 28672, 1), (9, 11008, 2),
+                                   (3, 8192, 3)])
+def test_w4a16_fewer_rows_than_a_workgroup(mm, orc, dev, N, K, B):
+    # the 8-wave workgroups (16 rows each) with fewer rows than that
+    W, qs, d = _q4(mm, N, K, dev, "few")
+    X = synth.activations(B, K, 0, "w4a16few", N, K, B, device=dev)
+    y = mm.gemv_q4_0_f32(W, X)
+    torch.cuda.synchronize()
+    assert y.shape == (B, N)
+    assert rel_l2_rows(npc(y), orc.gemv_q4_0_f32(qs, d, npc(X))) <= W4A16_ARITH_TOL
+
+
 def test_w4a16_strided_x_and_y(mm, orc, dev):
     N, K, B = 1200, 1024, 5
     W, qs, d = _q4(mm, N, K, dev, "stride")
