@@ -1873,7 +1873,9 @@ void launch_gate_up(const MoeArgs &a, hipStream_t s) {
 
 // waves per workgroup: the 4 output rows' experts are split over them by id;
 // 8 waves measured faster at B = 4 (E = 512: 38.9 against 39.6 us per
-// layer), slower at B = 8 (registers then allow one workgroup per CU)
+// layer), slower at B = 8 (registers then allow one workgroup per CU) and at
+// B <= 2 (E = 256, B = 1: 19.3 against 15.7 us; E = 512, B = 2: 29.9 against
+// 24.9 us)
 template <int B>
 constexpr int down_waves() { return (B == 3 || B == 4) ? 8 : 4; }
 
