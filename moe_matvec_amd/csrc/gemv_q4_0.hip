@@ -190,14 +190,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_q4_0_t(
   const int sub = lane % G, grp = lane / G;
   const int wv = threadIdx.x >> 6;
 
-  // first pass of the activation loads, ahead of the weights: B * G * T / 32
-  // float4 tasks (or B * G * T / 128 16-byte code tasks) per thread in all
-  // (one row of a ragged long row: all of x in the first pass, 2T tasks,
-  // where the registers allow it, so that no L2 round trip of x follows the
+  // first pass of the activation loads, ahead of the weights: 8 B G T / NT
+  // float4 tasks (or 2 B G T / NT 16-byte code tasks) per thread in all
+  // (one row of a ragged long row: all of x in the first pass, 8 G T / NT
+  // tasks, where the registers allow it, so that no L2 round trip of x follows the
   // weight loads)
   constexpr int MAXT = (RAG && B == 1 && T <= 7) ? cmax(1, 8 * G * T / NT)
-                                                 : cmin(kStageMaxT, cmax(1, B * G * T / 32));
-  constexpr int MAXC = cmin(kStageMaxC, cmax(1, B * G * T / 128));
+                                                 : cmin(kStageMaxT, cmax(1, 8 * B * G * T / NT));
+  constexpr int MAXC = cmin(kStageMaxC, cmax(1, 2 * B * G * T / NT));
   XPre<FROM_X ? MAXT : 1> xp;
   XqPre<FROM_X ? 1 : MAXC> qp;
   if constexpr (FROM_X) xpre_load(X, ldx, nullptr, B, K, xp, 0, NT);
