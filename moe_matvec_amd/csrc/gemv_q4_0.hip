@@ -774,12 +774,28 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // one tile of a wave: load i of lane l holds row (64 / kMfCB) i + l / kMfCB,
 // block l % kMfCB of the wave's blocks (kMfCB lanes read a row's codes, one
-// contiguous run); the scales of row l % 16 at blocks kMfLD (l / 16) + i
+// contiguous run); the scales of row l % 16 at blocks kMfLD (l / 16) + i.
+// The two scales of a lane are adjacent: with D4 (an even number of blocks
+// per row and per wave, and a 4-byte aligned scale plane) they come as one
+// 4-byte load (a past-the-end pair is clamped to the row's last two blocks,
+// which weigh 0 there), else as two 2-byte loads.  These loads touch each
+// 64-byte line of scales from four lanes, so they keep the default cache
+// policy: the non-temporal hint made the pair 1-1.5 us slower.  D4 is a
+// template parameter: a run-time branch around the loads made the compiler
+// wait for the next tile's code loads at its join.
 struct MfChunk {
   u32x4 w[kMfLD];
-  uint16_t d[kMfLD];
+  uint32_t dp;        // D4: the pair as loaded
+  uint16_t d[kMfLD];  // else
+  template <bool D4>
+  __device__ __forceinline__ uint16_t scale(int i) const {
+    if constexpr (D4) return (uint16_t)(dp >> (16 * i));
+    else return d[i];
+  }
 };
+static_assert(kMfLD == 2, "scale pairs");
 
+template <bool D4>
 __device__ __forceinline__ void mf_load(MfChunk &c, const uint8_t *__restrict__ qs,
                                         const uint16_t *__restrict__ dw, int N, int nb,
                                         int row0, int jb, int lane) {
@@ -790,12 +806,59 @@ __device__ __forceinline__ void mf_load(MfChunk &c, const uint8_t *__restrict__ 
     c.w[i] = load_stream16(qs + (row * nb + jw) * 16);
   }
   const int64_t rowd = min(row0 + (lane & 15), N - 1);
+  if constexpr (D4) {
+    c.dp = *reinterpret_cast<const uint32_t *>(dw + rowd * nb + min(jb + 2 * (lane >> 4), nb - 2));
+  } else {
 #pragma unroll
-  for (int i = 0; i < kMfLD; ++i)
-    c.d[i] = dw[rowd * nb + min(jb + kMfLD * (lane >> 4) + i, nb - 1)];
+    for (int i = 0; i < kMfLD; ++i)
+      c.d[i] = dw[rowd * nb + min(jb + kMfLD * (lane >> 4) + i, nb - 1)];
+  }
 }
 
-template <int B>
+// The workgroup's tiles t, t + G, ... with two chunk buffers taken in turn:
+// each tile but the last is computed with the next one's loads in flight,
+// issued before the compute (unconditionally; the scheduling barrier keeps
+// the compute below them).  Two named buffers instead of "cur = next": a
+// register copy of a chunk waits for its loads, which left one tile's
+// latency per tile.
+template <bool D4, typename Tile>
+__device__ __forceinline__ void mf_walk(MfChunk &a, MfChunk &b, int t, int G, int ntiles,
+                                        const uint8_t *__restrict__ qs,
+                                        const uint16_t *__restrict__ dw, int N, int nb, int jw0,
+                                        int lane, Tile &tile) {
+  // the first tile's loads, issued before x was staged, are in by now;
+  // waiting for them here leaves the loop head no wait of its own (at the
+  // merge of this state with the loop's, the compiler waited there for the
+  // loads of the tile about to be computed)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  while (true) {  // every branch is uniform over the workgroup
+    const int t2 = t + G;
+    if (t2 >= ntiles) {
+      tile(a, t);
+      return;
+    }
+    mf_load<D4>(b, qs, dw, N, nb, 16 * t2, jw0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(a, t);
+    t = t2 + G;
+    if (t >= ntiles) {
+      tile(b, t2);
+      return;
+    }
+    mf_load<D4>(a, qs, dw, N, nb, 16 * t, jw0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(b, t2);
+  }
+}
+
+// the scale pairs of mf_load as 4-byte loads: even blocks per row and per
+// wave share (so every pair starts at an even block), aligned plane
+inline bool mf_d4(const uint16_t *dw, int K) {
+  const int nb = K >> 5, nbw = (nb + kMfW - 1) / kMfW;
+  return ((nb | nbw) & 1) == 0 && (reinterpret_cast<uintptr_t>(dw) & 3) == 0;
+}
+
+template <int B, bool D4>
 __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
     const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy) {
@@ -828,7 +891,7 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
   u32x4 xreg[kMfCB];
   f32x4 creg[kMfCB];  // -136 sum x_part in all four entries: the accumulator S starts from
   MfChunk cur;
-  mf_load(cur, qs, dw, N, nb, 16 * t, jw0, lane);
+  mf_load<D4>(cur, qs, dw, N, nb, 16 * t, jw0, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int h = 0; h < kMfXH; ++h) {
@@ -892,7 +955,7 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
 #pragma unroll
     for (int i = 0; i < kMfLD; ++i)
       sdw[(kMfLD * kg + i) * 16 + col] =
-          jw0 + kMfLD * kg + i < jw1 ? f16_bits_to_f32(c.d[i]) : 0.0f;
+          jw0 + kMfLD * kg + i < jw1 ? f16_bits_to_f32(c.template scale<D4>(i)) : 0.0f;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile stores
     __builtin_amdgcn_wave_barrier();
     f32x4 acc = zero;
@@ -940,12 +1003,14 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
   };
   // every tile but the last with the next one's loads in flight (issued
   // before the compute, unconditionally, so that only this tile's loads
-  // have to land); the last one without
+  // have to land); the last one without.  (mf_walk's two buffers, as the
+  // int8 kernel walks its tiles, measured 0.3 us slower per pair here at
+  // B = 2 / 3: at 128 VGPRs they spill.)
   while (true) {
     const int t2 = t + G;
     if (t2 >= ntiles) break;  // uniform over the workgroup
     MfChunk nxt;
-    mf_load(nxt, qs, dw, N, nb, 16 * t2, jw0, lane);
+    mf_load<D4>(nxt, qs, dw, N, nb, 16 * t2, jw0, lane);
     tile(cur, t);
     t = t2;
     cur = nxt;
@@ -971,7 +1036,7 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_f32_mf(
 // x comes as fp32 (quantized to Q8_1 in every workgroup by the one device
 // routine, so the codes equal the standalone quantizer's) or as a Q8_1
 // buffer. Rows are bit-identical across every B this kernel takes.
-template <int B, bool FROM_X>
+template <int B, bool FROM_X, bool D4>
 __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
     const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dw, int N, int K,
     const float *__restrict__ X, int64_t ldx, const uint8_t *__restrict__ Xq,
@@ -1017,7 +1082,7 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
   }
   __builtin_amdgcn_sched_barrier(0);
   MfChunk cur;
-  mf_load(cur, qs, dw, N, nb, 16 * t, jw0, lane);
+  mf_load<D4>(cur, qs, dw, N, nb, 16 * t, jw0, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int h = 0; h < kMfXH; ++h) {
@@ -1092,7 +1157,7 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
 #pragma unroll
     for (int i = 0; i < kMfLD; ++i)
       sdw[(kMfLD * kg + i) * 16 + col] =
-          jw0 + kMfLD * kg + i < jw1 ? f16_bits_to_f32(ch.d[i]) : 0.0f;
+          jw0 + kMfLD * kg + i < jw1 ? f16_bits_to_f32(ch.template scale<D4>(i)) : 0.0f;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile stores
     __builtin_amdgcn_wave_barrier();
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1138,18 +1203,8 @@ __global__ __launch_bounds__(kMfT) void k_gemv_q4_0_mf(
     }
     par ^= 1;
   };
-  // every tile but the last with the next one's loads in flight (issued
-  // before the compute, unconditionally); the last one without
-  while (true) {
-    const int t2 = t + G;
-    if (t2 >= ntiles) break;  // uniform over the workgroup
-    MfChunk nxt;
-    mf_load(nxt, qs, dw, N, nb, 16 * t2, jw0, lane);
-    tile(cur, t);
-    t = t2;
-    cur = nxt;
-  }
-  tile(cur, t);
+  MfChunk nxt;
+  mf_walk<D4>(cur, nxt, t, G, ntiles, qs, dw, N, nb, jw0, lane, tile);
 }
 
 // a persistent grid, one 16-wave workgroup per CU
@@ -1160,12 +1215,19 @@ hipError_t launch_q4_mf(const uint8_t *qs, const uint16_t *d, int N, int K, cons
   const size_t tiles = (size_t)kMfW * kMfTileBytes;
   const size_t lds = xb > tiles ? xb : tiles;  // at most 41 KiB (B = 8, K = 4096)
   const int grid = min((N + 15) / 16, cu_count());
-  if (X)
-    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, true>), dim3(grid), dim3(kMfT), lds, s, qs, d, N, K, X,
-                       ldx, Xq, Y, ldy);
+  const bool d4 = mf_d4(d, K);
+  if (X && d4)
+    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, true, true>), dim3(grid), dim3(kMfT), lds, s, qs, d, N,
+                       K, X, ldx, Xq, Y, ldy);
+  else if (X)
+    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, true, false>), dim3(grid), dim3(kMfT), lds, s, qs, d,
+                       N, K, X, ldx, Xq, Y, ldy);
+  else if (d4)
+    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, false, true>), dim3(grid), dim3(kMfT), lds, s, qs, d,
+                       N, K, X, ldx, Xq, Y, ldy);
   else
-    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, false>), dim3(grid), dim3(kMfT), lds, s, qs, d, N, K,
-                       X, ldx, Xq, Y, ldy);
+    hipLaunchKernelGGL((k_gemv_q4_0_mf<B, false, false>), dim3(grid), dim3(kMfT), lds, s, qs, d,
+                       N, K, X, ldx, Xq, Y, ldy);
   return hipGetLastError();
 }
 
@@ -1233,22 +1295,30 @@ hipError_t launch_q4_f32_rag(const uint8_t *qs, const uint16_t *d, int N, int K,
 }
 
 // W4A16 on the matrix cores: a persistent grid, one 16-wave workgroup per CU
-template <int B>
-hipError_t launch_q4_f32_mf(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
-                            int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+template <int B, bool D4>
+hipError_t launch_q4_f32_mf_d(const uint8_t *qs, const uint16_t *d, int N, int K,
+                              const float *X, int64_t ldx, float *Y, int64_t ldy,
+                              hipStream_t s) {
   constexpr size_t kMaxLds = (size_t)4 * kMfMaxXK + (size_t)4 * B * 8;
   const size_t xb = (size_t)4 * B * (K + 8), tiles = (size_t)kMfW * kMfTileBytes;
   const size_t lds = xb > tiles ? xb : tiles;
   if (lds > 65536) {  // above the default dynamic-LDS limit: raise it once per kernel
     static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_gemv_q4_0_f32_mf<B>),
+        reinterpret_cast<const void *>(&k_gemv_q4_0_f32_mf<B, D4>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
     if (raised != hipSuccess) return raised;
   }
   const int grid = min((N + 15) / 16, cu_count());
-  hipLaunchKernelGGL((k_gemv_q4_0_f32_mf<B>), dim3(grid), dim3(kMfT), lds, s, qs, d, N, K, X,
-                     ldx, Y, ldy);
+  hipLaunchKernelGGL((k_gemv_q4_0_f32_mf<B, D4>), dim3(grid), dim3(kMfT), lds, s, qs, d, N, K,
+                     X, ldx, Y, ldy);
   return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_q4_f32_mf(const uint8_t *qs, const uint16_t *d, int N, int K, const float *X,
+                            int64_t ldx, float *Y, int64_t ldy, hipStream_t s) {
+  return mf_d4(d, K) ? launch_q4_f32_mf_d<B, true>(qs, d, N, K, X, ldx, Y, ldy, s)
+                     : launch_q4_f32_mf_d<B, false>(qs, d, N, K, X, ldx, Y, ldy, s);
 }
 
 // the general kernel with NW waves per workgroup
