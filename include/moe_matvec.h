@@ -40,7 +40,7 @@
  *    are bit-identical across the B one kernel serves and agree within
  *    rounding across kernels.  gemv_bf16: B = 1 (fp32 fused multiply-adds)
  *    against B >= 2 (x split into bf16 high + low parts).  gemv_q4_0 at
- *    K <= 4096: B <= 2 against B >= 3 for fp32 x, B <= 5 against B >= 6
+ *    K <= 4096: B <= 2 against B >= 3 for fp32 x, B <= 4 against B >= 5
  *    for a Q8_1 buffer (the exact block integers are the same).
  *    gemv_q4_0_f32 at K <= 4096: B = 1 against B >= 2.
  *  - Outputs must not overlap inputs (MMV_E_ALIAS).
@@ -140,21 +140,23 @@ int quantize_q8_1(const float *X, int32_t K, int64_t ldx, int32_t B,
  *    K <= 512 in "Eight levers that worked"]
  *   Y[b*ldy + n] = sum_j d_w[n][j] * d_x[b][j] * I[b][n][j],
  *   I[b][n][j] = sum_i (code_i - 8) * q_x[b][32j + i]  (exact int32), then
- *   fp32 scaling and sums.  K <= 4096 with B >= 3 (fp32 x) or B >= 6 (a
+ *   fp32 scaling and sums.  K <= 4096 with B >= 3 (fp32 x) or B >= 5 (a
  *   Q8_1 buffer) runs on the int8 matrix cores, the rest on dot4 kernels;
  *   the two sum the blocks in different orders, so rows agree within
  *   rounding (rel-L2 ~1e-7) across them and bit for bit within each.
  *   Activations, one of three ways (the codes are bit-identical in all):
  *     X only:  fp32 B x K, quantized to Q8_1 inside every workgroup (one
- *              launch; the better choice at B = 1);
+ *              launch; the better choice at B = 1, and at B = 3 to 5 with
+ *              K <= 4096, where the matrix cores quantize x once per CU);
  *     Xq only: planar Q8_1 of B rows of K, read as given;
  *     both:    X is first quantized into the caller's Xq buffer
  *              (mmv_q8_1_bytes(K, B) bytes, an output, left holding
  *              Q8_1(X)), then the product reads Xq (two launches; the
- *              better choice at B >= 2, where repeating the quantization
- *              in every workgroup costs more than the extra launch).
+ *              better choice from B = 6, and at any B >= 2 with K > 4096,
+ *              where repeating the quantization in every workgroup costs
+ *              more than the extra launch).
  *   X only and Xq give bit-identical rows where they take the same kernel
- *   (B <= 2, B >= 6 or K > 4096).
+ *   (B <= 2, B >= 5 or K > 4096).
  *   B*K <= MMV_Q4_MAX_XK.  Y: B x N fp32, ldy >= N.
  * ------------------------------------------------------------------------ */
 int gemv_q4_0(const mmv_q4_0 *W, const float *X, int64_t ldx, const void *Xq,

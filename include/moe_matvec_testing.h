@@ -54,7 +54,7 @@ enum mmv_path_switch {
    * -1 = never (the fp32 kernels; rows agree within rounding) */
   MMV_PATH_Q4F32_MF = 9,
   /* gemv_q4_0 on the matrix cores (K <= 4096): 0 = from B = 3 for fp32 x,
-   * from B = 6 for a Q8_1 buffer; n > 0 = from B = n; -1 = never (the dot4
+   * from B = 5 for a Q8_1 buffer; n > 0 = from B = n; -1 = never (the dot4
    * kernels; rows agree within rounding) */
   MMV_PATH_Q4_MF = 10,
   MMV_PATH_COUNT = 11

@@ -708,11 +708,12 @@ static hipError_t dispatch_q4(const uint8_t *qs, const uint16_t *d, int N, int K
   constexpr int RP = B <= 2 ? 2 : 4;
   // K <= 4096: the matrix cores from B = 3 for fp32 x (quantized in every
   // workgroup: the dot4 kernels' repeated quantization is the bound there),
-  // from B = 6 for a Q8_1 buffer (4096^2 + 11008 x 4096 per pair, dot4 /
-  // matrix cores: B = 5 17.9 / 18.1 us, B = 6 19.3 / 18.3, B = 8 22.5 / 19.0)
+  // from B = 5 for a Q8_1 buffer (4096^2 + 11008 x 4096 per pair with the
+  // quantization pass, dot4 / matrix cores: B = 4 16.5 / 16.9 us, B = 5
+  // 18.0 / 17.7, B = 6 19.3 / 17.9)
   {
     const int sw = path_switch(MMV_PATH_Q4_MF);
-    if (sw >= 0 && B >= (sw > 0 ? sw : (X ? 3 : 6)) && nb <= kMfW * kMfCB)
+    if (sw >= 0 && B >= (sw > 0 ? sw : (X ? 3 : 5)) && nb <= kMfW * kMfCB)
       return launch_q4_mf<B>(qs, d, N, K, X, ldx, Xq, Y, ldy, s);
   }
   // whole blocks per lane: every load of a row group in flight together
